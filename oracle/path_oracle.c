@@ -1,0 +1,218 @@
+/*
+ * Plain fp64 CPU oracle for PaTH attention.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this code.  It shares nothing with the HIP library: no headers,
+ * no helpers, no constants.  Every routine below is the slow, obviously
+ * correct reading of the defining formulas, written for a reader who holds
+ * the source pages next to it.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "PaTH Attention" technical summary (gist.science 2505.16381)
+ *        §2 "Mecanismo Central"  - attention logit k_j^T (prod_{s=j+1..i} H_s) q_i,
+ *                                   causal softmax A_ij ∝ exp(logit),
+ *                                   H_s = I - beta_s w_s w_s^T, beta_s in (0,2).
+ *        §2 "Extensões: PaTH-FoX" - additive data-dependent forget-gate bias.
+ *        §3 "Representação de Transformação UT" - a product of the H_s is
+ *                                   I - W^T T^{-1} W with T triangular, built
+ *                                   from beta (and the Gram matrix W W^T).
+ *        §3 "Algoritmo Estilo FlashAttention" - boundary-adjusted Q/K per block.
+ *        §3 "Inferência"          - cached keys updated in place with the
+ *                                   current step's transition.
+ *
+ * Readings where the pages are silent (also listed in the design notes):
+ *   - the product prod_{s=j+1..i} H_s is H_{j+1} H_{j+2} ... H_i, so H_i is
+ *     the first factor to act on q_i; the empty product (j = i) is I;
+ *   - softmax is over j <= i, with an explicit logit multiplier `scale`;
+ *   - the FoX bias is sum_{s=j+1..i} log f_s, added after `scale`;
+ *   - lse is the natural log of the softmax denominator.
+ *
+ * All arithmetic is fp64 on the exact stored input values; loops run in the
+ * order the definitions are written.  OpenMP only spreads independent query
+ * rows over threads.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double dot(const double* a, const double* b, int64_t d) {
+  double s = 0.0;
+  for (int64_t t = 0; t < d; ++t) s += a[t] * b[t];
+  return s;
+}
+
+/* u <- H_s u = u - beta_s (w_s . u) w_s   [P1 §2 "Mecanismo Central"] */
+static void apply_H(double* u, const double* w_s, double beta_s, int64_t d) {
+  double c = beta_s * dot(w_s, u, d);
+  for (int64_t t = 0; t < d; ++t) u[t] -= c * w_s[t];
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * One head.  For every requested query row i:
+ *   u <- q_i
+ *   for j = i, i-1, ..., 0:
+ *       s_ij = scale * (k_j . u) + sum_{s=j+1..i} log f_s
+ *       u <- H_j u                       (so u = H_{j}...H_i q_i next round)
+ *   o_i = sum_j softmax_j(s_ij) v_j,  lse_i = log sum_j exp(s_ij)
+ * [P1 §2 "Mecanismo Central"; §2 "Extensões: PaTH-FoX" for the bias]
+ *
+ * q,k,v,w: [L,d] row-major; beta, log_forget: [L] (log_forget may be NULL).
+ * rows: n_rows query indices (NULL = all L rows in order).
+ * o: [n_rows,d]; lse: [n_rows]; logits (optional, may be NULL): [n_rows,L],
+ * entries j > i are set to -INFINITY.
+ */
+void oracle_path_fwd(int64_t L, int64_t d, const double* q, const double* k,
+                     const double* v, const double* w, const double* beta,
+                     const double* log_forget, double scale, int64_t n_rows,
+                     const int64_t* rows, double* o, double* lse,
+                     double* logits) {
+  if (rows == NULL) n_rows = L;
+#pragma omp parallel
+  {
+    double* u = (double*)malloc(sizeof(double) * (size_t)d);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t i = rows ? rows[r] : r;
+      memcpy(u, q + i * d, sizeof(double) * (size_t)d);
+      double bias = 0.0;
+      for (int64_t j = i; j >= 0; --j) {
+        s[j] = scale * dot(k + j * d, u, d) + bias;
+        apply_H(u, w + j * d, beta[j], d);
+        if (log_forget) bias += log_forget[j];
+      }
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= i; ++j) m = s[j] > m ? s[j] : m;
+      double l = 0.0;
+      for (int64_t j = 0; j <= i; ++j) l += exp(s[j] - m);
+      double* oi = o + r * d;
+      for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        double p = exp(s[j] - m) / l;
+        for (int64_t t = 0; t < d; ++t) oi[t] += p * v[j * d + t];
+      }
+      lse[r] = m + log(l);
+      if (logits) {
+        for (int64_t j = 0; j < L; ++j)
+          logits[r * L + j] = (j <= i) ? s[j] : -INFINITY;
+      }
+    }
+    free(u);
+    free(s);
+  }
+}
+
+/*
+ * One decode step for one head  [P1 §3 "Inferência"]:
+ *   k_j <- H_t k_j  for every cached j < len   (in place, in k_cache)
+ *   keys  = [k_0 .. k_{len-1} (updated), k_t],  values = [v_0 .. v_{len-1}, v_t]
+ *   s_j = scale * (k_j . q_t);  o = softmax(s) . values;  lse = log sum exp s
+ * The new key enters untransformed: its path product is empty.
+ * k_cache, v_cache: [len,d]; q_t,k_t,v_t,w_t: [d]; o: [d]; lse: scalar.
+ */
+void oracle_path_decode(int64_t len, int64_t d, const double* q_t,
+                        const double* k_t, const double* v_t,
+                        const double* w_t, double beta_t, double* k_cache,
+                        const double* v_cache, double scale, double* o,
+                        double* lse) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(len + 1));
+  for (int64_t j = 0; j < len; ++j) {
+    apply_H(k_cache + j * d, w_t, beta_t, d);
+    s[j] = scale * dot(k_cache + j * d, q_t, d);
+  }
+  s[len] = scale * dot(k_t, q_t, d);
+  double m = -INFINITY;
+  for (int64_t j = 0; j <= len; ++j) m = s[j] > m ? s[j] : m;
+  double l = 0.0;
+  for (int64_t j = 0; j <= len; ++j) l += exp(s[j] - m);
+  for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+  for (int64_t j = 0; j <= len; ++j) {
+    double p = exp(s[j] - m) / l;
+    const double* vj = (j < len) ? v_cache + j * d : v_t;
+    for (int64_t t = 0; t < d; ++t) o[t] += p * vj[t];
+  }
+  *lse = m + log(l);
+  free(s);
+}
+
+/*
+ * UT factor of one block of n tokens  [P1 §3 "Representação de Transformação UT"]:
+ * the product H_0 H_1 ... H_{n-1} equals I - W^T T^{-1} W, with W the n x d
+ * matrix of rows w_s and T upper triangular, T = diag(1/beta) + strict_upper(W W^T).
+ * To stay defined at beta_s = 0 the oracle never forms 1/beta: it solves
+ *     (I + diag(beta) strict_upper(W W^T)) X = diag(beta),   X = T^{-1},
+ * by plain back substitution, row n-1 first.
+ * w: [n,d]; beta: [n]; tinv: [n,n] (upper triangular, zeros below).
+ */
+void oracle_ut_tinv(int64_t n, int64_t d, const double* w, const double* beta,
+                    double* tinv) {
+  for (int64_t i = 0; i < n * n; ++i) tinv[i] = 0.0;
+  for (int64_t r = n - 1; r >= 0; --r) {
+    for (int64_t c = r; c < n; ++c) {
+      double acc = (r == c) ? beta[r] : 0.0;
+      for (int64_t t = r + 1; t <= c; ++t)
+        acc -= beta[r] * dot(w + r * d, w + t * d, d) * tinv[t * n + c];
+      tinv[r * n + c] = acc;
+    }
+  }
+}
+
+/*
+ * Boundary-adjusted queries and keys of one block and its transition
+ * [P1 §3 "Algoritmo Estilo FlashAttention"], taken straight from the
+ * definitions, one H at a time (independent of the UT factor above):
+ *   qhat_r = H_0 H_1 ... H_r q_r      (apply H_r first, H_0 last)
+ *   khat_c = H_{n-1} ... H_{c+1} k_c  (apply H_{c+1} first)
+ *   pT     = (H_0 H_1 ... H_{n-1})^T  as an explicit d x d matrix
+ * q,k,w: [n,d]; qhat,khat: [n,d]; pT: [d,d].
+ */
+void oracle_block_adjust(int64_t n, int64_t d, const double* q,
+                         const double* k, const double* w, const double* beta,
+                         double* qhat, double* khat, double* pT) {
+  for (int64_t r = 0; r < n; ++r) {
+    double* u = qhat + r * d;
+    memcpy(u, q + r * d, sizeof(double) * (size_t)d);
+    for (int64_t s = r; s >= 0; --s) apply_H(u, w + s * d, beta[s], d);
+  }
+  for (int64_t c = 0; c < n; ++c) {
+    double* u = khat + c * d;
+    memcpy(u, k + c * d, sizeof(double) * (size_t)d);
+    for (int64_t s = c + 1; s < n; ++s) apply_H(u, w + s * d, beta[s], d);
+  }
+  /* P <- I, then P <- P H_s for s = 0..n-1; column t of P is P e_t. */
+  double* P = (double*)malloc(sizeof(double) * (size_t)(d * d));
+  for (int64_t a = 0; a < d; ++a)
+    for (int64_t b = 0; b < d; ++b) P[a * d + b] = (a == b) ? 1.0 : 0.0;
+  double* Pw = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int64_t s = 0; s < n; ++s) {
+    const double* ws = w + s * d;
+    for (int64_t a = 0; a < d; ++a) Pw[a] = dot(P + a * d, ws, d);
+    for (int64_t a = 0; a < d; ++a)
+      for (int64_t b = 0; b < d; ++b) P[a * d + b] -= beta[s] * Pw[a] * ws[b];
+  }
+  for (int64_t a = 0; a < d; ++a)
+    for (int64_t b = 0; b < d; ++b) pT[a * d + b] = P[b * d + a];
+  free(Pw);
+  free(P);
+}
+
+/* c_i = sum_{s<=i} log f_s, so c_i - c_j is the FoX bias  [P1 §2 "Extensões: PaTH-FoX"] */
+void oracle_prefix_sum(int64_t L, const double* x, double* c) {
+  double acc = 0.0;
+  for (int64_t i = 0; i < L; ++i) {
+    acc += x[i];
+    c[i] = acc;
+  }
+}
