@@ -1,0 +1,227 @@
+"""PaTH attention on MI355X (gfx950): thin Python binding of libpath_attn.so.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, allocates outputs and workspaces with torch, and passes
+raw device pointers plus the current HIP stream through the C ABI declared in
+include/path_attn.h.  There is no fallback: if the shared library is missing
+the import of `lib()` raises.
+
+Method: "PaTH Attention" (gist.science 2505.16381) - causal softmax attention
+with logits k_j^T (H_{j+1}...H_i) q_i, H_s = I - beta_s w_s w_s^T (§2
+"Mecanismo Central"), optional PaTH-FoX forget bias (§2 "Extensões"), UT block
+transform and right-to-left block scan (§3), in-place key-cache decode (§3
+"Inferência").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpath_attn.so")
+
+PATH_F32, PATH_BF16 = 0, 1
+PRECISION = {"accurate": 0, "auto": 1}
+STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UNSUPPORTED",
+          4: "PATH_ERR_WORKSPACE", 5: "PATH_ERR_CAPACITY", 6: "PATH_ERR_HIP"}
+EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
+           "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
+           "path_decode_workspace_bytes", "path_decode_step"]
+
+_lib = None
+_I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class PathError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpath_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m dependent_position_encoding_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.path_status_string.restype = ctypes.c_char_p
+        L.path_status_string.argtypes = [_INT]
+        L.path_abi_version.restype = _INT
+        L.path_prepare.restype = _INT
+        L.path_prepare.argtypes = [_I64, _I64, _I64, _I64, _INT] + [_VP] * 10 + [_VP]
+        L.path_fwd_workspace_bytes.restype = _SZ
+        L.path_fwd_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _INT, _INT]
+        L.path_attn_fwd.restype = _INT
+        L.path_attn_fwd.argtypes = [_I64, _I64, _I64, _I64, _INT, _F, _INT] + [_VP] * 8 + [_VP, _SZ, _VP]
+        L.path_fwd_stage_prepare.restype = _INT
+        L.path_fwd_stage_prepare.argtypes = [_I64, _I64, _I64, _I64, _INT, _F, _INT] + [_VP] * 6 + [_VP, _SZ, _VP]
+        L.path_fwd_stage_scan.restype = _INT
+        L.path_fwd_stage_scan.argtypes = [_I64, _I64, _I64, _I64, _INT, _F, _INT] + [_VP] * 8 + [_VP, _SZ, _VP]
+        L.path_decode_workspace_bytes.restype = _SZ
+        L.path_decode_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+        L.path_decode_step.restype = _INT
+        L.path_decode_step.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 7 + [_I64, _I64] +
+                                       [_VP, _VP, _VP, _SZ, _VP])
+        _lib = L
+    return _lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().path_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PATH_F32
+    if t.dtype == torch.bfloat16:
+        return PATH_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (use float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _raise(st: int, what: str):
+    if st != 0:
+        raise PathError(st, what)
+
+
+def fwd_workspace_bytes(B, H, L, d, dtype_code, with_forget) -> int:
+    return int(lib().path_fwd_workspace_bytes(B, H, L, d, dtype_code, int(bool(with_forget))))
+
+
+def _fwd_args(q, k, v, w, beta, log_forget):
+    B, H, L, d = q.shape
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("w", w)):
+        _check(t, name, dt, (B, H, L, d))
+    _check(beta, "beta", torch.float32, (B, H, L))
+    if log_forget is not None:
+        _check(log_forget, "log_forget", torch.float32, (B, H, L))
+    return B, H, L, d, _dtype_code(q)
+
+
+def fwd_workspace(q, log_forget=None) -> torch.Tensor:
+    """A workspace tensor large enough for path_attn_fwd on inputs shaped like q."""
+    B, H, L, d = q.shape
+    nbytes = fwd_workspace_bytes(B, H, L, d, _dtype_code(q), log_forget is not None)
+    if nbytes == 0:
+        _raise(2, "path_fwd_workspace_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+
+def path_attn_fwd(q, k, v, w, beta, log_forget=None, scale=1.0, precision="auto", workspace=None,
+                  out=None):
+    """PaTH forward.  q,k,v,w [B,H,L,d] (fp32 or bf16, same dtype); beta, log_forget [B,H,L] fp32.
+
+    Returns (o [B,H,L,d] in the input dtype, lse [B,H,L] fp32)."""
+    B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
+    o, lse = out if out is not None else (torch.empty_like(q),
+                                          torch.empty((B, H, L), dtype=torch.float32, device=q.device))
+    if workspace is None:
+        workspace = fwd_workspace(q, log_forget)
+    st = lib().path_attn_fwd(B, H, L, d, code, float(scale), PRECISION[precision], _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(o), _ptr(lse), _ptr(workspace),
+                             int(workspace.numel()), _stream(q))
+    _raise(st, "path_attn_fwd")
+    return o, lse
+
+
+def path_fwd_stage_prepare(q, k, v, w, beta, log_forget=None, scale=1.0, precision="auto", workspace=None):
+    """First stage of path_attn_fwd: block UT data into `workspace` (returned)."""
+    B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
+    if workspace is None:
+        workspace = fwd_workspace(q, log_forget)
+    st = lib().path_fwd_stage_prepare(B, H, L, d, code, float(scale), PRECISION[precision], _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(workspace),
+                                      int(workspace.numel()), _stream(q))
+    _raise(st, "path_fwd_stage_prepare")
+    return workspace
+
+
+def path_fwd_stage_scan(q, k, v, w, beta, workspace, log_forget=None, scale=1.0, precision="auto", out=None):
+    """Second stage of path_attn_fwd: the right-to-left scan from a prepared workspace."""
+    B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
+    o, lse = out if out is not None else (torch.empty_like(q),
+                                          torch.empty((B, H, L), dtype=torch.float32, device=q.device))
+    st = lib().path_fwd_stage_scan(B, H, L, d, code, float(scale), PRECISION[precision], _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(o), _ptr(lse),
+                                   _ptr(workspace), int(workspace.numel()), _stream(q))
+    _raise(st, "path_fwd_stage_scan")
+    return o, lse
+
+
+def path_prepare(q, k, w, beta, log_forget=None):
+    """Per-block UT transform.  Returns dict of fp32 tensors tinv [B,H,Nb,64,64],
+    qhat/khat [B,H,L,d], pT [B,H,Nb,d,d] and (with log_forget) cum [B,H,L]."""
+    B, H, L, d = q.shape
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("w", w)):
+        _check(t, name, dt, (B, H, L, d))
+    _check(beta, "beta", torch.float32, (B, H, L))
+    Nb = (L + 63) // 64
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = {"tinv": torch.empty((B, H, Nb, 64, 64), **f32), "qhat": torch.empty((B, H, L, d), **f32),
+           "khat": torch.empty((B, H, L, d), **f32), "pT": torch.empty((B, H, Nb, d, d), **f32)}
+    if log_forget is not None:
+        _check(log_forget, "log_forget", torch.float32, (B, H, L))
+        out["cum"] = torch.empty((B, H, L), **f32)
+    st = lib().path_prepare(B, H, L, d, _dtype_code(q), _ptr(q), _ptr(k), _ptr(w), _ptr(beta), _ptr(log_forget),
+                            _ptr(out["tinv"]), _ptr(out["qhat"]), _ptr(out["khat"]), _ptr(out["pT"]),
+                            _ptr(out.get("cum")), _stream(q))
+    _raise(st, "path_prepare")
+    return out
+
+
+def decode_workspace_bytes(B, H, d, cache_len) -> int:
+    return int(lib().path_decode_workspace_bytes(B, H, d, cache_len))
+
+
+def path_decode_step(q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, cache_len, scale=1.0, workspace=None):
+    """One decode step.  q_t,k_t,v_t,w_t [B,H,d]; beta_t [B,H] fp32; caches [B,H,capacity,d].
+
+    Updates k_cache[:, :, :cache_len] in place, writes k_t, v_t at slot cache_len,
+    returns (o [B,H,d], lse [B,H] fp32)."""
+    B, H, d = q_t.shape
+    cap = k_cache.shape[2]
+    dt = q_t.dtype
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _check(t, name, dt, (B, H, d))
+    _check(beta_t, "beta_t", torch.float32, (B, H))
+    _check(k_cache, "k_cache", dt, (B, H, cap, d))
+    _check(v_cache, "v_cache", dt, (B, H, cap, d))
+    o = torch.empty_like(q_t)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_t.device)
+    nbytes = decode_workspace_bytes(B, H, d, cache_len)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q_t.device)
+    st = lib().path_decode_step(B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+                                _ptr(w_t), _ptr(beta_t), _ptr(k_cache), _ptr(v_cache), int(cache_len), int(cap),
+                                _ptr(o), _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream(q_t))
+    _raise(st, "path_decode_step")
+    return o, lse

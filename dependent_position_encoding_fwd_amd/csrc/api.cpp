@@ -1,0 +1,243 @@
+// C ABI of the PaTH attention library: argument checks on the host, workspace
+// carve-up, and kernel launches on the caller's stream.  Nothing here touches
+// the GPU before every argument has been validated.
+#include "../../include/path_attn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kBlk = 64;
+constexpr size_t kAlign = 256;
+// Largest element count accepted for one tensor (keeps byte sizes and 64-bit
+// index arithmetic far from overflow).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > kMaxElems / a) return false;
+  *out = a * b;
+  return *out <= kMaxElems;
+}
+
+int check_dtype(int dtype) {
+  return (dtype == PATH_F32 || dtype == PATH_BF16) ? PATH_OK : PATH_ERR_UNSUPPORTED;
+}
+
+int check_d(int64_t d) { return (d == 64 || d == 128) ? PATH_OK : PATH_ERR_UNSUPPORTED; }
+
+// Validates B, H, L, d and returns B*H and the padded block count.
+int check_shape(int64_t B, int64_t H, int64_t L, int64_t d, int64_t* BH, int64_t* Nb) {
+  if (B < 1 || H < 1 || L < 1) return PATH_ERR_SHAPE;
+  int st = check_d(d);
+  if (st) return st;
+  int64_t bh, bhl, n;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, L, &bhl) || !mul_ok(bhl, d, &n)) return PATH_ERR_SHAPE;
+  const int64_t nb = (L + kBlk - 1) / kBlk;
+  int64_t pt;
+  if (!mul_ok(bh * nb, d * d, &pt) || !mul_ok(bh * nb, kBlk * kBlk, &pt)) return PATH_ERR_SHAPE;
+  // one workgroup per (b, h, block) must fit a 32-bit grid
+  if (bh * nb > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
+  *BH = bh;
+  *Nb = nb;
+  return PATH_OK;
+}
+
+struct FwdWs {
+  size_t khat, pT, cum, total;
+};
+
+FwdWs fwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget) {
+  FwdWs w{};
+  size_t off = 0;
+  w.khat = off;
+  off += align_up(sizeof(float) * size_t(BH) * size_t(L) * size_t(d));
+  w.pT = off;
+  off += align_up(sizeof(float) * size_t(BH) * size_t(Nb) * size_t(d) * size_t(d));
+  w.cum = off;
+  if (with_forget) off += align_up(sizeof(float) * size_t(BH) * size_t(L));
+  w.total = off;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PATH_OK : PATH_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* path_status_string(int status) {
+  switch (status) {
+    case PATH_OK: return "ok";
+    case PATH_ERR_NULL: return "a required pointer is NULL";
+    case PATH_ERR_SHAPE: return "sizes out of range or overflowing";
+    case PATH_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or precision";
+    case PATH_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PATH_ERR_CAPACITY: return "decode cache is full (cache_len >= capacity)";
+    case PATH_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int path_abi_version(void) { return 1; }
+
+int path_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, const void* q,
+                 const void* k, const void* w, const float* beta, const float* log_forget,
+                 float* tinv, float* qhat, float* khat, float* pT, float* cum,
+                 hipStream_t stream) {
+  int64_t BH, Nb;
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_shape(B, H, L, d, &BH, &Nb))) return st;
+  if (!w || !beta) return PATH_ERR_NULL;
+  if (qhat && !q) return PATH_ERR_NULL;
+  if (khat && !k) return PATH_ERR_NULL;
+  if (cum && !log_forget) return PATH_ERR_NULL;
+  if (tinv || qhat || khat || pT) {
+    st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, tinv, qhat, khat, pT,
+                                             stream));
+    if (st) return st;
+  }
+  if (cum) st = hip_status(path::launch_prefix_sum(BH, L, log_forget, cum, stream));
+  return st;
+}
+
+size_t path_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype,
+                                int with_forget) {
+  int64_t BH, Nb;
+  if (check_dtype(dtype) || check_shape(B, H, L, d, &BH, &Nb)) return 0;
+  return fwd_layout(BH, L, d, Nb, with_forget != 0).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct FwdArgs {
+  int64_t BH, Nb;
+  FwdWs lay;
+};
+
+int fwd_check(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, int precision, const void* q,
+              const void* k, const void* v, const void* w, const float* beta,
+              const float* log_forget, void* workspace, size_t workspace_bytes, FwdArgs* a) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (precision != PATH_PREC_ACCURATE && precision != PATH_PREC_AUTO) return PATH_ERR_UNSUPPORTED;
+  if ((st = check_shape(B, H, L, d, &a->BH, &a->Nb))) return st;
+  if (!q || !k || !v || !w || !beta) return PATH_ERR_NULL;
+  a->lay = fwd_layout(a->BH, L, d, a->Nb, log_forget != nullptr);
+  if (!workspace || workspace_bytes < a->lay.total ||
+      (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return PATH_ERR_WORKSPACE;
+  return PATH_OK;
+}
+
+int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int dtype,
+                const void* k, const void* w, const float* beta, const float* log_forget,
+                void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  float* khat = reinterpret_cast<float*>(ws + a.lay.khat);
+  float* pT = reinterpret_cast<float*>(ws + a.lay.pT);
+  int st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, nullptr, k, w, beta, nullptr,
+                                               nullptr, khat, pT, stream));
+  if (st) return st;
+  if (log_forget) {
+    float* cum = reinterpret_cast<float*>(ws + a.lay.cum);
+    st = hip_status(path::launch_prefix_sum(a.BH, L, log_forget, cum, stream));
+  }
+  return st;
+}
+
+int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+             const void* q, const void* k, const void* v, const void* w, const float* beta,
+             const float* log_forget, void* o, float* lse, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const float* khat = reinterpret_cast<const float*>(ws + a.lay.khat);
+  const float* pT = reinterpret_cast<const float*>(ws + a.lay.pT);
+  const float* cum = log_forget ? reinterpret_cast<const float*>(ws + a.lay.cum) : nullptr;
+  return hip_status(path::launch_fwd_scan_f32(dtype, B, H, L, d, scale, q, k, v, w, beta, cum, khat,
+                                              pT, o, lse, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int path_fwd_stage_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+                           int precision, const void* q, const void* k, const void* v,
+                           const void* w, const float* beta, const float* log_forget,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)scale;
+  FwdArgs a;
+  int st = fwd_check(B, H, L, d, dtype, precision, q, k, v, w, beta, log_forget, workspace,
+                     workspace_bytes, &a);
+  if (st) return st;
+  return fwd_prepare(a, B, H, L, d, dtype, k, w, beta, log_forget, workspace, stream);
+}
+
+int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+                        int precision, const void* q, const void* k, const void* v, const void* w,
+                        const float* beta, const float* log_forget, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  FwdArgs a;
+  int st = fwd_check(B, H, L, d, dtype, precision, q, k, v, w, beta, log_forget, workspace,
+                     workspace_bytes, &a);
+  if (st) return st;
+  if (!o || !lse) return PATH_ERR_NULL;
+  return fwd_scan(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, o, lse, workspace,
+                  stream);
+}
+
+int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+                  int precision, const void* q, const void* k, const void* v, const void* w,
+                  const float* beta, const float* log_forget, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  FwdArgs a;
+  int st = fwd_check(B, H, L, d, dtype, precision, q, k, v, w, beta, log_forget, workspace,
+                     workspace_bytes, &a);
+  if (st) return st;
+  if (!o || !lse) return PATH_ERR_NULL;
+  if ((st = fwd_prepare(a, B, H, L, d, dtype, k, w, beta, log_forget, workspace, stream))) return st;
+  return fwd_scan(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, o, lse, workspace,
+                  stream);
+}
+
+size_t path_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int64_t cache_len) {
+  if (B < 1 || H < 1 || cache_len < 0 || check_d(d)) return 0;
+  int64_t BH, n;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, path::decode_num_chunks(cache_len), &n) ||
+      !mul_ok(n, d + 2, &n))
+    return 0;
+  return align_up(sizeof(float) * size_t(n > 0 ? n : 1));
+}
+
+int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                     const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                     void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_d(d))) return st;
+  if (B < 1 || H < 1 || capacity < 1 || cache_len < 0) return PATH_ERR_SHAPE;
+  int64_t BH, n;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, capacity, &n) || !mul_ok(n, d, &n)) return PATH_ERR_SHAPE;
+  if (cache_len >= capacity) return PATH_ERR_CAPACITY;
+  if (BH * path::decode_num_chunks(cache_len) > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
+  if (!q_t || !k_t || !v_t || !w_t || !beta_t || !k_cache || !v_cache || !o || !lse)
+    return PATH_ERR_NULL;
+  const size_t need = path_decode_workspace_bytes(B, H, d, cache_len);
+  if (!workspace || need == 0 || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return PATH_ERR_WORKSPACE;
+  return hip_status(path::launch_decode(dtype, BH, d, scale, q_t, k_t, v_t, w_t, beta_t, k_cache,
+                                        v_cache, cache_len, capacity, o, lse,
+                                        static_cast<float*>(workspace), stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,297 @@
+// Decode step of PaTH attention with an in-place key cache.
+//
+// [PaTH Attention summary (gist.science 2505.16381), §3 "Inferência"]: at step
+// t every cached key absorbs the new transition, k_j <- H_t k_j with
+// H_t = I - beta_t w_t w_t^T, so the cache always holds
+// (H_{j+1}...H_t)^T k_j and no transition vectors are kept; the new key k_t
+// enters untransformed (its path product is empty).  The attention itself is
+// single-query softmax attention, split over key chunks and merged by
+// log-sum-exp (the FlashDecoding pattern the same bullet names).
+//
+// Memory plan (HBM-bound): each cached key row is read once and written once,
+// each value row read once, all with 16-byte coalesced accesses; consecutive
+// lanes cover one row, so a wave touches 1 KiB of contiguous cache per pass.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace path {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecChunk = 1024;  // keys per workgroup
+
+template <typename T>
+struct Vec16;  // 16 bytes of storage
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  using raw = uint4;
+  __device__ static void unpack(const raw& x, float* f) {
+    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f[2 * t] = __uint_as_float(u[t] << 16);
+      f[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+    }
+  }
+  __device__ static raw pack(const float* f) {
+    uint32_t u[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      u[t] = static_cast<uint32_t>(f32_to_bf16(f[2 * t])) |
+             (static_cast<uint32_t>(f32_to_bf16(f[2 * t + 1])) << 16);
+    return make_uint4(u[0], u[1], u[2], u[3]);
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  using raw = float4;
+  __device__ static void unpack(const raw& x, float* f) {
+    f[0] = x.x;
+    f[1] = x.y;
+    f[2] = x.z;
+    f[3] = x.w;
+  }
+  __device__ static raw pack(const float* f) { return make_float4(f[0], f[1], f[2], f[3]); }
+};
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// partial layout per (bh, chunk): [m, l, acc[D]]
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
+    int64_t cache_len, int64_t capacity, int nchunks, float scale, const T* __restrict__ q_t,
+    const T* __restrict__ w_t, const float* __restrict__ beta_t, T* __restrict__ k_cache,
+    const T* __restrict__ v_cache, float* __restrict__ partials) {
+  using V = Vec16<T>;
+  constexpr int EPV = V::N;          // elements per 16-byte access
+  constexpr int LPK = D / EPV;       // lanes per key row
+  constexpr int KPW = 64 / LPK;      // key rows per wave pass
+  constexpr int NW = kDecThreads / 64;
+  constexpr int UNR = 4;             // key rows in flight per lane
+
+  const int chunk = static_cast<int>(blockIdx.x % nchunks);
+  const int64_t bh = blockIdx.x / nchunks;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPK;
+  const int slot = lane / LPK;
+
+  float qv[EPV], wv[EPV];
+  {
+    const typename V::raw* qp = reinterpret_cast<const typename V::raw*>(q_t + bh * D) + sub;
+    const typename V::raw* wp = reinterpret_cast<const typename V::raw*>(w_t + bh * D) + sub;
+    V::unpack(*qp, qv);
+    V::unpack(*wp, wv);
+  }
+  float wq = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) wq += wv[e] * qv[e];
+  wq = group_sum<LPK>(wq);
+  const float bt = beta_t[bh];
+
+  const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
+  const int64_t j1 = j0 + kDecChunk < cache_len ? j0 + kDecChunk : cache_len;
+  typename V::raw* kbase = reinterpret_cast<typename V::raw*>(k_cache + bh * capacity * D);
+  const typename V::raw* vbase =
+      reinterpret_cast<const typename V::raw*>(v_cache + bh * capacity * D);
+
+  float mrun = -INFINITY, lrun = 0.f;
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+
+  constexpr int STRIDE = NW * KPW;  // key rows per workgroup pass
+  for (int64_t jb = j0 + wave * KPW + slot; jb < j1; jb += STRIDE * UNR) {
+    typename V::raw kr[UNR], vr[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
+      if (j < j1) {
+        kr[u] = kbase[j * LPK + sub];
+        vr[u] = vbase[j * LPK + sub];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
+      // Lanes of one key row share j, so the group reductions below see
+      // a consistent set of lanes; rows past j1 contribute nothing.
+      const bool live = j < j1;
+      float kf[EPV], vf[EPV];
+      V::unpack(kr[u], kf);
+      V::unpack(vr[u], vf);
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        a += wv[e] * kf[e];
+        b += qv[e] * kf[e];
+      }
+      a = group_sum<LPK>(a);
+      b = group_sum<LPK>(b);
+      const float ba = bt * a;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) kf[e] -= ba * wv[e];
+      if (live) {
+        kbase[j * LPK + sub] = V::pack(kf);
+        // q . (k - beta a w) from the fp32 updated key
+        const float s = scale * (b - ba * wq);
+        const float mnew = fmaxf(mrun, s);
+        const float alpha = expf(mrun - mnew);
+        const float p = expf(s - mnew);
+        lrun = lrun * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] = acc[e] * alpha + p * vf[e];
+        mrun = mnew;
+      }
+    }
+  }
+
+  // Merge the key slots of the wave (lanes with equal `sub`).
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(mrun, off, 64);
+    const float l2 = __shfl_xor(lrun, off, 64);
+    const float mnew = fmaxf(mrun, m2);
+    const float a1 = (mrun == -INFINITY) ? 0.f : expf(mrun - mnew);
+    const float a2 = (m2 == -INFINITY) ? 0.f : expf(m2 - mnew);
+    lrun = lrun * a1 + l2 * a2;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float o2 = __shfl_xor(acc[e], off, 64);
+      acc[e] = acc[e] * a1 + o2 * a2;
+    }
+    mrun = mnew;
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float sm[NW], sl[NW];
+  __shared__ float sacc[NW][D];
+  if (slot == 0) {
+    if (sub == 0) {
+      sm[wave] = mrun;
+      sl[wave] = lrun;
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) sacc[wave][sub * EPV + e] = acc[e];
+  }
+  __syncthreads();
+  float* out = partials + (bh * nchunks + chunk) * (D + 2);
+  if (threadIdx.x < D) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) mm = fmaxf(mm, sm[t]);
+    float ll = 0.f, oo = 0.f;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      const float a = (sm[t] == -INFINITY) ? 0.f : expf(sm[t] - mm);
+      ll += sl[t] * a;
+      oo += sacc[t][threadIdx.x] * a;
+    }
+    out[2 + threadIdx.x] = oo;
+    if (threadIdx.x == 0) {
+      out[0] = mm;
+      out[1] = ll;
+    }
+  }
+}
+
+// One wave per (b,h): merge chunk partials with the new key, write o and lse,
+// then append k_t, v_t at slot cache_len.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    int64_t cache_len, int64_t capacity, int nchunks, float scale, const T* __restrict__ q_t,
+    const T* __restrict__ k_t, const T* __restrict__ v_t, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, const float* __restrict__ partials, T* __restrict__ o,
+    float* __restrict__ lse) {
+  constexpr int PER = D / 64;
+  const int64_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  float qf[PER], kf[PER], vf[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = lane + 64 * t;
+    qf[t] = load_f32(q_t + bh * D + e);
+    kf[t] = load_f32(k_t + bh * D + e);
+    vf[t] = load_f32(v_t + bh * D + e);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) s += qf[t] * kf[t];
+  s = scale * wave_sum(s);
+
+  float mm = s;
+  const float* pb = partials + bh * nchunks * (D + 2);
+  for (int c = 0; c < nchunks; ++c) mm = fmaxf(mm, pb[c * (D + 2)]);
+  const float es = expf(s - mm);
+  float ll = es;
+  float oo[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) oo[t] = es * vf[t];
+  for (int c = 0; c < nchunks; ++c) {
+    const float* p = pb + c * (D + 2);
+    const float a = expf(p[0] - mm);
+    ll += a * p[1];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) oo[t] += a * p[2 + lane + 64 * t];
+  }
+  const float inv = 1.f / ll;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = lane + 64 * t;
+    store_f32(o + bh * D + e, oo[t] * inv);
+    k_cache[(bh * capacity + cache_len) * D + e] = k_t[bh * D + e];
+    v_cache[(bh * capacity + cache_len) * D + e] = v_t[bh * D + e];
+  }
+  if (lane == 0) lse[bh] = mm + logf(ll);
+}
+
+int64_t decode_num_chunks(int64_t cache_len) { return (cache_len + kDecChunk - 1) / kDecChunk; }
+
+template <typename T, int D>
+static hipError_t launch_dec_t(int64_t BH, float scale, const void* q_t, const void* k_t,
+                               const void* v_t, const void* w_t, const float* beta_t,
+                               void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity,
+                               void* o, float* lse, float* partials, hipStream_t stream) {
+  const int nchunks = static_cast<int>(decode_num_chunks(cache_len));
+  if (nchunks > 0) {
+    hipLaunchKernelGGL((decode_chunk_kernel<T, D>), dim3(static_cast<unsigned>(BH * nchunks)),
+                       dim3(kDecThreads), 0, stream, cache_len, capacity, nchunks, scale,
+                       static_cast<const T*>(q_t), static_cast<const T*>(w_t), beta_t,
+                       static_cast<T*>(k_cache), static_cast<const T*>(v_cache), partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+                     stream, cache_len, capacity, nchunks, scale, static_cast<const T*>(q_t),
+                     static_cast<const T*>(k_t), static_cast<const T*>(v_t),
+                     static_cast<T*>(k_cache), static_cast<T*>(v_cache), partials,
+                     static_cast<T*>(o), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const void* q_t,
+                         const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                         void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity,
+                         void* o, float* lse, float* partials, hipStream_t stream) {
+  if (dtype == 0) {
+    return d == 64 ? launch_dec_t<float, 64>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
+                                             cache_len, capacity, o, lse, partials, stream)
+                   : launch_dec_t<float, 128>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
+                                              cache_len, capacity, o, lse, partials, stream);
+  }
+  return d == 64 ? launch_dec_t<bf16_t, 64>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
+                                            cache_len, capacity, o, lse, partials, stream)
+                 : launch_dec_t<bf16_t, 128>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
+                                             cache_len, capacity, o, lse, partials, stream);
+}
+
+}  // namespace path

@@ -1,0 +1,34 @@
+// Host-side launchers of the gfx950 PaTH kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace path {
+
+// Per-block UT transform in fp32 (one workgroup per 64-token block).  Any of
+// the outputs may be null.  Layouts as documented for path_prepare.
+hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
+                              const void* q, const void* k, const void* w, const float* beta,
+                              float* tinv, float* qhat, float* khat, float* pT,
+                              hipStream_t stream);
+
+// c[bh, i] = sum_{s<=i} x[bh, s], accumulated in fp64.
+hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream);
+
+// Right-to-left block scan forward, fp32 arithmetic on the vector ALUs.
+hipError_t launch_fwd_scan_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d, float scale,
+                               const void* q, const void* k, const void* v, const void* w,
+                               const float* beta, const float* cum, const float* khat,
+                               const float* pT, void* o, float* lse, hipStream_t stream);
+
+// Decode: number of key chunks and partial-result floats per (b,h).
+int64_t decode_num_chunks(int64_t cache_len);
+hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const void* q_t,
+                         const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                         void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity,
+                         void* o, float* lse, float* partials, hipStream_t stream);
+
+}  // namespace path

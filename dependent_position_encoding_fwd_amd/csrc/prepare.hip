@@ -1,0 +1,232 @@
+// Per-block UT transform for PaTH attention, fp32 on the vector ALUs.
+//
+// [PaTH Attention summary (gist.science 2505.16381), §3 "Representação de
+// Transformação UT"]: the product of the transitions of one block,
+// H_0 H_1 ... H_63 with H_s = I - beta_s w_s w_s^T, equals I - W^T T^{-1} W
+// where W stacks the w_s and T is upper triangular,
+//     T = diag(1/beta) + strict_upper(W W^T).
+// T^{-1} is formed without dividing by beta (beta = 0 must give H = I) as the
+// solution of (I + diag(beta) strict_upper(W W^T)) X = diag(beta).
+// [§3 "Algoritmo Estilo FlashAttention"]: the boundary-adjusted query of local
+// row r carries the block's transitions up to r, and the adjusted key of row c
+// the transitions after c:
+//     qhat_r = H_0 ... H_r q_r       = q_r - W^T T^{-1} (W q_r masked to s <= r)
+//     khat_c = (H_{c+1}...H_63)^T k_c = k_c - W^T T^{-T} (W k_c masked to s > c)
+// These use that a contiguous principal block of the inverse of a triangular
+// matrix is the inverse of the same block of the matrix.  The block's
+// transition is also produced in row-update form, pT = P^T = I - W^T T^{-T} W.
+#include "common.h"
+#include "launch.h"
+
+namespace path {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prepare_f32_kernel(
+    int64_t L, int Nb, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ w, const float* __restrict__ beta, float* __restrict__ tinv_out,
+    float* __restrict__ qhat_out, float* __restrict__ khat_out, float* __restrict__ pT_out) {
+  constexpr int C = kBlk;
+  constexpr int CP = C + 1;
+  constexpr int DP = D + 1;
+  __shared__ float Ws[C][DP];  // rows w_s of the block (zero past L)
+  __shared__ float Xs[C][DP];  // k rows, then q rows, then F = T^{-T} W
+  __shared__ float Gs[C][CP];  // strict_upper(W W^T), then masked W k / W q products
+  __shared__ float Ts[C][CP];  // T^{-1}
+  __shared__ float Ys[C][CP];  // coefficient rows
+  __shared__ float bs[C];
+
+  const int tid = threadIdx.x;
+  const int n = blockIdx.x % Nb;
+  const int64_t bh = blockIdx.x / Nb;
+  const int64_t t0 = static_cast<int64_t>(n) * C;
+  const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
+  const int64_t base = bh * L * D;
+
+  for (int idx = tid; idx < C * D; idx += 256) {
+    int r = idx / D, e = idx % D;
+    Ws[r][e] = r < valid ? load_f32(w + base + (t0 + r) * D + e) : 0.f;
+  }
+  if (tid < C) bs[tid] = tid < valid ? beta[bh * L + t0 + tid] : 0.f;
+  __syncthreads();
+
+  for (int idx = tid; idx < C * C; idx += 256) {
+    int r = idx / C, t = idx % C;
+    float g = 0.f;
+    if (t > r) {
+      for (int e = 0; e < D; ++e) g += Ws[r][e] * Ws[t][e];
+    }
+    Gs[r][t] = g;
+  }
+  __syncthreads();
+
+  // Back substitution, one column of X = T^{-1} per thread, last row first:
+  // X[r][c] = beta_r * (delta_rc - sum_{r<t<=c} G[r][t] X[t][c]).
+  if (tid < C) {
+    const int c = tid;
+    for (int r = C - 1; r >= 0; --r) {
+      float x = 0.f;
+      if (r <= c) {
+        float acc = (r == c) ? 1.f : 0.f;
+        for (int t = r + 1; t <= c; ++t) acc -= Gs[r][t] * Ts[t][c];
+        x = bs[r] * acc;
+      }
+      Ts[r][c] = x;
+    }
+  }
+  __syncthreads();
+
+  if (tinv_out) {
+    float* dst = tinv_out + (bh * Nb + n) * (C * C);
+    for (int idx = tid; idx < C * C; idx += 256) dst[idx] = Ts[idx / C][idx % C];
+  }
+
+  if (khat_out) {
+    for (int idx = tid; idx < C * D; idx += 256) {
+      int r = idx / D, e = idx % D;
+      Xs[r][e] = r < valid ? load_f32(k + base + (t0 + r) * D + e) : 0.f;
+    }
+    __syncthreads();
+    // Z[c][s] = (w_s . k_c) for s > c
+    for (int idx = tid; idx < C * C; idx += 256) {
+      int c = idx / C, s = idx % C;
+      float z = 0.f;
+      if (s > c) {
+        for (int e = 0; e < D; ++e) z += Ws[s][e] * Xs[c][e];
+      }
+      Gs[c][s] = z;
+    }
+    __syncthreads();
+    // Y[c][a] = sum_s Z[c][s] T^{-1}[s][a]   (= (T^{-T} z_c)_a)
+    for (int idx = tid; idx < C * C; idx += 256) {
+      int c = idx / C, a = idx % C;
+      float y = 0.f;
+      for (int s = c + 1; s <= a; ++s) y += Gs[c][s] * Ts[s][a];
+      Ys[c][a] = y;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * D; idx += 256) {
+      int c = idx / D, e = idx % D;
+      if (c < valid) {
+        float x = Xs[c][e];
+        for (int a = c + 1; a < C; ++a) x -= Ys[c][a] * Ws[a][e];
+        khat_out[base + (t0 + c) * D + e] = x;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (qhat_out) {
+    for (int idx = tid; idx < C * D; idx += 256) {
+      int r = idx / D, e = idx % D;
+      Xs[r][e] = r < valid ? load_f32(q + base + (t0 + r) * D + e) : 0.f;
+    }
+    __syncthreads();
+    // A[r][t] = (w_t . q_r) for t <= r
+    for (int idx = tid; idx < C * C; idx += 256) {
+      int r = idx / C, t = idx % C;
+      float z = 0.f;
+      if (t <= r) {
+        for (int e = 0; e < D; ++e) z += Ws[t][e] * Xs[r][e];
+      }
+      Gs[r][t] = z;
+    }
+    __syncthreads();
+    // Y[r][a] = sum_t T^{-1}[a][t] A[r][t]   (= (T^{-1} a_r)_a, nonzero for a <= r)
+    for (int idx = tid; idx < C * C; idx += 256) {
+      int r = idx / C, a = idx % C;
+      float y = 0.f;
+      for (int t = a; t <= r; ++t) y += Ts[a][t] * Gs[r][t];
+      Ys[r][a] = y;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * D; idx += 256) {
+      int r = idx / D, e = idx % D;
+      if (r < valid) {
+        float x = Xs[r][e];
+        for (int a = 0; a <= r; ++a) x -= Ys[r][a] * Ws[a][e];
+        qhat_out[base + (t0 + r) * D + e] = x;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (pT_out) {
+    // F[s][e] = sum_t T^{-1}[t][s] W[t][e]   (F = T^{-T} W)
+    for (int idx = tid; idx < C * D; idx += 256) {
+      int s = idx / D, e = idx % D;
+      float f = 0.f;
+      for (int t = 0; t <= s; ++t) f += Ts[t][s] * Ws[t][e];
+      Xs[s][e] = f;
+    }
+    __syncthreads();
+    float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
+    for (int idx = tid; idx < D * D; idx += 256) {
+      int a = idx / D, b = idx % D;
+      float x = (a == b) ? 1.f : 0.f;
+      for (int s = 0; s < C; ++s) x -= Ws[s][a] * Xs[s][b];
+      dst[idx] = x;
+    }
+  }
+}
+
+// One workgroup per (b,h): fp64 prefix sum of log forget gates.
+__global__ __launch_bounds__(256) void prefix_sum_kernel(int64_t L, const float* __restrict__ x,
+                                                         float* __restrict__ c) {
+  __shared__ double part[256];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t per = (L + 255) / 256;
+  const int64_t lo = tid * per;
+  const int64_t hi = lo + per < L ? lo + per : L;
+  const float* xs = x + bh * L;
+  double acc = 0.0;
+  for (int64_t i = lo; i < hi; ++i) acc += static_cast<double>(xs[i]);
+  part[tid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double run = 0.0;
+    for (int t = 0; t < 256; ++t) {
+      double v = part[t];
+      part[t] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  double run = part[tid];
+  float* cs = c + bh * L;
+  for (int64_t i = lo; i < hi; ++i) {
+    run += static_cast<double>(xs[i]);
+    cs[i] = static_cast<float>(run);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_prepare_t(int64_t B, int64_t H, int64_t L, const void* q, const void* k,
+                                   const void* w, const float* beta, float* tinv, float* qhat,
+                                   float* khat, float* pT, hipStream_t stream) {
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  dim3 grid(static_cast<unsigned>(B * H * Nb));
+  hipLaunchKernelGGL((prepare_f32_kernel<T, D>), grid, dim3(256), 0, stream, L, Nb,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(w),
+                     beta, tinv, qhat, khat, pT);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
+                              const void* q, const void* k, const void* w, const float* beta,
+                              float* tinv, float* qhat, float* khat, float* pT,
+                              hipStream_t stream) {
+  if (dtype == 0) {
+    return d == 64 ? launch_prepare_t<float, 64>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream)
+                   : launch_prepare_t<float, 128>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream);
+  }
+  return d == 64 ? launch_prepare_t<bf16_t, 64>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream)
+                 : launch_prepare_t<bf16_t, 128>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream);
+}
+
+hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream) {
+  hipLaunchKernelGGL(prefix_sum_kernel, dim3(static_cast<unsigned>(BH)), dim3(256), 0, stream, L, x, c);
+  return hipGetLastError();
+}
+
+}  // namespace path

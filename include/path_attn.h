@@ -1,0 +1,157 @@
+/*
+ * path_attn.h - C ABI of the MI355X (gfx950) PaTH attention library.
+ *
+ * PaTH attention [PaTH Attention technical summary, gist.science 2505.16381,
+ * §2 "Mecanismo Central"]: causal softmax attention whose logit for query i
+ * and key j <= i is
+ *     s_ij = scale * k_j^T (H_{j+1} H_{j+2} ... H_i) q_i  (+ FoX bias),
+ * with data-dependent Householder-like transitions H_s = I - beta_s w_s w_s^T.
+ * The product for j = i is the identity; H_i is the first factor to act on q_i.
+ *
+ * Conventions shared by every call
+ *  - Layouts are dense row-major.  q, k, v, w, o: [B, H, L, d] in `dtype`;
+ *    beta, log_forget, lse: [B, H, L] fp32.
+ *  - dtype: PATH_F32 (fp32 storage) or PATH_BF16 (bfloat16 storage).  All
+ *    arithmetic accumulates in fp32 on the GPU.
+ *  - d (head dimension) must be 64 or 128.  Any L >= 1 is accepted: a partial
+ *    last 64-token block is padded internally with identity transitions.
+ *  - Every device pointer is owned by the caller; the library allocates no
+ *    memory and keeps no state between calls.  Work is enqueued on `stream`
+ *    (may be NULL for the null stream) and runs asynchronously: outputs are
+ *    ready once the stream reaches that point.
+ *  - Arguments are checked on the host before anything is enqueued.  A
+ *    non-zero return leaves all buffers untouched, except PATH_ERR_HIP, which
+ *    means a launch failed after earlier work may already have been enqueued
+ *    (for path_decode_step the key cache is then undefined).
+ *  - No exceptions cross the ABI; calls are thread-compatible (calls on
+ *    distinct buffers may run concurrently on different streams).
+ */
+#ifndef PATH_ATTN_H_
+#define PATH_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PATH_OK = 0,
+  PATH_ERR_NULL = 1,        /* a required pointer is NULL */
+  PATH_ERR_SHAPE = 2,       /* a size is out of range or the sizes overflow */
+  PATH_ERR_UNSUPPORTED = 3, /* d not 64/128, or unknown dtype / precision */
+  PATH_ERR_WORKSPACE = 4,   /* workspace NULL, too small or not 256-byte aligned */
+  PATH_ERR_CAPACITY = 5,    /* decode: cache_len >= capacity */
+  PATH_ERR_HIP = 6          /* a kernel launch failed (see hipGetLastError) */
+} path_status;
+
+typedef enum { PATH_F32 = 0, PATH_BF16 = 1 } path_dtype;
+
+/*
+ * Precision policy of the bf16 forward.  ACCURATE feeds every matrix-core
+ * product that involves a transported query or key with a two-term (hi + lo)
+ * split of its fp32 value.  AUTO uses the split only where a run-time bound on
+ * the logit rounding error exceeds a fixed budget and plain half precision
+ * elsewhere.  fp32 inputs always take the fp32 path and ignore this flag.
+ */
+typedef enum { PATH_PREC_ACCURATE = 0, PATH_PREC_AUTO = 1 } path_precision;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* path_status_string(int status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int path_abi_version(void);
+
+/*
+ * path_prepare - per-block UT transform and boundary-adjusted queries/keys.
+ * [PaTH summary §3 "Representação de Transformação UT" and "Algoritmo Estilo
+ * FlashAttention"]: the sequence is cut into Nb = ceil(L/64) blocks of 64
+ * tokens; for block n with rows w_s (local index s = 0..63) and beta_s,
+ *   tinv = T^{-1} = (I + diag(beta) strict_upper(W W^T))^{-1} diag(beta)
+ *          (upper triangular; T = diag(1/beta) + strict_upper(W W^T)),
+ *   qhat_r = H_0 H_1 ... H_r q_r                 = q_r - W^T T^{-1} ((W q_r) masked to s <= r),
+ *   khat_c = (H_{c+1} ... H_63)^T k_c            = k_c - W^T T^{-T} ((W k_c) masked to s > c),
+ *   pT     = (H_0 H_1 ... H_63)^T                = I - W^T T^{-T} W,
+ *   cum_i  = sum_{s <= i} log_forget_s           (accumulated in fp64, stored fp32).
+ * Inputs: q, k, w [B,H,L,d] (dtype); beta [B,H,L]; log_forget [B,H,L] or NULL.
+ * Outputs (fp32, caller-allocated, each may be NULL to skip it):
+ *   tinv [B,H,Nb,64,64], qhat [B,H,L,d], khat [B,H,L,d], pT [B,H,Nb,d,d],
+ *   cum [B,H,L] (requires log_forget).
+ */
+int path_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, const void* q,
+                 const void* k, const void* w, const float* beta, const float* log_forget,
+                 float* tinv, float* qhat, float* khat, float* pT, float* cum,
+                 hipStream_t stream);
+
+/* Workspace bytes path_attn_fwd needs for these sizes (0 on invalid sizes). */
+size_t path_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype,
+                                int with_forget);
+
+/*
+ * path_attn_fwd - PaTH causal attention forward [PaTH summary §2 "Mecanismo
+ * Central"; PaTH-FoX bias from §2 "Extensões: PaTH-FoX"]:
+ *   s_ij = scale * k_j^T (H_{j+1}...H_i) q_i + (log_forget ? sum_{s=j+1..i} log_forget_s : 0)
+ *   o_i  = sum_{j<=i} softmax_j(s_ij) v_j,   lse_i = log sum_{j<=i} exp(s_ij)  (natural log)
+ * Runs the block prepare into `workspace`, then a right-to-left scan over key
+ * blocks per query tile [§3 "Algoritmo Estilo FlashAttention"].
+ * Inputs: q, k, v, w [B,H,L,d] (dtype); beta [B,H,L] (any finite beta >= 0);
+ *   log_forget [B,H,L] or NULL; scale multiplies the PaTH term only.
+ * Outputs: o [B,H,L,d] (dtype, bf16 rounded to nearest even), lse [B,H,L] fp32.
+ * workspace: device buffer of at least path_fwd_workspace_bytes(...) bytes,
+ *   256-byte aligned; its contents on entry are irrelevant.
+ */
+int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+                  int precision, const void* q, const void* k, const void* v, const void* w,
+                  const float* beta, const float* log_forget, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two stages of path_attn_fwd, for callers that time or overlap them:
+ * path_fwd_stage_prepare writes the per-block UT data into `workspace`;
+ * path_fwd_stage_scan runs the right-to-left scan from it.  Called in that
+ * order on one stream with identical arguments they produce exactly what
+ * path_attn_fwd produces.  The workspace layout is internal.
+ */
+int path_fwd_stage_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+                           int precision, const void* q, const void* k, const void* v,
+                           const void* w, const float* beta, const float* log_forget,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
+                        int precision, const void* q, const void* k, const void* v, const void* w,
+                        const float* beta, const float* log_forget, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes path_decode_step needs (0 on invalid sizes). */
+size_t path_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int64_t cache_len);
+
+/*
+ * path_decode_step - one generation step with an in-place key cache
+ * [PaTH summary §3 "Inferência"]: with H_t = I - beta_t w_t w_t^T,
+ *   k_cache[b,h,j] <- H_t k_cache[b,h,j]   for every j < cache_len (in place;
+ *                                          stored in dtype, bf16 rounded to nearest even),
+ *   s_j = scale * q_t . k_j (j < cache_len, from the fp32 updated key before rounding),
+ *   s_t = scale * q_t . k_t (the new key enters untransformed),
+ *   o   = softmax over the cache_len + 1 keys applied to [v_cache[:cache_len], v_t],
+ *   lse = log of the softmax denominator,
+ *   then k_t, v_t are written to slot cache_len of the caches.
+ * Inputs: q_t, k_t, v_t, w_t [B,H,d] (dtype); beta_t [B,H] fp32.
+ * Caches: k_cache, v_cache [B,H,capacity,d] (dtype); slots >= cache_len + 1
+ *   are not touched.  Requires 0 <= cache_len < capacity (else PATH_ERR_CAPACITY).
+ * Outputs: o [B,H,d] (dtype), lse [B,H] fp32.
+ * workspace: >= path_decode_workspace_bytes(...) bytes, 256-byte aligned.
+ * After PATH_ERR_HIP the key cache contents are undefined (no undo exists for
+ * an in-place update).
+ */
+int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                     const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                     void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATH_ATTN_H_ */

@@ -1,0 +1,103 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU (every call
+here fails validation, so nothing is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dependent_position_encoding_fwd_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "path_attn.h")
+
+OK, NULL, SHAPE, UNSUP, WS, CAP = 0, 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(path_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = pa.lib()
+    names = header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(pa.EXPORTS) == names
+
+
+def test_status_strings_and_version():
+    L = pa.lib()
+    assert L.path_abi_version() == 1
+    for st in range(7):
+        assert len(L.path_status_string(st)) > 0
+    assert L.path_status_string(99) == b"unknown status"
+
+
+def _fwd(B=1, H=1, Lq=128, d=64, dtype=1, prec=1, ptr=FAKE, ws=FAKE, wsb=1 << 40, lf=None, o=FAKE):
+    return pa.lib().path_attn_fwd(B, H, Lq, d, dtype, 1.0, prec, ptr, ptr, ptr, ptr, ptr, lf, o, ptr, ws, wsb, None)
+
+
+def test_fwd_validation():
+    assert _fwd(d=96) == UNSUP
+    assert _fwd(d=32) == UNSUP
+    assert _fwd(dtype=7) == UNSUP
+    assert _fwd(prec=5) == UNSUP
+    assert _fwd(B=0) == SHAPE
+    assert _fwd(Lq=0) == SHAPE
+    assert _fwd(H=-3) == SHAPE
+    assert _fwd(B=1 << 40, H=1 << 20) == SHAPE   # element count overflow
+    assert _fwd(ptr=None) == NULL
+    assert _fwd(o=None) == NULL
+    assert _fwd(ws=None) == WS
+    assert _fwd(wsb=16) == WS
+    assert _fwd(ws=ctypes.c_void_p(0x1010)) == WS  # not 256-byte aligned
+
+
+def test_workspace_sizes():
+    L = pa.lib()
+    assert L.path_fwd_workspace_bytes(1, 1, 64, 96, 1, 0) == 0
+    a = L.path_fwd_workspace_bytes(2, 3, 200, 64, 1, 0)
+    b = L.path_fwd_workspace_bytes(2, 3, 200, 64, 1, 1)
+    assert a > 0 and b > a and a % 256 == 0 and b % 256 == 0
+    assert L.path_decode_workspace_bytes(1, 1, 64, 0) >= 256
+    assert L.path_decode_workspace_bytes(1, 1, 48, 10) == 0
+
+
+def test_prepare_validation():
+    L = pa.lib()
+    assert L.path_prepare(1, 1, 64, 64, 1, FAKE, FAKE, None, FAKE, None, FAKE, None, None, None, None, None) == NULL
+    assert L.path_prepare(1, 1, 64, 64, 1, None, FAKE, FAKE, FAKE, None, None, FAKE, None, None, None, None) == NULL
+    assert L.path_prepare(1, 1, 64, 64, 1, FAKE, FAKE, FAKE, FAKE, None, None, None, None, None, FAKE, None) == NULL
+    assert L.path_prepare(1, 1, 64, 80, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, None, None) == UNSUP
+    # nothing requested: valid no-op, no launch
+    assert L.path_prepare(1, 1, 64, 64, 1, FAKE, FAKE, FAKE, FAKE, None, None, None, None, None, None, None) == OK
+
+
+def _dec(cache_len=10, capacity=11, d=64, dtype=1, ptr=FAKE, ws=FAKE, wsb=1 << 30):
+    return pa.lib().path_decode_step(2, 2, d, dtype, 1.0, ptr, ptr, ptr, ptr, ptr, ptr, ptr, cache_len, capacity,
+                                     ptr, ptr, ws, wsb, None)
+
+
+def test_decode_validation():
+    assert _dec(cache_len=11, capacity=11) == CAP
+    assert _dec(cache_len=20, capacity=11) == CAP
+    assert _dec(cache_len=-1) == SHAPE
+    assert _dec(capacity=0, cache_len=0) == SHAPE
+    assert _dec(d=100) == UNSUP
+    assert _dec(dtype=3) == UNSUP
+    assert _dec(ptr=None) == NULL
+    assert _dec(ws=None) == WS
+    assert _dec(wsb=8) == WS
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    b = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError):
+        pa.path_attn_fwd(x, x, x, x, b)
