@@ -143,7 +143,7 @@ def _decode_case(B, H, d, n, cap, dtype, scale, seed, heads_to_check=None):
         if dtype == "bf16":
             assert np.all(np.abs(got - kupd) <= 0.5 * _bf16_ulp(kupd) + 1e-5)
         else:
-            assert np.max(np.abs(got - kupd)) <= 1e-5
+            assert np.all(np.abs(got - kupd) <= 1e-5)
         assert torch.equal(kc_gpu[b, h, n].cpu(), x["k_t"][b, h])
         assert torch.equal(g["v_cache"][b, h, n].cpu(), x["v_t"][b, h])
         if n + 1 < cap:
