@@ -48,19 +48,41 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t d, int64_t* BH, int64_t
   return PATH_OK;
 }
 
+// Logit budget (log2 units) under which the bf16 forward drops the lo terms
+// of a key block: |Qt|_max * |khat|_max * 2^-10 <= kAutoTau.
+constexpr float kAutoTau = 2e-3f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workspace of the forward.  fp32 inputs: khat, pT (fp32) and cum.  bf16
+// inputs: the matrix-core layout written by the prepare stage.
 struct FwdWs {
-  size_t khat, pT, cum, total;
+  size_t khat, pT, cum;                       // fp32 path
+  size_t khl, pmat, qhat, sdiag, kmax, kmaxh;  // bf16 path (cum shared)
+  size_t total;
 };
 
-FwdWs fwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget) {
+FwdWs fwd_layout(int dtype, int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget) {
   FwdWs w{};
   size_t off = 0;
-  w.khat = off;
-  off += align_up(sizeof(float) * size_t(BH) * size_t(L) * size_t(d));
-  w.pT = off;
-  off += align_up(sizeof(float) * size_t(BH) * size_t(Nb) * size_t(d) * size_t(d));
-  w.cum = off;
-  if (with_forget) off += align_up(sizeof(float) * size_t(BH) * size_t(L));
+  const size_t bh = size_t(BH), nb = size_t(Nb), dd = size_t(d), lp = nb * size_t(kBlk);
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  if (dtype == PATH_F32) {
+    w.khat = take(sizeof(float) * bh * size_t(L) * dd);
+    w.pT = take(sizeof(float) * bh * nb * dd * dd);
+    if (with_forget) w.cum = take(sizeof(float) * bh * size_t(L));
+  } else {
+    w.khl = take(2 * bh * nb * 2 * size_t(kBlk) * dd);
+    w.pmat = take(2 * bh * nb * 2 * dd * dd);
+    w.qhat = take(sizeof(float) * bh * lp * dd);
+    w.sdiag = take(sizeof(float) * bh * nb * size_t(kBlk) * size_t(kBlk));
+    w.kmax = take(sizeof(float) * bh * nb);
+    w.kmaxh = take(sizeof(float) * bh);
+    if (with_forget) w.cum = take(sizeof(float) * bh * lp);
+  }
   w.total = off;
   return w;
 }
@@ -111,7 +133,7 @@ size_t path_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
                                 int with_forget) {
   int64_t BH, Nb;
   if (check_dtype(dtype) || check_shape(B, H, L, d, &BH, &Nb)) return 0;
-  return fwd_layout(BH, L, d, Nb, with_forget != 0).total;
+  return fwd_layout(dtype, BH, L, d, Nb, with_forget != 0).total;
 }
 
 }  // extern "C"
@@ -131,7 +153,7 @@ int fwd_check(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, int precisi
   if (precision != PATH_PREC_ACCURATE && precision != PATH_PREC_AUTO) return PATH_ERR_UNSUPPORTED;
   if ((st = check_shape(B, H, L, d, &a->BH, &a->Nb))) return st;
   if (!q || !k || !v || !w || !beta) return PATH_ERR_NULL;
-  a->lay = fwd_layout(a->BH, L, d, a->Nb, log_forget != nullptr);
+  a->lay = fwd_layout(dtype, a->BH, L, d, a->Nb, log_forget != nullptr);
   if (!workspace || workspace_bytes < a->lay.total ||
       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return PATH_ERR_WORKSPACE;
@@ -139,30 +161,52 @@ int fwd_check(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, int precisi
 }
 
 int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int dtype,
-                const void* k, const void* w, const float* beta, const float* log_forget,
-                void* workspace, hipStream_t stream) {
+                float scale, const void* q, const void* k, const void* w, const float* beta,
+                const float* log_forget, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
-  float* khat = reinterpret_cast<float*>(ws + a.lay.khat);
-  float* pT = reinterpret_cast<float*>(ws + a.lay.pT);
-  int st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, nullptr, k, w, beta, nullptr,
-                                               nullptr, khat, pT, stream));
-  if (st) return st;
-  if (log_forget) {
-    float* cum = reinterpret_cast<float*>(ws + a.lay.cum);
-    st = hip_status(path::launch_prefix_sum(a.BH, L, log_forget, cum, stream));
+  int st;
+  if (dtype == PATH_F32) {
+    float* khat = reinterpret_cast<float*>(ws + a.lay.khat);
+    float* pT = reinterpret_cast<float*>(ws + a.lay.pT);
+    st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, nullptr, k, w, beta, nullptr,
+                                             nullptr, khat, pT, stream));
+    if (st) return st;
+    if (log_forget) {
+      float* cum = reinterpret_cast<float*>(ws + a.lay.cum);
+      st = hip_status(path::launch_prefix_sum(a.BH, L, log_forget, cum, stream));
+    }
+    return st;
   }
-  return st;
+  float* kmax = reinterpret_cast<float*>(ws + a.lay.kmax);
+  st = hip_status(path::launch_prepare_scan(
+      B, H, L, d, scale * kLog2e, q, k, w, beta, reinterpret_cast<_Float16*>(ws + a.lay.khl),
+      reinterpret_cast<_Float16*>(ws + a.lay.pmat), reinterpret_cast<float*>(ws + a.lay.qhat),
+      reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, stream));
+  if (st) return st;
+  return hip_status(path::launch_head_reduce(
+      a.BH, L, kmax, reinterpret_cast<float*>(ws + a.lay.kmaxh), log_forget, kLog2e,
+      log_forget ? reinterpret_cast<float*>(ws + a.lay.cum) : nullptr, stream));
 }
 
 int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
-             const void* q, const void* k, const void* v, const void* w, const float* beta,
-             const float* log_forget, void* o, float* lse, void* workspace, hipStream_t stream) {
+             int precision, const void* q, const void* k, const void* v, const void* w,
+             const float* beta, const float* log_forget, void* o, float* lse, void* workspace,
+             hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
-  const float* khat = reinterpret_cast<const float*>(ws + a.lay.khat);
-  const float* pT = reinterpret_cast<const float*>(ws + a.lay.pT);
   const float* cum = log_forget ? reinterpret_cast<const float*>(ws + a.lay.cum) : nullptr;
-  return hip_status(path::launch_fwd_scan_f32(dtype, B, H, L, d, scale, q, k, v, w, beta, cum, khat,
-                                              pT, o, lse, stream));
+  if (dtype == PATH_F32) {
+    const float* khat = reinterpret_cast<const float*>(ws + a.lay.khat);
+    const float* pT = reinterpret_cast<const float*>(ws + a.lay.pT);
+    return hip_status(path::launch_fwd_scan_f32(dtype, B, H, L, d, scale, q, k, v, w, beta, cum,
+                                                khat, pT, o, lse, stream));
+  }
+  return hip_status(path::launch_fwd_mfma(
+      B, H, L, d, precision == PATH_PREC_ACCURATE ? 1 : 0, kAutoTau, v,
+      reinterpret_cast<const _Float16*>(ws + a.lay.khl),
+      reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
+      reinterpret_cast<const float*>(ws + a.lay.qhat),
+      reinterpret_cast<const float*>(ws + a.lay.sdiag),
+      reinterpret_cast<const float*>(ws + a.lay.kmaxh), cum, o, lse, stream));
 }
 
 }  // namespace
@@ -173,12 +217,11 @@ int path_fwd_stage_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype
                            int precision, const void* q, const void* k, const void* v,
                            const void* w, const float* beta, const float* log_forget,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)scale;
   FwdArgs a;
   int st = fwd_check(B, H, L, d, dtype, precision, q, k, v, w, beta, log_forget, workspace,
                      workspace_bytes, &a);
   if (st) return st;
-  return fwd_prepare(a, B, H, L, d, dtype, k, w, beta, log_forget, workspace, stream);
+  return fwd_prepare(a, B, H, L, d, dtype, scale, q, k, w, beta, log_forget, workspace, stream);
 }
 
 int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
@@ -190,8 +233,8 @@ int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, f
                      workspace_bytes, &a);
   if (st) return st;
   if (!o || !lse) return PATH_ERR_NULL;
-  return fwd_scan(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, o, lse, workspace,
-                  stream);
+  return fwd_scan(a, B, H, L, d, dtype, scale, precision, q, k, v, w, beta, log_forget, o, lse,
+                  workspace, stream);
 }
 
 int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
@@ -203,9 +246,10 @@ int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
                      workspace_bytes, &a);
   if (st) return st;
   if (!o || !lse) return PATH_ERR_NULL;
-  if ((st = fwd_prepare(a, B, H, L, d, dtype, k, w, beta, log_forget, workspace, stream))) return st;
-  return fwd_scan(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, o, lse, workspace,
-                  stream);
+  if ((st = fwd_prepare(a, B, H, L, d, dtype, scale, q, k, w, beta, log_forget, workspace, stream)))
+    return st;
+  return fwd_scan(a, B, H, L, d, dtype, scale, precision, q, k, v, w, beta, log_forget, o, lse,
+                  workspace, stream);
 }
 
 size_t path_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int64_t cache_len) {

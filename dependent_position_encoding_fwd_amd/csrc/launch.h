@@ -15,6 +15,24 @@ hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_
                               float* tinv, float* qhat, float* khat, float* pT,
                               hipStream_t stream);
 
+// Per-block UT data in the layout of the matrix-core forward (bf16 inputs).
+// c2 = scale * log2(e) multiplies the stored adjusted queries and in-block logits.
+hipError_t launch_prepare_scan(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
+                               const void* k, const void* w, const float* beta, _Float16* khat,
+                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               hipStream_t stream);
+
+// Per head: kmax_head = max over blocks of kmax; cum = mult * prefix sum of
+// log_forget (fp64 accumulation, padded to whole blocks) when log_forget != null.
+hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head,
+                              const float* log_forget, float mult, float* cum, hipStream_t stream);
+
+// Matrix-core right-to-left scan forward (bf16 storage).
+hipError_t launch_fwd_mfma(int64_t B, int64_t H, int64_t L, int64_t d, int accurate, float tau,
+                           const void* v, const _Float16* khat, const _Float16* pmat,
+                           const float* qhat, const float* sdiag, const float* kmax_head,
+                           const float* cum, void* o, float* lse, hipStream_t stream);
+
 // c[bh, i] = sum_{s<=i} x[bh, s], accumulated in fp64.
 hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream);
 

@@ -20,11 +20,37 @@
 
 namespace path {
 
-template <typename T, int D>
+// Outputs of the scan layout (consumed by the matrix-core forward).
+struct ScanOut {
+  _Float16* khat;  // [BH][Nb][2 (hi,lo)][64][D]  khat rows, columns in mfma_perm order
+  _Float16* pmat;  // [BH][Nb][2][D][D]           P = H_0...H_63 rows, columns permuted
+  float* qhat;     // [BH][Nb*64][D]              c2 * qhat (padded rows zero)
+  float* sdiag;    // [BH][Nb][64 query][64 key]  c2 * in-block logits (key <= query)
+  float* kmax;     // [BH][Nb]                    max_c |khat_c|
+  float c2;        // logit multiplier (scale * log2(e))
+};
+
+// Column order of matrix-core A operands.  A 32-wide slice of the reduction
+// index d = 32c + 16h + 4g + j is stored at 32c + 8g + 4h + j, so that lane
+// group g reads its 8 reduction slots with one 16-byte access, and those slots
+// line up with the accumulator layout of the 16x16 output tiles that feed the
+// B operand (rows 4g..4g+3 of two consecutive tiles).
+__device__ __forceinline__ int mfma_perm(int d) {
+  return (d & ~31) | (((d >> 2) & 3) << 3) | (((d >> 4) & 1) << 2) | (d & 3);
+}
+
+__device__ __forceinline__ void store_hilo(_Float16* hi, _Float16* lo, float x) {
+  const _Float16 h = static_cast<_Float16>(x);
+  *hi = h;
+  *lo = static_cast<_Float16>(x - static_cast<float>(h));
+}
+
+template <typename T, int D, bool SCAN>
 __global__ __launch_bounds__(256) void prepare_f32_kernel(
     int64_t L, int Nb, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ w, const float* __restrict__ beta, float* __restrict__ tinv_out,
-    float* __restrict__ qhat_out, float* __restrict__ khat_out, float* __restrict__ pT_out) {
+    float* __restrict__ qhat_out, float* __restrict__ khat_out, float* __restrict__ pT_out,
+    ScanOut so) {
   constexpr int C = kBlk;
   constexpr int CP = C + 1;
   constexpr int DP = D + 1;
@@ -75,12 +101,14 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
   }
   __syncthreads();
 
-  if (tinv_out) {
+  if (!SCAN && tinv_out) {
     float* dst = tinv_out + (bh * Nb + n) * (C * C);
     for (int idx = tid; idx < C * C; idx += 256) dst[idx] = Ts[idx / C][idx % C];
   }
 
-  if (khat_out) {
+  __shared__ float Y2[SCAN ? C : 1][CP];  // scan layout: keeps Y for the in-block logits
+  __shared__ float red[C];
+  if (SCAN || khat_out) {
     for (int idx = tid; idx < C * D; idx += 256) {
       int r = idx / D, e = idx % D;
       Xs[r][e] = r < valid ? load_f32(k + base + (t0 + r) * D + e) : 0.f;
@@ -106,16 +134,37 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     __syncthreads();
     for (int idx = tid; idx < C * D; idx += 256) {
       int c = idx / D, e = idx % D;
-      if (c < valid) {
-        float x = Xs[c][e];
-        for (int a = c + 1; a < C; ++a) x -= Ys[c][a] * Ws[a][e];
-        khat_out[base + (t0 + c) * D + e] = x;
+      float x = Xs[c][e];
+      for (int a = c + 1; a < C; ++a) x -= Ys[c][a] * Ws[a][e];
+      if (!SCAN && c < valid) khat_out[base + (t0 + c) * D + e] = x;
+      if (SCAN) Xs[c][e] = x;  // each element is read and written by one thread only
+    }
+    __syncthreads();
+    if constexpr (SCAN) {
+      const int64_t blk = bh * Nb + n;
+      _Float16* kh = so.khat + blk * (2 * C * D);
+      for (int idx = tid; idx < C * D; idx += 256) {
+        int c = idx / D, e = idx % D;
+        const int p = c * D + mfma_perm(e);
+        store_hilo(kh + p, kh + C * D + p, Xs[c][e]);
+      }
+      if (tid < C) {
+        float s2 = 0.f;
+        for (int e = 0; e < D; ++e) s2 += Xs[tid][e] * Xs[tid][e];
+        red[tid] = s2;
+      }
+      for (int idx = tid; idx < C * C; idx += 256) Y2[idx / C][idx % C] = Ys[idx / C][idx % C];
+      __syncthreads();
+      if (tid == 0) {
+        float mx = 0.f;
+        for (int c = 0; c < C; ++c) mx = fmaxf(mx, red[c]);
+        so.kmax[blk] = sqrtf(mx);
       }
     }
     __syncthreads();
   }
 
-  if (qhat_out) {
+  if (SCAN || qhat_out) {
     for (int idx = tid; idx < C * D; idx += 256) {
       int r = idx / D, e = idx % D;
       Xs[r][e] = r < valid ? load_f32(q + base + (t0 + r) * D + e) : 0.f;
@@ -131,6 +180,22 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       Gs[r][t] = z;
     }
     __syncthreads();
+    if constexpr (SCAN) {
+      // In-block logits, c <= r:  k_c^T H_{c+1} ... H_r q_r
+      //   = k_c . q_r - sum_b Y[c][b] A[r][b]   (Y from the key pass, b in (c, r])
+      float* sd = so.sdiag + (bh * Nb + n) * (C * C);
+      for (int idx = tid; idx < C * C; idx += 256) {
+        int r = idx / C, c = idx % C;
+        float x = 0.f;
+        if (c <= r && r < valid) {
+          const T* kc = k + base + (t0 + c) * D;
+          for (int e = 0; e < D; ++e) x += load_f32(kc + e) * Xs[r][e];
+          for (int b = c + 1; b <= r; ++b) x -= Y2[c][b] * Gs[r][b];
+          x *= so.c2;
+        }
+        sd[idx] = x;
+      }
+    }
     // Y[r][a] = sum_t T^{-1}[a][t] A[r][t]   (= (T^{-1} a_r)_a, nonzero for a <= r)
     for (int idx = tid; idx < C * C; idx += 256) {
       int r = idx / C, a = idx % C;
@@ -141,16 +206,18 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     __syncthreads();
     for (int idx = tid; idx < C * D; idx += 256) {
       int r = idx / D, e = idx % D;
+      float x = 0.f;
       if (r < valid) {
-        float x = Xs[r][e];
+        x = Xs[r][e];
         for (int a = 0; a <= r; ++a) x -= Ys[r][a] * Ws[a][e];
-        qhat_out[base + (t0 + r) * D + e] = x;
+        if (!SCAN) qhat_out[base + (t0 + r) * D + e] = x;
       }
+      if (SCAN) so.qhat[(bh * Nb * C + t0 + r) * D + e] = so.c2 * x;
     }
     __syncthreads();
   }
 
-  if (pT_out) {
+  if (SCAN || pT_out) {
     // F[s][e] = sum_t T^{-1}[t][s] W[t][e]   (F = T^{-T} W)
     for (int idx = tid; idx < C * D; idx += 256) {
       int s = idx / D, e = idx % D;
@@ -159,12 +226,24 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       Xs[s][e] = f;
     }
     __syncthreads();
-    float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
-    for (int idx = tid; idx < D * D; idx += 256) {
-      int a = idx / D, b = idx % D;
-      float x = (a == b) ? 1.f : 0.f;
-      for (int s = 0; s < C; ++s) x -= Ws[s][a] * Xs[s][b];
-      dst[idx] = x;
+    if constexpr (SCAN) {
+      // P[a][b] = (P^T)[b][a], stored as rows a with permuted columns
+      _Float16* pm = so.pmat + (bh * Nb + n) * (2 * D * D);
+      for (int idx = tid; idx < D * D; idx += 256) {
+        int a = idx / D, b = idx % D;
+        float x = (a == b) ? 1.f : 0.f;
+        for (int s = 0; s < C; ++s) x -= Ws[s][b] * Xs[s][a];
+        const int p = a * D + mfma_perm(b);
+        store_hilo(pm + p, pm + D * D + p, x);
+      }
+    } else {
+      float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
+      for (int idx = tid; idx < D * D; idx += 256) {
+        int a = idx / D, b = idx % D;
+        float x = (a == b) ? 1.f : 0.f;
+        for (int s = 0; s < C; ++s) x -= Ws[s][a] * Xs[s][b];
+        dst[idx] = x;
+      }
     }
   }
 }
@@ -200,16 +279,93 @@ __global__ __launch_bounds__(256) void prefix_sum_kernel(int64_t L, const float*
   }
 }
 
+// One workgroup per (b,h): the largest adjusted-key norm over all blocks, and
+// (with forget gates) the fp64-accumulated prefix sum of log f times `mult`,
+// padded to Nb*64 entries by repeating the last value.
+__global__ __launch_bounds__(256) void head_reduce_kernel(int64_t L, int Nb, const float* __restrict__ kmax,
+                                                          float* __restrict__ kmax_head,
+                                                          const float* __restrict__ x, float mult,
+                                                          float* __restrict__ c) {
+  __shared__ double part[256];
+  __shared__ float mx[256];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  float m = 0.f;
+  for (int n = tid; n < Nb; n += 256) m = fmaxf(m, kmax[bh * Nb + n]);
+  mx[tid] = m;
+  const int64_t Lp = static_cast<int64_t>(Nb) * kBlk;
+  const int64_t per = (L + 255) / 256;
+  const int64_t lo = tid * per;
+  const int64_t hi = lo + per < L ? lo + per : L;
+  double acc = 0.0;
+  if (x) {
+    for (int64_t i = lo; i < hi; ++i) acc += static_cast<double>(x[bh * L + i]);
+  }
+  part[tid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    float mm = 0.f;
+    for (int t = 0; t < 256; ++t) mm = fmaxf(mm, mx[t]);
+    kmax_head[bh] = mm;
+    double run = 0.0;
+    for (int t = 0; t < 256; ++t) {
+      double v = part[t];
+      part[t] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  if (!x) return;
+  double run = part[tid];
+  float* cs = c + bh * Lp;
+  for (int64_t i = lo; i < hi; ++i) {
+    run += static_cast<double>(x[bh * L + i]);
+    cs[i] = static_cast<float>(run * mult);
+  }
+  __syncthreads();
+  const float last = cs[L - 1];
+  for (int64_t i = L + tid; i < Lp; i += 256) cs[i] = last;
+}
+
+hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head,
+                              const float* log_forget, float mult, float* cum, hipStream_t stream) {
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL(head_reduce_kernel, dim3(static_cast<unsigned>(BH)), dim3(256), 0, stream, L, Nb,
+                     kmax, kmax_head, log_forget, mult, cum);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_prepare_t(int64_t B, int64_t H, int64_t L, const void* q, const void* k,
                                    const void* w, const float* beta, float* tinv, float* qhat,
                                    float* khat, float* pT, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   dim3 grid(static_cast<unsigned>(B * H * Nb));
-  hipLaunchKernelGGL((prepare_f32_kernel<T, D>), grid, dim3(256), 0, stream, L, Nb,
+  hipLaunchKernelGGL((prepare_f32_kernel<T, D, false>), grid, dim3(256), 0, stream, L, Nb,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(w),
-                     beta, tinv, qhat, khat, pT);
+                     beta, tinv, qhat, khat, pT, ScanOut{});
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prepare_scan_t(int64_t B, int64_t H, int64_t L, const void* q,
+                                        const void* k, const void* w, const float* beta,
+                                        const ScanOut& so, hipStream_t stream) {
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  dim3 grid(static_cast<unsigned>(B * H * Nb));
+  hipLaunchKernelGGL((prepare_f32_kernel<bf16_t, D, true>), grid, dim3(256), 0, stream, L, Nb,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(w), beta, nullptr, nullptr, nullptr, nullptr, so);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_scan(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
+                               const void* k, const void* w, const float* beta, _Float16* khat,
+                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               hipStream_t stream) {
+  ScanOut so{khat, pmat, qhat, sdiag, kmax, c2};
+  return d == 64 ? launch_prepare_scan_t<64>(B, H, L, q, k, w, beta, so, stream)
+                 : launch_prepare_scan_t<128>(B, H, L, q, k, w, beta, so, stream);
 }
 
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,

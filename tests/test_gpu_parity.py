@@ -57,6 +57,13 @@ def test_fwd_small(dtype, L, d):
     _fwd_case(1, 2, L, d, dtype, 1.0, seed=L * 7 + d)
 
 
+@pytest.mark.parametrize("L", [129, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("fox", [False, True])
+def test_fwd_bf16_accurate(L, d, fox):
+    _fwd_case(1, 3, L, d, "bf16", 1.0, seed=L + d + fox, fox=fox, precision="accurate")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_fwd_fox(dtype, d):
