@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libpath_attn.so")
-SOURCES = ["api.cpp", "prepare.hip", "fwd_scan.hip", "fwd_mfma.hip", "decode.hip"]
+SOURCES = ["api.cpp", "prepare.hip", "fwd_scan.hip", "fwd_mfma.hip", "prepare_mfma.hip", "decode.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

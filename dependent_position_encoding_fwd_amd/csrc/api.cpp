@@ -178,7 +178,7 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
     return st;
   }
   float* kmax = reinterpret_cast<float*>(ws + a.lay.kmax);
-  st = hip_status(path::launch_prepare_scan(
+  st = hip_status(path::launch_prepare_mfma(
       B, H, L, d, scale * kLog2e, q, k, w, beta, reinterpret_cast<_Float16*>(ws + a.lay.khl),
       reinterpret_cast<_Float16*>(ws + a.lay.pmat), reinterpret_cast<float*>(ws + a.lay.qhat),
       reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, stream));

@@ -22,6 +22,12 @@ hipError_t launch_prepare_scan(int64_t B, int64_t H, int64_t L, int64_t d, float
                                _Float16* pmat, float* qhat, float* sdiag, float* kmax,
                                hipStream_t stream);
 
+// Same outputs as launch_prepare_scan, computed on the matrix cores.
+hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
+                               const void* k, const void* w, const float* beta, _Float16* khat,
+                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               hipStream_t stream);
+
 // Per head: kmax_head = max over blocks of kmax; cum = mult * prefix sum of
 // log_forget (fp64 accumulation, padded to whole blocks) when log_forget != null.
 hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head,

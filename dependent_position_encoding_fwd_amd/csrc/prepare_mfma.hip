@@ -1,0 +1,435 @@
+// Matrix-core prepare stage of the bf16 PaTH forward (gfx950).
+//
+// One workgroup (4 waves) per 64-token block n of one head.  It computes the
+// UT factor of the block [PaTH Attention summary (gist.science 2505.16381),
+// §3 "Representação de Transformação UT"]:
+//     G = W W^T,  X = T^{-1} = (I + diag(beta) strict_upper(G))^{-1} diag(beta)
+// and from it [§3 "Algoritmo Estilo FlashAttention"]:
+//     Z^T  = mask_{a>c}(W K^T)          Y^T = X^T Z^T       (so Y = Z X)
+//     Khat = K - Y W                    (adjusted keys: H_{c+1}..H_63 folded into k_c)
+//     F    = X^T W                      P = I - W^T X W = I - W^T F... stored as P rows
+//     U    = W Q^T,  Ut = mask_{b<=r}(U)
+//     Qhat = Q - F^T Ut                 (adjusted queries: H_0..H_r applied to q_r)
+//     Sdiag^T = K Q^T - Y Ut            (in-block logits k_c^T H_{c+1}..H_r q_r, c <= r)
+// Outputs (per block): Khat and P as fp16 hi/lo rows with the reduction
+// index in mfma_perm order, c2*Qhat and c2*Sdiag in fp32, max |khat_c|.
+//
+// Every product is a 16x16x32 MFMA.  Wave w owns output column tile w (16
+// columns), so the accumulator tile of one product is, after conversion to
+// 16-bit, the B operand of the next one in the same wave.  Products of two
+// stored inputs (bf16) are exact in one pass; a computed fp32 operand is split
+// into fp16 hi + lo and costs two or three passes (hi*hi + hi*lo + lo*hi).
+// T^{-1} comes from a back substitution (last row first) spread over all 256
+// lanes: 4 lanes per column, each summing every fourth term.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace path {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f4 mma(const h8& a, const h8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mmb(const b8& a, const b8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+union H8u {
+  h8 v;
+  h2 p[4];
+  uint4 u;
+};
+
+__device__ __forceinline__ h8 to_h8(const f4& x, const f4& y) {
+  H8u r;
+  r.p[0] = __builtin_convertvector(f2{x[0], x[1]}, h2);
+  r.p[1] = __builtin_convertvector(f2{x[2], x[3]}, h2);
+  r.p[2] = __builtin_convertvector(f2{y[0], y[1]}, h2);
+  r.p[3] = __builtin_convertvector(f2{y[2], y[3]}, h2);
+  return r.v;
+}
+// hi/lo split of 8 fp32 values (two accumulator quads)
+struct HL {
+  h8 hi, lo;
+};
+__device__ __forceinline__ HL split8(const f4& x, const f4& y) {
+  HL r;
+  r.hi = to_h8(x, y);
+  f4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = x[i] - static_cast<float>(r.hi[i]);
+    b[i] = y[i] - static_cast<float>(r.hi[4 + i]);
+  }
+  r.lo = to_h8(a, b);
+  return r;
+}
+
+__device__ __forceinline__ int perm32(int d) {  // mfma_perm of the prepare stage
+  return (d & ~31) | (((d >> 2) & 3) << 3) | (((d >> 4) & 1) << 2) | (d & 3);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+template <int D>
+struct PGeo {
+  static constexpr int C = 64;
+  static constexpr int RP = D + 8;   // pitch (halfs) of input rows (bf16), natural column order
+  static constexpr int TP = 64 + 8;  // pitch of rows with 64 reduction columns (perm order)
+  static constexpr int DT = D / 16;  // head-dim tiles
+  static constexpr int DC = D / 32;  // head-dim K chunks
+  static constexpr int ET = DT / 4;  // head-dim tiles per wave
+};
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void prepare_mfma_kernel(
+    int64_t L, int Nb, float c2, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ w, const float* __restrict__ beta, _Float16* __restrict__ khat,
+    _Float16* __restrict__ pmat, float* __restrict__ qhat, float* __restrict__ sdiag,
+    float* __restrict__ kmax) {
+  using G = PGeo<D>;
+  constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
+
+  // LDS (halfs unless noted).  WK holds W rows then K rows; it is reused for
+  // -F^T rows once the products that read W and K rows are done.
+  __shared__ __attribute__((aligned(16))) uint16_t WK[2 * C * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qb[C * RP];
+  __shared__ __attribute__((aligned(16))) _Float16 Wt[D * TP];      // W^T rows, perm(b)
+  __shared__ __attribute__((aligned(16))) _Float16 XT[2][C * TP];   // X^T rows hi/lo, perm(a)
+  __shared__ __attribute__((aligned(16))) float GY[C * TP];         // G (quarter layout), then -Y rows hi/lo
+  __shared__ float bs[C];
+  __shared__ float kred[4];
+
+  uint16_t* Wb = WK;
+  uint16_t* Kb = WK + C * RP;
+  _Float16* NY = reinterpret_cast<_Float16*>(GY);  // [2][C*TP]
+  _Float16* NFT = reinterpret_cast<_Float16*>(WK); // [2][D*64] (pitch 64, no pad)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int n = blockIdx.x % Nb;
+  const int64_t bh = blockIdx.x / Nb;
+  const int64_t t0 = static_cast<int64_t>(n) * C;
+  const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
+  const int64_t base = (bh * L + t0) * D;
+
+  // ---- load W, K, Q rows (bf16) and W^T (fp16, perm columns) -----------------
+  for (int idx = tid; idx < C * (D / 8); idx += 256) {
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    uint4 wv = make_uint4(0, 0, 0, 0), kv = wv, qv = wv;
+    if (r < valid) {
+      wv = *reinterpret_cast<const uint4*>(w + base + r * D + 8 * c8);
+      kv = *reinterpret_cast<const uint4*>(k + base + r * D + 8 * c8);
+      qv = *reinterpret_cast<const uint4*>(q + base + r * D + 8 * c8);
+    }
+    *reinterpret_cast<uint4*>(Wb + r * RP + 8 * c8) = wv;
+    *reinterpret_cast<uint4*>(Kb + r * RP + 8 * c8) = kv;
+    *reinterpret_cast<uint4*>(Qb + r * RP + 8 * c8) = qv;
+    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    const int pb = perm32(r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Wt[(8 * c8 + 2 * e) * TP + pb] = static_cast<_Float16>(__uint_as_float(ww[e] << 16));
+      Wt[(8 * c8 + 2 * e + 1) * TP + pb] = static_cast<_Float16>(__uint_as_float(ww[e] & 0xffff0000u));
+    }
+  }
+  if (tid < C) bs[tid] = tid < valid ? beta[bh * L + t0 + tid] : 0.f;
+  __syncthreads();
+
+  // ---- products of stored inputs (exact, one bf16 pass); wave w = column tile w
+  f4 gt[4], zt[4], ut[4], skq[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) gt[mt] = zt[mt] = ut[mt] = skq[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    const int col = 32 * c + 8 * lg;
+    const b8 bw = *reinterpret_cast<const b8*>(Wb + (16 * wave + ln) * RP + col);
+    const b8 bk = *reinterpret_cast<const b8*>(Kb + (16 * wave + ln) * RP + col);
+    const b8 bq = *reinterpret_cast<const b8*>(Qb + (16 * wave + ln) * RP + col);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const b8 aw = *reinterpret_cast<const b8*>(Wb + (16 * mt + ln) * RP + col);
+      const b8 ak = *reinterpret_cast<const b8*>(Kb + (16 * mt + ln) * RP + col);
+      gt[mt] = mmb(aw, bw, gt[mt]);    // G[s][t]      = w_s . w_t
+      zt[mt] = mmb(aw, bk, zt[mt]);    // Z^T[a][c]    = w_a . k_c
+      ut[mt] = mmb(aw, bq, ut[mt]);    // U[b][r]      = w_b . q_r
+      skq[mt] = mmb(ak, bq, skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
+    }
+  }
+  // G (strict upper) into the quarter layout GY[r*64 + q*16 + u] = G[r][4u+q]
+  {
+    const int t = 16 * wave + ln;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * lg + i;
+        GY[r * 64 + (t & 3) * 16 + (t >> 2)] = (t > r) ? gt[mt][i] : 0.f;
+      }
+  }
+  __syncthreads();
+
+  // ---- X = T^{-1}: back substitution, 4 lanes per column --------------------------
+  {
+    const int c = 16 * wave + (lane >> 2);
+    const int qq = lane & 3;
+    float xr[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) xr[u] = 0.f;
+#pragma unroll
+    for (int r = C - 1; r >= 0; --r) {
+      constexpr int dummy = 0;
+      (void)dummy;
+      const int u0 = r >= 3 ? (r - 3) / 4 + 1 : 0;
+      const float* grow = GY + r * 64 + qq * 16;
+      float part = 0.f;
+#pragma unroll
+      for (int u = u0; u < 16; ++u) part += grow[u] * xr[u];
+      part += dpp_xor1(part);
+      part += dpp_xor2(part);
+      float x = bs[r] * ((r == c ? 1.f : 0.f) - part);
+      x = (r <= c) ? x : 0.f;
+      if (qq == (r & 3)) xr[r >> 2] = x;
+    }
+    // X^T rows: XT[c][perm(a)] = X[a][c], a = 4u + qq
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int a = 4 * u + qq;
+      const _Float16 hi = static_cast<_Float16>(xr[u]);
+      XT[0][c * TP + perm32(a)] = hi;
+      XT[1][c * TP + perm32(a)] = static_cast<_Float16>(xr[u] - static_cast<float>(hi));
+    }
+  }
+  __syncthreads();  // XT ready; G no longer needed (GY becomes -Y)
+
+  // ---- Y^T = X^T Z^T (wave w: columns c in tile w) ------------------------------
+  f4 yt[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) yt[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  {
+    // mask Z^T to a > c (a = row, c = column)
+    const int cc = 16 * wave + ln;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * mt + 4 * lg + i <= cc) zt[mt][i] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const HL b = split8(zt[2 * kc], zt[2 * kc + 1]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
+        const h8 ah = *reinterpret_cast<const h8*>(&XT[0][off]);
+        const h8 al = *reinterpret_cast<const h8*>(&XT[1][off]);
+        yt[mt] = mma(al, b.hi, yt[mt]);
+        yt[mt] = mma(ah, b.lo, yt[mt]);
+        yt[mt] = mma(ah, b.hi, yt[mt]);
+      }
+    }
+  }
+  // -Y rows into NY: lane holds Y^T[b = 16mt+4lg+i][c] = Y[c][b]
+  HL yb[2];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    yb[kc] = split8(yt[2 * kc], yt[2 * kc + 1]);
+    const int off = (16 * wave + ln) * TP + 32 * kc + 8 * lg;
+    *reinterpret_cast<h8*>(&NY[off]) = -yb[kc].hi;
+    *reinterpret_cast<h8*>(&NY[C * TP + off]) = -yb[kc].lo;
+  }
+
+  // ---- Khat^T = K^T - W^T Y^T (rows e, columns c in tile w) -----------------------
+  {
+    const int cc = 16 * wave + ln;
+    float s2 = 0.f;
+#pragma unroll
+    for (int et = 0; et < DT; ++et) {
+      f4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = -bf2f(Kb[cc * RP + 16 * et + 4 * lg + i]);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const h8 a = *reinterpret_cast<const h8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
+        acc = mma(a, yb[kc].lo, acc);
+        acc = mma(a, yb[kc].hi, acc);
+      }
+      acc = -acc;  // Khat[c][e], e = 16et + 4lg + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s2 += acc[i] * acc[i];
+      const f4 x = acc;
+      // store as rows c with perm columns: e = 32(et/2) + 16(et%2) + 4lg + i -> 32(et/2) + 8lg + 4(et%2) + i
+      _Float16* dst = khat + (bh * Nb + n) * (2 * C * D) + cc * D + 32 * (et / 2) + 8 * lg + 4 * (et % 2);
+      const H8u hv = {to_h8(x, x)};
+      f4 lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo[i] = x[i] - static_cast<float>(hv.v[i]);
+      const H8u lv = {to_h8(lo, lo)};
+      *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
+      *reinterpret_cast<uint2*>(dst + C * D) = make_uint2(lv.u.x, lv.u.y);
+    }
+    s2 += __shfl_xor(s2, 16, 64);
+    s2 += __shfl_xor(s2, 32, 64);
+    s2 = wave_max(s2);
+    if (lane == 0) kred[wave] = s2;
+  }
+
+  // ---- F = X^T W (rows b, columns e) and P^T = I - W^T F ---------------------------
+  // wave w owns head-dim column tiles et = ET*w .. ET*w + ET - 1
+  __syncthreads();  // all waves are done with Kb and Wb (WK becomes -F^T rows)
+#pragma unroll
+  for (int j = 0; j < ET; ++j) {
+    const int et = ET * wave + j;
+    f4 ft[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) ft[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const h8 bwt = *reinterpret_cast<const h8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
+        const h8 ah = *reinterpret_cast<const h8*>(&XT[0][off]);
+        const h8 al = *reinterpret_cast<const h8*>(&XT[1][off]);
+        ft[mt] = mma(al, bwt, ft[mt]);
+        ft[mt] = mma(ah, bwt, ft[mt]);
+      }
+    }
+    // lane holds F[b = 16mt+4lg+i][e = 16et+ln] = F^T[e][b] -> -F^T rows (pitch 64, perm b)
+    HL fb[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      fb[kc] = split8(ft[2 * kc], ft[2 * kc + 1]);
+      const int off = (16 * et + ln) * 64 + 32 * kc + 8 * lg;
+      *reinterpret_cast<h8*>(&NFT[off]) = -fb[kc].hi;
+      *reinterpret_cast<h8*>(&NFT[D * 64 + off]) = -fb[kc].lo;
+    }
+    // P^T[f][e] = delta - sum_b W^T[f][b] F[b][e]; stored as P rows e, perm(f)
+    const int e = 16 * et + ln;
+    _Float16* prow = pmat + (bh * Nb + n) * (2 * D * D) + e * D;
+#pragma unroll
+    for (int ft2 = 0; ft2 < DT; ++ft2) {
+      f4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = (16 * ft2 + 4 * lg + i == e) ? -1.f : 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const h8 a = *reinterpret_cast<const h8*>(&Wt[(16 * ft2 + ln) * TP + 32 * kc + 8 * lg]);
+        acc = mma(a, fb[kc].lo, acc);
+        acc = mma(a, fb[kc].hi, acc);
+      }
+      acc = -acc;
+      const H8u hv = {to_h8(acc, acc)};
+      f4 lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo[i] = acc[i] - static_cast<float>(hv.v[i]);
+      const H8u lv = {to_h8(lo, lo)};
+      _Float16* dst = prow + 32 * (ft2 / 2) + 8 * lg + 4 * (ft2 % 2);
+      *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
+      *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lv.u.x, lv.u.y);
+    }
+  }
+  __syncthreads();  // -Y and -F^T rows complete
+
+  if (tid == 0) {
+    const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
+    kmax[bh * Nb + n] = sqrtf(mx);
+  }
+
+  // ---- in-block logits and adjusted queries (wave w: queries r in tile w) -------
+  {
+    const int r = 16 * wave + ln;
+    // Ut = mask_{b <= r}(U)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * mt + 4 * lg + i > r) ut[mt][i] = 0.f;
+    HL ub[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) ub[kc] = split8(ut[2 * kc], ut[2 * kc + 1]);
+
+    // Sdiag^T[c][r] = (K Q^T)[c][r] - sum_b Y[c][b] Ut[b][r]
+    float* sd = sdiag + (bh * Nb + n) * (C * C);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f4 acc = skq[mt];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
+        const h8 ah = *reinterpret_cast<const h8*>(&NY[off]);
+        const h8 al = *reinterpret_cast<const h8*>(&NY[C * TP + off]);
+        acc = mma(al, ub[kc].hi, acc);
+        acc = mma(ah, ub[kc].lo, acc);
+        acc = mma(ah, ub[kc].hi, acc);
+      }
+      f4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * mt + 4 * lg + i;
+        out[i] = (c <= r && r < valid) ? c2 * acc[i] : 0.f;
+      }
+      *reinterpret_cast<f4*>(sd + r * C + 16 * mt + 4 * lg) = out;
+    }
+
+    // Qhat^T[e][r] = Q^T[e][r] - sum_b F^T[e][b] Ut[b][r]
+    float* qd = qhat + ((bh * Nb + n) * C + r) * D;
+#pragma unroll
+    for (int et = 0; et < DT; ++et) {
+      f4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = bf2f(Qb[r * RP + 16 * et + 4 * lg + i]);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int off = (16 * et + ln) * 64 + 32 * kc + 8 * lg;
+        const h8 ah = *reinterpret_cast<const h8*>(&NFT[off]);
+        const h8 al = *reinterpret_cast<const h8*>(&NFT[D * 64 + off]);
+        acc = mma(al, ub[kc].hi, acc);
+        acc = mma(ah, ub[kc].lo, acc);
+        acc = mma(ah, ub[kc].hi, acc);
+      }
+      *reinterpret_cast<f4*>(qd + 16 * et + 4 * lg) = (r < valid) ? acc * c2 : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_prepare_mfma_t(int64_t BH, int64_t L, float c2, const void* q, const void* k,
+                                        const void* w, const float* beta, _Float16* khat,
+                                        _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                                        hipStream_t stream) {
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL((prepare_mfma_kernel<D>), dim3(static_cast<unsigned>(BH * Nb)), dim3(256), 0, stream,
+                     L, Nb, c2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(w), beta, khat, pmat, qhat, sdiag, kmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
+                               const void* k, const void* w, const float* beta, _Float16* khat,
+                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               hipStream_t stream) {
+  return d == 64 ? launch_prepare_mfma_t<64>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, stream)
+                 : launch_prepare_mfma_t<128>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, stream);
+}
+
+}  // namespace path
