@@ -57,7 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // inputs: the matrix-core layout written by the prepare stage.
 struct FwdWs {
   size_t khat, pT, cum;                       // fp32 path
-  size_t khl, pmat, qhat, sdiag, kmax, kmaxh;  // bf16 path (cum shared)
+  size_t khl, pmat, qhat, sdiag, kmax, kmaxh, pnorm;  // bf16 path (cum shared)
   size_t total;
 };
 
@@ -81,6 +81,7 @@ FwdWs fwd_layout(int dtype, int64_t BH, int64_t L, int64_t d, int64_t Nb, bool w
     w.sdiag = take(sizeof(float) * bh * nb * size_t(kBlk) * size_t(kBlk));
     w.kmax = take(sizeof(float) * bh * nb);
     w.kmaxh = take(sizeof(float) * bh);
+    w.pnorm = take(sizeof(float) * bh * nb);
     if (with_forget) w.cum = take(sizeof(float) * bh * lp);
   }
   w.total = off;
@@ -181,7 +182,8 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
   st = hip_status(path::launch_prepare_mfma(
       B, H, L, d, scale * kLog2e, q, k, w, beta, reinterpret_cast<_Float16*>(ws + a.lay.khl),
       reinterpret_cast<_Float16*>(ws + a.lay.pmat), reinterpret_cast<float*>(ws + a.lay.qhat),
-      reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, stream));
+      reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, reinterpret_cast<float*>(ws + a.lay.pnorm),
+      stream));
   if (st) return st;
   return hip_status(path::launch_head_reduce(
       a.BH, L, kmax, reinterpret_cast<float*>(ws + a.lay.kmaxh), log_forget, kLog2e,
@@ -206,7 +208,8 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
       reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
       reinterpret_cast<const float*>(ws + a.lay.qhat),
       reinterpret_cast<const float*>(ws + a.lay.sdiag),
-      reinterpret_cast<const float*>(ws + a.lay.kmaxh), cum, o, lse, stream));
+      reinterpret_cast<const float*>(ws + a.lay.kmaxh),
+      reinterpret_cast<const float*>(ws + a.lay.pnorm), cum, o, lse, stream));
 }
 
 }  // namespace

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     int64_t L, int Nb, float c2, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ w, const float* __restrict__ beta, _Float16* __restrict__ khat,
     _Float16* __restrict__ pmat, float* __restrict__ qhat, float* __restrict__ sdiag,
-    float* __restrict__ kmax) {
+    float* __restrict__ kmax, float* __restrict__ pnorm) {
   using G = PGeo<D>;
   constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
 
@@ -115,6 +115,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   __shared__ __attribute__((aligned(16))) _Float16 XT[2][C * TP];   // X^T rows hi/lo, perm(a)
   __shared__ __attribute__((aligned(16))) float GY[C * TP];         // G (quarter layout), then -Y rows hi/lo
   __shared__ float bs[C];
+  __shared__ float hn[C];
   __shared__ float kred[4];
 
   uint16_t* Wb = WK;
@@ -155,6 +156,16 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   }
   if (tid < C) bs[tid] = tid < valid ? beta[bh * L + t0 + tid] : 0.f;
   __syncthreads();
+  // |H_s|_2 = max(1, |1 - beta_s |w_s|^2|): its product bounds the growth of a
+  // transported query across the block
+  if (tid < C) {
+    float ww = 0.f;
+    for (int e = 0; e < D; ++e) {
+      const float x = bf2f(Wb[tid * RP + e]);
+      ww += x * x;
+    }
+    hn[tid] = fmaxf(1.f, fabsf(1.f - bs[tid] * ww));
+  }
 
   // ---- products of stored inputs (exact, one bf16 pass); wave w = column tile w
   f4 gt[4], zt[4], ut[4], skq[4];
@@ -353,6 +364,9 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   if (tid == 0) {
     const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
     kmax[bh * Nb + n] = sqrtf(mx);
+    float g = 1.f;
+    for (int t = 0; t < C; ++t) g *= hn[t];
+    pnorm[bh * Nb + n] = g;
   }
 
   // ---- in-block logits and adjusted queries (wave w: queries r in tile w) -------
@@ -416,20 +430,22 @@ template <int D>
 static hipError_t launch_prepare_mfma_t(int64_t BH, int64_t L, float c2, const void* q, const void* k,
                                         const void* w, const float* beta, _Float16* khat,
                                         _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                                        hipStream_t stream) {
+                                        float* pnorm, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   hipLaunchKernelGGL((prepare_mfma_kernel<D>), dim3(static_cast<unsigned>(BH * Nb)), dim3(256), 0, stream,
                      L, Nb, c2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(w), beta, khat, pmat, qhat, sdiag, kmax);
+                     static_cast<const uint16_t*>(w), beta, khat, pmat, qhat, sdiag, kmax, pnorm);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
                                const void* k, const void* w, const float* beta, _Float16* khat,
-                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               _Float16* pmat, float* qhat, float* sdiag, float* kmax, float* pnorm,
                                hipStream_t stream) {
-  return d == 64 ? launch_prepare_mfma_t<64>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, stream)
-                 : launch_prepare_mfma_t<128>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, stream);
+  return d == 64 ? launch_prepare_mfma_t<64>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, pnorm,
+                                             stream)
+                 : launch_prepare_mfma_t<128>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, pnorm,
+                                              stream);
 }
 
 }  // namespace path
