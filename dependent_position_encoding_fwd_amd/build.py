@@ -27,6 +27,10 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags (none at present).
+EXTRA = {}
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source (always) and link libpath_attn.so; returns its path."""
     os.makedirs(OUT_DIR, exist_ok=True)
@@ -35,7 +39,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -152,8 +152,19 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   __shared__ float red[2][NW];
 
   const int NP = (Nb + 1) / 2;
-  const int p = NP - 1 - static_cast<int>(blockIdx.x / BH);  // longest tiles first
-  const int64_t bh = blockIdx.x % BH;
+  int p;
+  int64_t bh;
+  if (BH % 8 == 0) {
+    // workgroups go to the 8 XCDs round robin; give XCD x the heads x, x+8, ...
+    // so that the key blocks a head's tiles share stay in one L2, longest tiles first
+    const int xcd = blockIdx.x % 8;
+    const int j = blockIdx.x / 8;
+    p = NP - 1 - (j % NP);
+    bh = xcd + 8 * static_cast<int64_t>(j / NP);
+  } else {
+    p = NP - 1 - static_cast<int>(blockIdx.x / BH);  // longest tiles first
+    bh = blockIdx.x % BH;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -169,6 +180,16 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
 
   // ---- per-wave state ------------------------------------------------------------
   f4 oacc[NCT][DT], lacc[NCT], qf[NCT][DT];
+  h8 qhi[NCT][DC], qlo[NCT][DC];  // Qt as fp16 B operands (lo only when the split is used)
+  auto to_b_operands = [&](bool with_lo) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        qhi[ct][c] = pack_h8(qf[ct][2 * c], qf[ct][2 * c + 1]);
+        if (with_lo) qlo[ct][c] = pack_lo(qf[ct][2 * c], qf[ct][2 * c + 1], qhi[ct][c]);
+      }
+  };
   float mrun[NCT], cq[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -187,7 +208,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   // ---- staging helpers ----------------------------------------------------------
   // registers of the next key block (global -> VGPR prefetch)
   struct Pre {
-    u4 kh[KCH], kl[KCH], ph[PCH], pl[PCH], v[VIT][2];
+    u4 kh[KCH], ph[PCH], v[VIT][2];
     f4 ck[4];
   } pre;
   auto load_v = [&](int n) __attribute__((always_inline)) {
@@ -209,19 +230,12 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
     const int64_t blk = bh * Nb + n;
     const u4* ksrc = reinterpret_cast<const u4*>(khat + blk * (2 * C * D)) + tid;
     const u4* psrc = reinterpret_cast<const u4*>(pmat + blk * (2 * D * D)) + tid;
+    (void)acc;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) pre.kh[j] = ksrc[j * NT];
     if (n > 0) {
 #pragma unroll
       for (int j = 0; j < PCH; ++j) pre.ph[j] = psrc[j * NT];
-    }
-    if (acc) {
-#pragma unroll
-      for (int j = 0; j < KCH; ++j) pre.kl[j] = ksrc[C * D / 8 + j * NT];
-      if (n > 0) {
-#pragma unroll
-        for (int j = 0; j < PCH; ++j) pre.pl[j] = psrc[D * D / 8 + j * NT];
-      }
     }
     load_v(n);
     if constexpr (FOX) {
@@ -264,18 +278,22 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       }
     }
     if (acc) {
+      // lo parts (split-precision blocks only) are fetched here, not prefetched
+      const int64_t blk = bh * Nb + n;
+      const u4* ksrc = reinterpret_cast<const u4*>(khat + blk * (2 * C * D) + C * D) + tid;
 #pragma unroll
       for (int j = 0; j < KCH; ++j) {
         const int idx = tid + j * NT;
         const int r = idx / (D / 8), c8 = idx % (D / 8);
-        *reinterpret_cast<u4*>(&Ks[1][r * KP + 8 * c8]) = pre.kl[j];
+        *reinterpret_cast<u4*>(&Ks[1][r * KP + 8 * c8]) = ksrc[j * NT];
       }
       if (n > 0) {
+        const u4* psrc = reinterpret_cast<const u4*>(pmat + blk * (2 * D * D) + D * D) + tid;
 #pragma unroll
         for (int j = 0; j < PCH; ++j) {
           const int idx = tid + j * NT;
           const int r = idx / (D / 8), c8 = idx % (D / 8);
-          *reinterpret_cast<u4*>(&Ps[1][r * KP + 8 * c8]) = pre.pl[j];
+          *reinterpret_cast<u4*>(&Ps[1][r * KP + 8 * c8]) = psrc[j * NT];
         }
       }
     }
@@ -310,6 +328,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       }
     }
     h8 pb[NCT][2];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f4 pe[4];
@@ -406,6 +425,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   for (int w2 = 0; w2 < NW; ++w2) qbound = fmaxf(qbound, red[0][w2]);
   bool acc_cur = accurate_all || (qbound * khmax * 0.0009765625f > tau);
   load_tile(2 * p, acc_cur);
+  to_b_operands(acc_cur);
 
   // ---- right-to-left scan ----------------------------------------------------------
   for (int n = 2 * p; n >= 0; --n) {
@@ -424,37 +444,39 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
     const bool work = live && !(half == 0 && n == 2 * p);
 
     if (work) {
-      h8 qhi[NCT][DC], qlo[NCT][DC];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          qhi[ct][c] = pack_h8(qf[ct][2 * c], qf[ct][2 * c + 1]);
-          if (acc) qlo[ct][c] = pack_lo(qf[ct][2 * c], qf[ct][2 * c + 1], qhi[ct][c]);
-        }
-      // S^T - m = Khat Qt - m
+      // S^T - m = Khat Qt - m: the first chunk's products start from the seed
+      // quad (-m, or cum_i - m with forget gates); the lo passes come last
       f4 x[NCT][4];
+      f4 seed[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const float seed = (FOX ? cq[ct] : 0.f) - mrun[ct];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) x[ct][kt] = f4{seed, seed, seed, seed};
+        const float sv = (FOX ? cq[ct] : 0.f) - mrun[ct];
+        seed[ct] = f4{sv, sv, sv, sv};
       }
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           const h8 ah = *reinterpret_cast<const h8*>(&Ks[0][(16 * kt + ln) * KP + 32 * c + 8 * lg]);
-          if (acc) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) x[ct][kt] = mma16(ah, qhi[ct][c], c == 0 ? seed[ct] : x[ct][kt]);
+        }
+      }
+      if (acc) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
             const h8 al = *reinterpret_cast<const h8*>(&Ks[1][(16 * kt + ln) * KP + 32 * c + 8 * lg]);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-              x[ct][kt] = mma16(al, qhi[ct][c], x[ct][kt]);
-              x[ct][kt] = mma16(ah, qlo[ct][c], x[ct][kt]);
-            }
+            for (int ct = 0; ct < NCT; ++ct) x[ct][kt] = mma16(al, qhi[ct][c], x[ct][kt]);
           }
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) x[ct][kt] = mma16(ah, qhi[ct][c], x[ct][kt]);
+          for (int kt = 0; kt < 4; ++kt) {
+            const h8 ah = *reinterpret_cast<const h8*>(&Ks[0][(16 * kt + ln) * KP + 32 * c + 8 * lg]);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) x[ct][kt] = mma16(ah, qlo[ct][c], x[ct][kt]);
+          }
         }
       }
       if constexpr (FOX) {
@@ -463,29 +485,37 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= ck[kt];
       }
+      __builtin_amdgcn_sched_barrier(0);
       softmax_pv(x, Vt);
+      __builtin_amdgcn_sched_barrier(0);
 
       if (n > 0) {
-        // Qt <- P_n Qt
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int t = 0; t < DT; ++t) qf[ct][t] = f4{0.f, 0.f, 0.f, 0.f};
+        // Qt <- P_n Qt (first chunk from zero; lo passes last)
+        const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
 #pragma unroll
           for (int t = 0; t < DT; ++t) {
             const h8 ah = *reinterpret_cast<const h8*>(&Ps[0][(16 * t + ln) * KP + 32 * c + 8 * lg]);
-            if (acc) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) qf[ct][t] = mma16(ah, qhi[ct][c], c == 0 ? zero : qf[ct][t]);
+          }
+        }
+        if (acc) {
+#pragma unroll
+          for (int c = 0; c < DC; ++c) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
               const h8 al = *reinterpret_cast<const h8*>(&Ps[1][(16 * t + ln) * KP + 32 * c + 8 * lg]);
 #pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) {
-                qf[ct][t] = mma16(al, qhi[ct][c], qf[ct][t]);
-                qf[ct][t] = mma16(ah, qlo[ct][c], qf[ct][t]);
-              }
+              for (int ct = 0; ct < NCT; ++ct) qf[ct][t] = mma16(al, qhi[ct][c], qf[ct][t]);
             }
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) qf[ct][t] = mma16(ah, qhi[ct][c], qf[ct][t]);
+            for (int t = 0; t < DT; ++t) {
+              const h8 ah = *reinterpret_cast<const h8*>(&Ps[0][(16 * t + ln) * KP + 32 * c + 8 * lg]);
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) qf[ct][t] = mma16(ah, qlo[ct][c], qf[ct][t]);
+            }
           }
         }
       }
@@ -496,6 +526,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       const float qn = (work || !live) ? wave_qnorm() : 0.f;
       if (lane == 0) red[slot][wave] = qn;
     }
+    if (work && n > 0) to_b_operands(acc_next);
     __syncthreads();  // LDS reads of this block are done; norms visible
     if (acc_next && n > 0) {
       float qm = 0.f;
