@@ -20,7 +20,7 @@
 // stored inputs (bf16) are exact in one pass; a computed fp32 operand is split
 // into fp16 hi + lo and costs two or three passes (hi*hi + hi*lo + lo*hi).
 // T^{-1} comes from a back substitution (last row first) spread over all 256
-// lanes: 4 lanes per column, each summing every fourth term.
+// lanes: 4 lanes per column, each keeping the partial sums of every fourth row.
 #include <math.h>
 
 #include "common.h"
@@ -79,11 +79,16 @@ __device__ __forceinline__ int perm32(int d) {  // mfma_perm of the prepare stag
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-__device__ __forceinline__ float dpp_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+
+// Broadcast lane k of each quad of lanes to the whole quad (k folds to a constant).
+__device__ __forceinline__ float quad_bcast(float x, int k) {
+  const int v = __float_as_int(x);
+  switch (k) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false));
+  }
 }
 
 template <int D>
@@ -187,40 +192,42 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       skq[mt] = mmb(ak, bq, skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
     }
   }
-  // G (strict upper) into the quarter layout GY[r*64 + q*16 + u] = G[r][4u+q]
+  // G by columns in the quarter layout GY[t*64 + q*16 + u] = G[4u+q][t] (rows above t only)
   {
     const int t = 16 * wave + ln;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * lg + i;
-        GY[r * 64 + (t & 3) * 16 + (t >> 2)] = (t > r) ? gt[mt][i] : 0.f;
+        const int s = 16 * mt + 4 * lg + i;
+        GY[t * 64 + (s & 3) * 16 + (s >> 2)] = (s < t) ? gt[mt][i] : 0.f;
       }
   }
   __syncthreads();
 
   // ---- X = T^{-1}: back substitution, 4 lanes per column --------------------------
+  // Row r of X (last row first) is X[r][c] = beta_r (delta_rc - acc_r) with
+  // acc_r = sum_{t>r} G[r][t] X[t][c].  Once row r is known it is added into the
+  // partial sums of all rows above it (independent FMAs), so the serial chain
+  // per row is a handful of operations.  Lane (c, qq) keeps acc and X for the
+  // rows r = 4u + qq.
   {
     const int c = 16 * wave + (lane >> 2);
     const int qq = lane & 3;
-    float xr[16];
+    float acc[16], xr[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) xr[u] = 0.f;
+    for (int u = 0; u < 16; ++u) acc[u] = xr[u] = 0.f;
 #pragma unroll
     for (int r = C - 1; r >= 0; --r) {
-      constexpr int dummy = 0;
-      (void)dummy;
-      const int u0 = r >= 3 ? (r - 3) / 4 + 1 : 0;
-      const float* grow = GY + r * 64 + qq * 16;
-      float part = 0.f;
-#pragma unroll
-      for (int u = u0; u < 16; ++u) part += grow[u] * xr[u];
-      part += dpp_xor1(part);
-      part += dpp_xor2(part);
-      float x = bs[r] * ((r == c ? 1.f : 0.f) - part);
+      const int ur = r >> 2;
+      float x = bs[r] * ((r == c ? 1.f : 0.f) - acc[ur]);
       x = (r <= c) ? x : 0.f;
-      if (qq == (r & 3)) xr[r >> 2] = x;
+      // the lane with qq == r % 4 holds the right acc; share its x within the quad
+      x = quad_bcast(x, r & 3);
+      if (qq == (r & 3)) xr[ur] = x;
+      const float* gcol = GY + r * 64 + qq * 16;  // G[4u+qq][r]
+#pragma unroll
+      for (int u = 0; u < (r + 3) / 4; ++u) acc[u] += gcol[u] * x;
     }
     // X^T rows: XT[c][perm(a)] = X[a][c], a = 4u + qq
 #pragma unroll
