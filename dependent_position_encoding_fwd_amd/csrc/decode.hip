@@ -13,6 +13,8 @@
 // lanes cover one row, so a wave touches 1 KiB of contiguous cache per pass.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -21,47 +23,57 @@ namespace path {
 constexpr int kDecThreads = 256;
 constexpr int kDecChunk = 1024;  // keys per workgroup
 
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
-struct Vec16;  // 16 bytes of storage
+struct Vec16;  // 16 bytes of storage, moved as one native 128-bit vector
 template <>
 struct Vec16<bf16_t> {
   static constexpr int N = 8;
-  using raw = uint4;
+  using raw = u4;
   __device__ static void unpack(const raw& x, float* f) {
-    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      f[2 * t] = __uint_as_float(u[t] << 16);
-      f[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+      f[2 * t] = __uint_as_float(x[t] << 16);
+      f[2 * t + 1] = __uint_as_float(x[t] & 0xffff0000u);
     }
   }
   __device__ static raw pack(const float* f) {
-    uint32_t u[4];
+    raw u;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       u[t] = static_cast<uint32_t>(f32_to_bf16(f[2 * t])) |
              (static_cast<uint32_t>(f32_to_bf16(f[2 * t + 1])) << 16);
-    return make_uint4(u[0], u[1], u[2], u[3]);
+    return u;
   }
 };
 template <>
 struct Vec16<float> {
   static constexpr int N = 4;
-  using raw = float4;
+  using raw = u4;
   __device__ static void unpack(const raw& x, float* f) {
-    f[0] = x.x;
-    f[1] = x.y;
-    f[2] = x.z;
-    f[3] = x.w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f[t] = __uint_as_float(x[t]);
   }
-  __device__ static raw pack(const float* f) { return make_float4(f[0], f[1], f[2], f[3]); }
+  __device__ static raw pack(const float* f) {
+    return raw{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  }
 };
 
 // Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+// Groups of up to 16 lanes use DPP lane moves (quad swaps, then mirrors within
+// 8- and 16-lane rows); wider groups fall back to cross-lane permutes.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < G; off <<= 1) x += __shfl_xor(x, off, 64);
+  const auto mv = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if constexpr (G >= 2) x += mv(x, std::integral_constant<int, 0xB1>{});   // lanes i ^ 1
+  if constexpr (G >= 4) x += mv(x, std::integral_constant<int, 0x4E>{});   // lanes i ^ 2
+  if constexpr (G >= 8) x += mv(x, std::integral_constant<int, 0x141>{});  // mirror within 8
+  if constexpr (G >= 16) x += mv(x, std::integral_constant<int, 0x140>{}); // mirror within 16
+  if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
   return x;
 }
 
@@ -76,7 +88,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   constexpr int LPK = D / EPV;       // lanes per key row
   constexpr int KPW = 64 / LPK;      // key rows per wave pass
   constexpr int NW = kDecThreads / 64;
-  constexpr int UNR = 4;             // key rows in flight per lane
+  constexpr int UNR = 8;             // key rows in flight per lane
 
   const int chunk = static_cast<int>(blockIdx.x % nchunks);
   const int64_t bh = blockIdx.x / nchunks;
@@ -97,6 +109,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   for (int e = 0; e < EPV; ++e) wq += wv[e] * qv[e];
   wq = group_sum<LPK>(wq);
   const float bt = beta_t[bh];
+  const float scale2 = scale * 1.4426950408889634f;  // logits in log2 units
 
   const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
   const int64_t j1 = j0 + kDecChunk < cache_len ? j0 + kDecChunk : cache_len;
@@ -115,20 +128,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
+      kr[u] = typename V::raw{0u, 0u, 0u, 0u};
+      vr[u] = kr[u];
       if (j < j1) {
-        kr[u] = kbase[j * LPK + sub];
-        vr[u] = vbase[j * LPK + sub];
+        kr[u] = __builtin_nontemporal_load(&kbase[j * LPK + sub]);
+        vr[u] = __builtin_nontemporal_load(&vbase[j * LPK + sub]);
       }
     }
+    float sv[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
       // Lanes of one key row share j, so the group reductions below see
       // a consistent set of lanes; rows past j1 contribute nothing.
       const bool live = j < j1;
-      float kf[EPV], vf[EPV];
+      float kf[EPV];
       V::unpack(kr[u], kf);
-      V::unpack(vr[u], vf);
       float a = 0.f, b = 0.f;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
@@ -140,18 +155,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       const float ba = bt * a;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) kf[e] -= ba * wv[e];
-      if (live) {
-        kbase[j * LPK + sub] = V::pack(kf);
-        // q . (k - beta a w) from the fp32 updated key
-        const float s = scale * (b - ba * wq);
-        const float mnew = fmaxf(mrun, s);
-        const float alpha = expf(mrun - mnew);
-        const float p = expf(s - mnew);
-        lrun = lrun * alpha + p;
+      if (live) __builtin_nontemporal_store(V::pack(kf), &kbase[j * LPK + sub]);
+      // q . (k - beta a w) from the fp32 updated key, in log2 units
+      sv[u] = live ? scale2 * (b - ba * wq) : -INFINITY;
+    }
+    float mb = sv[0];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] = acc[e] * alpha + p * vf[e];
-        mrun = mnew;
+    for (int u = 1; u < UNR; ++u) mb = fmaxf(mb, sv[u]);
+    const float mnew = fmaxf(mrun, mb);
+    if (mnew != -INFINITY) {
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float p = __builtin_amdgcn_exp2f(sv[u] - mnew);
+        float vf[EPV];
+        V::unpack(vr[u], vf);
+        lrun += p;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += p * vf[e];
       }
+      mrun = mnew;
     }
   }
 
@@ -161,8 +187,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
     const float m2 = __shfl_xor(mrun, off, 64);
     const float l2 = __shfl_xor(lrun, off, 64);
     const float mnew = fmaxf(mrun, m2);
-    const float a1 = (mrun == -INFINITY) ? 0.f : expf(mrun - mnew);
-    const float a2 = (m2 == -INFINITY) ? 0.f : expf(m2 - mnew);
+    const float a1 = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mnew);
+    const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - mnew);
     lrun = lrun * a1 + l2 * a2;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
@@ -192,7 +218,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
     float ll = 0.f, oo = 0.f;
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
-      const float a = (sm[t] == -INFINITY) ? 0.f : expf(sm[t] - mm);
+      const float a = (sm[t] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[t] - mm);
       ll += sl[t] * a;
       oo += sacc[t][threadIdx.x] * a;
     }
@@ -226,19 +252,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   float s = 0.f;
 #pragma unroll
   for (int t = 0; t < PER; ++t) s += qf[t] * kf[t];
-  s = scale * wave_sum(s);
+  s = scale * 1.4426950408889634f * wave_sum(s);  // log2 units, like the partials
 
   float mm = s;
   const float* pb = partials + bh * nchunks * (D + 2);
   for (int c = 0; c < nchunks; ++c) mm = fmaxf(mm, pb[c * (D + 2)]);
-  const float es = expf(s - mm);
+  const float es = __builtin_amdgcn_exp2f(s - mm);
   float ll = es;
   float oo[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) oo[t] = es * vf[t];
   for (int c = 0; c < nchunks; ++c) {
     const float* p = pb + c * (D + 2);
-    const float a = expf(p[0] - mm);
+    const float a = __builtin_amdgcn_exp2f(p[0] - mm);
     ll += a * p[1];
 #pragma unroll
     for (int t = 0; t < PER; ++t) oo[t] += a * p[2 + lane + 64 * t];
@@ -251,7 +277,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     k_cache[(bh * capacity + cache_len) * D + e] = k_t[bh * D + e];
     v_cache[(bh * capacity + cache_len) * D + e] = v_t[bh * D + e];
   }
-  if (lane == 0) lse[bh] = mm + logf(ll);
+  if (lane == 0) lse[bh] = (mm + __log2f(ll)) * 0.69314718055994531f;
 }
 
 int64_t decode_num_chunks(int64_t cache_len) { return (cache_len + kDecChunk - 1) / kDecChunk; }

@@ -12,8 +12,8 @@
 //                                     running max m enters as the accumulator seed)
 //     online softmax over keys       (exp2; the max is only raised when a logit
 //                                     exceeds it by more than kTheta)
-//     O^T += V_n^T P^T, l += 1^T P^T (16x16x32 f16 MFMA; a row of ones gives the
-//                                     softmax denominator)
+//     O^T += V_n^T P^T               (16x16x32 f16 MFMA; the softmax denominator
+//                                     is summed in fp32 from the unrounded exp2)
 //     Qt   = P_n Qt                  (block transition P_n = H_0...H_63, f16 MFMA)
 // [§2 "Extensões: PaTH-FoX"] adds cum_i - cum_j (log2 units) to each logit.
 //
@@ -33,9 +33,7 @@
 //     max|Qt| * max|khat| * 2^-10     (log2-logit units)
 // is at most `tau`, where max|Qt| is measured while the split is in use and
 // afterwards carried forward with the per-block bound |P_n|_2 <= pnorm_n.
-// Probabilities (<= 2^kTheta) and values meet in fp16 (fp32 accumulate); the
-// denominator is summed from the same rounded probabilities, each within 2^-11
-// relative of its fp32 value, so lse stays within 2^-11 of the exact log-sum.
+// Probabilities (<= 2^kTheta) and values meet in fp16 (fp32 accumulate).
 #include <math.h>
 
 #include "common.h"
@@ -179,7 +177,8 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   const float* cumh = FOX ? cum + bh * Nb * C : nullptr;
 
   // ---- per-wave state ------------------------------------------------------------
-  f4 oacc[NCT][DT], lacc[NCT], qf[NCT][DT];
+  f4 oacc[NCT][DT], qf[NCT][DT];
+  float lsum[NCT];  // per-lane partial softmax denominators (fp32)
   h8 qhi[NCT][DC], qlo[NCT][DC];  // Qt as fp16 B operands (lo only when the split is used)
   auto to_b_operands = [&](bool with_lo) __attribute__((always_inline)) {
 #pragma unroll
@@ -193,16 +192,10 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   float mrun[NCT], cq[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    lacc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+    lsum[ct] = 0.f;
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[ct][t] = f4{0.f, 0.f, 0.f, 0.f};
     cq[ct] = (FOX && live) ? cumh[mb * C + r0 + 16 * ct + ln] : 0.f;
-  }
-  // A operand of the ones row: row 0 of a 16-row tile is 1, rows 1..15 are 0
-  h8 ones;
-  {
-    const _Float16 one = (ln == 0) ? static_cast<_Float16>(1.f) : static_cast<_Float16>(0.f);
-    ones = h8{one, one, one, one, one, one, one, one};
   }
 
   // ---- staging helpers ----------------------------------------------------------
@@ -320,7 +313,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
         const float sh = fmaxf(mx[ct], 0.f);
         const float alpha = __builtin_amdgcn_exp2f(-sh);
         mrun[ct] += sh;
-        lacc[ct] *= alpha;
+        lsum[ct] *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[ct][t] *= alpha;
 #pragma unroll
@@ -336,13 +329,13 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pe[kt][i] = __builtin_amdgcn_exp2f(x[ct][kt][i]);
+      lsum[ct] += ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3])) +
+                  ((pe[2][0] + pe[2][1]) + (pe[2][2] + pe[2][3])) + ((pe[3][0] + pe[3][1]) + (pe[3][2] + pe[3][3]));
       pb[ct][0] = pack_h8(pe[0], pe[1]);
       pb[ct][1] = pack_h8(pe[2], pe[3]);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) lacc[ct] = mma16(ones, pb[ct][c], lacc[ct]);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const h8 a = *reinterpret_cast<const h8*>(&vt[(16 * t + ln) * VP + 32 * c + 8 * lg]);
@@ -479,16 +472,8 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
           }
         }
       }
-      if constexpr (FOX) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= ck[kt];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      softmax_pv(x, Vt);
-      __builtin_amdgcn_sched_barrier(0);
-
+      // the transition of Qt needs neither the softmax nor PV: issue it first so
+      // that its products overlap the softmax arithmetic
       if (n > 0) {
         // Qt <- P_n Qt (first chunk from zero; lo passes last)
         const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
@@ -519,6 +504,13 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
           }
         }
       }
+      if constexpr (FOX) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= ck[kt];
+      }
+      softmax_pv(x, Vt);
     }
     // measured norms while the split is in use; the carried bound otherwise
     const int slot = n & 1;
@@ -546,7 +538,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   if (live) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float l = grp_sum(lacc[ct][0] + lacc[ct][1] + lacc[ct][2] + lacc[ct][3]);
+      const float l = grp_sum(lsum[ct]);
       const int r = r0 + 16 * ct + ln;
       const int64_t row = static_cast<int64_t>(mb) * C + r;
       if (row < L64) {
