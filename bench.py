@@ -1,32 +1,58 @@
 """Benchmark of the PaTH attention hot path on one MI355X.
 
-One step = one PaTH forward on the L=4096 workload (B=8, H=16, d=64, bf16,
-scale 1/sqrt(d): block prepare + right-to-left scan) followed by one decode
-step on the cache-8192 workload (B=64, H=16, d=64, bf16).  Inputs are seeded
-synthetic tensors already resident in HBM when timing starts.
+One step = one PaTH forward on the L=4096 workload (B=8, H=16, d=64, bf16
+storage, scale 1/8: block prepare + right-to-left scan) followed by one
+decode step on the cache-8192 workload (B=64, H=16, d=64, bf16).  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts; there is
+no cache flush between steps.  Decode steps keep mutating the same cache
+(each one applies a new transition to every cached key), which leaves the
+amount of work unchanged.
 
 Printed: ONE JSON line.  `value` is the forward throughput in TFLOP/s under
-the stated FLOP model F = sum_(b,h) (2 d L^2 + d^2 L^2 / 64) (QK^T and PV over
-the causal half, plus the Householder block transport); decode bandwidth is
-reported in `decode`.  Per-kernel durations come from HIP events recorded on
-the stream the kernels run on (torch's current stream).
+the FLOP model F = sum over (b,h) of (2 d L^2 + d^2 L^2 / 64): QK^T and PV
+over the causal half plus the Householder block transport of the query
+state; the prepare stage is timed but earns no FLOPs.  Decode bandwidth is
+reported in `decode` on 3 x B H n d x 2 bytes (keys read and written, values
+read).  Per-kernel durations come from HIP events recorded on the stream the
+kernels are launched on (torch's current stream, which the binding passes to
+every launch); the median over the timed steps is reported.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+`roofline` describes the dominant kernel, the matrix-core scan: achieved =
+F / scan duration against the 2.5 PFLOP/s dense fp16/bf16 matrix peak.  Its
+`traffic` (HBM bytes per launch) comes from the rocprofv3 counter summary
+profiles/hbm_traffic.json and is reported only while the kernel's source
+still hashes to the value recorded there; the decode kernel's traffic is
+reported the same way.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-ref]
+
+`--copy-ref` first runs a plain 1 GiB device copy, whose FETCH_SIZE and
+WRITE_SIZE counters calibrate those of the other kernels in a rocprofv3
+--pmc run of this script.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 matrix peak
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak
+PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "scan": ("dependent_position_encoding_fwd_amd/csrc/fwd_mfma.hip",
+             "dependent_position_encoding_fwd_amd/csrc/common.h"),
+    "decode": ("dependent_position_encoding_fwd_amd/csrc/decode.hip",
+               "dependent_position_encoding_fwd_amd/csrc/common.h"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COPY_REF_BYTES = 1 << 30
 
 
 def flops_path(B, H, L, d):
@@ -37,20 +63,42 @@ def decode_bytes(B, H, n, d, esize):
     return B * H * n * d * esize * 3.0  # K read + K write + V read
 
 
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(kind: str):
+    """HBM bytes per launch of one kernel ("scan" or "decode") from the
+    committed counter summary, or None when there is none or the kernel's
+    source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(kind, {})
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash(kind):
+        return None
+    return t.get("bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--precision", default="auto", choices=["auto", "accurate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (got --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import dependent_position_encoding_fwd_amd as pa
@@ -69,6 +117,15 @@ def main():
     dws = torch.empty(max(256, pa.decode_workspace_bytes(cd.B, cd.H, cd.d, cd.cache_len)), dtype=torch.uint8,
                       device=dev)
 
+    if args.copy_ref:
+        src = torch.ones(COPY_REF_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy reference: {COPY_REF_BYTES} bytes read, {COPY_REF_BYTES} bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
@@ -85,7 +142,6 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -93,9 +149,10 @@ def main():
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    print(f"[bench] {args.steps} timed steps done in {wall:.3f} s", file=sys.stderr, flush=True)
+    prep_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    scan_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evs)
+    dec_ms = statistics.median(e[2].elapsed_time(e[3]) for e in evs)
     fwd_ms = prep_ms + scan_ms
     F = flops_path(cf.B, cf.H, cf.L, cf.d)
     tflops = F / (fwd_ms * 1e-3) / 1e12
@@ -103,18 +160,11 @@ def main():
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
     scan_tflops = F / (scan_ms * 1e-3) / 1e12
-    kind = os.environ.get("PATH_BENCH_KIND", "valu_f32")
-    peak = PEAK_FP32_VALU_TFLOPS if kind == "valu_f32" else PEAK_BF16_TFLOPS
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "fwd_scan_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            traffic = json.load(open(tfile)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
-    roofline = {"bound": "alu" if kind == "valu_f32" else "mfma", "achieved": round(scan_tflops, 3),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(scan_tflops / peak, 4), "traffic": traffic,
-                "kernel": "fwd_scan", "flops_per_launch": F}
+    traffic = load_traffic("scan")
+    roofline = {"bound": "mfma", "achieved": round(scan_tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "fwd_mfma_kernel<64> (right-to-left scan)", "flops_per_launch": F,
+                "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -124,15 +174,17 @@ def main():
         "metric": "PaTH fwd TFLOP/s & % bf16 MFMA peak at L=4096; decode-step HBM GB/s",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if kind == "valu_f32" else "bf16", "data": "synthetic",
-        "config": {"workload": "PaTH fwd bf16 B=8 H=16 L=4096 d=64 scale=1/8 + decode bf16 B=64 H=16 d=64 "
-                               "cache=8192", "global_batch": cf.B, "seq_len": cf.L, "heads": cf.H, "head_dim": cf.d,
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "PaTH fwd B=8 H=16 L=4096 d=64 scale=1/8 (bf16 in/out) + decode B=64 H=16 d=64 "
+                               "cache=8192 (bf16)", "storage": "bf16", "arith": "fp16 MFMA, fp32 accumulate",
+                   "global_batch": cf.B, "seq_len": cf.L, "heads": cf.H, "head_dim": cf.d,
                    "precision": args.precision, "parallelism": "single-gpu"},
         "fwd": {"ms": round(fwd_ms, 4), "prepare_ms": round(prep_ms, 4), "scan_ms": round(scan_ms, 4),
-                "tflops_model": F, "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "flops_model": F, "frac_bf16_peak": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
                 "fa_equiv_tflops": round(cf.B * cf.H * 2.0 * cf.d * cf.L ** 2 / (fwd_ms * 1e-3) / 1e12, 3)},
         "decode": {"ms": round(dec_ms, 4), "GB_per_s": round(dec_gbs, 1), "bytes_model": dbytes,
-                   "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)},
+                   "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode"),
+                   "source_sha256": source_hash("decode")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -154,6 +206,7 @@ def cpu_baseline(cf, budget_s=10.0):
         oracle.path_fwd_head(x["q"][0], x["k"][0], x["v"][0], x["w"][0], x["beta"][0], None, cf.scale)
         dt += time.perf_counter() - t0
         done += 1
+        print(f"[bench] oracle head {done}: {dt:.1f} s", file=sys.stderr, flush=True)
         if dt >= budget_s:
             break
     F = flops_path(1, done, cf.L, cf.d)
