@@ -57,7 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // inputs: the matrix-core layout written by the prepare stage.
 struct FwdWs {
   size_t khat, pT, cum;                       // fp32 path
-  size_t khl, pmat, qhat, sdiag, kmax, kmaxh, pnorm;  // bf16 path (cum shared)
+  size_t khl, pmat, qhat, sdiag, kmax, kmaxh, pnorm, vt;  // bf16 path (cum shared)
   size_t total;
 };
 
@@ -82,6 +82,7 @@ FwdWs fwd_layout(int dtype, int64_t BH, int64_t L, int64_t d, int64_t Nb, bool w
     w.kmax = take(sizeof(float) * bh * nb);
     w.kmaxh = take(sizeof(float) * bh);
     w.pnorm = take(sizeof(float) * bh * nb);
+    w.vt = take(2 * bh * nb * dd * size_t(kBlk));
     if (with_forget) w.cum = take(sizeof(float) * bh * lp);
   }
   w.total = off;
@@ -162,8 +163,8 @@ int fwd_check(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, int precisi
 }
 
 int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int dtype,
-                float scale, const void* q, const void* k, const void* w, const float* beta,
-                const float* log_forget, void* workspace, hipStream_t stream) {
+                float scale, const void* q, const void* k, const void* v, const void* w,
+                const float* beta, const float* log_forget, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   int st;
   if (dtype == PATH_F32) {
@@ -180,10 +181,10 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
   }
   float* kmax = reinterpret_cast<float*>(ws + a.lay.kmax);
   st = hip_status(path::launch_prepare_mfma(
-      B, H, L, d, scale * kLog2e, q, k, w, beta, reinterpret_cast<_Float16*>(ws + a.lay.khl),
+      B, H, L, d, scale * kLog2e, q, k, w, v, beta, reinterpret_cast<_Float16*>(ws + a.lay.khl),
       reinterpret_cast<_Float16*>(ws + a.lay.pmat), reinterpret_cast<float*>(ws + a.lay.qhat),
       reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, reinterpret_cast<float*>(ws + a.lay.pnorm),
-      stream));
+      reinterpret_cast<_Float16*>(ws + a.lay.vt), stream));
   if (st) return st;
   return hip_status(path::launch_head_reduce(
       a.BH, L, kmax, reinterpret_cast<float*>(ws + a.lay.kmaxh), log_forget, kLog2e,
@@ -203,8 +204,8 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
                                                 khat, pT, o, lse, stream));
   }
   return hip_status(path::launch_fwd_mfma(
-      B, H, L, d, precision == PATH_PREC_ACCURATE ? 1 : 0, kAutoTau, v,
-      reinterpret_cast<const _Float16*>(ws + a.lay.khl),
+      B, H, L, d, precision == PATH_PREC_ACCURATE ? 1 : 0, kAutoTau,
+      reinterpret_cast<const _Float16*>(ws + a.lay.vt), reinterpret_cast<const _Float16*>(ws + a.lay.khl),
       reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
       reinterpret_cast<const float*>(ws + a.lay.qhat),
       reinterpret_cast<const float*>(ws + a.lay.sdiag),
@@ -224,7 +225,7 @@ int path_fwd_stage_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype
   int st = fwd_check(B, H, L, d, dtype, precision, q, k, v, w, beta, log_forget, workspace,
                      workspace_bytes, &a);
   if (st) return st;
-  return fwd_prepare(a, B, H, L, d, dtype, scale, q, k, w, beta, log_forget, workspace, stream);
+  return fwd_prepare(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, workspace, stream);
 }
 
 int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
@@ -249,7 +250,7 @@ int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
                      workspace_bytes, &a);
   if (st) return st;
   if (!o || !lse) return PATH_ERR_NULL;
-  if ((st = fwd_prepare(a, B, H, L, d, dtype, scale, q, k, w, beta, log_forget, workspace, stream)))
+  if ((st = fwd_prepare(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, workspace, stream)))
     return st;
   return fwd_scan(a, B, H, L, d, dtype, scale, precision, q, k, v, w, beta, log_forget, o, lse,
                   workspace, stream);

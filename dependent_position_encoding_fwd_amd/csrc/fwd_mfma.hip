@@ -12,8 +12,8 @@
 //                                     running max m enters as the accumulator seed)
 //     online softmax over keys       (exp2; the max is only raised when a logit
 //                                     exceeds it by more than kTheta)
-//     O^T += V_n^T P^T               (16x16x32 f16 MFMA; the softmax denominator
-//                                     is summed in fp32 from the unrounded exp2)
+//     O^T += V_n^T P^T               (16x16x32 f16 MFMA; an all-ones A operand
+//                                     sums the same fp16 P for the denominator)
 //     Qt   = P_n Qt                  (block transition P_n = H_0...H_63, f16 MFMA)
 // [§2 "Extensões: PaTH-FoX"] adds cum_i - cum_j (log2 units) to each logit.
 //
@@ -33,7 +33,10 @@
 //     max|Qt| * max|khat| * 2^-10     (log2-logit units)
 // is at most `tau`, where max|Qt| is measured while the split is in use and
 // afterwards carried forward with the per-block bound |P_n|_2 <= pnorm_n.
-// Probabilities (<= 2^kTheta) and values meet in fp16 (fp32 accumulate).
+// Probabilities and values meet in fp16 (fp32 accumulate).  Probabilities
+// are formed as 2^(s - m + kOff): the offset keeps them clear of fp16's
+// subnormal range while the lazy maximum keeps them below 2^(kTheta + kOff);
+// numerator and denominator carry the same factor.
 #include <math.h>
 
 #include "common.h"
@@ -110,7 +113,8 @@ __device__ __forceinline__ float grp_sum(float x) {
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -INFINITY;
-constexpr float kTheta = 8.f;  // probabilities may reach 2^kTheta before the max is raised
+constexpr float kTheta = 8.f;  // logits may exceed the running max by kTheta before it is raised
+constexpr float kOff = 7.f;    // probabilities are scaled by 2^kOff (<= 2^15 < fp16 max)
 
 // Kernel geometry: 128 queries (two UT blocks) per workgroup.
 template <int D>
@@ -126,14 +130,14 @@ struct Geo {
   static constexpr int DC = D / 32;            // 32-wide K chunks over the head dim
   static constexpr int KCH = kBlk * (D / 8) / NT;  // 16-byte Khat chunks per thread
   static constexpr int PCH = D * (D / 8) / NT;     // 16-byte P chunks per thread
-  static constexpr int VIT = 32 * (D / 8) / NT;    // V items (2 keys x 8 dims) per thread
+  static constexpr int VCH = D * (kBlk / 8) / NT;  // 16-byte V^T chunks per thread
 };
 
 }  // namespace
 
 template <int D, bool FOX>
 __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
-    int64_t L, int Nb, int BH, int accurate_all, float tau, const uint16_t* __restrict__ v,
+    int64_t L, int Nb, int BH, int accurate_all, float tau, const _Float16* __restrict__ vt,
     const _Float16* __restrict__ khat, const _Float16* __restrict__ pmat,
     const float* __restrict__ qhat, const float* __restrict__ sdiag,
     const float* __restrict__ kmax_head, const float* __restrict__ pnorm,
@@ -141,12 +145,12 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   using G = Geo<D>;
   constexpr int NW = G::NW, NCT = G::NCT, QPW = G::QPW, WPB = G::WPB, NT = G::NT;
   constexpr int KP = G::KP, VP = G::VP, DT = G::DT, DC = G::DC;
-  constexpr int KCH = G::KCH, PCH = G::PCH, VIT = G::VIT;
+  constexpr int KCH = G::KCH, PCH = G::PCH, VCH = G::VCH;
   constexpr int C = kBlk;
 
   __shared__ __attribute__((aligned(16))) _Float16 Ks[2][C * KP];
   __shared__ __attribute__((aligned(16))) _Float16 Ps[2][D * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[D * VP];
   __shared__ float red[2][NW];
 
   const int NP = (Nb + 1) / 2;
@@ -175,10 +179,15 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   const int64_t L64 = L;
   const float khmax = kmax_head[bh];
   const float* cumh = FOX ? cum + bh * Nb * C : nullptr;
+  // this head's prepared blocks; per-block offsets stay 32-bit
+  const u4* kh_h = reinterpret_cast<const u4*>(khat + bh * Nb * (2 * C * D));
+  const u4* pm_h = reinterpret_cast<const u4*>(pmat + bh * Nb * (2 * D * D));
+  const u4* vt_h = reinterpret_cast<const u4*>(vt + bh * Nb * (D * C));
+  constexpr int KBLK = 2 * C * D / 8, PBLK = 2 * D * D / 8, VBLK = D * C / 8;  // u4 per block
 
   // ---- per-wave state ------------------------------------------------------------
   f4 oacc[NCT][DT], qf[NCT][DT];
-  float lsum[NCT];  // per-lane partial softmax denominators (fp32)
+  f4 lacc[NCT];  // softmax denominators (every element holds the column sum)
   h8 qhi[NCT][DC], qlo[NCT][DC];  // Qt as fp16 B operands (lo only when the split is used)
   auto to_b_operands = [&](bool with_lo) __attribute__((always_inline)) {
 #pragma unroll
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   float mrun[NCT], cq[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    lsum[ct] = 0.f;
+    lacc[ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[ct][t] = f4{0.f, 0.f, 0.f, 0.f};
     cq[ct] = (FOX && live) ? cumh[mb * C + r0 + 16 * ct + ln] : 0.f;
@@ -201,101 +210,59 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   // ---- staging helpers ----------------------------------------------------------
   // registers of the next key block (global -> VGPR prefetch)
   struct Pre {
-    u4 kh[KCH], ph[PCH], v[VIT][2];
+    u4 kh[KCH], ph[PCH], vh[VCH];
     f4 ck[4];
   } pre;
-  auto load_v = [&](int n) __attribute__((always_inline)) {
-    const uint16_t* vsrc = v + (bh * L64 + static_cast<int64_t>(n) * C) * D;
-#pragma unroll
-    for (int j = 0; j < VIT; ++j) {
-      const int it = tid + j * NT;
-      const int kk = it % 32, dg = it / 32;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int key = 2 * kk + e;
-        u4 t = u4{0u, 0u, 0u, 0u};
-        if (static_cast<int64_t>(n) * C + key < L64) t = *reinterpret_cast<const u4*>(vsrc + key * D + 8 * dg);
-        pre.v[j][e] = t;
-      }
-    }
-  };
-  auto load_tile = [&](int n, bool acc) __attribute__((always_inline)) {
-    const int64_t blk = bh * Nb + n;
-    const u4* ksrc = reinterpret_cast<const u4*>(khat + blk * (2 * C * D)) + tid;
-    const u4* psrc = reinterpret_cast<const u4*>(pmat + blk * (2 * D * D)) + tid;
-    (void)acc;
+  auto load_tile = [&](int n) __attribute__((always_inline)) {
+    const u4* ksrc = kh_h + n * KBLK + tid;
+    const u4* psrc = pm_h + n * PBLK + tid;
+    const u4* vsrc = vt_h + n * VBLK + tid;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) pre.kh[j] = ksrc[j * NT];
     if (n > 0) {
 #pragma unroll
       for (int j = 0; j < PCH; ++j) pre.ph[j] = psrc[j * NT];
     }
-    load_v(n);
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) pre.vh[j] = vsrc[j * NT];
     if constexpr (FOX) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) pre.ck[kt] = *reinterpret_cast<const f4*>(cumh + n * C + 16 * kt + 4 * lg);
     }
   };
-  // V^T[d][perm(key)] (fp16) from two bf16 key rows x 8 dims
-  auto store_v = [&](uint16_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < VIT; ++j) {
-      const int it = tid + j * NT;
-      const int kk = it % 32, dg = it / 32;
-      const int key0 = 2 * kk;
-      const int pos = (key0 & ~31) | (((key0 >> 2) & 3) << 3) | (((key0 >> 4) & 1) << 2) | (key0 & 3);
-      const u4 a0 = pre.v[j][0], a1 = pre.v[j][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const h2 lo = __builtin_convertvector(f2{__uint_as_float(a0[e] << 16), __uint_as_float(a1[e] << 16)}, h2);
-        const h2 hi = __builtin_convertvector(
-            f2{__uint_as_float(a0[e] & 0xffff0000u), __uint_as_float(a1[e] & 0xffff0000u)}, h2);
-        *reinterpret_cast<h2*>(&vt[(8 * dg + 2 * e) * VP + pos]) = lo;
-        *reinterpret_cast<h2*>(&vt[(8 * dg + 2 * e + 1) * VP + pos]) = hi;
-      }
-    }
+  // 16-byte chunk idx of a row-major tile with 8 chunks (D chunks) per row -> LDS
+  auto put_v = [&](_Float16* dst, int idx, const u4& x) __attribute__((always_inline)) {
+    *reinterpret_cast<u4*>(&dst[(idx >> 3) * VP + 8 * (idx & 7)]) = x;
+  };
+  auto put_kp = [&](_Float16* dst, int idx, const u4& x) __attribute__((always_inline)) {
+    *reinterpret_cast<u4*>(&dst[(idx / (D / 8)) * KP + 8 * (idx % (D / 8))]) = x;
   };
   auto store_tile = [&](int n, bool acc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int idx = tid + j * NT;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      *reinterpret_cast<u4*>(&Ks[0][r * KP + 8 * c8]) = pre.kh[j];
-    }
+    for (int j = 0; j < KCH; ++j) put_kp(Ks[0], tid + j * NT, pre.kh[j]);
     if (n > 0) {
 #pragma unroll
-      for (int j = 0; j < PCH; ++j) {
-        const int idx = tid + j * NT;
-        const int r = idx / (D / 8), c8 = idx % (D / 8);
-        *reinterpret_cast<u4*>(&Ps[0][r * KP + 8 * c8]) = pre.ph[j];
-      }
+      for (int j = 0; j < PCH; ++j) put_kp(Ps[0], tid + j * NT, pre.ph[j]);
     }
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) put_v(Vt, tid + j * NT, pre.vh[j]);
     if (acc) {
       // lo parts (split-precision blocks only) are fetched here, not prefetched
-      const int64_t blk = bh * Nb + n;
-      const u4* ksrc = reinterpret_cast<const u4*>(khat + blk * (2 * C * D) + C * D) + tid;
+      const u4* ksrc = kh_h + n * KBLK + KBLK / 2 + tid;
 #pragma unroll
-      for (int j = 0; j < KCH; ++j) {
-        const int idx = tid + j * NT;
-        const int r = idx / (D / 8), c8 = idx % (D / 8);
-        *reinterpret_cast<u4*>(&Ks[1][r * KP + 8 * c8]) = ksrc[j * NT];
-      }
+      for (int j = 0; j < KCH; ++j) put_kp(Ks[1], tid + j * NT, ksrc[j * NT]);
       if (n > 0) {
-        const u4* psrc = reinterpret_cast<const u4*>(pmat + blk * (2 * D * D) + D * D) + tid;
+        const u4* psrc = pm_h + n * PBLK + PBLK / 2 + tid;
 #pragma unroll
-        for (int j = 0; j < PCH; ++j) {
-          const int idx = tid + j * NT;
-          const int r = idx / (D / 8), c8 = idx % (D / 8);
-          *reinterpret_cast<u4*>(&Ps[1][r * KP + 8 * c8]) = psrc[j * NT];
-        }
+        for (int j = 0; j < PCH; ++j) put_kp(Ps[1], tid + j * NT, psrc[j * NT]);
       }
     }
-    store_v(Vt);
   };
+  const h8 ones = h8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 
   // ---- softmax step on logits relative to the running max -------------------------
-  // x[ct][kt][i] = logit - mrun (log2 units) of key 16kt+4lg+i, query column ct.
-  auto softmax_pv = [&](f4 (&x)[NCT][4], const uint16_t* vt) {
+  // x[ct][kt][i] = logit - mrun + kOff (log2 units) of key 16kt+4lg+i, query column ct.
+  auto softmax_pv = [&](f4 (&x)[NCT][4], const _Float16* vts) {
     float mx[NCT];
     bool need = false;
 #pragma unroll
@@ -305,15 +272,15 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       for (int kt = 1; kt < 4; ++kt)
         a = fmaxf(a, fmaxf(fmaxf(x[ct][kt][0], x[ct][kt][1]), fmaxf(x[ct][kt][2], x[ct][kt][3])));
       mx[ct] = grp_max(a);
-      need |= mx[ct] > kTheta;
+      need |= mx[ct] > kTheta + kOff;
     }
     if (__any(need)) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const float sh = fmaxf(mx[ct], 0.f);
+        const float sh = fmaxf(mx[ct] - kOff, 0.f);
         const float alpha = __builtin_amdgcn_exp2f(-sh);
         mrun[ct] += sh;
-        lsum[ct] *= alpha;
+        lacc[ct] *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[ct][t] *= alpha;
 #pragma unroll
@@ -329,8 +296,6 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) pe[kt][i] = __builtin_amdgcn_exp2f(x[ct][kt][i]);
-      lsum[ct] += ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3])) +
-                  ((pe[2][0] + pe[2][1]) + (pe[2][2] + pe[2][3])) + ((pe[3][0] + pe[3][1]) + (pe[3][2] + pe[3][3]));
       pb[ct][0] = pack_h8(pe[0], pe[1]);
       pb[ct][1] = pack_h8(pe[2], pe[3]);
     }
@@ -338,10 +303,12 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const h8 a = *reinterpret_cast<const h8*>(&vt[(16 * t + ln) * VP + 32 * c + 8 * lg]);
+        const h8 a = *reinterpret_cast<const h8*>(&vts[(16 * t + ln) * VP + 32 * c + 8 * lg]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) oacc[ct][t] = mma16(a, pb[ct][c], oacc[ct][t]);
       }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) lacc[ct] = mma16(ones, pb[ct][c], lacc[ct]);
     }
   };
 
@@ -360,12 +327,16 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   };
 
   // ---- diagonal blocks: V^T of block 2p in Vt, of block 2p+1 in the Ps area -------
-  uint16_t* vt2 = reinterpret_cast<uint16_t*>(&Ps[0][0]);
-  load_v(2 * p);
-  store_v(Vt);
-  if (2 * p + 1 < Nb) {
-    load_v(2 * p + 1);
-    store_v(vt2);
+  _Float16* vt2 = &Ps[0][0];
+  {
+    const u4* va = vt_h + (2 * p) * VBLK + tid;
+    const u4* vb = vt_h + (2 * p + 1) * VBLK + tid;
+    const bool two = 2 * p + 1 < Nb;
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      put_v(Vt, tid + j * NT, va[j * NT]);
+      if (two) put_v(vt2, tid + j * NT, vb[j * NT]);
+    }
   }
   __syncthreads();
   if (live) {
@@ -391,7 +362,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       }
       mrun[ct] = grp_max(a);  // finite: key r is always present
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= mrun[ct];
+      for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= mrun[ct] - kOff;
     }
     softmax_pv(x, half == 0 ? Vt : vt2);
 #pragma unroll
@@ -417,7 +388,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
 #pragma unroll
   for (int w2 = 0; w2 < NW; ++w2) qbound = fmaxf(qbound, red[0][w2]);
   bool acc_cur = accurate_all || (qbound * khmax * 0.0009765625f > tau);
-  load_tile(2 * p, acc_cur);
+  load_tile(2 * p);
   to_b_operands(acc_cur);
 
   // ---- right-to-left scan ----------------------------------------------------------
@@ -432,7 +403,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
     // precision of block n-1: bound on |Qt| after this block's transition
     const float qb_next = qbound * pnorm[bh * Nb + n];
     const bool acc_next = accurate_all || (qb_next * khmax * 0.0009765625f > tau);
-    if (n > 0) load_tile(n - 1, acc_next);
+    if (n > 0) load_tile(n - 1);
     const bool acc = acc_cur;
     const bool work = live && !(half == 0 && n == 2 * p);
 
@@ -443,7 +414,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
       f4 seed[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const float sv = (FOX ? cq[ct] : 0.f) - mrun[ct];
+        const float sv = (FOX ? cq[ct] : 0.f) - mrun[ct] + kOff;
         seed[ct] = f4{sv, sv, sv, sv};
       }
 #pragma unroll
@@ -538,7 +509,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
   if (live) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float l = grp_sum(lsum[ct]);
+      const float l = lacc[ct][0];
       const int r = r0 + 16 * ct + ln;
       const int64_t row = static_cast<int64_t>(mb) * C + r;
       if (row < L64) {
@@ -552,14 +523,14 @@ __global__ __launch_bounds__(Geo<D>::NT, 2) void fwd_mfma_kernel(
           pk.p[1] = __builtin_convertvector(f2{y[2], y[3]}, b2);
           *reinterpret_cast<uint2*>(dst + 16 * t + 4 * lg) = make_uint2(pk.u.x, pk.u.y);
         }
-        if (lg == 0) lse[bh * L64 + row] = (mrun[ct] + __log2f(l)) * kLn2;
+        if (lg == 0) lse[bh * L64 + row] = (mrun[ct] - kOff + __log2f(l)) * kLn2;
       }
     }
   }
 }
 
 template <int D>
-static hipError_t launch_fwd_mfma_t(int64_t BH, int64_t L, int accurate, float tau, const void* v,
+static hipError_t launch_fwd_mfma_t(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                                     const _Float16* khat, const _Float16* pmat, const float* qhat,
                                     const float* sdiag, const float* kmax_head, const float* pnorm,
                                     const float* cum, void* o, float* lse, hipStream_t stream) {
@@ -569,24 +540,24 @@ static hipError_t launch_fwd_mfma_t(int64_t BH, int64_t L, int accurate, float t
   dim3 block(Geo<D>::NT);
   if (cum) {
     hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), grid, block, 0, stream, L, Nb, static_cast<int>(BH),
-                       accurate, tau, static_cast<const uint16_t*>(v), khat, pmat, qhat, sdiag,
+                       accurate, tau, vt, khat, pmat, qhat, sdiag,
                        kmax_head, pnorm, cum, static_cast<uint16_t*>(o), lse);
   } else {
     hipLaunchKernelGGL((fwd_mfma_kernel<D, false>), grid, block, 0, stream, L, Nb, static_cast<int>(BH),
-                       accurate, tau, static_cast<const uint16_t*>(v), khat, pmat, qhat, sdiag,
+                       accurate, tau, vt, khat, pmat, qhat, sdiag,
                        kmax_head, pnorm, cum, static_cast<uint16_t*>(o), lse);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_mfma(int64_t B, int64_t H, int64_t L, int64_t d, int accurate, float tau,
-                           const void* v, const _Float16* khat, const _Float16* pmat,
+                           const _Float16* vt, const _Float16* khat, const _Float16* pmat,
                            const float* qhat, const float* sdiag, const float* kmax_head,
                            const float* pnorm, const float* cum, void* o, float* lse,
                            hipStream_t stream) {
-  return d == 64 ? launch_fwd_mfma_t<64>(B * H, L, accurate, tau, v, khat, pmat, qhat, sdiag, kmax_head,
+  return d == 64 ? launch_fwd_mfma_t<64>(B * H, L, accurate, tau, vt, khat, pmat, qhat, sdiag, kmax_head,
                                          pnorm, cum, o, lse, stream)
-                 : launch_fwd_mfma_t<128>(B * H, L, accurate, tau, v, khat, pmat, qhat, sdiag, kmax_head,
+                 : launch_fwd_mfma_t<128>(B * H, L, accurate, tau, vt, khat, pmat, qhat, sdiag, kmax_head,
                                           pnorm, cum, o, lse, stream);
 }
 

@@ -25,9 +25,9 @@ hipError_t launch_prepare_scan(int64_t B, int64_t H, int64_t L, int64_t d, float
 // Same outputs as launch_prepare_scan, computed on the matrix cores, plus
 // pnorm[bh][n] >= |P_n|_2 (product of the transitions' spectral norms).
 hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
-                               const void* k, const void* w, const float* beta, _Float16* khat,
-                               _Float16* pmat, float* qhat, float* sdiag, float* kmax, float* pnorm,
-                               hipStream_t stream);
+                               const void* k, const void* w, const void* v, const float* beta,
+                               _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               float* pnorm, _Float16* vt, hipStream_t stream);
 
 // Per head: kmax_head = max over blocks of kmax; cum = mult * prefix sum of
 // log_forget (fp64 accumulation, padded to whole blocks) when log_forget != null.
@@ -36,7 +36,7 @@ hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* k
 
 // Matrix-core right-to-left scan forward (bf16 storage).
 hipError_t launch_fwd_mfma(int64_t B, int64_t H, int64_t L, int64_t d, int accurate, float tau,
-                           const void* v, const _Float16* khat, const _Float16* pmat,
+                           const _Float16* vt, const _Float16* khat, const _Float16* pmat,
                            const float* qhat, const float* sdiag, const float* kmax_head,
                            const float* pnorm, const float* cum, void* o, float* lse,
                            hipStream_t stream);

@@ -12,7 +12,9 @@
 //     Qhat = Q - F^T Ut                 (adjusted queries: H_0..H_r applied to q_r)
 //     Sdiag^T = K Q^T - Y Ut            (in-block logits k_c^T H_{c+1}..H_r q_r, c <= r)
 // Outputs (per block): Khat and P as fp16 hi/lo rows with the reduction
-// index in mfma_perm order, c2*Qhat and c2*Sdiag in fp32, max |khat_c|.
+// index in mfma_perm order, c2*Qhat and c2*Sdiag in fp32, max |khat_c|, and
+// V^T in fp16 with the keys in mfma_perm order (zero past the sequence end),
+// the layout in which the scan feeds values to the matrix cores.
 //
 // Every product is a 16x16x32 MFMA.  Wave w owns output column tile w (16
 // columns), so the accumulator tile of one product is, after conversion to
@@ -106,9 +108,10 @@ struct PGeo {
 template <int D>
 __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     int64_t L, int Nb, float c2, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ w, const float* __restrict__ beta, _Float16* __restrict__ khat,
-    _Float16* __restrict__ pmat, float* __restrict__ qhat, float* __restrict__ sdiag,
-    float* __restrict__ kmax, float* __restrict__ pnorm) {
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    _Float16* __restrict__ khat, _Float16* __restrict__ pmat, float* __restrict__ qhat,
+    float* __restrict__ sdiag, float* __restrict__ kmax, float* __restrict__ pnorm,
+    _Float16* __restrict__ vt) {
   using G = PGeo<D>;
   constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
 
@@ -138,6 +141,16 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   const int64_t t0 = static_cast<int64_t>(n) * C;
   const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
   const int64_t base = (bh * L + t0) * D;
+
+  // value rows of the block, fetched now and transposed at the end
+  constexpr int VCH = C * (D / 8) / 256;
+  uint4 vraw[VCH];
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) {
+    const int idx = tid + 256 * j;
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    vraw[j] = r < valid ? *reinterpret_cast<const uint4*>(v + base + r * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+  }
 
   // ---- load W, K, Q rows (bf16) and W^T (fp16, perm columns) -----------------
   for (int idx = tid; idx < C * (D / 8); idx += 256) {
@@ -366,7 +379,24 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lv.u.x, lv.u.y);
     }
   }
-  __syncthreads();  // -Y and -F^T rows complete
+  __syncthreads();  // -Y and -F^T rows complete; XT is free
+
+  // V^T[e][perm(c)] in fp16 through the XT area (pitch 64, no pad), then out in 16-byte rows
+  {
+    _Float16* VS = &XT[0][0];
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      const int idx = tid + 256 * j;
+      const int r = idx / (D / 8), c8 = idx % (D / 8);
+      const uint32_t vv[4] = {vraw[j].x, vraw[j].y, vraw[j].z, vraw[j].w};
+      const int pc = perm32(r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        VS[(8 * c8 + 2 * e) * C + pc] = static_cast<_Float16>(__uint_as_float(vv[e] << 16));
+        VS[(8 * c8 + 2 * e + 1) * C + pc] = static_cast<_Float16>(__uint_as_float(vv[e] & 0xffff0000u));
+      }
+    }
+  }
 
   if (tid == 0) {
     const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
@@ -374,6 +404,17 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     float g = 1.f;
     for (int t = 0; t < C; ++t) g *= hn[t];
     pnorm[bh * Nb + n] = g;
+  }
+
+  __syncthreads();
+  {
+    const _Float16* VS = &XT[0][0];
+    uint4* dst = reinterpret_cast<uint4*>(vt + (bh * Nb + n) * (D * C));
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      const int idx = tid + 256 * j;
+      dst[idx] = *reinterpret_cast<const uint4*>(&VS[8 * idx]);
+    }
   }
 
   // ---- in-block logits and adjusted queries (wave w: queries r in tile w) -------
@@ -435,24 +476,25 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 
 template <int D>
 static hipError_t launch_prepare_mfma_t(int64_t BH, int64_t L, float c2, const void* q, const void* k,
-                                        const void* w, const float* beta, _Float16* khat,
+                                        const void* w, const void* v, const float* beta, _Float16* khat,
                                         _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                                        float* pnorm, hipStream_t stream) {
+                                        float* pnorm, _Float16* vt, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   hipLaunchKernelGGL((prepare_mfma_kernel<D>), dim3(static_cast<unsigned>(BH * Nb)), dim3(256), 0, stream,
                      L, Nb, c2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(w), beta, khat, pmat, qhat, sdiag, kmax, pnorm);
+                     static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(v), beta, khat, pmat,
+                     qhat, sdiag, kmax, pnorm, vt);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
-                               const void* k, const void* w, const float* beta, _Float16* khat,
-                               _Float16* pmat, float* qhat, float* sdiag, float* kmax, float* pnorm,
-                               hipStream_t stream) {
-  return d == 64 ? launch_prepare_mfma_t<64>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, pnorm,
-                                             stream)
-                 : launch_prepare_mfma_t<128>(B * H, L, c2, q, k, w, beta, khat, pmat, qhat, sdiag, kmax, pnorm,
-                                              stream);
+                               const void* k, const void* w, const void* v, const float* beta,
+                               _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
+                               float* pnorm, _Float16* vt, hipStream_t stream) {
+  return d == 64 ? launch_prepare_mfma_t<64>(B * H, L, c2, q, k, w, v, beta, khat, pmat, qhat, sdiag, kmax,
+                                             pnorm, vt, stream)
+                 : launch_prepare_mfma_t<128>(B * H, L, c2, q, k, w, v, beta, khat, pmat, qhat, sdiag, kmax,
+                                              pnorm, vt, stream);
 }
 
 }  // namespace path
