@@ -209,7 +209,7 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
       reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
       reinterpret_cast<const float*>(ws + a.lay.qhat),
       reinterpret_cast<const float*>(ws + a.lay.sdiag),
-      reinterpret_cast<const float*>(ws + a.lay.kmaxh),
+      reinterpret_cast<const float*>(ws + a.lay.kmaxh), reinterpret_cast<const float*>(ws + a.lay.kmax),
       reinterpret_cast<const float*>(ws + a.lay.pnorm), cum, o, lse, stream));
 }
 
