@@ -11,6 +11,8 @@
 // Memory plan (HBM-bound): each cached key row is read once and written once,
 // each value row read once, all with 16-byte coalesced accesses; consecutive
 // lanes cover one row, so a wave touches 1 KiB of contiguous cache per pass.
+// The chunk loop is software-pipelined: the loads of the next group of 8 rows
+// per lane are issued before the current group is updated and attended to.
 #include <math.h>
 
 #include <type_traits>
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
 
   constexpr int STRIDE = NW * KPW;  // key rows per workgroup pass
-  for (int64_t jb = j0 + wave * KPW + slot; jb < j1; jb += STRIDE * UNR) {
-    typename V::raw kr[UNR], vr[UNR];
+  typename V::raw kr[UNR], vr[UNR];
+  auto fetch = [&](int64_t jb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
@@ -135,15 +137,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
         vr[u] = __builtin_nontemporal_load(&vbase[j * LPK + sub]);
       }
     }
+  };
+  const int64_t jstart = j0 + wave * KPW + slot;
+  if (jstart < j1) fetch(jstart);
+  for (int64_t jb = jstart; jb < j1; jb += STRIDE * UNR) {
+    typename V::raw kc[UNR], vc[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      kc[u] = kr[u];
+      vc[u] = vr[u];
+    }
+    if (jb + STRIDE * UNR < j1) fetch(jb + STRIDE * UNR);
     float sv[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
-      // Lanes of one key row share j, so the group reductions below see
-      // a consistent set of lanes; rows past j1 contribute nothing.
       const bool live = j < j1;
       float kf[EPV];
-      V::unpack(kr[u], kf);
+      V::unpack(kc[u], kf);
       float a = 0.f, b = 0.f;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
@@ -156,7 +167,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < EPV; ++e) kf[e] -= ba * wv[e];
       if (live) __builtin_nontemporal_store(V::pack(kf), &kbase[j * LPK + sub]);
-      // q . (k - beta a w) from the fp32 updated key, in log2 units
       sv[u] = live ? scale2 * (b - ba * wq) : -INFINITY;
     }
     float mb = sv[0];
@@ -172,7 +182,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       for (int u = 0; u < UNR; ++u) {
         const float p = __builtin_amdgcn_exp2f(sv[u] - mnew);
         float vf[EPV];
-        V::unpack(vr[u], vf);
+        V::unpack(vc[u], vf);
         lrun += p;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[e] += p * vf[e];

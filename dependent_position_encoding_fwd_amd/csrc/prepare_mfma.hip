@@ -142,48 +142,53 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
   const int64_t base = (bh * L + t0) * D;
 
-  // value rows of the block, fetched now and transposed at the end
+  // ---- load W, K, Q rows (bf16) and W^T (fp16, perm columns) -----------------
+  // Lanes idx .. idx + D/8 - 1 (consecutive, same wave) hold one row, so the
+  // row norms |w_s|^2 come from a shuffle reduction over them.  The value rows
+  // are fetched last (they are needed only at the end; loads complete in order).
   constexpr int VCH = C * (D / 8) / 256;
   uint4 vraw[VCH];
 #pragma unroll
   for (int j = 0; j < VCH; ++j) {
     const int idx = tid + 256 * j;
     const int r = idx / (D / 8), c8 = idx % (D / 8);
-    vraw[j] = r < valid ? *reinterpret_cast<const uint4*>(v + base + r * D + 8 * c8) : make_uint4(0, 0, 0, 0);
-  }
-
-  // ---- load W, K, Q rows (bf16) and W^T (fp16, perm columns) -----------------
-  for (int idx = tid; idx < C * (D / 8); idx += 256) {
-    const int r = idx / (D / 8), c8 = idx % (D / 8);
     uint4 wv = make_uint4(0, 0, 0, 0), kv = wv, qv = wv;
+    float br = 0.f;
     if (r < valid) {
       wv = *reinterpret_cast<const uint4*>(w + base + r * D + 8 * c8);
       kv = *reinterpret_cast<const uint4*>(k + base + r * D + 8 * c8);
       qv = *reinterpret_cast<const uint4*>(q + base + r * D + 8 * c8);
+      br = beta[bh * L + t0 + r];
     }
     *reinterpret_cast<uint4*>(Wb + r * RP + 8 * c8) = wv;
     *reinterpret_cast<uint4*>(Kb + r * RP + 8 * c8) = kv;
     *reinterpret_cast<uint4*>(Qb + r * RP + 8 * c8) = qv;
     const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
     const int pb = perm32(r);
+    float sq = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      Wt[(8 * c8 + 2 * e) * TP + pb] = static_cast<_Float16>(__uint_as_float(ww[e] << 16));
-      Wt[(8 * c8 + 2 * e + 1) * TP + pb] = static_cast<_Float16>(__uint_as_float(ww[e] & 0xffff0000u));
+      const float lo = __uint_as_float(ww[e] << 16), hi = __uint_as_float(ww[e] & 0xffff0000u);
+      Wt[(8 * c8 + 2 * e) * TP + pb] = static_cast<_Float16>(lo);
+      Wt[(8 * c8 + 2 * e + 1) * TP + pb] = static_cast<_Float16>(hi);
+      sq += lo * lo + hi * hi;
+    }
+#pragma unroll
+    for (int off = 1; off < D / 8; off <<= 1) sq += __shfl_xor(sq, off, 64);
+    if (c8 == 0) {
+      bs[r] = br;
+      // |H_s|_2 = max(1, |1 - beta_s |w_s|^2|): its product bounds the growth
+      // of a transported query across the block
+      hn[r] = fmaxf(1.f, fabsf(1.f - br * sq));
     }
   }
-  if (tid < C) bs[tid] = tid < valid ? beta[bh * L + t0 + tid] : 0.f;
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) {
+    const int idx = tid + 256 * j;
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    vraw[j] = r < valid ? *reinterpret_cast<const uint4*>(v + base + r * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+  }
   __syncthreads();
-  // |H_s|_2 = max(1, |1 - beta_s |w_s|^2|): its product bounds the growth of a
-  // transported query across the block
-  if (tid < C) {
-    float ww = 0.f;
-    for (int e = 0; e < D; ++e) {
-      const float x = bf2f(Wb[tid * RP + e]);
-      ww += x * x;
-    }
-    hn[tid] = fmaxf(1.f, fabsf(1.f - bs[tid] * ww));
-  }
 
   // ---- products of stored inputs (exact, one bf16 pass); wave w = column tile w
   f4 gt[4], zt[4], ut[4], skq[4];
@@ -230,17 +235,35 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     float acc[16], xr[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) acc[u] = xr[u] = 0.f;
+    // Column r of G (rows 4u+qq, u < (r+3)/4) and beta_r are read one row
+    // ahead, so the LDS latency stays off the serial chain.
+    f4 gc[4], gn[4];
+    float bc, bn = 0.f;
+    auto ldcol = [&](int r, f4 (&g)[4]) __attribute__((always_inline)) {
+      const f4* src = reinterpret_cast<const f4*>(GY + r * 64 + qq * 16);  // G[4u+qq][r]
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * j < (r + 3) / 4) g[j] = src[j];
+    };
+    ldcol(C - 1, gc);
+    bc = bs[C - 1];
 #pragma unroll
     for (int r = C - 1; r >= 0; --r) {
+      if (r > 0) {
+        ldcol(r - 1, gn);
+        bn = bs[r - 1];
+      }
       const int ur = r >> 2;
-      float x = bs[r] * ((r == c ? 1.f : 0.f) - acc[ur]);
+      float x = bc * ((r == c ? 1.f : 0.f) - acc[ur]);
       x = (r <= c) ? x : 0.f;
       // the lane with qq == r % 4 holds the right acc; share its x within the quad
       x = quad_bcast(x, r & 3);
       if (qq == (r & 3)) xr[ur] = x;
-      const float* gcol = GY + r * 64 + qq * 16;  // G[4u+qq][r]
 #pragma unroll
-      for (int u = 0; u < (r + 3) / 4; ++u) acc[u] += gcol[u] * x;
+      for (int u = 0; u < (r + 3) / 4; ++u) acc[u] += gc[u >> 2][u & 3] * x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gc[j] = gn[j];
+      bc = bn;
     }
     // X^T rows: XT[c][perm(a)] = X[a][c], a = 4u + qq
 #pragma unroll
