@@ -33,7 +33,6 @@ WRITE_SIZE counters calibrate those of the other kernels in a rocprofv3
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -43,14 +42,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from dependent_position_encoding_fwd_amd.profsum import source_hash  # noqa: E402
+
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {
-    "scan": ("dependent_position_encoding_fwd_amd/csrc/fwd_mfma.hip",
-             "dependent_position_encoding_fwd_amd/csrc/common.h"),
-    "decode": ("dependent_position_encoding_fwd_amd/csrc/decode.hip",
-               "dependent_position_encoding_fwd_amd/csrc/common.h"),
-}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 COPY_REF_BYTES = 1 << 30
 
@@ -61,14 +56,6 @@ def flops_path(B, H, L, d):
 
 def decode_bytes(B, H, n, d, esize):
     return B * H * n * d * esize * 3.0  # K read + K write + V read
-
-
-def source_hash(kind: str) -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
 
 
 def load_traffic(kind: str):
@@ -163,7 +150,7 @@ def main():
     traffic = load_traffic("scan")
     roofline = {"bound": "mfma", "achieved": round(scan_tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "fwd_mfma_kernel<64> (right-to-left scan)", "flops_per_launch": F,
+                "kernel": "scan64_kernel (right-to-left scan, d=64)", "flops_per_launch": F,
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
     cpu = None

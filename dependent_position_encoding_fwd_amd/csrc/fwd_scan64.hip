@@ -288,10 +288,28 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) ckn[kt] = *reinterpret_cast<const f4*>(cumh + (2 * p) * C + 16 * kt + 4 * lg);
   }
+  // the in-block logits, forget-gate prefix and adjusted queries travel with
+  // the first stage (one latency, not three)
+  f4 sdv[NCT][4], ckd[4];
+  if (live) {
+    const float* sd = sdiag + (bh * Nb + mb) * (C * C);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int r = r0 + 16 * ct + ln;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sdv[ct][kt] = *reinterpret_cast<const f4*>(sd + r * C + 16 * kt + 4 * lg);
+      const float* src = qhat + (bh * Nb * C + mb * C + r) * D;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) qf[ct][t] = *reinterpret_cast<const f4*>(src + 16 * t + 4 * lg);
+    }
+    if constexpr (FOX) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) ckd[kt] = *reinterpret_cast<const f4*>(cumh + mb * C + 16 * kt + 4 * lg);
+    }
+  }
   sync_dma();
   if (live) {
     f4 x[NCT][4];
-    const float* sd = sdiag + (bh * Nb + mb) * (C * C);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int r = r0 + 16 * ct + ln;
@@ -299,13 +317,10 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int c0 = 16 * kt + 4 * lg;
-        const f4 s = *reinterpret_cast<const f4*>(sd + r * C + c0);
-        f4 ck;
-        if constexpr (FOX) ck = *reinterpret_cast<const f4*>(cumh + mb * C + c0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float val = s[i];
-          if constexpr (FOX) val += cq[ct] - ck[i];
+          float val = sdv[ct][kt][i];
+          if constexpr (FOX) val += cq[ct] - ckd[kt][i];
           x[ct][kt][i] = (c0 + i <= r) ? val : kNegInf;
           a = fmaxf(a, x[ct][kt][i]);
         }
@@ -315,12 +330,6 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
       for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= mrun[ct] - kOff;
     }
     softmax_pv(x, half == 0 ? sV0 : sV1);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const float* src = qhat + (bh * Nb * C + mb * C + r0 + 16 * ct + ln) * D;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) qf[ct][t] = *reinterpret_cast<const f4*>(src + 16 * t + 4 * lg);
-    }
   } else {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {

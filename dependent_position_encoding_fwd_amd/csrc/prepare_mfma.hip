@@ -235,10 +235,10 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     float acc[16], xr[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) acc[u] = xr[u] = 0.f;
-    // Column r of G (rows 4u+qq, u < (r+3)/4) and beta_r are read one row
+    // Column r of G (rows 4u+qq, u < (r+3)/4) and beta_r are read two rows
     // ahead, so the LDS latency stays off the serial chain.
-    f4 gc[4], gn[4];
-    float bc, bn = 0.f;
+    f4 gc[4], gn[4], gnn[4];
+    float bc, bn, bnn = 0.f;
     auto ldcol = [&](int r, f4 (&g)[4]) __attribute__((always_inline)) {
       const f4* src = reinterpret_cast<const f4*>(GY + r * 64 + qq * 16);  // G[4u+qq][r]
 #pragma unroll
@@ -246,12 +246,14 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
         if (4 * j < (r + 3) / 4) g[j] = src[j];
     };
     ldcol(C - 1, gc);
+    ldcol(C - 2, gn);
     bc = bs[C - 1];
+    bn = bs[C - 2];
 #pragma unroll
     for (int r = C - 1; r >= 0; --r) {
-      if (r > 0) {
-        ldcol(r - 1, gn);
-        bn = bs[r - 1];
+      if (r > 1) {
+        ldcol(r - 2, gnn);
+        bnn = bs[r - 2];
       }
       const int ur = r >> 2;
       float x = bc * ((r == c ? 1.f : 0.f) - acc[ur]);
@@ -262,8 +264,12 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
       for (int u = 0; u < (r + 3) / 4; ++u) acc[u] += gc[u >> 2][u & 3] * x;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gc[j] = gn[j];
+      for (int j = 0; j < 4; ++j) {
+        gc[j] = gn[j];
+        gn[j] = gnn[j];
+      }
       bc = bn;
+      bn = bnn;
     }
     // X^T rows: XT[c][perm(a)] = X[a][c], a = 4u + qq
 #pragma unroll

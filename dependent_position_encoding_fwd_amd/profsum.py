@@ -23,16 +23,33 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
+import hashlib
 import json
 import os
 import statistics
 from collections import defaultdict
 
 COPY_REF_BYTES = 1 << 30
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# Sources whose text determines each measured kernel; a traffic figure is
+# reported only while their hash matches the one recorded with it.
+KERNEL_SOURCES = {
+    "scan": ("fwd_scan64.hip", "mfma_util.h", "common.h"),
+    "decode": ("decode.hip", "common.h"),
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 # kernel classes, by a substring of the (mangled or demangled) name
 CLASSES = (
-    ("scan", "fwd_mfma_kernel"),
+    ("scan", "scan64_kernel"),
     ("prepare", "prepare_mfma_kernel"),
     ("head_reduce", "head_reduce_kernel"),
     ("decode_chunk", "decode_chunk_kernel"),
@@ -105,7 +122,7 @@ def read_bench(d: str):
 
 def short(name: str) -> str:
     c = classify(name)
-    return {"scan": "fwd_mfma_kernel<64> (scan)", "prepare": "prepare_mfma_kernel<64>",
+    return {"scan": "scan64_kernel (d=64 scan)", "prepare": "prepare_mfma_kernel<64>",
             "head_reduce": "head_reduce_kernel", "decode_chunk": "decode_chunk_kernel<bf16,64>",
             "decode_merge": "decode_merge_kernel<bf16,64>", "copy": "__amd_rocclr_copyBuffer"}.get(c, name[:60])
 
@@ -113,7 +130,7 @@ def short(name: str) -> str:
 def scan_algorithmic_bytes(B, H, L, d):
     """Bytes the scan must move at least once: its workspace inputs (fp16
     hi/lo keys, fp16 hi/lo block transitions, fp32 adjusted queries, fp32
-    diagonal logits, per-block norms and prefix) plus v in and o, lse out."""
+    diagonal logits, fp16 V^T, per-block norms and prefix) and o, lse out."""
     Nb = (L + 63) // 64
     bh = B * H
     khl = bh * Nb * 2 * 64 * d * 2
@@ -144,6 +161,10 @@ def main():
         hs = {b[k]["source_sha256"] for b in (bs, bf, bw)}
         if len(hs) != 1:
             raise ValueError(f"the three runs did not profile the same {k} kernel source")
+    # the runs' sources must be the tree's: the hashes recorded below are this tree's
+    for k, kind in (("roofline", "scan"), ("decode", "decode")):
+        if bs[k]["source_sha256"] != source_hash(kind):
+            raise ValueError(f"the {kind} kernel source changed since the profiled runs")
     fref, ffac, fetch = per_class(read_counters(a.fetch, "FETCH_SIZE"), True)
     wref, wfac, write = per_class(read_counters(a.write, "WRITE_SIZE"), True)
 
@@ -163,7 +184,7 @@ def main():
         "what": "HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a 1 GiB device copy",
         "copy_ref": {"bytes_each_way": COPY_REF_BYTES, "fetch_kib": fref, "write_kib": wref,
                      "fetch_factor": ffac, "write_factor": wfac},
-        "scan": {"kernel": "fwd_mfma_kernel<64>", "source_sha256": bs["roofline"]["source_sha256"],
+        "scan": {"kernel": "scan64_kernel<false>", "source_sha256": bs["roofline"]["source_sha256"],
                  "fetch_bytes_per_launch": scan_f, "write_bytes_per_launch": scan_w,
                  "bytes_per_launch": scan_f + scan_w, "algorithmic_bytes": alg_scan},
         "decode": {"kernel": "decode_chunk_kernel + decode_merge_kernel", "source_sha256":
