@@ -396,12 +396,22 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
     // bias is left out of the bound, so gated attention always takes the maxima.
     const bool skip_max = !FOX && (qbound * kn_cur * 1.01f <= mrun_min + kTheta);
     f4 x[NCT][4];
+    h8 ap[DC][DT];
     if (work) {
       h8 ak[DC][4];
 #pragma unroll
       for (int c = 0; c < DC; ++c)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) ak[c][kt] = rdA(tK, kt, c);
+      // the transition's operands are read now, in registers by R2 (the
+      // gated variant, short of registers, reads them at R2)
+      if constexpr (!FOX) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) ap[c][t] = rdA(tP, t, c);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -431,11 +441,12 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
     if (work) {
       const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
       // ---- R2: first half of Qt <- P_n Qt beside the row maxima
-      h8 ap[DC][DT];
+      if constexpr (FOX) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c)
+        for (int c = 0; c < DC; ++c)
 #pragma unroll
-        for (int t = 0; t < DT; ++t) ap[c][t] = rdA(tP, t, c);
+          for (int t = 0; t < DT; ++t) ap[c][t] = rdA(tP, t, c);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (skip_max) {
 #pragma unroll

@@ -21,8 +21,9 @@
 // 16-bit, the B operand of the next one in the same wave.  Products of two
 // stored inputs (bf16) are exact in one pass; a computed fp32 operand is split
 // into fp16 hi + lo and costs two or three passes (hi*hi + hi*lo + lo*hi).
-// T^{-1} comes from a back substitution (last row first) spread over all 256
-// lanes: 4 lanes per column, each keeping the partial sums of every fourth row.
+// T^{-1} is formed by 16-row blocks: each wave inverts one diagonal block by
+// back substitution (4 lanes per column), and the off-diagonal blocks follow
+// from fp32 16x16x4 MFMA products of those inverses with blocks of G.
 #include <math.h>
 
 #include "common.h"
@@ -210,74 +211,129 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       skq[mt] = mmb(ak, bq, skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
     }
   }
-  // G by columns in the quarter layout GY[t*64 + q*16 + u] = G[4u+q][t] (rows above t only)
+  // Diagonal 16x16 blocks of G by columns in the quarter layout
+  // GY[t*64 + q*16 + u] = G[4u+q][t] (rows above t only); wave w holds block (w, w).
   {
     const int t = 16 * wave + ln;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
+      if (mt == wave) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 16 * mt + 4 * lg + i;
-        GY[t * 64 + (s & 3) * 16 + (s >> 2)] = (s < t) ? gt[mt][i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * mt + 4 * lg + i;
+          GY[t * 64 + (s & 3) * 16 + (s >> 2)] = (s < t) ? gt[mt][i] : 0.f;
+        }
       }
   }
   __syncthreads();
 
-  // ---- X = T^{-1}: back substitution, 4 lanes per column --------------------------
-  // Row r of X (last row first) is X[r][c] = beta_r (delta_rc - acc_r) with
-  // acc_r = sum_{t>r} G[r][t] X[t][c].  Once row r is known it is added into the
-  // partial sums of all rows above it (independent FMAs), so the serial chain
-  // per row is a handful of operations.  Lane (c, qq) keeps acc and X for the
-  // rows r = 4u + qq.
+  // ---- X = T^{-1} diag(beta), T = I + diag(beta) strict_upper(G), by 16-row blocks -------
+  // Row r of T^{-1} (last row first) is  Tinv[r][c] = delta_rc - beta_r sum_{t>r} G[r][t] Tinv[t][c].
+  // With 16-row blocks I, J (T is block upper triangular):
+  //   D_I = T_II^{-1}                          (wave I: a 16-step back substitution)
+  //   E_IK = -D_I T_IK  (I < K)                (wave K: its G block column is in registers)
+  //   Tinv_IJ = sum_{K=I+1..J} E_IK Tinv_KJ    (wave J, nearest block first; Tinv_JJ = D_J)
+  // The block products are fp32 16x16x4 MFMAs.  Their operand B is the accumulator
+  // layout of a 16x16 tile (lane (g, j) holds rows 4g..4g+3 of column j); the
+  // reduction index of MFMA kc is then 4g + kc, which operand A (from LDS) follows.
+  constexpr int BP = 17;       // pitch (floats) of a 16x16 block in LDS
+  constexpr int BS = 16 * BP;  // floats per block
+  float* SD = reinterpret_cast<float*>(&XT[0][0]);  // D_0..D_3 (XT is written only at the end)
+  float* SE = SD + 4 * BS;                         // E_IK, I < K, at index I(7-I)/2 + K-I-1
   {
-    const int c = 16 * wave + (lane >> 2);
-    const int qq = lane & 3;
-    float acc[16], xr[16];
+    const int c = lane >> 2, qq = lane & 3;  // column c of block `wave`, rows 4u + qq
+    const int I = wave;
+    float bq[4], acc[4], d[4];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc[u] = xr[u] = 0.f;
-    // Column r of G (rows 4u+qq, u < (r+3)/4) and beta_r are read two rows
-    // ahead, so the LDS latency stays off the serial chain.
-    f4 gc[4], gn[4], gnn[4];
-    float bc, bn, bnn = 0.f;
-    auto ldcol = [&](int r, f4 (&g)[4]) __attribute__((always_inline)) {
-      const f4* src = reinterpret_cast<const f4*>(GY + r * 64 + qq * 16);  // G[4u+qq][r]
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (4 * j < (r + 3) / 4) g[j] = src[j];
-    };
-    ldcol(C - 1, gc);
-    ldcol(C - 2, gn);
-    bc = bs[C - 1];
-    bn = bs[C - 2];
-#pragma unroll
-    for (int r = C - 1; r >= 0; --r) {
-      if (r > 1) {
-        ldcol(r - 2, gnn);
-        bnn = bs[r - 2];
-      }
-      const int ur = r >> 2;
-      float x = bc * ((r == c ? 1.f : 0.f) - acc[ur]);
-      x = (r <= c) ? x : 0.f;
-      // the lane with qq == r % 4 holds the right acc; share its x within the quad
-      x = quad_bcast(x, r & 3);
-      if (qq == (r & 3)) xr[ur] = x;
-#pragma unroll
-      for (int u = 0; u < (r + 3) / 4; ++u) acc[u] += gc[u >> 2][u & 3] * x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        gc[j] = gn[j];
-        gn[j] = gnn[j];
-      }
-      bc = bn;
-      bn = bnn;
+    for (int u = 0; u < 4; ++u) {
+      bq[u] = bs[16 * I + 4 * u + qq];
+      acc[u] = d[u] = 0.f;
     }
-    // X^T rows: XT[c][perm(a)] = X[a][c], a = 4u + qq
+    const float* gcol = GY + 16 * I * 64 + qq * 16 + 4 * I;  // + r*64: G[16I+4u+qq][16I+r], u = 0..3
+    f4 gc = *reinterpret_cast<const f4*>(gcol + 15 * 64), gn = *reinterpret_cast<const f4*>(gcol + 14 * 64);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int a = 4 * u + qq;
-      const _Float16 hi = static_cast<_Float16>(xr[u]);
-      XT[0][c * TP + perm32(a)] = hi;
-      XT[1][c * TP + perm32(a)] = static_cast<_Float16>(xr[u] - static_cast<float>(hi));
+    for (int r = 15; r >= 0; --r) {
+      f4 gnn = gn;
+      if (r > 1) gnn = *reinterpret_cast<const f4*>(gcol + (r - 2) * 64);
+      const int ur = r >> 2;
+      float x = (r == c ? 1.f : 0.f) - bq[ur] * acc[ur];  // right on lanes qq == r % 4
+      x = quad_bcast(x, r & 3);
+      if (qq == (r & 3)) d[ur] = x;
+#pragma unroll
+      for (int u = 0; u < (r + 3) / 4; ++u) acc[u] += gc[u] * x;
+      gc = gn;
+      gn = gnn;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) SD[I * BS + (4 * u + qq) * BP + c] = d[u];
+  }
+  __syncthreads();
+  const int K = wave;
+  {
+    // E_IK = -D_I (diag(beta_I) G_IK); lane (lg, ln) holds G[16I+4lg+i][16K+ln] in gt[I][i]
+#pragma unroll
+    for (int I = 0; I < 3; ++I) {
+      if (I < K) {
+        f4 e = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const float b = bs[16 * I + 4 * lg + kc] * gt[I][kc];
+          const float av = SD[I * BS + ln * BP + 4 * lg + kc];
+          e = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b, e, 0, 0, 0);
+        }
+        float* dst = SE + (I * (7 - I) / 2 + K - I - 1) * BS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(4 * lg + i) * BP + ln] = -e[i];
+      }
+    }
+  }
+  __syncthreads();
+  // column block J = wave of T^{-1}: tc[I] holds Tinv_IJ in the accumulator layout
+  f4 tc[4];
+  {
+    const int J = wave;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) tc[I] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (I == J) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tc[I][i] = SD[J * BS + (4 * lg + i) * BP + ln];
+      }
+#pragma unroll
+    for (int I = 2; I >= 0; --I) {
+      if (I < J) {
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int Kb2 = I + 1; Kb2 < 4; ++Kb2) {
+          if (Kb2 <= J) {
+            const float* ea = SE + (I * (7 - I) / 2 + Kb2 - I - 1) * BS + ln * BP + 4 * lg;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kc], tc[Kb2][kc], acc, 0, 0, 0);
+          }
+        }
+        tc[I] = acc;
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with SD and SE (they share XT's space)
+  {
+    // X^T rows: XT[c][perm(a)] = X[a][c] = Tinv[a][c] beta_c, c = 16J + ln, a = 16I + 4lg + i
+    const int cc = 16 * wave + ln;
+    const float bc = bs[cc];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f4 x = tc[I] * bc;
+      H8u hv, lv;
+      hv.v = to_h8(x, x);
+      f4 lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo[i] = x[i] - static_cast<float>(hv.v[i]);
+      lv.v = to_h8(lo, lo);
+      const int off = cc * TP + 32 * (I >> 1) + 8 * lg + 4 * (I & 1);
+      *reinterpret_cast<uint2*>(&XT[0][off]) = make_uint2(hv.u.x, hv.u.y);
+      *reinterpret_cast<uint2*>(&XT[1][off]) = make_uint2(lv.u.x, lv.u.y);
     }
   }
   __syncthreads();  // XT ready; G no longer needed (GY becomes -Y)
