@@ -75,8 +75,9 @@ def load_traffic(kind: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # about 0.15 s of warm-up: the clocks take tens of milliseconds of load to settle
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--precision", default="auto", choices=["auto", "accurate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", action="store_true")

@@ -85,12 +85,24 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
   int p;
   int64_t bh;
   if (BH % 8 == 0) {
-    // workgroups go to the 8 XCDs round robin; give XCD x the heads x, x+8, ...
-    // so that the key blocks a head's tiles share stay in one L2, longest tiles first
+    // Workgroups go to the 8 XCDs round robin; XCD x gets the heads x, x+8, ...
+    // so that the key blocks a head's tiles share stay in one L2.  An XCD has
+    // about two heads' tiles in flight, so its heads are taken in pairs and the
+    // tiles of a pair longest first (a tile of query block pair p scans 2p+1 key
+    // blocks): the short tiles of both heads fill in at the end.
     const int xcd = blockIdx.x % 8;
     const int j = blockIdx.x / 8;
-    p = NP - 1 - (j % NP);
-    bh = xcd + 8 * static_cast<int64_t>(j / NP);
+    const int HX = BH / 8;
+    const int g = j / (2 * NP), r = j % (2 * NP);
+    int hh;
+    if (2 * g + 1 < HX) {
+      p = NP - 1 - r / 2;
+      hh = 2 * g + (r & 1);
+    } else {
+      p = NP - 1 - r;  // a last, unpaired head
+      hh = 2 * g;
+    }
+    bh = xcd + 8 * static_cast<int64_t>(hh);
   } else {
     p = NP - 1 - static_cast<int>(blockIdx.x / BH);  // longest tiles first
     bh = blockIdx.x % BH;
