@@ -148,23 +148,41 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   // row norms |w_s|^2 come from a shuffle reduction over them.  The value rows
   // are fetched last (they are needed only at the end; loads complete in order).
   constexpr int VCH = C * (D / 8) / 256;
-  uint4 vraw[VCH];
+  // Every load is issued before any is used, from a row clamped into the
+  // sequence (rows past its end are zeroed when stored), so they are all in
+  // flight together.
+  uint4 wv[VCH], kv[VCH], qv[VCH], vraw[VCH];
+  float br[VCH];
 #pragma unroll
   for (int j = 0; j < VCH; ++j) {
     const int idx = tid + 256 * j;
     const int r = idx / (D / 8), c8 = idx % (D / 8);
-    uint4 wv = make_uint4(0, 0, 0, 0), kv = wv, qv = wv;
-    float br = 0.f;
-    if (r < valid) {
-      wv = *reinterpret_cast<const uint4*>(w + base + r * D + 8 * c8);
-      kv = *reinterpret_cast<const uint4*>(k + base + r * D + 8 * c8);
-      qv = *reinterpret_cast<const uint4*>(q + base + r * D + 8 * c8);
-      br = beta[bh * L + t0 + r];
+    const int rr = r < valid ? r : valid - 1;
+    wv[j] = *reinterpret_cast<const uint4*>(w + base + rr * D + 8 * c8);
+    kv[j] = *reinterpret_cast<const uint4*>(k + base + rr * D + 8 * c8);
+    qv[j] = *reinterpret_cast<const uint4*>(q + base + rr * D + 8 * c8);
+    br[j] = beta[bh * L + t0 + rr];
+  }
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) {
+    const int idx = tid + 256 * j;
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    const int rr = r < valid ? r : valid - 1;
+    vraw[j] = *reinterpret_cast<const uint4*>(v + base + rr * D + 8 * c8);
+  }
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) {
+    const int idx = tid + 256 * j;
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    if (r >= valid) {
+      wv[j] = kv[j] = qv[j] = zero;
+      br[j] = 0.f;
     }
-    *reinterpret_cast<uint4*>(Wb + r * RP + 8 * c8) = wv;
-    *reinterpret_cast<uint4*>(Kb + r * RP + 8 * c8) = kv;
-    *reinterpret_cast<uint4*>(Qb + r * RP + 8 * c8) = qv;
-    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    *reinterpret_cast<uint4*>(Wb + r * RP + 8 * c8) = wv[j];
+    *reinterpret_cast<uint4*>(Kb + r * RP + 8 * c8) = kv[j];
+    *reinterpret_cast<uint4*>(Qb + r * RP + 8 * c8) = qv[j];
+    const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
     const int pb = perm32(r);
     float sq = 0.f;
 #pragma unroll
@@ -177,17 +195,11 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
     for (int off = 1; off < D / 8; off <<= 1) sq += __shfl_xor(sq, off, 64);
     if (c8 == 0) {
-      bs[r] = br;
+      bs[r] = br[j];
       // |H_s|_2 = max(1, |1 - beta_s |w_s|^2|): its product bounds the growth
       // of a transported query across the block
-      hn[r] = fmaxf(1.f, fabsf(1.f - br * sq));
+      hn[r] = fmaxf(1.f, fabsf(1.f - br[j] * sq));
     }
-  }
-#pragma unroll
-  for (int j = 0; j < VCH; ++j) {
-    const int idx = tid + 256 * j;
-    const int r = idx / (D / 8), c8 = idx % (D / 8);
-    vraw[j] = r < valid ? *reinterpret_cast<const uint4*>(v + base + r * D + 8 * c8) : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
@@ -473,7 +485,8 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     for (int j = 0; j < VCH; ++j) {
       const int idx = tid + 256 * j;
       const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const uint32_t vv[4] = {vraw[j].x, vraw[j].y, vraw[j].z, vraw[j].w};
+      const uint4 vr = r < valid ? vraw[j] : make_uint4(0, 0, 0, 0);
+      const uint32_t vv[4] = {vr.x, vr.y, vr.z, vr.w};
       const int pc = perm32(r);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
