@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   // Every load is issued before any is used, from a row clamped into the
   // sequence (rows past its end are zeroed when stored), so they are all in
   // flight together.
-  uint4 wv[VCH], kv[VCH], qv[VCH], vraw[VCH];
+  uint4 wv[VCH], kv[VCH], qv[VCH];
   float br[VCH];
 #pragma unroll
   for (int j = 0; j < VCH; ++j) {
@@ -163,12 +163,15 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     qv[j] = *reinterpret_cast<const uint4*>(q + base + rr * D + 8 * c8);
     br[j] = beta[bh * L + t0 + rr];
   }
-#pragma unroll
-  for (int j = 0; j < VCH; ++j) {
-    const int idx = tid + 256 * j;
-    const int r = idx / (D / 8), c8 = idx % (D / 8);
+  // value rows, already in the A-operand layout of the transposing product:
+  // lane (ln, lg) of wave w holds row 16w + ln, columns 32h + 8lg .. 32h + 8lg + 7
+  uint4 vraw[D / 32];
+  {
+    const int r = 16 * wave + ln;
     const int rr = r < valid ? r : valid - 1;
-    vraw[j] = *reinterpret_cast<const uint4*>(v + base + rr * D + 8 * c8);
+#pragma unroll
+    for (int h = 0; h < D / 32; ++h)
+      vraw[h] = *reinterpret_cast<const uint4*>(v + base + rr * D + 32 * h + 8 * lg);
   }
 #pragma unroll
   for (int j = 0; j < VCH; ++j) {
@@ -478,40 +481,42 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   }
   __syncthreads();  // -Y and -F^T rows complete; XT is free
 
-  // V^T[e][perm(c)] in fp16 through the XT area (pitch 64, no pad), then out in 16-byte rows
+  // V^T[e][perm(c)] in fp16, transposed on the matrix cores: with the value
+  // rows as operand A and a 32x16 slice of the identity as operand B, the
+  // product is V[:, slice] in the accumulator layout, where lane (lg, ln) holds
+  // the 4 consecutive keys 16w + 4lg .. 16w + 4lg + 3 of column 32h + 16s + ln:
+  // 8 contiguous bytes of a V^T row.  Exact: every product is by 1 or 0.
   {
-    _Float16* VS = &XT[0][0];
+    const int r = 16 * wave + ln;
+    _Float16* vtb = vt + (bh * Nb + n) * (D * C) + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int idx = tid + 256 * j;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const uint4 vr = r < valid ? vraw[j] : make_uint4(0, 0, 0, 0);
-      const uint32_t vv[4] = {vr.x, vr.y, vr.z, vr.w};
-      const int pc = perm32(r);
+    for (int s = 0; s < 2; ++s) {
+      b8 id;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        VS[(8 * c8 + 2 * e) * C + pc] = static_cast<_Float16>(__uint_as_float(vv[e] << 16));
-        VS[(8 * c8 + 2 * e + 1) * C + pc] = static_cast<_Float16>(__uint_as_float(vv[e] & 0xffff0000u));
+      for (int t = 0; t < 8; ++t) id[t] = static_cast<__bf16>((lg == ln / 8 + 2 * s && t == ln % 8) ? 1.f : 0.f);
+#pragma unroll
+      for (int h = 0; h < D / 32; ++h) {
+        union {
+          uint4 u;
+          b8 v;
+        } av;
+        av.u = r < valid ? vraw[h] : make_uint4(0, 0, 0, 0);
+        const f4 y = mmb(av.v, id, f4{0.f, 0.f, 0.f, 0.f});
+        const H8u hv = {to_h8(y, y)};
+        *reinterpret_cast<uint2*>(vtb + (32 * h + 16 * s + ln) * C) = make_uint2(hv.u.x, hv.u.y);
       }
     }
   }
 
-  if (tid == 0) {
-    const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
-    kmax[bh * Nb + n] = sqrtf(mx);
-    float g = 1.f;
-    for (int t = 0; t < C; ++t) g *= hn[t];
-    pnorm[bh * Nb + n] = g;
-  }
-
-  __syncthreads();
-  {
-    const _Float16* VS = &XT[0][0];
-    uint4* dst = reinterpret_cast<uint4*>(vt + (bh * Nb + n) * (D * C));
+  if (wave == 0) {
+    // product of the 64 factors |H_s|_2 by a butterfly over the wave
+    float g = hn[lane];
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int idx = tid + 256 * j;
-      dst[idx] = *reinterpret_cast<const uint4*>(&VS[8 * idx]);
+    for (int off = 1; off < 64; off <<= 1) g *= __shfl_xor(g, off, 64);
+    if (lane == 0) {
+      const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
+      kmax[bh * Nb + n] = sqrtf(mx);
+      pnorm[bh * Nb + n] = g;
     }
   }
 
