@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
   const int64_t base = (bh * L + t0) * D;
 
-  // ---- load W, K, Q rows (bf16) and W^T (fp16, perm columns) -----------------
+  // ---- load W, K, Q rows (bf16) ----------------------------------------------
   // Lanes idx .. idx + D/8 - 1 (consecutive, same wave) hold one row, so the
   // row norms |w_s|^2 come from a shuffle reduction over them.  The value rows
   // are fetched last (they are needed only at the end; loads complete in order).
@@ -186,13 +186,10 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     *reinterpret_cast<uint4*>(Kb + r * RP + 8 * c8) = kv[j];
     *reinterpret_cast<uint4*>(Qb + r * RP + 8 * c8) = qv[j];
     const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-    const int pb = perm32(r);
     float sq = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float lo = __uint_as_float(ww[e] << 16), hi = __uint_as_float(ww[e] & 0xffff0000u);
-      Wt[(8 * c8 + 2 * e) * TP + pb] = static_cast<_Float16>(lo);
-      Wt[(8 * c8 + 2 * e + 1) * TP + pb] = static_cast<_Float16>(hi);
       sq += lo * lo + hi * hi;
     }
 #pragma unroll
@@ -207,9 +204,19 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   __syncthreads();
 
   // ---- products of stored inputs (exact, one bf16 pass); wave w = column tile w
+  // W^T (fp16, rows e, columns perm(b)) comes from the same pass: this wave's
+  // W rows b = 16w .. 16w + 15, the B operand below, times a 32x16 slice of the
+  // identity give W[b][32c + 16s + ln] for b = 16w + 4lg .. 16w + 4lg + 3 in
+  // lane (lg, ln), 8 contiguous bytes of W^T row 32c + 16s + ln.
   f4 gt[4], zt[4], ut[4], skq[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) gt[mt] = zt[mt] = ut[mt] = skq[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  b8 ident[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ident[s][t] = static_cast<__bf16>((lg == ln / 8 + 2 * s && t == ln % 8) ? 1.f : 0.f);
+  _Float16* wtb = Wt + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     const int col = 32 * c + 8 * lg;
@@ -224,6 +231,12 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       zt[mt] = mmb(aw, bk, zt[mt]);    // Z^T[a][c]    = w_a . k_c
       ut[mt] = mmb(aw, bq, ut[mt]);    // U[b][r]      = w_b . q_r
       skq[mt] = mmb(ak, bq, skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f4 y = mmb(bw, ident[s], f4{0.f, 0.f, 0.f, 0.f});
+      const H8u hv = {to_h8(y, y)};
+      *reinterpret_cast<uint2*>(wtb + (32 * c + 16 * s + ln) * TP) = make_uint2(hv.u.x, hv.u.y);
     }
   }
   // Diagonal 16x16 blocks of G by columns in the quarter layout
@@ -491,9 +504,6 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     _Float16* vtb = vt + (bh * Nb + n) * (D * C) + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      b8 id;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) id[t] = static_cast<__bf16>((lg == ln / 8 + 2 * s && t == ln % 8) ? 1.f : 0.f);
 #pragma unroll
       for (int h = 0; h < D / 32; ++h) {
         union {
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
           b8 v;
         } av;
         av.u = r < valid ? vraw[h] : make_uint4(0, 0, 0, 0);
-        const f4 y = mmb(av.v, id, f4{0.f, 0.f, 0.f, 0.f});
+        const f4 y = mmb(av.v, ident[s], f4{0.f, 0.f, 0.f, 0.f});
         const H8u hv = {to_h8(y, y)};
         *reinterpret_cast<uint2*>(vtb + (32 * h + 16 * s + ln) * C) = make_uint2(hv.u.x, hv.u.y);
       }
