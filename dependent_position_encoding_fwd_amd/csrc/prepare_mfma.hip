@@ -163,6 +163,16 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     qv[j] = *reinterpret_cast<const uint4*>(q + base + rr * D + 8 * c8);
     br[j] = beta[bh * L + t0 + rr];
   }
+  // this lane's key entries for the adjusted keys: row 16w + ln, columns 16et + 4lg .. + 3
+  uint2 kr[DT];
+  {
+    const int r = 16 * wave + ln;
+    const int rr = r < valid ? r : valid - 1;
+#pragma unroll
+    for (int et = 0; et < DT; ++et) {
+      kr[et] = *reinterpret_cast<const uint2*>(k + base + rr * D + 16 * et + 4 * lg);  // masked at use
+    }
+  }
   // value rows, already in the A-operand layout of the transposing product:
   // lane (ln, lg) of wave w holds row 16w + ln, columns 32h + 8lg .. 32h + 8lg + 7
   uint4 vraw[D / 32];
@@ -266,8 +276,10 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   // reduction index of MFMA kc is then 4g + kc, which operand A (from LDS) follows.
   constexpr int BP = 17;       // pitch (floats) of a 16x16 block in LDS
   constexpr int BS = 16 * BP;  // floats per block
-  float* SD = reinterpret_cast<float*>(&XT[0][0]);  // D_0..D_3 (XT is written only at the end)
-  float* SE = SD + 4 * BS;                         // E_IK, I < K, at index I(7-I)/2 + K-I-1
+  // The W and K rows are dead once the products are formed (the adjusted keys
+  // read K again from global memory), so the blocks live in their space.
+  float* SD = reinterpret_cast<float*>(WK);  // D_0..D_3
+  float* SE = SD + 4 * BS;                   // E_IK, I < K, at index I(7-I)/2 + K-I-1
   {
     const int c = lane >> 2, qq = lane & 3;  // column c of block `wave`, rows 4u + qq
     const int I = wave;
@@ -345,7 +357,6 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       }
     }
   }
-  __syncthreads();  // every wave is done with SD and SE (they share XT's space)
   {
     // X^T rows: XT[c][perm(a)] = X[a][c] = Tinv[a][c] beta_c, c = 16J + ln, a = 16I + 4lg + i
     const int cc = 16 * wave + ln;
@@ -410,7 +421,10 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     for (int et = 0; et < DT; ++et) {
       f4 acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = -bf2f(Kb[cc * RP + 16 * et + 4 * lg + i]);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wd = i < 2 ? kr[et].x : kr[et].y;
+        acc[i] = cc < valid ? -__uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16)) : 0.f;
+      }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const h8 a = *reinterpret_cast<const h8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
@@ -439,7 +453,6 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 
   // ---- F = X^T W (rows b, columns e) and P^T = I - W^T F ---------------------------
   // wave w owns head-dim column tiles et = ET*w .. ET*w + ET - 1
-  __syncthreads();  // all waves are done with Kb and Wb (WK becomes -F^T rows)
 #pragma unroll
   for (int j = 0; j < ET; ++j) {
     const int et = ET * wave + j;
