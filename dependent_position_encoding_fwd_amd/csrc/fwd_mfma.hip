@@ -495,8 +495,8 @@ hipError_t launch_fwd_mfma(int64_t B, int64_t H, int64_t L, int64_t d, int accur
   if (d == 64)
     return launch_scan64(B * H, L, accurate, tau, vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, o,
                          lse, stream);
-  return launch_fwd_mfma_t<128>(B * H, L, accurate, tau, vt, khat, pmat, qhat, sdiag, kmax_head, pnorm, cum, o,
-                                lse, stream);
+  return launch_scan128(B * H, L, accurate, tau, vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, o,
+                        lse, stream);
 }
 
 }  // namespace path

@@ -1,0 +1,529 @@
+// Right-to-left scan forward of PaTH attention for head dimension 128 (gfx950),
+// with the key-side operands streamed into LDS by direct-to-LDS loads.
+//
+// [PaTH Attention summary (gist.science 2505.16381), §2 "Mecanismo Central"]
+//     s_ij = scale * k_j^T (H_{j+1} ... H_i) q_i   (+ FoX bias), softmax over j <= i
+// [§3 "Algoritmo Estilo FlashAttention"]  A workgroup of 8 waves owns the
+// 64-query blocks 2p and 2p+1 (4 waves of 16 queries each), starts each from
+// its in-block logits and boundary-adjusted queries, and walks key blocks
+// n = 2p .. 0 with
+//     S^T = Khat_n Qt - m,  online softmax (exp2),  O^T += V_n^T P^T,  Qt = P_n Qt.
+// [§2 "Extensões: PaTH-FoX"] adds cum_i - cum_j (log2 units) to each logit.
+//
+// The arithmetic and data layouts are those of the head-dimension-64 scan; the
+// tiles are larger (Khat_n 64x128, P_n 128x128, V_n^T 128x64 in fp16: 16, 32
+// and 16 KB), which sets the LDS plan (144 KB, one workgroup per CU):
+//   * Khat_n and V_n^T have two stages: block n-1 is fetched while block n is
+//     computed; one barrier at the end of a block publishes it.
+//   * P_n has one stage.  Once every wave has finished the transition of the
+//     queries (the only reader of P_n), a barrier frees it and P_{n-1} is
+//     fetched; it lands during the PV products and is published by the same
+//     end-of-block barrier.
+//   * The fp16 lo parts of Khat_n and P_n (split-precision blocks only) are
+//     fetched one block ahead into registers and stored into one LDS stage.
+//   * Rows of 16 chunks (Khat, P) keep chunk j of row r at j ^ (r & 15), rows
+//     of 8 chunks (V^T) at j ^ (r & 7), so that the MFMA operand reads (16
+//     rows, one chunk column) run at the full LDS read rate.
+// Each tile is its own LDS object and every access names it at compile time.
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "mfma_util.h"
+
+namespace path {
+namespace {
+
+using namespace mfma;
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kNegInf = -INFINITY;
+constexpr float kTheta = 8.f;  // logits may exceed the running max by kTheta before it is raised
+constexpr float kOff = 7.f;    // probabilities are scaled by 2^kOff (<= 2^15 < fp16 max)
+
+constexpr int kD = 128;            // head dimension
+constexpr int kNW = 8;             // waves
+constexpr int kNT = 64 * kNW;      // threads
+constexpr int kWPB = 4;            // waves per 64-query block
+constexpr int kKT = 64 * kD;       // halfs of a Khat tile (64 x 128)
+constexpr int kPT = kD * kD;       // halfs of a P tile (128 x 128)
+constexpr int kVT = kD * 64;       // halfs of a V^T tile (128 x 64)
+
+// Barrier that also publishes every direct-to-LDS load this wave issued (see
+// the head-dimension-64 scan for why the wait is a builtin and the barrier an
+// asm statement with a memory clobber).
+__device__ __forceinline__ void sync_dma() {
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  asm volatile("s_barrier" ::: "memory");
+}
+// Barrier after this wave's LDS reads are done (no wait on global loads).
+__device__ __forceinline__ void sync_lds() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+}  // namespace
+
+template <bool FOX>
+__global__ __launch_bounds__(kNT, 1) void scan128_kernel(
+    int64_t L, int Nb, int BH, int accurate_all, float tau, const _Float16* __restrict__ vt,
+    const _Float16* __restrict__ khat, const _Float16* __restrict__ pmat,
+    const float* __restrict__ qhat, const float* __restrict__ sdiag,
+    const float* __restrict__ kmax_head, const float* __restrict__ kmax_blk, const float* __restrict__ pnorm,
+    const float* __restrict__ cum, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  constexpr int D = kD, C = kBlk, DT = D / 16, DC = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) _Float16 sK0[kKT], sV0[kVT];
+  __shared__ __attribute__((aligned(1024))) _Float16 sK1[kKT], sV1[kVT];
+  __shared__ __attribute__((aligned(1024))) _Float16 sP[kPT];
+  __shared__ __attribute__((aligned(1024))) _Float16 sKl[kKT], sPl[kPT];
+  __shared__ float red[2][kNW];
+
+  const int NP = (Nb + 1) / 2;
+  int p;
+  int64_t bh;
+  if (BH % 8 == 0) {
+    // XCD x takes the heads x, x+8, ... (their key blocks stay in one L2),
+    // in pairs, the tiles of a pair longest first
+    const int xcd = blockIdx.x % 8;
+    const int j = blockIdx.x / 8;
+    const int HX = BH / 8;
+    const int g = j / (2 * NP), r = j % (2 * NP);
+    int hh;
+    if (2 * g + 1 < HX) {
+      p = NP - 1 - r / 2;
+      hh = 2 * g + (r & 1);
+    } else {
+      p = NP - 1 - r;
+      hh = 2 * g;
+    }
+    bh = xcd + 8 * static_cast<int64_t>(hh);
+  } else {
+    p = NP - 1 - static_cast<int>(blockIdx.x / BH);  // longest tiles first
+    bh = blockIdx.x % BH;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int half = wave / kWPB;
+  const int mb = 2 * p + half;        // this wave's query block
+  const bool live = mb < Nb;
+  const int r0 = (wave % kWPB) * 16;  // first query row (local to block mb)
+  const float khmax = kmax_head[bh];
+  const float* cumh = FOX ? cum + bh * Nb * C : nullptr;
+
+  // this head's prepared blocks (hi tile, then lo tile, per block)
+  const char* kh_h = reinterpret_cast<const char*>(khat + bh * Nb * (2 * kKT));
+  const char* pm_h = reinterpret_cast<const char*>(pmat + bh * Nb * (2 * kPT));
+  const char* vt_h = reinterpret_cast<const char*>(vt + bh * Nb * kVT);
+  constexpr int TBK = kKT * 2, TBP = kPT * 2, TBV = kVT * 2;  // bytes per tile
+
+  // ---- direct-to-LDS staging ------------------------------------------------------
+  // Slot i of this wave covers LDS chunks (NS*wave + i)*64 + lane of a tile; the
+  // lane fetches the logical chunk that belongs there.
+  uint32_t goffK[2], goffP[4], goffV[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pos = (2 * wave + i) * 64 + lane;
+    const int r = pos >> 4;
+    goffK[i] = static_cast<uint32_t>(r * 256 + ((pos & 15) ^ (r & 15)) * 16);
+    const int rv = pos >> 3;
+    goffV[i] = static_cast<uint32_t>(rv * 128 + ((pos & 7) ^ (rv & 7)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (4 * wave + i) * 64 + lane;
+    const int r = pos >> 4;
+    goffP[i] = static_cast<uint32_t>(r * 256 + ((pos & 15) ^ (r & 15)) * 16);
+  }
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto tileK = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return sK0; else return sK1;
+  };
+  auto tileV = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return sV0; else return sV1;
+  };
+  auto dmaK = [&](int n, _Float16* ltile) __attribute__((always_inline)) {
+    const char* g = kh_h + static_cast<int64_t>(n) * (2 * TBK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(g + goffK[i], ltile + (2 * wave + i) * 512, 16, 0, 0);
+  };
+  auto dmaV = [&](int n, _Float16* ltile) __attribute__((always_inline)) {
+    const char* g = vt_h + static_cast<int64_t>(n) * TBV;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(g + goffV[i], ltile + (2 * wave + i) * 512, 16, 0, 0);
+  };
+  auto dmaP = [&](int n) __attribute__((always_inline)) {
+    const char* g = pm_h + static_cast<int64_t>(n) * (2 * TBP);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(g + goffP[i], sP + (4 * wave + i) * 512, 16, 0, 0);
+  };
+  // lo parts: thread t owns LDS chunks t + 512 j of each lo tile
+  uint32_t loffK[2], loffP[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pos = tid + kNT * j;
+    const int r = pos >> 4;
+    const uint32_t off = static_cast<uint32_t>(r * 256 + ((pos & 15) ^ (r & 15)) * 16);
+    if (j < 2) loffK[j] = off;
+    loffP[j] = off;
+  }
+  u4 lopre[6];  // lo parts of the next split-precision block (Khat lo x2, P lo x4)
+  auto fetch_lo = [&](int n) __attribute__((always_inline)) {
+    const char* kb = kh_h + static_cast<int64_t>(n) * (2 * TBK) + TBK;
+    const char* pb = pm_h + static_cast<int64_t>(n) * (2 * TBP) + TBP;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lopre[j] = *reinterpret_cast<const u4*>(kb + loffK[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lopre[2 + j] = *reinterpret_cast<const u4*>(pb + loffP[j]);
+  };
+  auto put_lo = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u4*>(sKl + 8 * (tid + kNT * j)) = lopre[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u4*>(sPl + 8 * (tid + kNT * j)) = lopre[2 + j];
+  };
+  // MFMA A operands.  Khat / P (16 chunks per row): rows 16t + ln, logical chunk
+  // 4c + lg.  V^T (8 chunks per row): rows 16t + ln, logical chunk 4c + lg, c < 2.
+  int aoff16[DC], aoffV[2];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) aoff16[c] = ln * 128 + ((4 * c + lg) ^ ln) * 8;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) aoffV[c] = ln * 64 + ((4 * c + lg) ^ (ln & 7)) * 8;
+  auto rdA16 = [&](const _Float16* tile, int t, int c) __attribute__((always_inline)) {
+    return *reinterpret_cast<const h8*>(tile + t * 2048 + aoff16[c]);
+  };
+  auto rdV = [&](const _Float16* tile, int t, int c) __attribute__((always_inline)) {
+    return *reinterpret_cast<const h8*>(tile + t * 1024 + aoffV[c]);
+  };
+
+  // ---- per-wave state (16 queries: column ln of the accumulator tiles) ------------
+  f4 oacc[DT], qf[DT];
+  f4 lacc;  // softmax denominator (every element holds the column sum)
+  h8 qhi[DC], qlo[DC];
+  auto to_b_operands = [&](bool with_lo) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      qhi[c] = pack_h8(qf[2 * c], qf[2 * c + 1]);
+      if (with_lo) qlo[c] = pack_lo(qf[2 * c], qf[2 * c + 1], qhi[c]);
+    }
+  };
+  float mrun, cq;
+  f4 seed;         // cq - mrun + kOff: the accumulator start of S^T
+  float mrun_min;  // min of mrun over the wave's queries
+  auto set_seeds = [&]() __attribute__((always_inline)) {
+    const float sv = (FOX ? cq : 0.f) - mrun + kOff;
+    seed = f4{sv, sv, sv, sv};
+    mrun_min = -wave_max(-mrun);
+  };
+  lacc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f4{0.f, 0.f, 0.f, 0.f};
+  cq = (FOX && live) ? cumh[mb * C + r0 + ln] : 0.f;
+  const h8 ones = h8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+
+  // exponentials of x (logit - mrun + kOff) as the two fp16 B operands of PV
+  auto exps = [&](const f4 (&x)[4], h8 (&pb)[2]) __attribute__((always_inline)) {
+    f4 pe[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe[kt][i] = __builtin_amdgcn_exp2f(x[kt][i]);
+    pb[0] = pack_h8(pe[0], pe[1]);
+    pb[1] = pack_h8(pe[2], pe[3]);
+  };
+  auto rowmax = [&](const f4 (&x)[4]) __attribute__((always_inline)) {
+    float a = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3]));
+#pragma unroll
+    for (int kt = 1; kt < 4; ++kt) a = fmaxf(a, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+    return grp_max(a);
+  };
+  auto rescale = [&](float mx, f4 (&x)[4]) __attribute__((always_inline)) {
+    const float sh = fmaxf(mx - kOff, 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-sh);
+    mrun += sh;
+    lacc *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x[kt] -= sh;
+  };
+  auto pv = [&](const _Float16* vtile, const h8 (&pb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] = mma16(rdV(vtile, t, c), pb[c], oacc[t]);
+      lacc = mma16(ones, pb[c], lacc);
+    }
+  };
+
+  auto wave_qnorm = [&]() __attribute__((always_inline)) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s2 += qf[t][i] * qf[t][i];
+    return sqrtf(wave_max(grp_sum(s2)));
+  };
+
+  // ---- diagonal blocks, and the operands of key block 2p ------------------------------
+  // V^T of block 2p lands in stage 0 (it is also the first scanned block); that
+  // of block 2p+1 uses stage 1's V^T tile, free until the first prefetch.
+  dmaK(2 * p, sK0);
+  dmaV(2 * p, sV0);
+  dmaP(2 * p);
+  if (2 * p + 1 < Nb) dmaV(2 * p + 1, sV1);
+  fetch_lo(2 * p);  // used only if block 2p runs the split products
+  f4 ckn[4];  // FoX prefix of the key block being scanned
+  if constexpr (FOX) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) ckn[kt] = *reinterpret_cast<const f4*>(cumh + (2 * p) * C + 16 * kt + 4 * lg);
+  }
+  f4 sdv[4], ckd[4];
+  if (live) {
+    const float* sd = sdiag + (bh * Nb + mb) * (C * C);
+    const int r = r0 + ln;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) sdv[kt] = *reinterpret_cast<const f4*>(sd + r * C + 16 * kt + 4 * lg);
+    const float* src = qhat + (bh * Nb * C + mb * C + r) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) qf[t] = *reinterpret_cast<const f4*>(src + 16 * t + 4 * lg);
+    if constexpr (FOX) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) ckd[kt] = *reinterpret_cast<const f4*>(cumh + mb * C + 16 * kt + 4 * lg);
+    }
+  }
+  sync_dma();
+  if (live) {
+    f4 x[4];
+    const int r = r0 + ln;
+    float a = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int c0 = 16 * kt + 4 * lg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float val = sdv[kt][i];
+        if constexpr (FOX) val += cq - ckd[kt][i];
+        x[kt][i] = (c0 + i <= r) ? val : kNegInf;
+        a = fmaxf(a, x[kt][i]);
+      }
+    }
+    mrun = grp_max(a);  // finite: key r is always present
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) x[kt] -= mrun - kOff;
+    h8 pb[2];
+    exps(x, pb);
+    pv(half == 0 ? sV0 : sV1, pb);
+  } else {
+    mrun = 0.f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) qf[t] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  set_seeds();
+  const float qn0 = wave_qnorm();
+  if (lane == 0) red[0][wave] = qn0;
+  sync_dma();  // stage 1 is free for the first prefetch; norms visible
+
+  float qbound = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < kNW; ++w2) qbound = fmaxf(qbound, red[0][w2]);
+  bool acc_cur = accurate_all || (qbound * khmax * 0.0009765625f > tau);
+  to_b_operands(acc_cur);
+
+  // ---- right-to-left scan ----------------------------------------------------------
+  float pn = pnorm[bh * Nb + 2 * p];
+  float kn = kmax_blk[bh * Nb + 2 * p];
+  auto step = [&](int n, auto st) __attribute__((always_inline)) {
+    using SN = std::integral_constant<int, 1 - decltype(st)::value>;
+    const _Float16* tK = tileK(st);
+    const _Float16* tV = tileV(st);
+    f4 ck[4];
+    if constexpr (FOX) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        ck[kt] = ckn[kt];
+        if (n > 0) ckn[kt] = *reinterpret_cast<const f4*>(cumh + (n - 1) * C + 16 * kt + 4 * lg);
+      }
+    }
+    const float pn_cur = pn, kn_cur = kn;
+    if (n > 0) {
+      pn = pnorm[bh * Nb + n - 1];
+      kn = kmax_blk[bh * Nb + n - 1];
+    }
+    if (acc_cur) put_lo();
+    if (n > 0) {
+      dmaK(n - 1, tileK(SN{}));
+      dmaV(n - 1, tileV(SN{}));
+    }
+    const float qb_next = qbound * pn_cur;
+    const bool acc_next = accurate_all || (qb_next * khmax * 0.0009765625f > tau);
+    if (acc_next && n > 0) fetch_lo(n - 1);
+    const bool work = live && !(half == 0 && n == 2 * p);
+    // no logit of this block can pass the running max by kTheta when
+    // |Qt| * max|khat| (Cauchy-Schwarz; 1.01 covers the fp16 operands) stays below it
+    const bool skip_max = !FOX && (qbound * kn_cur * 1.01f <= mrun_min + kTheta);
+
+    // ---- R1: S^T = Khat Qt - m + kOff
+    f4 x[4];
+    if (work) {
+      h8 ak[DC][4];
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) ak[c][kt] = rdA16(tK, kt, c);
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(ak[c][kt], qhi[c], c == 0 ? seed : x[kt]);
+    }
+    if (acc_cur) {
+      sync_lds();  // every thread's share of the lo tiles is in LDS
+      if (work) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            x[kt] = mma16(rdA16(sKl, kt, c), qhi[c], x[kt]);
+            x[kt] = mma16(rdA16(tK, kt, c), qlo[c], x[kt]);
+          }
+      }
+    }
+    h8 pb[2];
+    if (work) {
+      const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
+      // ---- R2: first half of Qt <- P_n Qt beside the row maximum
+      {
+        h8 ap[2][DT];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) ap[c][t] = rdA16(sP, t, c);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) qf[t] = mma16(ap[0][t], qhi[0], zero);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) qf[t] = mma16(ap[1][t], qhi[1], qf[t]);
+      }
+      if (!skip_max) {
+        if constexpr (FOX) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) x[kt] -= ck[kt];
+        }
+        const float mx = rowmax(x);
+        if (__any(mx > kTheta + kOff)) {  // rare: raise the running max
+          rescale(mx, x);
+          set_seeds();
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- R3: second half of the transition beside the exponentials
+      {
+        h8 ap[2][DT];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) ap[c][t] = rdA16(sP, t, 2 + c);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) qf[t] = mma16(ap[c][t], qhi[2 + c], qf[t]);
+      }
+      exps(x, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (acc_cur) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            qf[t] = mma16(rdA16(sPl, t, c), qhi[c], qf[t]);
+            qf[t] = mma16(rdA16(sP, t, c), qlo[c], qf[t]);
+          }
+      }
+    }
+    // P_n is read by no one any more: fetch P_{n-1} into its place
+    if (n > 0) {
+      sync_lds();
+      dmaP(n - 1);
+    }
+    if (work) {
+      // ---- R4: PV beside the conversion of the transported queries
+      pv(tV, pb);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) qhi[c] = pack_h8(qf[2 * c], qf[2 * c + 1]);
+      if (acc_next) {
+        asm volatile("");  // a real branch: the lo parts are rarely needed
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qlo[c] = pack_lo(qf[2 * c], qf[2 * c + 1], qhi[c]);
+      }
+    }
+    // measured norms while the split is in use; the carried bound otherwise
+    const int slot = n & 1;
+    if (acc_next && n > 0) {
+      const float qn = (work || !live) ? wave_qnorm() : 0.f;
+      if (lane == 0) red[slot][wave] = qn;
+    }
+    sync_dma();  // next stages landed; this stage's reads done; norms visible
+    if (acc_next && n > 0) {
+      float qm = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kNW; ++w2) qm = fmaxf(qm, red[slot][w2]);
+      // waves that skipped this block still hold their previous (untransported) queries
+      qbound = fmaxf(qm, (n == 2 * p) ? qbound : 0.f);
+    } else {
+      qbound = qb_next;
+    }
+    acc_cur = acc_next && (accurate_all || (qbound * khmax * 0.0009765625f > tau));
+  };
+
+  for (int n = 2 * p; n >= 0; n -= 2) {
+    step(n, S0{});
+    if (n > 0) step(n - 1, S1{});
+  }
+
+  // ---- epilogue -------------------------------------------------------------------
+  if (live) {
+    const float l = lacc[0];
+    const int r = r0 + ln;
+    const int64_t row = static_cast<int64_t>(mb) * C + r;
+    if (row < L) {
+      const float inv = 1.f / l;
+      uint16_t* dst = o + (bh * L + row) * D;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const f4 y = oacc[t] * inv;
+        B8 pk;
+        pk.p[0] = __builtin_convertvector(f2{y[0], y[1]}, b2);
+        pk.p[1] = __builtin_convertvector(f2{y[2], y[3]}, b2);
+        *reinterpret_cast<uint2*>(dst + 16 * t + 4 * lg) = make_uint2(pk.u.x, pk.u.y);
+      }
+      if (lg == 0) lse[bh * L + row] = (mrun - kOff + __log2f(l)) * kLn2;
+    }
+  }
+}
+
+hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
+                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
+                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
+                          void* o, float* lse, hipStream_t stream) {
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  const int NP = (Nb + 1) / 2;
+  dim3 grid(static_cast<unsigned>(BH * NP));
+  dim3 block(kNT);
+  if (cum) {
+    hipLaunchKernelGGL((scan128_kernel<true>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
+                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, static_cast<uint16_t*>(o), lse);
+  } else {
+    hipLaunchKernelGGL((scan128_kernel<false>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
+                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, static_cast<uint16_t*>(o), lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace path

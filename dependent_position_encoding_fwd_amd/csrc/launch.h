@@ -40,6 +40,10 @@ hipError_t launch_scan64(int64_t BH, int64_t L, int accurate, float tau, const _
                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
                          void* o, float* lse, hipStream_t stream);
+hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
+                         const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
+                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
+                         void* o, float* lse, hipStream_t stream);
 
 hipError_t launch_fwd_mfma(int64_t B, int64_t H, int64_t L, int64_t d, int accurate, float tau,
                            const _Float16* vt, const _Float16* khat, const _Float16* pmat,
