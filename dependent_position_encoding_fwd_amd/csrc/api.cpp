@@ -203,8 +203,10 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
     return hip_status(path::launch_fwd_scan_f32(dtype, B, H, L, d, scale, q, k, v, w, beta, cum,
                                                 khat, pT, o, lse, stream));
   }
-  return hip_status(path::launch_fwd_mfma(
-      B, H, L, d, precision == PATH_PREC_ACCURATE ? 1 : 0, kAutoTau,
+  // one matrix-core scan per head dimension (64 or 128; check_d rejects others)
+  auto scan = d == 64 ? path::launch_scan64 : path::launch_scan128;
+  return hip_status(scan(
+      B * H, L, precision == PATH_PREC_ACCURATE ? 1 : 0, kAutoTau,
       reinterpret_cast<const _Float16*>(ws + a.lay.vt), reinterpret_cast<const _Float16*>(ws + a.lay.khl),
       reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
       reinterpret_cast<const float*>(ws + a.lay.qhat),

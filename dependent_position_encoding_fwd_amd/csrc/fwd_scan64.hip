@@ -3,13 +3,15 @@
 //
 // [PaTH Attention summary (gist.science 2505.16381), §2 "Mecanismo Central"]
 //     s_ij = scale * k_j^T (H_{j+1} ... H_i) q_i   (+ FoX bias), softmax over j <= i
-// [§3 "Algoritmo Estilo FlashAttention"]  The arithmetic is that of the
-// general matrix-core scan (fwd_mfma.hip): a workgroup of 4 waves owns the
+// [§3 "Algoritmo Estilo FlashAttention"]  A workgroup of 4 waves owns the
 // 64-query blocks 2p and 2p+1, starts each from its in-block logits and
 // boundary-adjusted queries, and walks key blocks n = 2p .. 0 with
 //     S^T = Khat_n Qt - m,  online softmax (exp2),  O^T += V_n^T P^T,  Qt = P_n Qt.
+// Products take fp16 operands and fp32 accumulators; a computed fp32 operand
+// (Qt) is split into fp16 hi + lo on the blocks where a bound says the lo part
+// matters (split precision), and probabilities are 2^(s - m + 7) in fp16.
 //
-// What differs is the data movement, built for CDNA4:
+// The data movement is built for CDNA4:
 //   * Khat_n, P_n and V_n^T (fp16, 8 KB each) travel global -> LDS with
 //     global_load_lds_dwordx4: each lane names its source, the data land at
 //     consecutive 16-byte slots, no VGPRs or LDS store instructions involved.

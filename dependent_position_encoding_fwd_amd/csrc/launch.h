@@ -34,22 +34,16 @@ hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float
 hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head,
                               const float* log_forget, float mult, float* cum, hipStream_t stream);
 
-// Matrix-core right-to-left scan forward (bf16 storage).
-// Head dimension 64: the same scan with direct-to-LDS double-buffered operands.
+// Matrix-core right-to-left scan forward (bf16 storage), head dimension 64
+// and 128, from the prepared blocks; operands reach LDS by direct-to-LDS loads.
 hipError_t launch_scan64(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
                          void* o, float* lse, hipStream_t stream);
 hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
-                         const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
-                         void* o, float* lse, hipStream_t stream);
-
-hipError_t launch_fwd_mfma(int64_t B, int64_t H, int64_t L, int64_t d, int accurate, float tau,
-                           const _Float16* vt, const _Float16* khat, const _Float16* pmat,
-                           const float* qhat, const float* sdiag, const float* kmax_head,
-                           const float* kmax_blk, const float* pnorm, const float* cum, void* o, float* lse,
-                           hipStream_t stream);
+                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
+                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
+                          void* o, float* lse, hipStream_t stream);
 
 // c[bh, i] = sum_{s<=i} x[bh, s], accumulated in fp64.
 hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream);
