@@ -19,8 +19,11 @@
 //     queries (the only reader of P_n), a barrier frees it and P_{n-1} is
 //     fetched; it lands during the PV products and is published by the same
 //     end-of-block barrier.
-//   * The fp16 lo parts of Khat_n and P_n (split-precision blocks only) are
-//     fetched one block ahead into registers and stored into one LDS stage.
+//   * The fp16 lo parts of Khat_n and P_n (split-precision blocks only) have
+//     one stage.  They are fetched with P_{n-1}, once this block's
+//     split-precision products are done.
+//   * With forget gates, the gate prefix of the 64 keys (256 bytes) travels
+//     with Khat and V^T.
 //   * Rows of 16 chunks (Khat, P) keep chunk j of row r at j ^ (r & 15), rows
 //     of 8 chunks (V^T) at j ^ (r & 7), so that the MFMA operand reads (16
 //     rows, one chunk column) run at the full LDS read rate.
@@ -79,6 +82,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   __shared__ __attribute__((aligned(1024))) _Float16 sK1[kKT], sV1[kVT];
   __shared__ __attribute__((aligned(1024))) _Float16 sP[kPT];
   __shared__ __attribute__((aligned(1024))) _Float16 sKl[kKT], sPl[kPT];
+  __shared__ __attribute__((aligned(16))) float sC0[64], sC1[64];  // gate prefix of the keys
   __shared__ float red[2][kNW];
 
   const int NP = (Nb + 1) / 2;
@@ -163,30 +167,22 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(g + goffP[i], sP + (4 * wave + i) * 512, 16, 0, 0);
   };
-  // lo parts: thread t owns LDS chunks t + 512 j of each lo tile
-  uint32_t loffK[2], loffP[4];
+  // lo parts: the same slots in the lo tiles
+  auto dmaLo = [&](int n) __attribute__((always_inline)) {
+    const char* gk = kh_h + static_cast<int64_t>(n) * (2 * TBK) + TBK;
+    const char* gp = pm_h + static_cast<int64_t>(n) * (2 * TBP) + TBP;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pos = tid + kNT * j;
-    const int r = pos >> 4;
-    const uint32_t off = static_cast<uint32_t>(r * 256 + ((pos & 15) ^ (r & 15)) * 16);
-    if (j < 2) loffK[j] = off;
-    loffP[j] = off;
-  }
-  u4 lopre[6];  // lo parts of the next split-precision block (Khat lo x2, P lo x4)
-  auto fetch_lo = [&](int n) __attribute__((always_inline)) {
-    const char* kb = kh_h + static_cast<int64_t>(n) * (2 * TBK) + TBK;
-    const char* pb = pm_h + static_cast<int64_t>(n) * (2 * TBP) + TBP;
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(gk + goffK[i], sKl + (2 * wave + i) * 512, 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lopre[j] = *reinterpret_cast<const u4*>(kb + loffK[j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lopre[2 + j] = *reinterpret_cast<const u4*>(pb + loffP[j]);
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(gp + goffP[i], sPl + (4 * wave + i) * 512, 16, 0, 0);
   };
-  auto put_lo = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u4*>(sKl + 8 * (tid + kNT * j)) = lopre[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u4*>(sPl + 8 * (tid + kNT * j)) = lopre[2 + j];
+  // gate prefix of block n's keys: 16 lanes of wave 0 move its 256 bytes
+  auto tileC = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return sC0; else return sC1;
+  };
+  auto dmaC = [&](int n, float* ltile) __attribute__((always_inline)) {
+    if (wave == 0 && lane < 16)
+      __builtin_amdgcn_global_load_lds(cumh + n * C + 4 * lane, ltile, 16, 0, 0);
   };
   // MFMA A operands.  Khat / P (16 chunks per row): rows 16t + ln, logical chunk
   // 4c + lg.  V^T (8 chunks per row): rows 16t + ln, logical chunk 4c + lg, c < 2.
@@ -278,12 +274,8 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   dmaV(2 * p, sV0);
   dmaP(2 * p);
   if (2 * p + 1 < Nb) dmaV(2 * p + 1, sV1);
-  fetch_lo(2 * p);  // used only if block 2p runs the split products
-  f4 ckn[4];  // FoX prefix of the key block being scanned
-  if constexpr (FOX) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) ckn[kt] = *reinterpret_cast<const f4*>(cumh + (2 * p) * C + 16 * kt + 4 * lg);
-  }
+  dmaLo(2 * p);  // used only if block 2p runs the split products
+  if constexpr (FOX) dmaC(2 * p, sC0);
   f4 sdv[4], ckd[4];
   if (live) {
     const float* sd = sdiag + (bh * Nb + mb) * (C * C);
@@ -343,27 +335,18 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     using SN = std::integral_constant<int, 1 - decltype(st)::value>;
     const _Float16* tK = tileK(st);
     const _Float16* tV = tileV(st);
-    f4 ck[4];
-    if constexpr (FOX) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        ck[kt] = ckn[kt];
-        if (n > 0) ckn[kt] = *reinterpret_cast<const f4*>(cumh + (n - 1) * C + 16 * kt + 4 * lg);
-      }
-    }
     const float pn_cur = pn, kn_cur = kn;
     if (n > 0) {
       pn = pnorm[bh * Nb + n - 1];
       kn = kmax_blk[bh * Nb + n - 1];
     }
-    if (acc_cur) put_lo();
     if (n > 0) {
       dmaK(n - 1, tileK(SN{}));
       dmaV(n - 1, tileV(SN{}));
+      if constexpr (FOX) dmaC(n - 1, tileC(SN{}));
     }
     const float qb_next = qbound * pn_cur;
     const bool acc_next = accurate_all || (qb_next * khmax * 0.0009765625f > tau);
-    if (acc_next && n > 0) fetch_lo(n - 1);
     const bool work = live && !(half == 0 && n == 2 * p);
     // no logit of this block can pass the running max by kTheta when
     // |Qt| * max|khat| (Cauchy-Schwarz; 1.01 covers the fp16 operands) stays below it
@@ -383,8 +366,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
         for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(ak[c][kt], qhi[c], c == 0 ? seed : x[kt]);
     }
     if (acc_cur) {
-      sync_lds();  // every thread's share of the lo tiles is in LDS
-      if (work) {
+      if (work) {  // the lo tiles were published by the previous block's barrier
 #pragma unroll
         for (int c = 0; c < DC; ++c)
 #pragma unroll
@@ -412,8 +394,9 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
       }
       if (!skip_max) {
         if constexpr (FOX) {
+          const float* cs = tileC(st);
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) x[kt] -= ck[kt];
+          for (int kt = 0; kt < 4; ++kt) x[kt] -= *reinterpret_cast<const f4*>(cs + 16 * kt + 4 * lg);
         }
         const float mx = rowmax(x);
         if (__any(mx > kTheta + kOff)) {  // rare: raise the running max
@@ -447,10 +430,11 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
           }
       }
     }
-    // P_n is read by no one any more: fetch P_{n-1} into its place
+    // P_n and the lo tiles are read by no one any more: fetch block n-1's
     if (n > 0) {
       sync_lds();
       dmaP(n - 1);
+      if (acc_next) dmaLo(n - 1);
     }
     if (work) {
       // ---- R4: PV beside the conversion of the transported queries
