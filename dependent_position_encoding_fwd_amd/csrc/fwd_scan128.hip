@@ -352,18 +352,55 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     // |Qt| * max|khat| (Cauchy-Schwarz; 1.01 covers the fp16 operands) stays below it
     const bool skip_max = !FOX && (qbound * kn_cur * 1.01f <= mrun_min + kTheta);
 
-    // ---- R1: S^T = Khat Qt - m + kOff
+    // The block's operands stream from LDS in chunks of 8 reads (one 16-row
+    // tile column each): Khat c=0,1 | Khat c=2,3 | P c=0 | P c=1 | P c=2 | P c=3 |
+    // V^T c=0 | V^T c=1.  Each group issues the reads of the next chunk, then the
+    // products of the current one, so one chunk's reads run under the previous
+    // chunk's products; two chunks are live at a time.  The vector work (row
+    // maximum, exponentials, conversion of the transported queries) sits beside
+    // the products it does not feed.
     f4 x[4];
+    h8 pb[2];
+    h8 ch0[8], ch1[8];
+    auto rdK = [&](h8 (&b)[8], int c0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) b[4 * cc + kt] = rdA16(tK, kt, c0 + cc);
+    };
+    auto rdP = [&](h8 (&b)[8], int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) b[t] = rdA16(sP, t, c);
+    };
+    auto rdVc = [&](h8 (&b)[8], int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) b[t] = rdV(tV, t, c);
+    };
+    auto mmP = [&](const h8 (&b)[8], int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) qf[t] = mma16(b[t], qhi[c], c == 0 ? f4{0.f, 0.f, 0.f, 0.f} : qf[t]);
+    };
+    auto mmV = [&](const h8 (&b)[8], int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] = mma16(b[t], pb[c], oacc[t]);
+      lacc = mma16(ones, pb[c], lacc);
+    };
     if (work) {
-      h8 ak[DC][4];
+      // ---- S^T = Khat Qt - m + kOff
+      rdK(ch0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      rdK(ch1, 2);
 #pragma unroll
-      for (int c = 0; c < DC; ++c)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) ak[c][kt] = rdA16(tK, kt, c);
+        for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(ch0[4 * cc + kt], qhi[cc], cc == 0 ? seed : x[kt]);
+      __builtin_amdgcn_sched_barrier(0);
+      rdP(ch0, 0);
 #pragma unroll
-      for (int c = 0; c < DC; ++c)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(ak[c][kt], qhi[c], c == 0 ? seed : x[kt]);
+        for (int kt = 0; kt < 4; ++kt) x[kt] = mma16(ch1[4 * cc + kt], qhi[2 + cc], x[kt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (acc_cur) {
       if (work) {  // the lo tiles were published by the previous block's barrier
@@ -375,50 +412,44 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
             x[kt] = mma16(rdA16(tK, kt, c), qlo[c], x[kt]);
           }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    h8 pb[2];
     if (work) {
-      const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
-      // ---- R2: first half of Qt <- P_n Qt beside the row maximum
-      {
-        h8 ap[2][DT];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int t = 0; t < DT; ++t) ap[c][t] = rdA16(sP, t, c);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) qf[t] = mma16(ap[0][t], qhi[0], zero);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) qf[t] = mma16(ap[1][t], qhi[1], qf[t]);
-      }
+      // ---- Qt <- P_n Qt, chunk 0, beside the row maximum
+      rdP(ch1, 1);
+      mmP(ch0, 0);
+      float mx = 0.f;
       if (!skip_max) {
         if constexpr (FOX) {
           const float* cs = tileC(st);
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) x[kt] -= *reinterpret_cast<const f4*>(cs + 16 * kt + 4 * lg);
         }
-        const float mx = rowmax(x);
-        if (__any(mx > kTheta + kOff)) {  // rare: raise the running max
-          rescale(mx, x);
-          set_seeds();
-        }
+        mx = rowmax(x);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- R3: second half of the transition beside the exponentials
-      {
-        h8 ap[2][DT];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int t = 0; t < DT; ++t) ap[c][t] = rdA16(sP, t, 2 + c);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int t = 0; t < DT; ++t) qf[t] = mma16(ap[c][t], qhi[2 + c], qf[t]);
+      if (!skip_max && __any(mx > kTheta + kOff)) {  // rare: raise the running max
+        rescale(mx, x);
+        set_seeds();
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- chunk 1 beside the exponentials
+      rdP(ch0, 2);
+      mmP(ch1, 1);
       exps(x, pb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // exp
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // other vector ALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- chunks 2 and 3
+      rdP(ch1, 3);
+      mmP(ch0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      rdVc(ch0, 0);
+      mmP(ch1, 3);
       __builtin_amdgcn_sched_barrier(0);
       if (acc_cur) {
 #pragma unroll
@@ -428,6 +459,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
             qf[t] = mma16(rdA16(sPl, t, c), qhi[c], qf[t]);
             qf[t] = mma16(rdA16(sP, t, c), qlo[c], qf[t]);
           }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // P_n and the lo tiles are read by no one any more: fetch block n-1's
@@ -437,10 +469,13 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
       if (acc_next) dmaLo(n - 1);
     }
     if (work) {
-      // ---- R4: PV beside the conversion of the transported queries
-      pv(tV, pb);
+      // ---- PV beside the conversion of the transported queries
+      rdVc(ch1, 1);
+      mmV(ch0, 0);
 #pragma unroll
       for (int c = 0; c < DC; ++c) qhi[c] = pack_h8(qf[2 * c], qf[2 * c + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mmV(ch1, 1);
       if (acc_next) {
         asm volatile("");  // a real branch: the lo parts are rarely needed
 #pragma unroll
