@@ -25,6 +25,13 @@ still hashes to the value recorded there; the decode kernel's traffic is
 reported the same way.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-ref]
+                    [--fwd-config {2,3,4}]
+
+`--fwd-config` swaps the forward workload for another of the synthetic
+configurations (3: B=1 H=16 L=16384 d=64; 4: B=4 H=16 L=8192 d=128 with forget
+gates); the default, 2, is the headline workload above.  The roofline then
+describes that configuration's scan kernel, and its traffic is reported only
+for the default workload, whose counters are recorded.
 
 `--copy-ref` first runs a plain 1 GiB device copy, whose FETCH_SIZE and
 WRITE_SIZE counters calibrate those of the other kernels in a rocprofv3
@@ -81,6 +88,7 @@ def main():
     ap.add_argument("--precision", default="auto", choices=["auto", "accurate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", action="store_true")
+    ap.add_argument("--fwd-config", type=int, default=2, choices=[2, 3, 4])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path (got --gpus {args.gpus})",
@@ -93,13 +101,15 @@ def main():
     import synthetic
 
     dev = torch.device("cuda:0")
-    cf = synthetic.CONFIGS[2]
+    cid = args.fwd_config
+    cf = synthetic.CONFIGS[cid]
     cd = synthetic.CONFIGS[5]
     print(f"[bench] generating inputs: {cf.desc}; {cd.desc}", file=sys.stderr, flush=True)
-    xf = {n: (t.to(dev) if t is not None else None) for n, t in synthetic.config_inputs(2).items()}
+    xf = {n: (t.to(dev) if t is not None else None) for n, t in synthetic.config_inputs(cid).items()}
+    gates = xf.get("log_forget")
     xd = {n: t.to(dev) for n, t in synthetic.config_inputs(5).items()}
     fargs = (xf["q"], xf["k"], xf["v"], xf["w"], xf["beta"])
-    ws = pa.fwd_workspace(xf["q"], None)
+    ws = pa.fwd_workspace(xf["q"], gates)
     o = torch.empty_like(xf["q"])
     lse = torch.empty(xf["beta"].shape, dtype=torch.float32, device=dev)
     dws = torch.empty(max(256, pa.decode_workspace_bytes(cd.B, cd.H, cd.d, cd.cache_len)), dtype=torch.uint8,
@@ -117,10 +127,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        pa.path_fwd_stage_prepare(*fargs, None, scale=cf.scale, precision=args.precision, workspace=ws)
+        pa.path_fwd_stage_prepare(*fargs, gates, scale=cf.scale, precision=args.precision, workspace=ws)
         if ev is not None:
             ev[1].record()
-        pa.path_fwd_stage_scan(*fargs, ws, None, scale=cf.scale, precision=args.precision, out=(o, lse))
+        pa.path_fwd_stage_scan(*fargs, ws, gates, scale=cf.scale, precision=args.precision, out=(o, lse))
         if ev is not None:
             ev[2].record()
         pa.path_decode_step(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], xd["k_cache"],
@@ -148,10 +158,10 @@ def main():
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
     scan_tflops = F / (scan_ms * 1e-3) / 1e12
-    traffic = load_traffic("scan")
+    traffic = load_traffic("scan") if cid == 2 else None
     roofline = {"bound": "mfma", "achieved": round(scan_tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(scan_tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "scan64_kernel (right-to-left scan, d=64)", "flops_per_launch": F,
+                "kernel": f"scan{cf.d}_kernel (right-to-left scan, d={cf.d})", "flops_per_launch": F,
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
     cpu = None
@@ -163,7 +173,8 @@ def main():
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "PaTH fwd B=8 H=16 L=4096 d=64 scale=1/8 (bf16 in/out) + decode B=64 H=16 d=64 "
+        "config": {"workload": f"PaTH fwd B={cf.B} H={cf.H} L={cf.L} d={cf.d} scale={cf.scale:g}"
+                               f"{' forget gates' if cf.fox else ''} (bf16 in/out) + decode B=64 H=16 d=64 "
                                "cache=8192 (bf16)", "storage": "bf16", "arith": "fp16 MFMA, fp32 accumulate",
                    "global_batch": cf.B, "seq_len": cf.L, "heads": cf.H, "head_dim": cf.d,
                    "precision": args.precision, "parallelism": "single-gpu"},
@@ -189,9 +200,10 @@ def cpu_baseline(cf, budget_s=10.0):
     done = 0
     dt = 0.0
     for (b, h) in heads:
-        x = synthetic.fwd_inputs(cf.B, cf.H, cf.L, cf.d, cf.dtype, cf.seed, heads=[(b, h)])
+        x = synthetic.fwd_inputs(cf.B, cf.H, cf.L, cf.d, cf.dtype, cf.seed, cf.near2_frac, cf.fox, heads=[(b, h)])
+        gate = x["log_forget"][0] if cf.fox else None
         t0 = time.perf_counter()
-        oracle.path_fwd_head(x["q"][0], x["k"][0], x["v"][0], x["w"][0], x["beta"][0], None, cf.scale)
+        oracle.path_fwd_head(x["q"][0], x["k"][0], x["v"][0], x["w"][0], x["beta"][0], gate, cf.scale)
         dt += time.perf_counter() - t0
         done += 1
         print(f"[bench] oracle head {done}: {dt:.1f} s", file=sys.stderr, flush=True)
@@ -199,7 +211,7 @@ def cpu_baseline(cf, budget_s=10.0):
             break
     F = flops_path(1, done, cf.L, cf.d)
     return {"value": round(F / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads (all {cf.L} query rows each) of the L=4096 workload, "
+            "sample": f"{done} of {len(heads)} heads (all {cf.L} query rows each) of the L={cf.L} workload, "
                       f"{dt:.1f} s of oracle wall time"}
 
 

@@ -15,6 +15,9 @@ the last device-copy dispatch before the first forward-prepare dispatch.
         --stats DIR --fetch DIR --write DIR --md OUT.md --json OUT.json \
         --cmd-stats "..." --cmd-fetch "..." --cmd-write "..."
 
+With only --stats, --md and --cmd-stats it summarises the kernel trace alone
+(for example a run of `bench.py --fwd-config 4`).
+
 Each DIR holds the run's CSV files and `bench.json`, the JSON line bench.py
 printed in that run.
 """
@@ -144,17 +147,64 @@ def scan_algorithmic_bytes(B, H, L, d):
     return khl + pmat + qhat + sdiag + small + v + o + lse
 
 
+def demangle(name: str) -> str:
+    """Readable kernel name.  Mangled names of this library's kernels have the
+    form _ZN<len><ns><len><name>I<arg>E...: the nested names and one template
+    argument (Lb0/Lb1 for a bool, Li<n> for an int) are decoded; other names are
+    cut at their parameter list."""
+    import re
+    if name.startswith("_ZN"):
+        s, parts = name[3:], []
+        while s and s[0].isdigit():
+            m = re.match(r"(\d+)", s)
+            n = int(m.group(1))
+            parts.append(s[len(m.group(1)):len(m.group(1)) + n])
+            s = s[len(m.group(1)) + n:]
+        targ = ""
+        m = re.match(r"IL(b|i)(\d+)E", s)
+        if m:
+            targ = "<" + ({"0": "false", "1": "true"}[m.group(2)] if m.group(1) == "b" else m.group(2)) + ">"
+        if parts:
+            return "::".join(parts) + targ
+    return name.split("(")[0].replace("void ", "")
+
+
+def trace_only(a):
+    """Summary of one --kernel-trace --stats run (no counters): per-kernel
+    durations and the bench line of the same run."""
+    bs = read_bench(a.stats)
+    rows = read_stats(a.stats)
+    cfg = bs["config"]
+    fwd, roof = bs["fwd"], bs["roofline"]
+    lines = [f"# rocprofv3 summary: {cfg['workload']}", "",
+             "Kernel trace (from the repository root on one MI355X):", "", f"    {a.cmd_stats}", "",
+             "| kernel | calls | avg us | share |", "|---|---|---|---|"]
+    for name, calls, avg_ns, pct in sorted(rows, key=lambda r: -r[3]):
+        lines.append(f"| {demangle(name)} | {calls} | {avg_ns / 1e3:.1f} | {pct:.1f} % |")
+    lines += ["", f"bench.py HIP events in the same run (median of {bs['steps']} steps): prepare {fwd['prepare_ms']} ms, "
+              f"scan {fwd['scan_ms']} ms, forward {fwd['ms']} ms.",
+              f"Forward: {fwd['flops_model']:.4e} FLOP per launch / {fwd['ms']} ms = {bs['value']} TFLOP/s "
+              f"= {100 * fwd['frac_bf16_peak']:.1f} % of 2.5 PFLOP/s.",
+              f"Scan ({roof['kernel']}): {roof['achieved']} TFLOP/s = {100 * roof['frac']:.1f} % of the MFMA peak.",
+              ""]
+    with open(a.md, "w") as f:
+        f.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--md", required=True)
-    ap.add_argument("--json", required=True)
+    ap.add_argument("--json")
     ap.add_argument("--cmd-stats", required=True)
-    ap.add_argument("--cmd-fetch", required=True)
-    ap.add_argument("--cmd-write", required=True)
+    ap.add_argument("--cmd-fetch")
+    ap.add_argument("--cmd-write")
     a = ap.parse_args()
+    if a.fetch is None:
+        trace_only(a)
+        return
 
     bs, bf, bw = read_bench(a.stats), read_bench(a.fetch), read_bench(a.write)
     for k in ("roofline", "decode"):
