@@ -70,6 +70,15 @@ def test_fwd_fox(dtype, d):
     _fwd_case(2, 2, 300, d, dtype, 1.0, seed=d + 3, fox=True)
 
 
+@pytest.mark.parametrize("BH", [(1, 8), (2, 8), (3, 8)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_xcd_head_order(BH, d):
+    # B*H a multiple of 8: workgroups are dealt to the 8 XCDs by head, heads in
+    # pairs (8: one unpaired head per XCD; 16: one pair; 24: a pair and one unpaired)
+    B, H = BH
+    _fwd_case(B, H, 330, d, "bf16", 0.5, seed=B * 10 + d, fox=(B == 2))
+
+
 @pytest.mark.parametrize("beta", [0.0, 1.0, 2.0])
 def test_fwd_beta_edges(beta):
     # beta = 1 with unit w makes every H singular; beta = 0 is plain attention
@@ -86,8 +95,9 @@ def test_fwd_config1_full():
     _fwd_case(c.B, c.H, c.L, c.d, c.dtype, c.scale, c.seed)
 
 
-def test_fwd_deterministic_and_stages():
-    x = _dev(synthetic.fwd_inputs(1, 4, 333, 64, "bf16", 5, fox=True))
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_deterministic_and_stages(d):
+    x = _dev(synthetic.fwd_inputs(1, 4, 333, d, "bf16", 5, fox=True))
     args = (x["q"], x["k"], x["v"], x["w"], x["beta"], x["log_forget"])
     o1, l1 = pa.path_attn_fwd(*args, scale=0.3)
     o2, l2 = pa.path_attn_fwd(*args, scale=0.3)
