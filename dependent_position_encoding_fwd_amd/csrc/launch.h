@@ -15,15 +15,11 @@ hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_
                               float* tinv, float* qhat, float* khat, float* pT,
                               hipStream_t stream);
 
-// Per-block UT data in the layout of the matrix-core forward (bf16 inputs).
-// c2 = scale * log2(e) multiplies the stored adjusted queries and in-block logits.
-hipError_t launch_prepare_scan(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
-                               const void* k, const void* w, const float* beta, _Float16* khat,
-                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                               hipStream_t stream);
-
-// Same outputs as launch_prepare_scan, computed on the matrix cores, plus
-// pnorm[bh][n] >= |P_n|_2 (product of the transitions' spectral norms).
+// Per-block UT data in the layout of the matrix-core forward (bf16 inputs),
+// computed on the matrix cores: khat and P (fp16 hi/lo rows, reduction index in
+// mfma_perm order), c2 * adjusted queries and c2 * in-block logits (fp32, c2 =
+// scale * log2(e)), kmax[bh][n] = max_c |khat_c|, pnorm[bh][n] >= |P_n|_2
+// (product of the transitions' spectral norms) and V^T (fp16, keys permuted).
 hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
                                const void* k, const void* w, const void* v, const float* beta,
                                _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,

@@ -20,37 +20,11 @@
 
 namespace path {
 
-// Outputs of the scan layout (consumed by the matrix-core forward).
-struct ScanOut {
-  _Float16* khat;  // [BH][Nb][2 (hi,lo)][64][D]  khat rows, columns in mfma_perm order
-  _Float16* pmat;  // [BH][Nb][2][D][D]           P = H_0...H_63 rows, columns permuted
-  float* qhat;     // [BH][Nb*64][D]              c2 * qhat (padded rows zero)
-  float* sdiag;    // [BH][Nb][64 query][64 key]  c2 * in-block logits (key <= query)
-  float* kmax;     // [BH][Nb]                    max_c |khat_c|
-  float c2;        // logit multiplier (scale * log2(e))
-};
-
-// Column order of matrix-core A operands.  A 32-wide slice of the reduction
-// index d = 32c + 16h + 4g + j is stored at 32c + 8g + 4h + j, so that lane
-// group g reads its 8 reduction slots with one 16-byte access, and those slots
-// line up with the accumulator layout of the 16x16 output tiles that feed the
-// B operand (rows 4g..4g+3 of two consecutive tiles).
-__device__ __forceinline__ int mfma_perm(int d) {
-  return (d & ~31) | (((d >> 2) & 3) << 3) | (((d >> 4) & 1) << 2) | (d & 3);
-}
-
-__device__ __forceinline__ void store_hilo(_Float16* hi, _Float16* lo, float x) {
-  const _Float16 h = static_cast<_Float16>(x);
-  *hi = h;
-  *lo = static_cast<_Float16>(x - static_cast<float>(h));
-}
-
-template <typename T, int D, bool SCAN>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void prepare_f32_kernel(
     int64_t L, int Nb, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ w, const float* __restrict__ beta, float* __restrict__ tinv_out,
-    float* __restrict__ qhat_out, float* __restrict__ khat_out, float* __restrict__ pT_out,
-    ScanOut so) {
+    float* __restrict__ qhat_out, float* __restrict__ khat_out, float* __restrict__ pT_out) {
   constexpr int C = kBlk;
   constexpr int CP = C + 1;
   constexpr int DP = D + 1;
@@ -101,14 +75,12 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
   }
   __syncthreads();
 
-  if (!SCAN && tinv_out) {
+  if (tinv_out) {
     float* dst = tinv_out + (bh * Nb + n) * (C * C);
     for (int idx = tid; idx < C * C; idx += 256) dst[idx] = Ts[idx / C][idx % C];
   }
 
-  __shared__ float Y2[SCAN ? C : 1][CP];  // scan layout: keeps Y for the in-block logits
-  __shared__ float red[C];
-  if (SCAN || khat_out) {
+  if (khat_out) {
     for (int idx = tid; idx < C * D; idx += 256) {
       int r = idx / D, e = idx % D;
       Xs[r][e] = r < valid ? load_f32(k + base + (t0 + r) * D + e) : 0.f;
@@ -136,35 +108,12 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       int c = idx / D, e = idx % D;
       float x = Xs[c][e];
       for (int a = c + 1; a < C; ++a) x -= Ys[c][a] * Ws[a][e];
-      if (!SCAN && c < valid) khat_out[base + (t0 + c) * D + e] = x;
-      if (SCAN) Xs[c][e] = x;  // each element is read and written by one thread only
-    }
-    __syncthreads();
-    if constexpr (SCAN) {
-      const int64_t blk = bh * Nb + n;
-      _Float16* kh = so.khat + blk * (2 * C * D);
-      for (int idx = tid; idx < C * D; idx += 256) {
-        int c = idx / D, e = idx % D;
-        const int p = c * D + mfma_perm(e);
-        store_hilo(kh + p, kh + C * D + p, Xs[c][e]);
-      }
-      if (tid < C) {
-        float s2 = 0.f;
-        for (int e = 0; e < D; ++e) s2 += Xs[tid][e] * Xs[tid][e];
-        red[tid] = s2;
-      }
-      for (int idx = tid; idx < C * C; idx += 256) Y2[idx / C][idx % C] = Ys[idx / C][idx % C];
-      __syncthreads();
-      if (tid == 0) {
-        float mx = 0.f;
-        for (int c = 0; c < C; ++c) mx = fmaxf(mx, red[c]);
-        so.kmax[blk] = sqrtf(mx);
-      }
+      if (c < valid) khat_out[base + (t0 + c) * D + e] = x;
     }
     __syncthreads();
   }
 
-  if (SCAN || qhat_out) {
+  if (qhat_out) {
     for (int idx = tid; idx < C * D; idx += 256) {
       int r = idx / D, e = idx % D;
       Xs[r][e] = r < valid ? load_f32(q + base + (t0 + r) * D + e) : 0.f;
@@ -180,22 +129,6 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       Gs[r][t] = z;
     }
     __syncthreads();
-    if constexpr (SCAN) {
-      // In-block logits, c <= r:  k_c^T H_{c+1} ... H_r q_r
-      //   = k_c . q_r - sum_b Y[c][b] A[r][b]   (Y from the key pass, b in (c, r])
-      float* sd = so.sdiag + (bh * Nb + n) * (C * C);
-      for (int idx = tid; idx < C * C; idx += 256) {
-        int r = idx / C, c = idx % C;
-        float x = 0.f;
-        if (c <= r && r < valid) {
-          const T* kc = k + base + (t0 + c) * D;
-          for (int e = 0; e < D; ++e) x += load_f32(kc + e) * Xs[r][e];
-          for (int b = c + 1; b <= r; ++b) x -= Y2[c][b] * Gs[r][b];
-          x *= so.c2;
-        }
-        sd[idx] = x;
-      }
-    }
     // Y[r][a] = sum_t T^{-1}[a][t] A[r][t]   (= (T^{-1} a_r)_a, nonzero for a <= r)
     for (int idx = tid; idx < C * C; idx += 256) {
       int r = idx / C, a = idx % C;
@@ -210,14 +143,13 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       if (r < valid) {
         x = Xs[r][e];
         for (int a = 0; a <= r; ++a) x -= Ys[r][a] * Ws[a][e];
-        if (!SCAN) qhat_out[base + (t0 + r) * D + e] = x;
+        qhat_out[base + (t0 + r) * D + e] = x;
       }
-      if (SCAN) so.qhat[(bh * Nb * C + t0 + r) * D + e] = so.c2 * x;
     }
     __syncthreads();
   }
 
-  if (SCAN || pT_out) {
+  if (pT_out) {
     // F[s][e] = sum_t T^{-1}[t][s] W[t][e]   (F = T^{-T} W)
     for (int idx = tid; idx < C * D; idx += 256) {
       int s = idx / D, e = idx % D;
@@ -226,24 +158,12 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       Xs[s][e] = f;
     }
     __syncthreads();
-    if constexpr (SCAN) {
-      // P[a][b] = (P^T)[b][a], stored as rows a with permuted columns
-      _Float16* pm = so.pmat + (bh * Nb + n) * (2 * D * D);
-      for (int idx = tid; idx < D * D; idx += 256) {
-        int a = idx / D, b = idx % D;
-        float x = (a == b) ? 1.f : 0.f;
-        for (int s = 0; s < C; ++s) x -= Ws[s][b] * Xs[s][a];
-        const int p = a * D + mfma_perm(b);
-        store_hilo(pm + p, pm + D * D + p, x);
-      }
-    } else {
-      float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
-      for (int idx = tid; idx < D * D; idx += 256) {
-        int a = idx / D, b = idx % D;
-        float x = (a == b) ? 1.f : 0.f;
-        for (int s = 0; s < C; ++s) x -= Ws[s][a] * Xs[s][b];
-        dst[idx] = x;
-      }
+    float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
+    for (int idx = tid; idx < D * D; idx += 256) {
+      int a = idx / D, b = idx % D;
+      float x = (a == b) ? 1.f : 0.f;
+      for (int s = 0; s < C; ++s) x -= Ws[s][a] * Xs[s][b];
+      dst[idx] = x;
     }
   }
 }
@@ -341,31 +261,10 @@ static hipError_t launch_prepare_t(int64_t B, int64_t H, int64_t L, const void* 
                                    float* khat, float* pT, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   dim3 grid(static_cast<unsigned>(B * H * Nb));
-  hipLaunchKernelGGL((prepare_f32_kernel<T, D, false>), grid, dim3(256), 0, stream, L, Nb,
+  hipLaunchKernelGGL((prepare_f32_kernel<T, D>), grid, dim3(256), 0, stream, L, Nb,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(w),
-                     beta, tinv, qhat, khat, pT, ScanOut{});
+                     beta, tinv, qhat, khat, pT);
   return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_prepare_scan_t(int64_t B, int64_t H, int64_t L, const void* q,
-                                        const void* k, const void* w, const float* beta,
-                                        const ScanOut& so, hipStream_t stream) {
-  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
-  dim3 grid(static_cast<unsigned>(B * H * Nb));
-  hipLaunchKernelGGL((prepare_f32_kernel<bf16_t, D, true>), grid, dim3(256), 0, stream, L, Nb,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(w), beta, nullptr, nullptr, nullptr, nullptr, so);
-  return hipGetLastError();
-}
-
-hipError_t launch_prepare_scan(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
-                               const void* k, const void* w, const float* beta, _Float16* khat,
-                               _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                               hipStream_t stream) {
-  ScanOut so{khat, pmat, qhat, sdiag, kmax, c2};
-  return d == 64 ? launch_prepare_scan_t<64>(B, H, L, q, k, w, beta, so, stream)
-                 : launch_prepare_scan_t<128>(B, H, L, q, k, w, beta, so, stream);
 }
 
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
