@@ -377,10 +377,16 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   }
   __syncthreads();  // XT ready; G no longer needed (GY becomes -Y)
 
-  // ---- Y^T = X^T Z^T (wave w: columns c in tile w) ------------------------------
-  f4 yt[4];
+  // ---- Y^T = X^T Z^T (wave w: columns c in tile w) and F = X^T W (rows b,
+  // columns e in head-dim tiles et = ET*w .. ET*w + ET - 1): one pass over the
+  // X^T operands serves both
+  f4 yt[4], ft[ET][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) yt[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 4; ++mt) {
+    yt[mt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < ET; ++j) ft[j][mt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
   {
     // mask Z^T to a > c (a = row, c = column)
     const int cc = 16 * wave + ln;
@@ -392,13 +398,21 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const HL b = split8(zt[2 * kc], zt[2 * kc + 1]);
+      h8 bwt[ET];
+#pragma unroll
+      for (int j = 0; j < ET; ++j)
+        bwt[j] = *reinterpret_cast<const h8*>(&Wt[(16 * (ET * wave + j) + ln) * TP + 32 * kc + 8 * lg]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
         const h8 ah = *reinterpret_cast<const h8*>(&XT[0][off]);
         const h8 al = *reinterpret_cast<const h8*>(&XT[1][off]);
         yt[mt] = mma(al, b.hi, yt[mt]);
+#pragma unroll
+        for (int j = 0; j < ET; ++j) ft[j][mt] = mma(al, bwt[j], ft[j][mt]);
         yt[mt] = mma(ah, b.lo, yt[mt]);
+#pragma unroll
+        for (int j = 0; j < ET; ++j) ft[j][mt] = mma(ah, bwt[j], ft[j][mt]);
         yt[mt] = mma(ah, b.hi, yt[mt]);
       }
     }
@@ -412,98 +426,75 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     *reinterpret_cast<h8*>(&NY[off]) = -yb[kc].hi;
     *reinterpret_cast<h8*>(&NY[C * TP + off]) = -yb[kc].lo;
   }
+  // lane holds F[b = 16mt+4lg+i][e = 16et+ln] = F^T[e][b] -> -F^T rows (pitch 64, perm b)
+  HL fb[ET][2];
+#pragma unroll
+  for (int j = 0; j < ET; ++j)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      fb[j][kc] = split8(ft[j][2 * kc], ft[j][2 * kc + 1]);
+      const int off = (16 * (ET * wave + j) + ln) * 64 + 32 * kc + 8 * lg;
+      *reinterpret_cast<h8*>(&NFT[off]) = -fb[j][kc].hi;
+      *reinterpret_cast<h8*>(&NFT[D * 64 + off]) = -fb[j][kc].lo;
+    }
 
-  // ---- Khat^T = K^T - W^T Y^T (rows e, columns c in tile w) -----------------------
+  // ---- Khat^T = K^T - W^T Y^T (rows e, columns c in tile w) and
+  // P^T = I - W^T F (stored as P rows e, perm(f)): one pass over the W^T operands
   {
     const int cc = 16 * wave + ln;
     float s2 = 0.f;
 #pragma unroll
     for (int et = 0; et < DT; ++et) {
-      f4 acc;
+      f4 acc, pacc[ET];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t wd = i < 2 ? kr[et].x : kr[et].y;
         acc[i] = cc < valid ? -__uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16)) : 0.f;
+#pragma unroll
+        for (int j = 0; j < ET; ++j) pacc[j][i] = (16 * et + 4 * lg + i == 16 * (ET * wave + j) + ln) ? -1.f : 0.f;
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const h8 a = *reinterpret_cast<const h8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
         acc = mma(a, yb[kc].lo, acc);
+#pragma unroll
+        for (int j = 0; j < ET; ++j) pacc[j] = mma(a, fb[j][kc].lo, pacc[j]);
         acc = mma(a, yb[kc].hi, acc);
+#pragma unroll
+        for (int j = 0; j < ET; ++j) pacc[j] = mma(a, fb[j][kc].hi, pacc[j]);
       }
       acc = -acc;  // Khat[c][e], e = 16et + 4lg + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) s2 += acc[i] * acc[i];
-      const f4 x = acc;
-      // store as rows c with perm columns: e = 32(et/2) + 16(et%2) + 4lg + i -> 32(et/2) + 8lg + 4(et%2) + i
-      _Float16* dst = khat + (bh * Nb + n) * (2 * C * D) + cc * D + 32 * (et / 2) + 8 * lg + 4 * (et % 2);
-      const H8u hv = {to_h8(x, x)};
-      f4 lo;
+      // rows with perm columns: e = 32(et/2) + 16(et%2) + 4lg + i -> 32(et/2) + 8lg + 4(et%2) + i
+      const int pcol = 32 * (et / 2) + 8 * lg + 4 * (et % 2);
+      {
+        _Float16* dst = khat + (bh * Nb + n) * (2 * C * D) + cc * D + pcol;
+        const H8u hv = {to_h8(acc, acc)};
+        f4 lo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo[i] = x[i] - static_cast<float>(hv.v[i]);
-      const H8u lv = {to_h8(lo, lo)};
-      *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
-      *reinterpret_cast<uint2*>(dst + C * D) = make_uint2(lv.u.x, lv.u.y);
+        for (int i = 0; i < 4; ++i) lo[i] = acc[i] - static_cast<float>(hv.v[i]);
+        const H8u lv = {to_h8(lo, lo)};
+        *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
+        *reinterpret_cast<uint2*>(dst + C * D) = make_uint2(lv.u.x, lv.u.y);
+      }
+#pragma unroll
+      for (int j = 0; j < ET; ++j) {
+        const f4 pv = -pacc[j];  // P[e][f], e = 16(ET w + j) + ln, f = 16et + 4lg + i
+        _Float16* dst = pmat + (bh * Nb + n) * (2 * D * D) + (16 * (ET * wave + j) + ln) * D + pcol;
+        const H8u hv = {to_h8(pv, pv)};
+        f4 lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = pv[i] - static_cast<float>(hv.v[i]);
+        const H8u lv = {to_h8(lo, lo)};
+        *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
+        *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lv.u.x, lv.u.y);
+      }
     }
     s2 += __shfl_xor(s2, 16, 64);
     s2 += __shfl_xor(s2, 32, 64);
     s2 = wave_max(s2);
     if (lane == 0) kred[wave] = s2;
-  }
-
-  // ---- F = X^T W (rows b, columns e) and P^T = I - W^T F ---------------------------
-  // wave w owns head-dim column tiles et = ET*w .. ET*w + ET - 1
-#pragma unroll
-  for (int j = 0; j < ET; ++j) {
-    const int et = ET * wave + j;
-    f4 ft[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ft[mt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const h8 bwt = *reinterpret_cast<const h8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
-        const h8 ah = *reinterpret_cast<const h8*>(&XT[0][off]);
-        const h8 al = *reinterpret_cast<const h8*>(&XT[1][off]);
-        ft[mt] = mma(al, bwt, ft[mt]);
-        ft[mt] = mma(ah, bwt, ft[mt]);
-      }
-    }
-    // lane holds F[b = 16mt+4lg+i][e = 16et+ln] = F^T[e][b] -> -F^T rows (pitch 64, perm b)
-    HL fb[2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      fb[kc] = split8(ft[2 * kc], ft[2 * kc + 1]);
-      const int off = (16 * et + ln) * 64 + 32 * kc + 8 * lg;
-      *reinterpret_cast<h8*>(&NFT[off]) = -fb[kc].hi;
-      *reinterpret_cast<h8*>(&NFT[D * 64 + off]) = -fb[kc].lo;
-    }
-    // P^T[f][e] = delta - sum_b W^T[f][b] F[b][e]; stored as P rows e, perm(f)
-    const int e = 16 * et + ln;
-    _Float16* prow = pmat + (bh * Nb + n) * (2 * D * D) + e * D;
-#pragma unroll
-    for (int ft2 = 0; ft2 < DT; ++ft2) {
-      f4 acc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = (16 * ft2 + 4 * lg + i == e) ? -1.f : 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const h8 a = *reinterpret_cast<const h8*>(&Wt[(16 * ft2 + ln) * TP + 32 * kc + 8 * lg]);
-        acc = mma(a, fb[kc].lo, acc);
-        acc = mma(a, fb[kc].hi, acc);
-      }
-      acc = -acc;
-      const H8u hv = {to_h8(acc, acc)};
-      f4 lo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo[i] = acc[i] - static_cast<float>(hv.v[i]);
-      const H8u lv = {to_h8(lo, lo)};
-      _Float16* dst = prow + 32 * (ft2 / 2) + 8 * lg + 4 * (ft2 % 2);
-      *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
-      *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lv.u.x, lv.u.y);
-    }
   }
   __syncthreads();  // -Y and -F^T rows complete; XT is free
 
