@@ -547,46 +547,47 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) ub[kc] = split8(ut[2 * kc], ut[2 * kc + 1]);
 
-    // Sdiag^T[c][r] = (K Q^T)[c][r] - sum_b Y[c][b] Ut[b][r]
+    // Sdiag^T[c][r] = (K Q^T)[c][r] - sum_b Y[c][b] Ut[b][r]   (tiles mt < 4)
+    // Qhat^T[e][r] = Q^T[e][r] - sum_b F^T[e][b] Ut[b][r]     (tiles et < DT)
+    // formed side by side: independent products on the same B operands
     float* sd = sdiag + (bh * Nb + n) * (C * C);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f4 acc = skq[mt];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
-        const h8 ah = *reinterpret_cast<const h8*>(&NY[off]);
-        const h8 al = *reinterpret_cast<const h8*>(&NY[C * TP + off]);
-        acc = mma(al, ub[kc].hi, acc);
-        acc = mma(ah, ub[kc].lo, acc);
-        acc = mma(ah, ub[kc].hi, acc);
-      }
-      f4 out;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * mt + 4 * lg + i;
-        out[i] = (c <= r && r < valid) ? c2 * acc[i] : 0.f;
-      }
-      *reinterpret_cast<f4*>(sd + r * C + 16 * mt + 4 * lg) = out;
-    }
-
-    // Qhat^T[e][r] = Q^T[e][r] - sum_b F^T[e][b] Ut[b][r]
     float* qd = qhat + ((bh * Nb + n) * C + r) * D;
+    constexpr int NX = DT > 4 ? DT : 4;
 #pragma unroll
-    for (int et = 0; et < DT; ++et) {
-      f4 acc;
+    for (int x = 0; x < NX; ++x) {
+      f4 sacc = x < 4 ? skq[x < 4 ? x : 0] : f4{0.f, 0.f, 0.f, 0.f}, qacc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = bf2f(Qb[r * RP + 16 * et + 4 * lg + i]);
+      for (int i = 0; i < 4; ++i) qacc[i] = bf2f(Qb[r * RP + 16 * x + 4 * lg + i]);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const int off = (16 * et + ln) * 64 + 32 * kc + 8 * lg;
-        const h8 ah = *reinterpret_cast<const h8*>(&NFT[off]);
-        const h8 al = *reinterpret_cast<const h8*>(&NFT[D * 64 + off]);
-        acc = mma(al, ub[kc].hi, acc);
-        acc = mma(ah, ub[kc].lo, acc);
-        acc = mma(ah, ub[kc].hi, acc);
+        h8 sh, sl, qh, ql;
+        if (x < 4) {
+          const int off = (16 * x + ln) * TP + 32 * kc + 8 * lg;
+          sh = *reinterpret_cast<const h8*>(&NY[off]);
+          sl = *reinterpret_cast<const h8*>(&NY[C * TP + off]);
+        }
+        if (x < DT) {
+          const int off = (16 * x + ln) * 64 + 32 * kc + 8 * lg;
+          qh = *reinterpret_cast<const h8*>(&NFT[off]);
+          ql = *reinterpret_cast<const h8*>(&NFT[D * 64 + off]);
+        }
+        if (x < 4) sacc = mma(sl, ub[kc].hi, sacc);
+        if (x < DT) qacc = mma(ql, ub[kc].hi, qacc);
+        if (x < 4) sacc = mma(sh, ub[kc].lo, sacc);
+        if (x < DT) qacc = mma(qh, ub[kc].lo, qacc);
+        if (x < 4) sacc = mma(sh, ub[kc].hi, sacc);
+        if (x < DT) qacc = mma(qh, ub[kc].hi, qacc);
       }
-      *reinterpret_cast<f4*>(qd + 16 * et + 4 * lg) = (r < valid) ? acc * c2 : f4{0.f, 0.f, 0.f, 0.f};
+      if (x < 4) {
+        f4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * x + 4 * lg + i;
+          out[i] = (c <= r && r < valid) ? c2 * sacc[i] : 0.f;
+        }
+        *reinterpret_cast<f4*>(sd + r * C + 16 * x + 4 * lg) = out;
+      }
+      if (x < DT) *reinterpret_cast<f4*>(qd + 16 * x + 4 * lg) = (r < valid) ? qacc * c2 : f4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
