@@ -16,14 +16,18 @@
 // V^T in fp16 with the keys in mfma_perm order (zero past the sequence end),
 // the layout in which the scan feeds values to the matrix cores.
 //
-// Every product is a 16x16x32 MFMA.  Wave w owns output column tile w (16
+// The products are 16x16x32 MFMAs.  Wave w owns output column tile w (16
 // columns), so the accumulator tile of one product is, after conversion to
 // 16-bit, the B operand of the next one in the same wave.  Products of two
 // stored inputs (bf16) are exact in one pass; a computed fp32 operand is split
 // into fp16 hi + lo and costs two or three passes (hi*hi + hi*lo + lo*hi).
+// Products that share an operand (Y and F, Khat and P) run side by side.
 // T^{-1} is formed by 16-row blocks: each wave inverts one diagonal block by
 // back substitution (4 lanes per column), and the off-diagonal blocks follow
 // from fp32 16x16x4 MFMA products of those inverses with blocks of G.
+// The transposes W^T and V^T are products too: the rows times a 32x16 slice of
+// the identity leave 4 consecutive rows of one column in each lane.
+// All global loads of a block are issued before the first is used.
 #include <math.h>
 
 #include "common.h"
