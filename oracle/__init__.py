@@ -53,6 +53,8 @@ def _load():
                                             _I64, ctypes.POINTER(_I64), _D, _D, _D]
             lib.oracle_path_decode.argtypes = [_I64, _I64, _D, _D, _D, _D, ctypes.c_double, _D, _D,
                                                ctypes.c_double, _D, _D]
+            lib.oracle_path_decode_fox.argtypes = [_I64, _I64, _D, _D, _D, _D, ctypes.c_double,
+                                                   ctypes.c_double, _D, _D, _D, ctypes.c_double, _D, _D, _D]
             lib.oracle_ut_tinv.argtypes = [_I64, _I64, _D, _D, _D]
             lib.oracle_block_adjust.argtypes = [_I64, _I64, _D, _D, _D, _D, _D, _D, _D]
             lib.oracle_prefix_sum.argtypes = [_I64, _D, _D]
@@ -136,6 +138,24 @@ def path_decode_head(q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, scale=1.0):
     lib.oracle_path_decode(n, d, _p(q_t), _p(k_t), _p(v_t), _p(w_t), float(beta_t), _p(kc), _p(vc),
                            float(scale), _p(o), _p(lse))
     return o, float(lse[0]), kc
+
+
+def path_decode_fox_head(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, scale=1.0):
+    """One PaTH-FoX decode step of one head; cum_cache [len] holds the gate
+    prefixes of the cached keys.  Returns (o [d], lse, updated k_cache, c_t)."""
+    lib = _load()
+    q_t, k_t, v_t, w_t = (_f64(x) for x in (q_t, k_t, v_t, w_t))
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache)
+    cc = _f64(cum_cache)
+    n, d = kc.shape
+    assert cc.shape == (n,)
+    o = np.zeros((d,))
+    lse = np.zeros((1,))
+    ct = np.zeros((1,))
+    lib.oracle_path_decode_fox(n, d, _p(q_t), _p(k_t), _p(v_t), _p(w_t), float(beta_t), float(log_f_t),
+                               _p(kc), _p(vc), _p(cc), float(scale), _p(o), _p(lse), _p(ct))
+    return o, float(lse[0]), kc, float(ct[0])
 
 
 def ut_tinv(w, beta):

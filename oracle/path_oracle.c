@@ -118,14 +118,14 @@ void oracle_path_fwd(int64_t L, int64_t d, const double* q, const double* k,
  * One decode step for one head  [P1 §3 "Inferência"]:
  *   k_j <- H_t k_j  for every cached j < len   (in place, in k_cache)
  *   keys  = [k_0 .. k_{len-1} (updated), k_t],  values = [v_0 .. v_{len-1}, v_t]
- *   s_j = scale * (k_j . q_t);  o = softmax(s) . values;  lse = log sum exp s
+ *   s_j = scale * (k_j . q_t) + bias_j;  o = softmax(s) . values;  lse = log sum exp s
  * The new key enters untransformed: its path product is empty.
+ * bias is NULL (no bias) or [len + 1].
  * k_cache, v_cache: [len,d]; q_t,k_t,v_t,w_t: [d]; o: [d]; lse: scalar.
  */
-void oracle_path_decode(int64_t len, int64_t d, const double* q_t,
-                        const double* k_t, const double* v_t,
-                        const double* w_t, double beta_t, double* k_cache,
-                        const double* v_cache, double scale, double* o,
+static void decode_step(int64_t len, int64_t d, const double* q_t, const double* k_t,
+                        const double* v_t, const double* w_t, double beta_t, double* k_cache,
+                        const double* v_cache, double scale, const double* bias, double* o,
                         double* lse) {
   double* s = (double*)malloc(sizeof(double) * (size_t)(len + 1));
   for (int64_t j = 0; j < len; ++j) {
@@ -133,6 +133,8 @@ void oracle_path_decode(int64_t len, int64_t d, const double* q_t,
     s[j] = scale * dot(k_cache + j * d, q_t, d);
   }
   s[len] = scale * dot(k_t, q_t, d);
+  if (bias)
+    for (int64_t j = 0; j <= len; ++j) s[j] += bias[j];
   double m = -INFINITY;
   for (int64_t j = 0; j <= len; ++j) m = s[j] > m ? s[j] : m;
   double l = 0.0;
@@ -145,6 +147,38 @@ void oracle_path_decode(int64_t len, int64_t d, const double* q_t,
   }
   *lse = m + log(l);
   free(s);
+}
+
+void oracle_path_decode(int64_t len, int64_t d, const double* q_t,
+                        const double* k_t, const double* v_t,
+                        const double* w_t, double beta_t, double* k_cache,
+                        const double* v_cache, double scale, double* o,
+                        double* lse) {
+  decode_step(len, d, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, scale, NULL, o, lse);
+}
+
+/*
+ * PaTH-FoX decode step for one head  [P1 §2 "Extensões: PaTH-FoX" with §3
+ * "Inferência"]: the forget-gate bias of key j seen from query t is the sum
+ * of log f_s over j < s <= t.  With the running prefix c_j = sum_{s<=j} log f_s
+ * kept per cached key (cum_cache[j], j < len), the new prefix is
+ *   c_t = c_{len-1} + log_f_t   (c_{-1} = 0),
+ * the bias of cached key j is c_t - c_j and that of the new key is 0.
+ * Everything else is the plain decode step above.  *c_t_out receives c_t.
+ */
+void oracle_path_decode_fox(int64_t len, int64_t d, const double* q_t,
+                            const double* k_t, const double* v_t,
+                            const double* w_t, double beta_t, double log_f_t,
+                            double* k_cache, const double* v_cache,
+                            const double* cum_cache, double scale, double* o,
+                            double* lse, double* c_t_out) {
+  const double c_t = (len > 0 ? cum_cache[len - 1] : 0.0) + log_f_t;
+  double* bias = (double*)malloc(sizeof(double) * (size_t)(len + 1));
+  for (int64_t j = 0; j < len; ++j) bias[j] = c_t - cum_cache[j];
+  bias[len] = 0.0;
+  decode_step(len, d, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, scale, bias, o, lse);
+  *c_t_out = c_t;
+  free(bias);
 }
 
 /*

@@ -233,6 +233,54 @@ def test_decode_steps_reproduce_forward_rows():
         kc = np.concatenate([kc_new, k[t:t + 1]], axis=0)
 
 
+def test_fox_decode_steps_reproduce_brute_force_rows():
+    """§2 "Extensões: PaTH-FoX" with §3 "Inferência": the gated decode step, fed the
+    running prefixes c_j of log f, gives at step t row t of the brute-force gated
+    attention (explicit Householder products plus sum_{j<s<=t} log f_s), and the
+    prefix it returns is the plain cumulative sum."""
+    rng = np.random.default_rng(31)
+    L, d, scale = 24, 6, 0.8
+    q, k, v, w, beta = _rand_head(rng, L, d)
+    lf = -rng.uniform(0.0, 0.7, size=L)
+    lf[5] = 0.0                     # an open gate
+    o_ref, lse_ref = tiny.attention(q, k, v, w, beta, lf, scale)
+    kc = np.zeros((0, d))
+    cum = np.zeros((0,))
+    for t in range(L):
+        o, lse, kc_new, ct = oracle.path_decode_fox_head(q[t], k[t], v[t], w[t], beta[t], lf[t], kc, v[:t],
+                                                         cum, scale)
+        np.testing.assert_allclose(o, o_ref[t], rtol=1e-11, atol=1e-11)
+        assert abs(lse - lse_ref[t]) < 1e-11
+        assert abs(ct - np.sum(lf[:t + 1])) < 1e-13
+        kc = np.concatenate([kc_new, k[t:t + 1]], axis=0)
+        cum = np.append(cum, ct)
+
+
+def test_fox_decode_open_gates_is_plain_decode():
+    """log f = 0 everywhere: every bias vanishes and the gated step is the plain one."""
+    rng = np.random.default_rng(37)
+    n, d = 17, 8
+    q_t, k_t, v_t, w_t = (rng.standard_normal(d) for _ in range(4))
+    kc, vc = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    o0, lse0, k0 = oracle.path_decode_head(q_t, k_t, v_t, w_t, 0.7, kc, vc, 0.5)
+    o1, lse1, k1, ct = oracle.path_decode_fox_head(q_t, k_t, v_t, w_t, 0.7, 0.0, kc, vc, np.zeros(n), 0.5)
+    assert np.array_equal(o0, o1) and lse0 == lse1 and np.array_equal(k0, k1) and ct == 0.0
+
+
+def test_fox_decode_closed_gate_keeps_only_new_key():
+    """A (numerically) closed gate at t, log f_t = -800, leaves the new key alone in the
+    softmax: o = v_t and lse = scale * q_t . k_t."""
+    rng = np.random.default_rng(41)
+    n, d = 9, 8
+    q_t, k_t, v_t, w_t = (rng.standard_normal(d) for _ in range(4))
+    kc, vc = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    cum = np.cumsum(-rng.uniform(0, 0.3, size=n))
+    o, lse, _, ct = oracle.path_decode_fox_head(q_t, k_t, v_t, w_t, 0.4, -800.0, kc, vc, cum, 1.1)
+    np.testing.assert_allclose(o, v_t, atol=1e-300)
+    assert abs(lse - 1.1 * float(q_t @ k_t)) < 1e-12
+    assert ct == cum[-1] - 800.0
+
+
 def test_decode_update_is_householder():
     rng = np.random.default_rng(29)
     n, d = 12, 6
