@@ -22,7 +22,10 @@ F / scan duration against the 2.5 PFLOP/s dense fp16/bf16 matrix peak.  Its
 `traffic` (HBM bytes per launch) comes from the rocprofv3 counter summary
 profiles/hbm_traffic.json and is reported only while the kernel's source
 still hashes to the value recorded there; the decode kernel's traffic is
-reported the same way.
+reported the same way.  After the timed steps the gated decode step
+(forget-gate prefix cache beside the key cache) runs on the same cache for
+the same numbers of warm-up and timed launches and is reported in
+`decode_fox` on the decode bytes plus 4 bytes per cached key.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-ref]
                     [--fwd-config {2,3,4}]
@@ -108,6 +111,9 @@ def main():
     xf = {n: (t.to(dev) if t is not None else None) for n, t in synthetic.config_inputs(cid).items()}
     gates = xf.get("log_forget")
     xd = {n: t.to(dev) for n, t in synthetic.config_inputs(5).items()}
+    gd = synthetic.decode_gate_inputs(cd.B, cd.H, cd.cache_len, cd.capacity, cd.seed)
+    log_f_t = gd["log_f_t"].to(dev)
+    cum_cache = torch.cumsum(gd["log_f_cache"].double(), dim=-1).float().to(dev)
     fargs = (xf["q"], xf["k"], xf["v"], xf["w"], xf["beta"])
     ws = pa.fwd_workspace(xf["q"], gates)
     o = torch.empty_like(xf["q"])
@@ -148,6 +154,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] {args.steps} timed steps done in {wall:.3f} s", file=sys.stderr, flush=True)
+    # The gated (forget-gate) decode step on the same cache, timed on its own
+    # after the steps above: the same number of launches, each bracketed by events.
+    fox_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.warmup + args.steps):
+        if k >= args.warmup:
+            fox_evs[k - args.warmup][0].record()
+        pa.path_decode_step_fox(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], log_f_t, xd["k_cache"],
+                                xd["v_cache"], cum_cache, cd.cache_len, scale=cd.scale, workspace=dws)
+        if k >= args.warmup:
+            fox_evs[k - args.warmup][1].record()
+    torch.cuda.synchronize()
+    fox_ms = statistics.median(e[0].elapsed_time(e[1]) for e in fox_evs)
     prep_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
     scan_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evs)
     dec_ms = statistics.median(e[2].elapsed_time(e[3]) for e in evs)
@@ -156,6 +174,8 @@ def main():
     tflops = F / (fwd_ms * 1e-3) / 1e12
     dbytes = decode_bytes(cd.B, cd.H, cd.cache_len, cd.d, 2)
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    fbytes = dbytes + 4 * cd.B * cd.H * cd.cache_len  # plus one fp32 gate prefix per cached key
+    fox_gbs = fbytes / (fox_ms * 1e-3) / 1e9
 
     scan_tflops = F / (scan_ms * 1e-3) / 1e12
     traffic = load_traffic("scan") if cid == 2 else None
@@ -184,6 +204,9 @@ def main():
         "decode": {"ms": round(dec_ms, 4), "GB_per_s": round(dec_gbs, 1), "bytes_model": dbytes,
                    "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode"),
                    "source_sha256": source_hash("decode")},
+        "decode_fox": {"ms": round(fox_ms, 4), "GB_per_s": round(fox_gbs, 1), "bytes_model": fbytes,
+                       "frac_hbm_peak": round(fox_gbs / PEAK_HBM_GBS, 4),
+                       "what": "gated decode step, same cache, forget-gate prefix cache (fp32)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -28,7 +28,7 @@ STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UN
           4: "PATH_ERR_WORKSPACE", 5: "PATH_ERR_CAPACITY", 6: "PATH_ERR_HIP"}
 EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
            "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
-           "path_decode_workspace_bytes", "path_decode_step"]
+           "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox"]
 
 _lib = None
 _I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.path_decode_step.restype = _INT
         L.path_decode_step.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 7 + [_I64, _I64] +
                                        [_VP, _VP, _VP, _SZ, _VP])
+        L.path_decode_step_fox.restype = _INT
+        L.path_decode_step_fox.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 9 + [_I64, _I64] +
+                                           [_VP, _VP, _VP, _SZ, _VP])
         _lib = L
     return _lib
 
@@ -207,6 +210,18 @@ def path_decode_step(q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, cache_len, sc
 
     Updates k_cache[:, :, :cache_len] in place, writes k_t, v_t at slot cache_len,
     returns (o [B,H,d], lse [B,H] fp32)."""
+    return _decode(q_t, k_t, v_t, w_t, beta_t, None, k_cache, v_cache, None, cache_len, scale, workspace)
+
+
+def path_decode_step_fox(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, cache_len,
+                         scale=1.0, workspace=None):
+    """One PaTH-FoX decode step: path_decode_step plus log_f_t [B,H] fp32 and the
+    gate-prefix cache cum_cache [B,H,capacity] fp32 (slots < cache_len hold c_j;
+    the step writes c_t at slot cache_len)."""
+    return _decode(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, cache_len, scale, workspace)
+
+
+def _decode(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, cache_len, scale, workspace):
     B, H, d = q_t.shape
     cap = k_cache.shape[2]
     dt = q_t.dtype
@@ -215,13 +230,21 @@ def path_decode_step(q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, cache_len, sc
     _check(beta_t, "beta_t", torch.float32, (B, H))
     _check(k_cache, "k_cache", dt, (B, H, cap, d))
     _check(v_cache, "v_cache", dt, (B, H, cap, d))
+    fox = log_f_t is not None
+    if fox:
+        _check(log_f_t, "log_f_t", torch.float32, (B, H))
+        _check(cum_cache, "cum_cache", torch.float32, (B, H, cap))
     o = torch.empty_like(q_t)
     lse = torch.empty((B, H), dtype=torch.float32, device=q_t.device)
     nbytes = decode_workspace_bytes(B, H, d, cache_len)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q_t.device)
-    st = lib().path_decode_step(B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t),
-                                _ptr(w_t), _ptr(beta_t), _ptr(k_cache), _ptr(v_cache), int(cache_len), int(cap),
-                                _ptr(o), _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream(q_t))
-    _raise(st, "path_decode_step")
+    head = (B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t))
+    tail = (int(cache_len), int(cap), _ptr(o), _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream(q_t))
+    if fox:
+        st = lib().path_decode_step_fox(*head, _ptr(log_f_t), _ptr(k_cache), _ptr(v_cache), _ptr(cum_cache), *tail)
+        _raise(st, "path_decode_step_fox")
+    else:
+        st = lib().path_decode_step(*head, _ptr(k_cache), _ptr(v_cache), *tail)
+        _raise(st, "path_decode_step")
     return o, lse

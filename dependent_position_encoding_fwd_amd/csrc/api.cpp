@@ -267,10 +267,14 @@ size_t path_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int64_t cach
   return align_up(sizeof(float) * size_t(n > 0 ? n : 1));
 }
 
-int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
-                     const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                     void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
-                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_common(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t, const void* k_t,
+                  const void* v_t, const void* w_t, const float* beta_t, const float* log_f_t, void* k_cache,
+                  void* v_cache, float* cum_cache, int64_t cache_len, int64_t capacity, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_d(d))) return st;
@@ -285,9 +289,31 @@ int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, co
   if (!workspace || need == 0 || workspace_bytes < need ||
       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return PATH_ERR_WORKSPACE;
-  return hip_status(path::launch_decode(dtype, BH, d, scale, q_t, k_t, v_t, w_t, beta_t, k_cache,
-                                        v_cache, cache_len, capacity, o, lse,
+  return hip_status(path::launch_decode(dtype, BH, d, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache,
+                                        v_cache, cum_cache, cache_len, capacity, o, lse,
                                         static_cast<float*>(workspace), stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                     const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                     void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(B, H, d, dtype, scale, q_t, k_t, v_t, w_t, beta_t, nullptr, k_cache, v_cache, nullptr,
+                       cache_len, capacity, o, lse, workspace, workspace_bytes, stream);
+}
+
+int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                         const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                         const float* log_f_t, void* k_cache, void* v_cache, float* cum_cache,
+                         int64_t cache_len, int64_t capacity, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!log_f_t || !cum_cache) return PATH_ERR_NULL;
+  return decode_common(B, H, d, dtype, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache,
+                       cum_cache, cache_len, capacity, o, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

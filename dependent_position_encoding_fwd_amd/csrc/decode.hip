@@ -13,6 +13,13 @@
 // lanes cover one row, so a wave touches 1 KiB of contiguous cache per pass.
 // The chunk loop is software-pipelined: the loads of the next group of 8 rows
 // per lane are issued before the current group is updated and attended to.
+//
+// Gated variant (FOX) [same summary, §2 "Extensões: PaTH-FoX"]: the logit of
+// cached key j gains the forget-gate sum over j < s <= t, kept as a difference
+// of running prefixes c_t - c_j.  The prefix of every cached key sits in an
+// fp32 cache beside the key cache (4 bytes per key against 2 d-element rows),
+// is fetched in the same pipelined group as the key and value rows, and the
+// step appends c_t = c_{t-1} + log f_t for the new key, whose own bias is 0.
 #include <math.h>
 
 #include <type_traits>
@@ -80,11 +87,12 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // partial layout per (bh, chunk): [m, l, acc[D]]
-template <typename T, int D>
+template <typename T, int D, bool FOX>
 __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
     int64_t cache_len, int64_t capacity, int nchunks, float scale, const T* __restrict__ q_t,
-    const T* __restrict__ w_t, const float* __restrict__ beta_t, T* __restrict__ k_cache,
-    const T* __restrict__ v_cache, float* __restrict__ partials) {
+    const T* __restrict__ w_t, const float* __restrict__ beta_t, const float* __restrict__ log_f_t,
+    T* __restrict__ k_cache, const T* __restrict__ v_cache, const float* __restrict__ cum_cache,
+    float* __restrict__ partials) {
   using V = Vec16<T>;
   constexpr int EPV = V::N;          // elements per 16-byte access
   constexpr int LPK = D / EPV;       // lanes per key row
@@ -111,7 +119,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   for (int e = 0; e < EPV; ++e) wq += wv[e] * qv[e];
   wq = group_sum<LPK>(wq);
   const float bt = beta_t[bh];
-  const float scale2 = scale * 1.4426950408889634f;  // logits in log2 units
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float scale2 = scale * kLog2e;  // logits in log2 units
+  const float* cbase = FOX ? cum_cache + bh * capacity : nullptr;
+  // c_t of the new query; this kernel only runs with cache_len >= 1.
+  const float ct = FOX ? cbase[cache_len - 1] + log_f_t[bh] : 0.f;
 
   const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
   const int64_t j1 = j0 + kDecChunk < cache_len ? j0 + kDecChunk : cache_len;
@@ -126,15 +138,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 
   constexpr int STRIDE = NW * KPW;  // key rows per workgroup pass
   typename V::raw kr[UNR], vr[UNR];
+  float cr[UNR];
   auto fetch = [&](int64_t jb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
       kr[u] = typename V::raw{0u, 0u, 0u, 0u};
       vr[u] = kr[u];
+      cr[u] = 0.f;
       if (j < j1) {
         kr[u] = __builtin_nontemporal_load(&kbase[j * LPK + sub]);
         vr[u] = __builtin_nontemporal_load(&vbase[j * LPK + sub]);
+        if constexpr (FOX) cr[u] = cbase[j];
       }
     }
   };
@@ -142,10 +157,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   if (jstart < j1) fetch(jstart);
   for (int64_t jb = jstart; jb < j1; jb += STRIDE * UNR) {
     typename V::raw kc[UNR], vc[UNR];
+    float cc[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       kc[u] = kr[u];
       vc[u] = vr[u];
+      cc[u] = cr[u];
     }
     if (jb + STRIDE * UNR < j1) fetch(jb + STRIDE * UNR);
     float sv[UNR];
@@ -167,7 +184,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < EPV; ++e) kf[e] -= ba * wv[e];
       if (live) __builtin_nontemporal_store(V::pack(kf), &kbase[j * LPK + sub]);
-      sv[u] = live ? scale2 * (b - ba * wq) : -INFINITY;
+      float su = scale2 * (b - ba * wq);
+      if constexpr (FOX) su += kLog2e * (ct - cc[u]);
+      sv[u] = live ? su : -INFINITY;
     }
     float mb = sv[0];
 #pragma unroll
@@ -241,13 +260,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 }
 
 // One wave per (b,h): merge chunk partials with the new key, write o and lse,
-// then append k_t, v_t at slot cache_len.
-template <typename T, int D>
+// then append k_t, v_t (and, gated, c_t) at slot cache_len.
+template <typename T, int D, bool FOX>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     int64_t cache_len, int64_t capacity, int nchunks, float scale, const T* __restrict__ q_t,
-    const T* __restrict__ k_t, const T* __restrict__ v_t, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, const float* __restrict__ partials, T* __restrict__ o,
-    float* __restrict__ lse) {
+    const T* __restrict__ k_t, const T* __restrict__ v_t, const float* __restrict__ log_f_t,
+    T* __restrict__ k_cache, T* __restrict__ v_cache, float* __restrict__ cum_cache,
+    const float* __restrict__ partials, T* __restrict__ o, float* __restrict__ lse) {
   constexpr int PER = D / 64;
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
@@ -287,47 +306,64 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     k_cache[(bh * capacity + cache_len) * D + e] = k_t[bh * D + e];
     v_cache[(bh * capacity + cache_len) * D + e] = v_t[bh * D + e];
   }
-  if (lane == 0) lse[bh] = (mm + __log2f(ll)) * 0.69314718055994531f;
+  if (lane == 0) {
+    lse[bh] = (mm + __log2f(ll)) * 0.69314718055994531f;
+    if constexpr (FOX) {
+      float* cbase = cum_cache + bh * capacity;
+      cbase[cache_len] = (cache_len > 0 ? cbase[cache_len - 1] : 0.f) + log_f_t[bh];
+    }
+  }
 }
 
 int64_t decode_num_chunks(int64_t cache_len) { return (cache_len + kDecChunk - 1) / kDecChunk; }
 
-template <typename T, int D>
+template <typename T, int D, bool FOX>
 static hipError_t launch_dec_t(int64_t BH, float scale, const void* q_t, const void* k_t,
                                const void* v_t, const void* w_t, const float* beta_t,
-                               void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity,
-                               void* o, float* lse, float* partials, hipStream_t stream) {
+                               const float* log_f_t, void* k_cache, void* v_cache, float* cum_cache,
+                               int64_t cache_len, int64_t capacity, void* o, float* lse,
+                               float* partials, hipStream_t stream) {
   const int nchunks = static_cast<int>(decode_num_chunks(cache_len));
   if (nchunks > 0) {
-    hipLaunchKernelGGL((decode_chunk_kernel<T, D>), dim3(static_cast<unsigned>(BH * nchunks)),
+    hipLaunchKernelGGL((decode_chunk_kernel<T, D, FOX>), dim3(static_cast<unsigned>(BH * nchunks)),
                        dim3(kDecThreads), 0, stream, cache_len, capacity, nchunks, scale,
-                       static_cast<const T*>(q_t), static_cast<const T*>(w_t), beta_t,
-                       static_cast<T*>(k_cache), static_cast<const T*>(v_cache), partials);
+                       static_cast<const T*>(q_t), static_cast<const T*>(w_t), beta_t, log_f_t,
+                       static_cast<T*>(k_cache), static_cast<const T*>(v_cache), cum_cache, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, FOX>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
                      stream, cache_len, capacity, nchunks, scale, static_cast<const T*>(q_t),
-                     static_cast<const T*>(k_t), static_cast<const T*>(v_t),
-                     static_cast<T*>(k_cache), static_cast<T*>(v_cache), partials,
+                     static_cast<const T*>(k_t), static_cast<const T*>(v_t), log_f_t,
+                     static_cast<T*>(k_cache), static_cast<T*>(v_cache), cum_cache, partials,
                      static_cast<T*>(o), lse);
   return hipGetLastError();
 }
 
+template <bool FOX>
+static hipError_t launch_dec_fox(int dtype, int64_t BH, int64_t d, float scale, const void* q_t,
+                                 const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                                 const float* log_f_t, void* k_cache, void* v_cache, float* cum_cache,
+                                 int64_t cache_len, int64_t capacity, void* o, float* lse,
+                                 float* partials, hipStream_t stream) {
+  auto go = [&](auto launch) {
+    return launch(BH, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, cache_len,
+                  capacity, o, lse, partials, stream);
+  };
+  if (dtype == 0) return d == 64 ? go(launch_dec_t<float, 64, FOX>) : go(launch_dec_t<float, 128, FOX>);
+  return d == 64 ? go(launch_dec_t<bf16_t, 64, FOX>) : go(launch_dec_t<bf16_t, 128, FOX>);
+}
+
 hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const void* q_t,
                          const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                         void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity,
-                         void* o, float* lse, float* partials, hipStream_t stream) {
-  if (dtype == 0) {
-    return d == 64 ? launch_dec_t<float, 64>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
-                                             cache_len, capacity, o, lse, partials, stream)
-                   : launch_dec_t<float, 128>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
-                                              cache_len, capacity, o, lse, partials, stream);
-  }
-  return d == 64 ? launch_dec_t<bf16_t, 64>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
-                                            cache_len, capacity, o, lse, partials, stream)
-                 : launch_dec_t<bf16_t, 128>(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache,
-                                             cache_len, capacity, o, lse, partials, stream);
+                         const float* log_f_t, void* k_cache, void* v_cache, float* cum_cache,
+                         int64_t cache_len, int64_t capacity, void* o, float* lse, float* partials,
+                         hipStream_t stream) {
+  if (log_f_t)
+    return launch_dec_fox<true>(dtype, BH, d, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache,
+                                v_cache, cum_cache, cache_len, capacity, o, lse, partials, stream);
+  return launch_dec_fox<false>(dtype, BH, d, scale, q_t, k_t, v_t, w_t, beta_t, nullptr, k_cache, v_cache,
+                               nullptr, cache_len, capacity, o, lse, partials, stream);
 }
 
 }  // namespace path

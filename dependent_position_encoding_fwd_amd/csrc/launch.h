@@ -50,11 +50,14 @@ hipError_t launch_fwd_scan_f32(int dtype, int64_t B, int64_t H, int64_t L, int64
                                const float* beta, const float* cum, const float* khat,
                                const float* pT, void* o, float* lse, hipStream_t stream);
 
-// Decode: number of key chunks and partial-result floats per (b,h).
+// Decode: number of key chunks and partial-result floats per (b,h).  With
+// log_f_t != null the step is gated: cum_cache [BH, capacity] holds the gate
+// prefixes of the cached keys and receives c_t at slot cache_len.
 int64_t decode_num_chunks(int64_t cache_len);
 hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const void* q_t,
                          const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                         void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity,
-                         void* o, float* lse, float* partials, hipStream_t stream);
+                         const float* log_f_t, void* k_cache, void* v_cache, float* cum_cache,
+                         int64_t cache_len, int64_t capacity, void* o, float* lse, float* partials,
+                         hipStream_t stream);
 
 }  // namespace path

@@ -150,6 +150,29 @@ int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, co
                      void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * path_decode_step_fox - one PaTH-FoX generation step [PaTH summary §2
+ * "Extensões: PaTH-FoX" with §3 "Inferência"]: path_decode_step with the
+ * forget-gate bias.  The gate prefix of key j is c_j = sum_{s<=j} log f_s
+ * (natural log); the logit of cached key j gains c_t - c_j, the new key's
+ * logit gains nothing, where
+ *   c_t = cum_cache[b,h,cache_len-1] + log_f_t[b,h]   (c_t = log_f_t[b,h] when cache_len == 0),
+ * formed in fp32.  Everything else is exactly path_decode_step.
+ * Inputs: as path_decode_step, plus log_f_t [B,H] fp32 (log of the gate, <= 0
+ *   for a forget gate; any finite value is accepted).
+ * cum_cache [B,H,capacity] fp32, caller-owned: slots j < cache_len hold c_j on
+ *   entry (for a prefilled prompt: path_prepare's cum); the step writes c_t at
+ *   slot cache_len and touches no other slot.
+ * Workspace: path_decode_workspace_bytes(...), as for path_decode_step.
+ * Errors: as path_decode_step; PATH_ERR_NULL also when log_f_t or cum_cache is
+ *   NULL.  After PATH_ERR_HIP the key cache and cum_cache[cache_len] are undefined.
+ */
+int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                         const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                         const float* log_f_t, void* k_cache, void* v_cache, float* cum_cache,
+                         int64_t cache_len, int64_t capacity, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,11 +128,15 @@ def fwd_inputs(B, H, L, d, dtype="bf16", seed=0, near2_frac=0.0, fox=False, head
     return res
 
 
-def decode_inputs(B, H, d, cache_len, capacity, dtype="bf16", seed=0, heads=None):
+def decode_inputs(B, H, d, cache_len, capacity, dtype="bf16", seed=0, heads=None, fox=False):
     """Decode-step inputs on the CPU.
 
     q_t, k_t, v_t, w_t: [.., d] in `dtype`; beta_t: [..] fp32; k_cache, v_cache:
-    [.., capacity, d] in `dtype` with slots >= cache_len zero.
+    [.., capacity, d] in `dtype` with slots >= cache_len zero.  With fox=True
+    also the gates of the new token, log_f_t [..] fp32, and of the cached
+    tokens, log_f_cache [.., capacity] fp32 (zero from slot cache_len on), drawn
+    like the forward's forget gates; turning the latter into the prefix cache
+    is left to the caller.
     """
     tdt = DTYPES[dtype]
     hl = _heads(B, H, heads)
@@ -153,7 +157,26 @@ def decode_inputs(B, H, d, cache_len, capacity, dtype="bf16", seed=0, heads=None
     res["beta_t"] = torch.stack(acc["beta_t"]).to(torch.float32).view(*lead)
     for name in ("k_cache", "v_cache"):
         res[name] = torch.stack(acc[name]).to(tdt).view(*lead, capacity, d)
+    if fox:
+        res.update(decode_gate_inputs(B, H, cache_len, capacity, seed, heads))
     return res
+
+
+def decode_gate_inputs(B, H, cache_len, capacity, seed=0, heads=None):
+    """The forget gates of a gated decode step alone (what decode_inputs adds
+    with fox=True): log_f_t [..] and log_f_cache [.., capacity] fp32."""
+    hl = _heads(B, H, heads)
+    lft, lfc = [], []
+    for (b, h) in hl:
+        y = 3.0 + torch.randn(cache_len + 1, generator=_gen(seed, "forget", b, h))
+        lf = torch.nn.functional.logsigmoid(y)
+        c = torch.zeros(capacity)
+        c[:cache_len] = lf[:cache_len]
+        lfc.append(c)
+        lft.append(lf[cache_len])
+    lead = (B, H) if heads is None else (len(hl),)
+    return {"log_f_t": torch.stack(lft).to(torch.float32).view(*lead),
+            "log_f_cache": torch.stack(lfc).to(torch.float32).view(*lead, capacity)}
 
 
 def config_inputs(cfg_id: int, heads=None, small=None):

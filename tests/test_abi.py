@@ -95,6 +95,20 @@ def test_decode_validation():
     assert _dec(wsb=8) == WS
 
 
+def _dec_fox(cache_len=10, capacity=11, lf=FAKE, cum=FAKE, ptr=FAKE, ws=FAKE, wsb=1 << 30):
+    return pa.lib().path_decode_step_fox(2, 2, 64, 1, 1.0, ptr, ptr, ptr, ptr, ptr, lf, ptr, ptr, cum, cache_len,
+                                         capacity, ptr, ptr, ws, wsb, None)
+
+
+def test_decode_fox_validation():
+    assert _dec_fox(lf=None) == NULL
+    assert _dec_fox(cum=None) == NULL
+    assert _dec_fox(ptr=None) == NULL
+    assert _dec_fox(cache_len=11, capacity=11) == CAP
+    assert _dec_fox(cache_len=-1) == SHAPE
+    assert _dec_fox(ws=None) == WS
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)

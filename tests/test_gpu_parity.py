@@ -141,19 +141,43 @@ def _bf16_ulp(x):
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-def _decode_case(B, H, d, n, cap, dtype, scale, seed, heads_to_check=None):
-    print(f"[decode] B={B} H={H} d={d} len={n} cap={cap} {dtype} seed={seed}", flush=True)
-    x = synthetic.decode_inputs(B, H, d, n, cap, dtype, seed)
+def _decode_case(B, H, d, n, cap, dtype, scale, seed, heads_to_check=None, fox=False, log_f_t=None):
+    print(f"[decode] B={B} H={H} d={d} len={n} cap={cap} {dtype} seed={seed} fox={fox} log_f_t={log_f_t}",
+          flush=True)
+    x = synthetic.decode_inputs(B, H, d, n, cap, dtype, seed, fox=fox)
     g = _dev(x)
-    o, lse = pa.path_decode_step(g["q_t"], g["k_t"], g["v_t"], g["w_t"], g["beta_t"], g["k_cache"], g["v_cache"],
-                                 n, scale=scale)
+    if fox:
+        if log_f_t is not None:
+            x["log_f_t"] = torch.full_like(x["log_f_t"], float(log_f_t))
+            g["log_f_t"] = x["log_f_t"].to(DEV)
+        # Cache state: running gate prefixes c_j of the cached tokens (fp64 sums
+        # stored fp32); slots past the cache hold a sentinel that must survive.
+        cum = torch.cumsum(x["log_f_cache"].double(), dim=-1).float()
+        cum[..., n:] = 12345.0
+        cum_dev = cum.to(DEV)
+        o, lse = pa.path_decode_step_fox(g["q_t"], g["k_t"], g["v_t"], g["w_t"], g["beta_t"], g["log_f_t"],
+                                         g["k_cache"], g["v_cache"], cum_dev, n, scale=scale)
+    else:
+        o, lse = pa.path_decode_step(g["q_t"], g["k_t"], g["v_t"], g["w_t"], g["beta_t"], g["k_cache"],
+                                     g["v_cache"], n, scale=scale)
     torch.cuda.synchronize()
     heads = heads_to_check or [(b, h) for b in range(B) for h in range(H)]
     kc_gpu = g["k_cache"]
     for (b, h) in heads:
-        ro, rl, kupd = oracle.path_decode_head(x["q_t"][b, h], x["k_t"][b, h], x["v_t"][b, h], x["w_t"][b, h],
-                                               float(x["beta_t"][b, h]), x["k_cache"][b, h, :n],
-                                               x["v_cache"][b, h, :n], scale)
+        if fox:
+            ro, rl, kupd, _ = oracle.path_decode_fox_head(
+                x["q_t"][b, h], x["k_t"][b, h], x["v_t"][b, h], x["w_t"][b, h], float(x["beta_t"][b, h]),
+                float(x["log_f_t"][b, h]), x["k_cache"][b, h, :n], x["v_cache"][b, h, :n], cum[b, h, :n], scale)
+            # The new prefix is one fp32 addition, c_{n-1} + log f_t (c_{-1} = 0).
+            prev = cum[b, h, n - 1] if n > 0 else torch.zeros((), dtype=torch.float32)
+            want = prev + x["log_f_t"][b, h]
+            got_c = cum_dev[b, h].cpu()
+            assert torch.equal(got_c[n], want)
+            assert torch.equal(got_c[:n], cum[b, h, :n]) and torch.equal(got_c[n + 1:], cum[b, h, n + 1:])
+        else:
+            ro, rl, kupd = oracle.path_decode_head(x["q_t"][b, h], x["k_t"][b, h], x["v_t"][b, h], x["w_t"][b, h],
+                                                   float(x["beta_t"][b, h]), x["k_cache"][b, h, :n],
+                                                   x["v_cache"][b, h, :n], scale)
         assert np.max(np.abs(_np(o[b, h]) - ro)) <= TOL_O[dtype]
         assert abs(float(lse[b, h]) - rl) <= TOL_LSE
         got = _np(kc_gpu[b, h, :n])
@@ -180,6 +204,53 @@ def test_decode_config5_full_sampled():
     c = synthetic.CONFIGS[5]
     heads = [(0, 0), (17, 5), (40, 11), (63, 15)]
     _decode_case(c.B, c.H, c.d, c.cache_len, c.capacity, c.dtype, c.scale, c.seed, heads)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [0, 1, 100, 1500])
+def test_decode_fox_small(dtype, d, n):
+    _decode_case(2, 3, d, n, n + 7, dtype, 1.0, seed=n + d + 7, fox=True)
+
+
+@pytest.mark.parametrize("log_f_t", [0.0, -800.0])
+def test_decode_fox_open_and_closed_gate(log_f_t):
+    """An open gate at t (log f_t = 0) and a closed one (-800: every cached key's
+    weight underflows to 0, so o = v_t and lse is the new key's logit)."""
+    o, lse = _decode_case(2, 2, 64, 700, 720, "f32", 0.7, seed=5, fox=True, log_f_t=log_f_t)
+    if log_f_t < -100:
+        x = synthetic.decode_inputs(2, 2, 64, 700, 720, "f32", 5, fox=True)
+        assert torch.allclose(o.cpu(), x["v_t"], atol=1e-6)
+
+
+def test_decode_fox_config5_full_sampled():
+    """The cache-8192 decode workload (B=64, H=16, d=64, bf16) with forget gates."""
+    c = synthetic.CONFIGS[5]
+    heads = [(0, 0), (17, 5), (40, 11), (63, 15)]
+    _decode_case(c.B, c.H, c.d, c.cache_len, c.capacity, c.dtype, c.scale, c.seed, heads, fox=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fox_decode_from_empty_matches_forward_rows(d):
+    """Gated decode steps from an empty cache, each appending its key and its gate
+    prefix, reproduce the gated forward's rows; the prefix cache they build is the
+    running sum of the gates."""
+    L, B, H = 96, 1, 2
+    x = synthetic.fwd_inputs(B, H, L, d, "f32", 321, fox=True)
+    ro, rl = oracle.path_fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["log_forget"], 0.5)
+    g = _dev(x)
+    kc = torch.zeros(B, H, L, d, device=DEV)
+    vc = torch.zeros(B, H, L, d, device=DEV)
+    cc = torch.zeros(B, H, L, device=DEV)
+    for t in range(L):
+        o, lse = pa.path_decode_step_fox(g["q"][:, :, t].contiguous(), g["k"][:, :, t].contiguous(),
+                                         g["v"][:, :, t].contiguous(), g["w"][:, :, t].contiguous(),
+                                         g["beta"][:, :, t].contiguous(), g["log_forget"][:, :, t].contiguous(),
+                                         kc, vc, cc, t, scale=0.5)
+        assert np.max(np.abs(_np(o) - ro[:, :, t])) <= 1e-4
+        assert np.max(np.abs(_np(lse) - rl[:, :, t])) <= 1e-4
+    want = np.stack([[oracle.prefix_sum(x["log_forget"][b, h]) for h in range(H)] for b in range(B)])
+    assert np.max(np.abs(_np(cc) - want)) <= 1e-4
 
 
 def test_decode_after_prefill_matches_forward_rows():
