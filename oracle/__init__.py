@@ -5,7 +5,8 @@ Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of
 package never imports the library: the two share no code.
 
 The arithmetic lives in `path_oracle.c` (plain C, fp64, OpenMP over query
-rows) and, for tiny explicit-matrix cross-checks, in `tiny.py`.  This module
+rows), for tiny explicit-matrix cross-checks in `tiny.py`, and for gradients
+in `grad.py` (float64 reverse-mode differentiation of the defining loop).  This module
 only compiles the C file with the host compiler and marshals numpy arrays.
 
 Source pages: "PaTH Attention" technical summary (gist.science 2505.16381),

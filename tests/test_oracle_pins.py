@@ -26,7 +26,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import tiny
+from oracle import grad, tiny
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -351,3 +351,67 @@ def test_boundary_adjusted_qk_and_block_scan():
 def test_prefix_sum():
     x = np.array([0.5, -1.25, 2.0, 0.125])
     np.testing.assert_array_equal(oracle.prefix_sum(x), np.array([0.5, -0.75, 1.25, 1.375]))
+
+
+# --- gradients (oracle/grad.py) -------------------------------------------
+
+def _bwd_case(rng, L, d, fox):
+    q, k, v, w, beta = _rand_head(rng, L, d)
+    lf = -rng.uniform(0.0, 0.5, size=L) if fox else None
+    do = rng.standard_normal((L, d))
+    return q, k, v, w, beta, lf, do
+
+
+def test_grad_forward_loop_matches_c_oracle():
+    """The differentiable loop computes the same o, lse as the C oracle."""
+    rng = np.random.default_rng(43)
+    q, k, v, w, beta, lf, _ = _bwd_case(rng, 37, 8, True)
+    o_c, lse_c = oracle.path_fwd_head(q, k, v, w, beta, lf, 0.7)
+    T = grad._t
+    o_t, lse_t = grad.forward_torch(T(q), T(k), T(v), T(w), T(beta), T(lf), 0.7)
+    np.testing.assert_allclose(o_t.numpy(), o_c, atol=1e-12)
+    np.testing.assert_allclose(lse_t.numpy(), lse_c, atol=1e-12)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_grad_matches_central_differences_of_c_oracle(fox):
+    """Every gradient against the directional derivative of <dO, o> taken by
+    central differences of the independent C forward."""
+    rng = np.random.default_rng(47 + fox)
+    L, d, scale = 21, 6, 0.9
+    q, k, v, w, beta, lf, do = _bwd_case(rng, L, d, fox)
+    g = grad.path_bwd_head(q, k, v, w, beta, lf, scale, do)
+    args = {"q": q, "k": k, "v": v, "w": w, "beta": beta}
+    if fox:
+        args["log_forget"] = lf
+
+    def loss(a):
+        o, _ = oracle.path_fwd_head(a["q"], a["k"], a["v"], a["w"], a["beta"], a.get("log_forget"), scale)
+        return float(np.sum(o * do))
+
+    eps = 1e-5
+    for name in args:
+        delta = rng.standard_normal(np.shape(args[name]))
+        ap = dict(args); ap[name] = args[name] + eps * delta
+        am = dict(args); am[name] = args[name] - eps * delta
+        fd = (loss(ap) - loss(am)) / (2 * eps)
+        an = float(np.sum(g["d" + name] * delta))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_grad_beta_zero_is_softmax_attention_grad():
+    """beta = 0: every H is I, so dq, dk, dv are those of causal softmax attention
+    (torch's scaled_dot_product_attention differentiated in float64) and dw = 0."""
+    rng = np.random.default_rng(53)
+    L, d, scale = 30, 8, 0.6
+    q, k, v, w, _, _, do = _bwd_case(rng, L, d, False)
+    beta = np.zeros(L)
+    g = grad.path_bwd_head(q, k, v, w, beta, None, scale, do)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], is_causal=True,
+                                                         scale=scale)[0]
+    rq, rk, rv = torch.autograd.grad((o * torch.tensor(do)).sum(), (tq, tk, tv))
+    np.testing.assert_allclose(g["dq"], rq.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dk"], rk.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dv"], rv.numpy(), atol=1e-12)
+    assert np.all(g["dw"] == 0.0)
