@@ -56,7 +56,10 @@ def path_bwd_head(q, k, v, w, beta, log_forget, scale, do):
     o, _ = forward_torch(xs["q"], xs["k"], xs["v"], xs["w"], xs["beta"], lf, float(scale))
     loss = (o * _t(do)).sum()
     inputs = [xs[n] for n in ("q", "k", "v", "w", "beta")] + ([lf] if lf is not None else [])
-    grads = torch.autograd.grad(loss, inputs)
+    # w_0 and beta_0 never enter a logit (the product for j = i is empty), so at
+    # L = 1 they are unused: their gradient is zero.
+    grads = torch.autograd.grad(loss, inputs, allow_unused=True)
+    grads = [torch.zeros_like(x) if g is None else g for x, g in zip(inputs, grads)]
     out = {f"d{n}": g.numpy() for n, g in zip(("q", "k", "v", "w", "beta"), grads)}
     out["dlog_forget"] = grads[5].numpy() if lf is not None else None
     return out

@@ -415,3 +415,13 @@ def test_grad_beta_zero_is_softmax_attention_grad():
     np.testing.assert_allclose(g["dk"], rk.numpy(), atol=1e-12)
     np.testing.assert_allclose(g["dv"], rv.numpy(), atol=1e-12)
     assert np.all(g["dw"] == 0.0)
+
+
+def test_grad_single_token_has_no_transition_gradient():
+    """L = 1: o = v_0 whatever q, k, w, beta are, so only dv is non-zero."""
+    rng = np.random.default_rng(59)
+    q, k, v, w, beta, _, do = _bwd_case(rng, 1, 5, False)
+    g = grad.path_bwd_head(q, k, v, w, beta, None, 1.0, do)
+    np.testing.assert_allclose(g["dv"], do, atol=1e-15)
+    for n in ("dq", "dk", "dw", "dbeta"):
+        assert np.all(g[n] == 0.0), n
