@@ -28,7 +28,8 @@ STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UN
           4: "PATH_ERR_WORKSPACE", 5: "PATH_ERR_CAPACITY", 6: "PATH_ERR_HIP"}
 EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
            "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
-           "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox"]
+           "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox",
+           "path_bwd_workspace_bytes", "path_attn_bwd"]
 
 _lib = None
 _I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.path_decode_step.restype = _INT
         L.path_decode_step.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 7 + [_I64, _I64] +
                                        [_VP, _VP, _VP, _SZ, _VP])
+        L.path_bwd_workspace_bytes.restype = _SZ
+        L.path_bwd_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _INT, _INT]
+        L.path_attn_bwd.restype = _INT
+        L.path_attn_bwd.argtypes = [_I64, _I64, _I64, _I64, _INT, _F] + [_VP] * 15 + [_VP, _SZ, _VP]
         L.path_decode_step_fox.restype = _INT
         L.path_decode_step_fox.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 9 + [_I64, _I64] +
                                            [_VP, _VP, _VP, _SZ, _VP])
@@ -153,6 +158,32 @@ def path_attn_fwd(q, k, v, w, beta, log_forget=None, scale=1.0, precision="auto"
                              int(workspace.numel()), _stream(q))
     _raise(st, "path_attn_fwd")
     return o, lse
+
+
+def bwd_workspace_bytes(B, H, L, d, dtype_code, with_forget) -> int:
+    return int(lib().path_bwd_workspace_bytes(B, H, L, d, dtype_code, int(bool(with_forget))))
+
+
+def path_attn_bwd(q, k, v, w, beta, o, lse, do, log_forget=None, scale=1.0, workspace=None):
+    """PaTH backward: gradients of sum(do * o) for the forward path_attn_fwd(q, k, v, w,
+    beta, log_forget, scale) that returned (o, lse).
+
+    Returns (dq, dk, dv, dw in the input dtype, dbeta fp32, dlog_forget fp32 or None)."""
+    B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
+    _check(o, "o", q.dtype, (B, H, L, d))
+    _check(do, "do", q.dtype, (B, H, L, d))
+    _check(lse, "lse", torch.float32, (B, H, L))
+    dq, dk, dv, dw = (torch.empty_like(q) for _ in range(4))
+    dbeta = torch.empty_like(beta)
+    dlf = torch.empty_like(log_forget) if log_forget is not None else None
+    nbytes = bwd_workspace_bytes(B, H, L, d, code, log_forget is not None)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    st = lib().path_attn_bwd(B, H, L, d, code, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+                             _ptr(log_forget), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw),
+                             _ptr(dbeta), _ptr(dlf), _ptr(workspace), int(workspace.numel()), _stream(q))
+    _raise(st, "path_attn_bwd")
+    return dq, dk, dv, dw, dbeta, dlf
 
 
 def path_fwd_stage_prepare(q, k, v, w, beta, log_forget=None, scale=1.0, precision="auto", workspace=None):

@@ -317,3 +317,101 @@ int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale
 }
 
 }  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+  size_t qhat, khat, pT, cum, Dv, dqh, rsum, dkh, dP, dV, csum, dc, scratch, total;
+  int64_t zero_count;
+};
+
+// Returns false when the sizes overflow.
+bool bwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget, BwdLayout* w) {
+  int64_t pairs, scr;
+  if (!mul_ok(BH, Nb * (Nb - 1) / 2, &pairs) || !mul_ok(pairs, d * kBlk, &scr)) return false;
+  size_t off = 0;
+  const size_t bh = size_t(BH), nb = size_t(Nb), dd = size_t(d), l = size_t(L);
+  auto take = [&](size_t floats) {
+    size_t at = off;
+    off += align_up(sizeof(float) * floats);
+    return at;
+  };
+  *w = BwdLayout{};
+  w->qhat = take(bh * l * dd);
+  w->khat = take(bh * l * dd);
+  w->pT = take(bh * nb * dd * dd);
+  if (with_forget) w->cum = take(bh * l);
+  w->Dv = take(bh * l);
+  w->dqh = take(bh * l * dd);
+  w->rsum = take(bh * l);
+  w->dc = take(bh * l);
+  // cleared together, in this order and without gaps
+  w->dkh = take(bh * l * dd);
+  w->dP = take(bh * nb * dd * dd);
+  w->dV = take(bh * l * dd);
+  w->csum = take(bh * l);
+  w->zero_count = int64_t((off - w->dkh) / sizeof(float));
+  w->scratch = take(size_t(scr));
+  w->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, int with_forget) {
+  int64_t BH, Nb;
+  if (check_dtype(dtype) || check_shape(B, H, L, d, &BH, &Nb)) return 0;
+  BwdLayout lay;
+  if (!bwd_layout(BH, L, d, Nb, with_forget != 0, &lay)) return 0;
+  return lay.total;
+}
+
+int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale, const void* q,
+                  const void* k, const void* v, const void* w, const float* beta, const float* log_forget,
+                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dw,
+                  float* dbeta, float* dlog_forget, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  int64_t BH, Nb;
+  if ((st = check_shape(B, H, L, d, &BH, &Nb))) return st;
+  if (!q || !k || !v || !w || !beta || !o || !lse || !dout || !dq || !dk || !dv || !dw || !dbeta)
+    return PATH_ERR_NULL;
+  if (log_forget && !dlog_forget) return PATH_ERR_NULL;
+  BwdLayout lay;
+  if (!bwd_layout(BH, L, d, Nb, log_forget != nullptr, &lay)) return PATH_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return PATH_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  path::BwdArgs a{};
+  a.BH = BH;
+  a.L = L;
+  a.scale = scale;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.w = w;
+  a.beta = beta;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw = dw;
+  a.dbeta = dbeta;
+  a.dlog_forget = log_forget ? dlog_forget : nullptr;
+  a.ws = path::BwdWs{at(lay.qhat), at(lay.khat), at(lay.pT), log_forget ? at(lay.cum) : nullptr, at(lay.Dv),
+                     at(lay.dqh), at(lay.rsum), at(lay.dkh), at(lay.dP), at(lay.dV), at(lay.csum), at(lay.dc),
+                     at(lay.scratch), at(lay.dkh), lay.zero_count};
+  if ((st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.qhat, a.ws.khat,
+                                                a.ws.pT, stream))))
+    return st;
+  if (log_forget && (st = hip_status(path::launch_prefix_sum(BH, L, log_forget, a.ws.cum, stream)))) return st;
+  return hip_status(path::launch_bwd(dtype, d, a, stream));
+}
+
+}  // extern "C"

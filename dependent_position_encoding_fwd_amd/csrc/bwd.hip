@@ -1,0 +1,495 @@
+// Backward pass of PaTH attention: gradients of <dO, o> with respect to q, k,
+// v, w, beta and the log forget gates, in fp32 arithmetic on the vector ALUs.
+//
+// The forward [PaTH Attention summary (gist.science 2505.16381), §2 "Mecanismo
+// Central", §2 "Extensões: PaTH-FoX"; blockwise as in §3 "Representação de
+// Transformação UT" and §3 "Algoritmo Estilo FlashAttention"] gives, for query
+// i in block m and key j in block n < m,
+//     s_ij = scale * khat_j . Qt_i^(n) + (c_i - c_j),
+//     Qt^(m-1) = Qhat_m,   Qt^(n-1) = P_n Qt^(n),   P_n = H_{64n} ... H_{64n+63},
+// and inside a block the logit of keys c <= r is scale * k_c . (H_{c+1}...H_r q_r).
+// The pages say nothing about training; this file differentiates that forward.
+//
+// Cross-block part (bwd_pair_kernel, one workgroup per query block m):
+//   pass 1, right to left: Qt^(n) for n = m-1..0, kept in a scratch buffer;
+//   pass 2, left to right: with dS_ij = p_ij (dO_i . v_j - D_i), D_i = dO_i . o_i,
+//     the adjoint of the transported queries obeys
+//       Lam^(n) = P_n^T Lam^(n-1) + scale Khat_n^T dS_n,   Lam^(-1) = 0,
+//     so Lam^(m-1) is the gradient reaching Qhat_m, P_n receives Lam^(n-1) Qt^(n)^T,
+//     Khat_n receives scale dS_n Qt^(n)^T and V_n receives p_n dO_m; the last
+//     three are summed over query blocks with fp32 atomics.
+// In-block part (bwd_block_kernel, one workgroup per block): every Householder
+// chain of the block is replayed by one wave and then differentiated in reverse:
+// query chains x <- H_t x from q_r down to qhat_r (they meet the in-block keys
+// on the way), key chains from k_c up to khat_c, and one chain per column of
+// P_n.  Running a chain backwards needs its states in the opposite order; each
+// state is rebuilt from the next one as x^(t+1) = x^(t) + beta_t a_t w_t, where
+// a_t = w_t . x^(t+1) is the one scalar the forward replay keeps per step.  For
+// H_t = I - beta_t w_t w_t^T receiving dH_t = sum xbar x^T over its uses,
+//     dw_t = -beta_t (dH_t + dH_t^T) w_t,   dbeta_t = -w_t^T dH_t w_t.
+// Gate gradient: dc_i = sum_{j<i} dS_ij - sum_{i'>i} dS_i'i, and
+// d log f_s = sum_{i>=s} dc_i (fp64 suffix sums).
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace path {
+namespace {
+
+constexpr int kT = 256;  // threads per workgroup (a 16 x 16 grid for the tile products)
+
+// acc(m, n) += sum_{kk<K} a(m, kk) b(kk, n) over a 16 x 16 thread grid; thread
+// (tm, tn) owns rows m = tm + 16 i and columns n = tn + 16 j.
+template <int M, int N, int K, typename FA, typename FB>
+__device__ __forceinline__ void tile_acc(const FA& a, const FB& b, float (&acc)[M / 16][N / 16]) {
+  constexpr int TM = M / 16, TN = N / 16;
+  const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
+#pragma unroll 4
+  for (int kk = 0; kk < K; ++kk) {
+    float av[TM], bv[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) av[i] = a(tm + 16 * i, kk);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bv[j] = b(kk, tn + 16 * j);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+  }
+}
+
+template <int M, int N, typename FE>
+__device__ __forceinline__ void tile_emit(const float (&acc)[M / 16][N / 16], const FE& emit) {
+  const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
+#pragma unroll
+  for (int i = 0; i < M / 16; ++i)
+#pragma unroll
+    for (int j = 0; j < N / 16; ++j) emit(tm + 16 * i, tn + 16 * j, acc[i][j]);
+}
+
+template <int M, int N, int K, typename FA, typename FB, typename FE>
+__device__ __forceinline__ void tile_mm(const FA& a, const FB& b, const FE& emit) {
+  float acc[M / 16][N / 16];
+#pragma unroll
+  for (int i = 0; i < M / 16; ++i)
+#pragma unroll
+    for (int j = 0; j < N / 16; ++j) acc[i][j] = 0.f;
+  tile_acc<M, N, K>(a, b, acc);
+  tile_emit<M, N>(acc, emit);
+}
+
+__device__ __forceinline__ float lane_of(float x, int t) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
+}
+
+}  // namespace
+
+// D_i = dO_i . o_i, one thread per row.
+template <typename T, int D>
+__global__ __launch_bounds__(kT) void bwd_rowdot_kernel(int64_t rows, const T* __restrict__ dO,
+                                                        const T* __restrict__ o, float* __restrict__ out) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kT + threadIdx.x;
+  if (r >= rows) return;
+  float s = 0.f;
+#pragma unroll 8
+  for (int e = 0; e < D; ++e) s = fmaf(load_f32(dO + r * D + e), load_f32(o + r * D + e), s);
+  out[r] = s;
+}
+
+__global__ __launch_bounds__(kT) void bwd_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kT + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kT)
+    p[i] = 0.f;
+}
+
+// out[s] = sum_{i >= s} dc[i] per head, accumulated in fp64.
+__global__ __launch_bounds__(kT) void bwd_suffix_kernel(int64_t L, const float* __restrict__ dc,
+                                                        float* __restrict__ out) {
+  __shared__ double tot[kT];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * L;
+  const int64_t chunk = (L + kT - 1) / kT;
+  const int64_t lo = threadIdx.x * chunk;
+  const int64_t hi = lo + chunk < L ? lo + chunk : L;
+  double s = 0.0;
+  for (int64_t i = lo; i < hi; ++i) s += dc[base + i];
+  tot[threadIdx.x] = s;
+  __syncthreads();
+  double run = 0.0;
+  for (int t = threadIdx.x + 1; t < kT; ++t) run += tot[t];
+  for (int64_t i = hi - 1; i >= lo; --i) {
+    run += dc[base + i];
+    out[base + i] = static_cast<float>(run);
+  }
+}
+
+template <typename T, int D, bool FOX>
+__global__ __launch_bounds__(kT) void bwd_pair_kernel(
+    int64_t L, int Nb, int64_t BH, float scale, const T* __restrict__ v, const T* __restrict__ dO,
+    const float* __restrict__ qhat, const float* __restrict__ khat, const float* __restrict__ pT,
+    const float* __restrict__ cum, const float* __restrict__ lse, const float* __restrict__ Dv,
+    float* __restrict__ qt_scratch, float* __restrict__ dqh, float* __restrict__ rsum,
+    float* __restrict__ dkh, float* __restrict__ dPacc, float* __restrict__ dVacc,
+    float* __restrict__ csum) {
+  constexpr int C = kBlk, CP = C + 1, DP = D + 1;
+  __shared__ float Qt[D][CP];   // transported queries of the block, column i = query i
+  __shared__ float Lam[D][CP];  // their adjoint; also the transport's output
+  __shared__ float Kh[C][DP];   // khat rows of key block n
+  __shared__ float Vn[C][DP];   // value rows of key block n
+  __shared__ float X[C][CP];    // [key j][query i]: p, then dS
+  __shared__ float sD[C], sL[C], sCm[C], sCn[C], sRs[C];
+
+  const int tid = threadIdx.x;
+  const int m = Nb - 1 - static_cast<int>(blockIdx.x / BH);  // longest query blocks first
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t i0 = static_cast<int64_t>(m) * C;
+  const int valid = static_cast<int>(L - i0 < C ? L - i0 : C);
+  const int64_t hb = bh * L;
+  const T* dOm = dO + (hb + i0) * D;
+  const auto dO_at = [&](int i, int e) { return i < valid ? load_f32(dOm + static_cast<int64_t>(i) * D + e) : 0.f; };
+
+  if (tid < C) {
+    const bool ok = tid < valid;
+    sD[tid] = ok ? Dv[hb + i0 + tid] : 0.f;
+    sL[tid] = ok ? lse[hb + i0 + tid] : 0.f;
+    sCm[tid] = (FOX && ok) ? cum[hb + i0 + tid] : 0.f;
+    sRs[tid] = 0.f;
+  }
+  for (int idx = tid; idx < C * D; idx += kT) {
+    const int i = idx / D, e = idx % D;
+    Qt[e][i] = i < valid ? qhat[(hb + i0 + i) * D + e] : 0.f;
+    Lam[e][i] = 0.f;
+  }
+  __syncthreads();
+
+  const int64_t npairs = static_cast<int64_t>(Nb) * (Nb - 1) / 2;
+  float* scr = qt_scratch + (bh * npairs + static_cast<int64_t>(m) * (m - 1) / 2) * (D * C);
+
+  // Pass 1: Qt^(n) for n = m-1 .. 0.
+  for (int n = m - 1; n >= 0; --n) {
+    float* dst = scr + static_cast<int64_t>(n) * (D * C);
+    for (int idx = tid; idx < D * C; idx += kT) dst[idx] = Qt[idx / C][idx % C];
+    if (n == 0) break;
+    const float* P = pT + (bh * Nb + n) * D * D;  // P^T row-major: P[a][b] = P[b * D + a]
+    tile_mm<D, C, D>([&](int a, int b) { return P[b * D + a]; }, [&](int b, int i) { return Qt[b][i]; },
+                     [&](int a, int i, float x) { Lam[a][i] = x; });
+    __syncthreads();
+    for (int idx = tid; idx < D * C; idx += kT) Qt[idx / C][idx % C] = Lam[idx / C][idx % C];
+    __syncthreads();
+  }
+  __syncthreads();
+  for (int idx = tid; idx < D * C; idx += kT) Lam[idx / C][idx % C] = 0.f;
+
+  // Pass 2: key blocks left to right.
+  for (int n = 0; n < m; ++n) {
+    const int64_t j0 = static_cast<int64_t>(n) * C;
+    __syncthreads();
+    const float* src = scr + static_cast<int64_t>(n) * (D * C);
+    for (int idx = tid; idx < D * C; idx += kT) Qt[idx / C][idx % C] = src[idx];
+    for (int idx = tid; idx < C * D; idx += kT) {
+      const int j = idx / D, e = idx % D;
+      Kh[j][e] = khat[(hb + j0 + j) * D + e];
+      Vn[j][e] = load_f32(v + (hb + j0 + j) * D + e);
+    }
+    if (tid < C) sCn[tid] = FOX ? cum[hb + j0 + tid] : 0.f;
+    __syncthreads();
+
+    // p_ij
+    tile_mm<C, C, D>([&](int j, int e) { return Kh[j][e]; }, [&](int e, int i) { return Qt[e][i]; },
+                     [&](int j, int i, float s) {
+                       const float sv = scale * s + (FOX ? sCm[i] - sCn[j] : 0.f);
+                       X[j][i] = i < valid ? expf(sv - sL[i]) : 0.f;
+                     });
+    __syncthreads();
+    // dV_n += p dO_m
+    tile_mm<C, D, C>([&](int j, int i) { return X[j][i]; }, dO_at, [&](int j, int e, float x) {
+      unsafeAtomicAdd(dVacc + (hb + j0 + j) * D + e, x);
+    });
+    __syncthreads();
+    // dS = p (dO . v - D)
+    tile_mm<C, C, D>([&](int j, int e) { return Vn[j][e]; }, [&](int e, int i) { return dO_at(i, e); },
+                     [&](int j, int i, float x) { X[j][i] = X[j][i] * (x - sD[i]); });
+    __syncthreads();
+    if (FOX) {
+      if (tid < C) {
+        float r = 0.f;
+        for (int j = 0; j < C; ++j) r += X[j][tid];
+        sRs[tid] += r;
+      } else if (tid < 2 * C) {
+        const int j = tid - C;
+        float c = 0.f;
+        for (int i = 0; i < C; ++i) c += X[j][i];
+        unsafeAtomicAdd(csum + hb + j0 + j, c);
+      }
+    }
+    // dKhat_n += scale dS Qt^T
+    tile_mm<C, D, C>([&](int j, int i) { return X[j][i]; }, [&](int i, int e) { return Qt[e][i]; },
+                     [&](int j, int e, float x) { unsafeAtomicAdd(dkh + (hb + j0 + j) * D + e, scale * x); });
+    // dP_n += Lam^(n-1) Qt^(n)^T
+    if (n >= 1)
+      tile_mm<D, D, C>([&](int a, int i) { return Lam[a][i]; }, [&](int i, int b) { return Qt[b][i]; },
+                       [&](int a, int b, float x) { unsafeAtomicAdd(dPacc + ((bh * Nb + n) * D + a) * D + b, x); });
+    // Lam <- P_n^T Lam + scale Khat_n^T dS
+    float acc[D / 16][C / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < C / 16; ++j) acc[i][j] = 0.f;
+    if (n >= 1) {
+      const float* P = pT + (bh * Nb + n) * D * D;
+      tile_acc<D, C, D>([&](int a, int b) { return P[a * D + b]; }, [&](int b, int i) { return Lam[b][i]; }, acc);
+    }
+    tile_acc<D, C, C>([&](int a, int j) { return scale * Kh[j][a]; }, [&](int j, int i) { return X[j][i]; }, acc);
+    __syncthreads();
+    tile_emit<D, C>(acc, [&](int a, int i, float x) { Lam[a][i] = x; });
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * D; idx += kT) {
+    const int i = idx / D, e = idx % D;
+    if (i < valid) dqh[(hb + i0 + i) * D + e] = Lam[e][i];
+  }
+  if (FOX && tid < valid) rsum[hb + i0 + tid] = sRs[tid];
+}
+
+template <typename T, int D, bool FOX>
+__global__ __launch_bounds__(kT) void bwd_block_kernel(
+    int64_t L, int Nb, int64_t BH, float scale, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const T* __restrict__ w, const float* __restrict__ beta,
+    const T* __restrict__ dO, const float* __restrict__ cum, const float* __restrict__ lse,
+    const float* __restrict__ Dv, const float* __restrict__ dqh, const float* __restrict__ dkh,
+    const float* __restrict__ dPacc, const float* __restrict__ dVacc, const float* __restrict__ rsum,
+    const float* __restrict__ csum, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    T* __restrict__ dw, float* __restrict__ dbeta, float* __restrict__ dc) {
+  constexpr int C = kBlk, CP = C + 1, NE = D / 64;
+  __shared__ float Ws[C][D], Ks[C][D], gW[C][D], gK[C][D];
+  __shared__ float PD[C][CP];  // [key c][query r]: dO_r . v_c, then p
+  __shared__ float sB[C], sL[C], sD[C], sC[C], gB[C], cs[C], rs[C];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = static_cast<int>(blockIdx.x / BH);
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t t0 = static_cast<int64_t>(n) * C;
+  const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
+  const int64_t hb = bh * L;
+  const int64_t rb = (hb + t0) * D;  // first element of the block's rows
+
+  for (int idx = tid; idx < C * D; idx += kT) {
+    const int r = idx / D, e = idx % D;
+    const bool ok = r < valid;
+    Ws[r][e] = ok ? load_f32(w + rb + idx) : 0.f;
+    Ks[r][e] = ok ? load_f32(k + rb + idx) : 0.f;
+    gW[r][e] = 0.f;
+    gK[r][e] = 0.f;
+  }
+  if (tid < C) {
+    const bool ok = tid < valid;
+    sB[tid] = ok ? beta[hb + t0 + tid] : 0.f;
+    sL[tid] = ok ? lse[hb + t0 + tid] : 0.f;
+    sD[tid] = ok ? Dv[hb + t0 + tid] : 0.f;
+    sC[tid] = (FOX && ok) ? cum[hb + t0 + tid] : 0.f;
+    gB[tid] = 0.f;
+    cs[tid] = 0.f;
+    rs[tid] = 0.f;
+  }
+  const auto dO_at = [&](int r, int e) { return r < valid ? load_f32(dO + rb + static_cast<int64_t>(r) * D + e) : 0.f; };
+  tile_mm<C, C, D>([&](int c, int e) { return c < valid ? load_f32(v + rb + static_cast<int64_t>(c) * D + e) : 0.f; },
+                   [&](int e, int r) { return dO_at(r, e); },
+                   [&](int c, int r, float x) { PD[c][r] = c <= r ? x : 0.f; });  // p = 0 above the causal edge
+  __syncthreads();
+
+  const bool haveP = n >= 1 && n <= Nb - 2;  // P_n takes part in some transport
+  const int nchains = 2 * valid + (haveP ? D : 0);
+  for (int ch = wave; ch < nchains; ch += kT / 64) {
+    float x[NE], xb[NE];
+    float alph = 0.f;
+    if (ch < valid) {
+      // Query chain r: x = H_{t+1}...H_r q_r meets key t, then takes H_t.
+      const int r = ch;
+      const float lr = sL[r], dr = sD[r], cr = sC[r];
+      float Ereg = 0.f, dsreg = 0.f;
+#pragma unroll
+      for (int u = 0; u < NE; ++u) x[u] = load_f32(q + rb + static_cast<int64_t>(r) * D + lane + 64 * u);
+      for (int t = r; t >= 0; --t) {
+        float kx = 0.f, wx = 0.f;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          kx = fmaf(Ks[t][lane + 64 * u], x[u], kx);
+          wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
+        }
+        kx = wave_sum(kx);
+        wx = wave_sum(wx);
+        const float sv = scale * kx + (FOX ? cr - sC[t] : 0.f);
+        const float p = expf(sv - lr);
+        const float ds = p * (PD[t][r] - dr);
+        if (lane == t) {
+          Ereg = scale * ds;
+          dsreg = ds;
+          alph = wx;
+        }
+        if (lane == 0) PD[t][r] = p;
+        const float bw = sB[t] * wx;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
+      }
+      if (FOX) {
+        const float rsv = wave_sum(lane < r ? dsreg : 0.f);
+        if (lane == 0) rs[r] = rsv;
+        if (lane < r) atomicAdd(&cs[lane], dsreg);
+      }
+#pragma unroll
+      for (int u = 0; u < NE; ++u) xb[u] = dqh[rb + static_cast<int64_t>(r) * D + lane + 64 * u];
+      for (int t = 0; t <= r; ++t) {
+        const float a = lane_of(alph, t), E = lane_of(Ereg, t), bt = sB[t];
+        float xn[NE], g = 0.f;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          xn[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
+          g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
+        }
+        g = wave_sum(g);
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xn[u]));
+          xb[u] = fmaf(-bt * g, Ws[t][lane + 64 * u], xb[u]);
+          xb[u] = fmaf(E, Ks[t][lane + 64 * u], xb[u]);
+          atomicAdd(&gK[t][lane + 64 * u], E * xn[u]);
+          x[u] = xn[u];
+        }
+        if (lane == 0) atomicAdd(&gB[t], -g * a);
+      }
+#pragma unroll
+      for (int u = 0; u < NE; ++u) store_f32(dq + rb + static_cast<int64_t>(r) * D + lane + 64 * u, xb[u]);
+    } else if (ch < 2 * valid) {
+      // Key chain c: y = H_t...H_{c+1} k_c, from k_c up to khat_c.
+      const int c = ch - valid;
+#pragma unroll
+      for (int u = 0; u < NE; ++u) x[u] = Ks[c][lane + 64 * u];
+      for (int t = c + 1; t < valid; ++t) {
+        float wx = 0.f;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
+        wx = wave_sum(wx);
+        if (lane == t) alph = wx;
+        const float bw = sB[t] * wx;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NE; ++u) xb[u] = dkh[rb + static_cast<int64_t>(c) * D + lane + 64 * u];
+      for (int t = valid - 1; t > c; --t) {
+        const float a = lane_of(alph, t), bt = sB[t];
+        float xp[NE], g = 0.f;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          xp[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
+          g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
+        }
+        g = wave_sum(g);
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xp[u]));
+          xb[u] = fmaf(-bt * g, Ws[t][lane + 64 * u], xb[u]);
+          x[u] = xp[u];
+        }
+        if (lane == 0) atomicAdd(&gB[t], -g * a);
+      }
+#pragma unroll
+      for (int u = 0; u < NE; ++u) atomicAdd(&gK[c][lane + 64 * u], xb[u]);
+    } else {
+      // Column col of P_n = H_0 ... H_63: x = H_t...H_63 e_col.
+      const int col = ch - 2 * valid;
+#pragma unroll
+      for (int u = 0; u < NE; ++u) x[u] = (lane + 64 * u == col) ? 1.f : 0.f;
+      for (int t = valid - 1; t >= 0; --t) {
+        float wx = 0.f;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
+        wx = wave_sum(wx);
+        if (lane == t) alph = wx;
+        const float bw = sB[t] * wx;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
+      }
+      const float* gP = dPacc + (bh * Nb + n) * D * D;
+#pragma unroll
+      for (int u = 0; u < NE; ++u) xb[u] = gP[(lane + 64 * u) * D + col];
+      for (int t = 0; t < valid; ++t) {
+        const float a = lane_of(alph, t), bt = sB[t];
+        float xn[NE], g = 0.f;
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          xn[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
+          g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
+        }
+        g = wave_sum(g);
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+          atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xn[u]));
+          xb[u] = fmaf(-bt * g, Ws[t][lane + 64 * u], xb[u]);
+          x[u] = xn[u];
+        }
+        if (lane == 0) atomicAdd(&gB[t], -g * a);
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < C * D; idx += kT) {
+    const int r = idx / D, e = idx % D;
+    if (r < valid) {
+      store_f32(dk + rb + idx, gK[r][e]);
+      store_f32(dw + rb + idx, gW[r][e]);
+    }
+  }
+  if (tid < valid) {
+    dbeta[hb + t0 + tid] = gB[tid];
+    if (FOX) dc[hb + t0 + tid] = rsum[hb + t0 + tid] + rs[tid] - csum[hb + t0 + tid] - cs[tid];
+  }
+  // dv_c = cross-block part + sum_r p_cr dO_r
+  tile_mm<C, D, C>([&](int c, int r) { return PD[c][r]; }, dO_at, [&](int c, int e, float x) {
+    if (c < valid) store_f32(dv + rb + static_cast<int64_t>(c) * D + e, x + dVacc[rb + static_cast<int64_t>(c) * D + e]);
+  });
+}
+
+template <typename T, int D, bool FOX>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int64_t BH = a.BH, L = a.L;
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  const T* v = static_cast<const T*>(a.v);
+  const T* dO = static_cast<const T*>(a.dout);
+  hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3(static_cast<unsigned>((BH * L + kT - 1) / kT)), dim3(kT), 0,
+                     stream, BH * L, dO, static_cast<const T*>(a.o), a.ws.Dv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3(2048), dim3(kT), 0, stream, a.ws.zero_begin, a.ws.zero_count);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(BH * Nb));
+  hipLaunchKernelGGL((bwd_pair_kernel<T, D, FOX>), grid, dim3(kT), 0, stream, L, Nb, BH, a.scale, v, dO,
+                     a.ws.qhat, a.ws.khat, a.ws.pT, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum,
+                     a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.csum);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(kT), 0, stream, L, Nb, BH, a.scale,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k), v, static_cast<const T*>(a.w), a.beta, dO,
+                     a.ws.cum, a.lse, a.ws.Dv, a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum,
+                     static_cast<T*>(a.dq), static_cast<T*>(a.dk), static_cast<T*>(a.dv), static_cast<T*>(a.dw),
+                     a.dbeta, a.ws.dc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (FOX) {
+    hipLaunchKernelGGL(bwd_suffix_kernel, dim3(static_cast<unsigned>(BH)), dim3(kT), 0, stream, L, a.ws.dc,
+                       a.dlog_forget);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream) {
+  const bool fox = a.ws.cum != nullptr;
+  if (dtype == 0) {
+    if (d == 64) return fox ? launch_bwd_t<float, 64, true>(a, stream) : launch_bwd_t<float, 64, false>(a, stream);
+    return fox ? launch_bwd_t<float, 128, true>(a, stream) : launch_bwd_t<float, 128, false>(a, stream);
+  }
+  if (d == 64) return fox ? launch_bwd_t<bf16_t, 64, true>(a, stream) : launch_bwd_t<bf16_t, 64, false>(a, stream);
+  return fox ? launch_bwd_t<bf16_t, 128, true>(a, stream) : launch_bwd_t<bf16_t, 128, false>(a, stream);
+}
+
+}  // namespace path

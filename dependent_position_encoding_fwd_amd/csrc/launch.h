@@ -60,4 +60,27 @@ hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const vo
                          int64_t cache_len, int64_t capacity, void* o, float* lse, float* partials,
                          hipStream_t stream);
 
+// Backward pass (fp32 arithmetic).  Workspace regions, all fp32; the run from
+// zero_begin over zero_count floats (dkh, dP, dV, csum) is cleared first.
+struct BwdWs {
+  float *qhat, *khat, *pT, *cum, *Dv, *dqh, *rsum, *dkh, *dP, *dV, *csum, *dc, *scratch;
+  float* zero_begin;
+  int64_t zero_count;
+};
+struct BwdArgs {
+  int64_t BH, L;
+  float scale;
+  const void *q, *k, *v, *w;
+  const float* beta;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void *dq, *dk, *dv, *dw;
+  float* dbeta;
+  float* dlog_forget;
+  BwdWs ws;  // ws.cum != null selects the gated form
+};
+// Launches everything after the fp32 prepare and the gate prefix sums.
+hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream);
+
 }  // namespace path

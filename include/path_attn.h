@@ -124,6 +124,37 @@ int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, f
                         const float* beta, const float* log_forget, void* o, float* lse,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes path_attn_bwd needs for these sizes (0 on invalid sizes). */
+size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype,
+                                int with_forget);
+
+/*
+ * path_attn_bwd - gradients of the PaTH forward [PaTH summary §2 "Mecanismo
+ * Central", §2 "Extensões: PaTH-FoX", in the blockwise form of §3
+ * "Representação de Transformação UT" and "Algoritmo Estilo FlashAttention";
+ * the pages describe no backward pass, so this is the exact derivative of
+ * path_attn_fwd's definition]: with dO the gradient reaching o (lse receives
+ * none), writes the gradients of sum(dO * o) with respect to every input.
+ * Inputs: q, k, v, w, beta, log_forget (or NULL), scale as given to
+ *   path_attn_fwd; o [B,H,L,d] (dtype) and lse [B,H,L] fp32 as it returned
+ *   them (used to rebuild the softmax: p = exp(s - lse), D_i = dO_i . o_i);
+ *   dout = dO [B,H,L,d] (dtype).
+ * Outputs (caller-allocated): dq, dk, dv, dw [B,H,L,d] in dtype (bf16 rounded
+ *   to nearest even); dbeta [B,H,L] fp32; dlog_forget [B,H,L] fp32, required
+ *   when log_forget is given and ignored otherwise.
+ * Arithmetic is fp32 throughout (a fp32 re-run of the prepare stage, then the
+ *   cross-block and in-block gradient kernels); the cross-block sums use fp32
+ *   atomics, so results may differ in the last bits between runs.
+ * workspace: >= path_bwd_workspace_bytes(...) bytes, 256-byte aligned.  It
+ *   holds, among fp32 intermediates, the transported queries of every
+ *   (query block, earlier key block) pair: B*H*Nb*(Nb-1)/2 * d * 64 floats.
+ */
+int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale, const void* q,
+                  const void* k, const void* v, const void* w, const float* beta, const float* log_forget,
+                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dw,
+                  float* dbeta, float* dlog_forget, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
 /* Workspace bytes path_decode_step needs (0 on invalid sizes). */
 size_t path_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int64_t cache_len);
 

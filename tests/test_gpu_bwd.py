@@ -1,0 +1,105 @@
+"""GPU parity of the backward pass: path_attn_bwd (through the C ABI) against
+the fp64 gradients of the oracle (oracle/grad.py) on identical seeded inputs.
+
+The oracle differentiates <dO, o> in float64 from the stored input values.
+The backward is fed the oracle's o (stored in the input dtype) and lse (fp32),
+as a forward would hand them over.  Bar, for every gradient tensor G: the
+largest element error is at most tol * max|G_ref|, with tol = 1e-4 for fp32
+storage and 2e-2 for bf16 storage (the gradients are rounded to bf16, and the
+softmax row terms D_i = dO_i . o_i use the bf16-rounded o).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dependent_position_encoding_fwd_amd as pa
+import synthetic
+from oracle import grad
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _cmp(name, got, ref, tol):
+    err = float(np.max(np.abs(_np(got) - ref))) if ref.size else 0.0
+    mag = float(np.max(np.abs(ref))) if ref.size else 0.0
+    print(f"  {name}: max|err|={err:.3e} max|ref|={mag:.3e} ratio={err / max(mag, 1e-30):.2e}", flush=True)
+    assert err <= tol * max(mag, 1e-6), (name, err, mag)
+
+
+def _bwd_case(B, H, L, d, dtype, scale, seed, fox, chain_forward=False):
+    print(f"[bwd] B={B} H={H} L={L} d={d} {dtype} scale={scale} fox={fox} seed={seed} "
+          f"chain_forward={chain_forward}", flush=True)
+    x = synthetic.fwd_inputs(B, H, L, d, dtype, seed, fox=fox)
+    g = torch.Generator().manual_seed(seed + 1000)
+    do = torch.randn(B, H, L, d, generator=g).to(synthetic.DTYPES[dtype])
+    refs = {}
+    o_ref = np.zeros((B, H, L, d))
+    lse_ref = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            lf = None if x["log_forget"] is None else x["log_forget"][b, h]
+            r = grad.path_bwd_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["w"][b, h], x["beta"][b, h], lf,
+                                   scale, do[b, h])
+            T = grad._t
+            ot, lt = grad.forward_torch(T(x["q"][b, h]), T(x["k"][b, h]), T(x["v"][b, h]), T(x["w"][b, h]),
+                                        T(x["beta"][b, h]), None if lf is None else T(lf), scale)
+            o_ref[b, h], lse_ref[b, h] = ot.numpy(), lt.numpy()
+            for n, val in r.items():
+                if val is not None:
+                    refs.setdefault(n, np.zeros((B, H) + val.shape))[b, h] = val
+    gx = {n: (t.to(DEV) if t is not None else None) for n, t in x.items()}
+    if chain_forward:
+        o, lse = pa.path_attn_fwd(gx["q"], gx["k"], gx["v"], gx["w"], gx["beta"], gx["log_forget"], scale=scale)
+    else:
+        o = torch.tensor(o_ref).to(synthetic.DTYPES[dtype]).to(DEV)
+        lse = torch.tensor(lse_ref, dtype=torch.float32).to(DEV)
+    dq, dk, dv, dw, dbeta, dlf = pa.path_attn_bwd(gx["q"], gx["k"], gx["v"], gx["w"], gx["beta"], o, lse,
+                                                  do.to(DEV), gx["log_forget"], scale=scale)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("dw", dw), ("dbeta", dbeta)):
+        _cmp(name, got, refs[name], tol)
+    if fox:
+        _cmp("dlog_forget", dlf, refs["dlog_forget"], tol)
+    else:
+        assert dlf is None
+
+
+@pytest.mark.parametrize("L,d,fox", [(1, 64, False), (64, 64, True), (200, 64, False), (200, 64, True),
+                                     (130, 128, True), (300, 128, False)])
+def test_bwd_f32(L, d, fox):
+    _bwd_case(1, 2, L, d, "f32", 0.3, seed=L + d + fox, fox=fox)
+
+
+@pytest.mark.parametrize("L,d,fox", [(200, 64, True), (130, 128, False)])
+def test_bwd_bf16(L, d, fox):
+    _bwd_case(1, 2, L, d, "bf16", 0.3, seed=L + d + 7 * fox, fox=fox)
+
+
+def test_bwd_long_f32():
+    """Ten blocks: transports across up to nine block transitions."""
+    _bwd_case(1, 1, 600, 64, "f32", 0.25, seed=600, fox=True)
+
+
+def test_bwd_after_gpu_forward_bf16():
+    """The backward fed the GPU forward's own o and lse."""
+    _bwd_case(2, 2, 257, 64, "bf16", 0.125, seed=257, fox=False, chain_forward=True)
+
+
+def test_bwd_deterministic_up_to_atomics():
+    """Two runs agree to fp32 summation-order differences."""
+    x = synthetic.fwd_inputs(1, 2, 300, 64, "f32", 11, fox=True)
+    g = {n: t.to(DEV) for n, t in x.items()}
+    do = torch.randn(1, 2, 300, 64, generator=torch.Generator().manual_seed(5)).to(DEV)
+    o, lse = pa.path_attn_fwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_forget"], scale=0.5)
+    r1 = pa.path_attn_bwd(g["q"], g["k"], g["v"], g["w"], g["beta"], o, lse, do, g["log_forget"], scale=0.5)
+    r2 = pa.path_attn_bwd(g["q"], g["k"], g["v"], g["w"], g["beta"], o, lse, do, g["log_forget"], scale=0.5)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.allclose(a, b, rtol=1e-5, atol=1e-5)
