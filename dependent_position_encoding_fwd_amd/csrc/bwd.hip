@@ -33,48 +33,92 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mfma_util.h"
 
 namespace path {
 namespace {
 
-constexpr int kT = 256;  // threads per workgroup (a 16 x 16 grid for the tile products)
+constexpr int kT = 256;    // threads per workgroup: 4 waves
+constexpr int kTB = 1024;  // in-block kernel: 16 waves, one Householder chain per wave at a time
 
-// acc(m, n) += sum_{kk<K} a(m, kk) b(kk, n) over a 16 x 16 thread grid; thread
-// (tm, tn) owns rows m = tm + 16 i and columns n = tn + 16 j.
+// Sum over the 64 lanes of a wave, the same bits in every lane: pairwise sums
+// within quads, 8-lane halves and 16-lane rows by DPP lane permutations, then
+// across the four rows by the permlane swaps.  Each step adds two partial sums
+// held by two lanes, and addition is commutative, so all lanes agree.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8-lane half
+  x += dpp_mov<0x140>(x);  // row_mirror: the other half of the 16-lane row
+  return mfma::grp_sum(x);
+}
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Tile products on the fp32 matrix cores (16x16x4 MFMA, fp32 in and out).  For
+// an M x N product, wave wv owns the 16-row tiles wv, wv + 4, ... and every
+// 16-column tile: acc[r][c] is rows 16 (wv + 4 r) .., columns 16 c ...  In one
+// MFMA lane l supplies A[l % 16][k] and B[k][l % 16] with k = l / 16 and holds
+// D[4 (l / 16) + i][l % 16] in element i.  The reduction index is visited in
+// chunks of 16, lane group g taking k = 16 c + 4 g + j in MFMA j of chunk c, so
+// each lane reads 4 consecutive k of its row.  a(m, k) and b(k, n) are read
+// through accessors; emit(m, n, value) receives each output element once.
+template <int M, int N>
+using Acc = f4[M / 64][N / 16];
+
 template <int M, int N, int K, typename FA, typename FB>
-__device__ __forceinline__ void tile_acc(const FA& a, const FB& b, float (&acc)[M / 16][N / 16]) {
-  constexpr int TM = M / 16, TN = N / 16;
-  const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
-#pragma unroll 4
-  for (int kk = 0; kk < K; ++kk) {
-    float av[TM], bv[TN];
+__device__ __forceinline__ void tile_acc(const FA& a, const FB& b, Acc<M, N>& acc) {
+  static_assert(M % 64 == 0 && N % 16 == 0 && K % 16 == 0, "tile shape");
+  constexpr int R = M / 64, NC = N / 16;
+  const int wv = threadIdx.x >> 6, lr = threadIdx.x & 15, lk = (threadIdx.x >> 4) & 3;
+#pragma unroll 2
+  for (int c = 0; c < K / 16; ++c) {
+    float av[4][R], bv[4][NC];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) av[i] = a(tm + 16 * i, kk);
+    for (int j = 0; j < 4; ++j) {
+      const int kk = 16 * c + 4 * lk + j;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bv[j] = b(kk, tn + 16 * j);
+      for (int r = 0; r < R; ++r) av[j][r] = a(16 * (wv + 4 * r) + lr, kk);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int n = 0; n < NC; ++n) bv[j][n] = b(kk, 16 * n + lr);
+    }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+          acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][r], bv[j][n], acc[r][n], 0, 0, 0);
   }
 }
 
+template <int M, int N>
+__device__ __forceinline__ void tile_zero(Acc<M, N>& acc) {
+#pragma unroll
+  for (int r = 0; r < M / 64; ++r)
+#pragma unroll
+    for (int n = 0; n < N / 16; ++n) acc[r][n] = f4{0.f, 0.f, 0.f, 0.f};
+}
+
 template <int M, int N, typename FE>
-__device__ __forceinline__ void tile_emit(const float (&acc)[M / 16][N / 16], const FE& emit) {
-  const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
+__device__ __forceinline__ void tile_emit(const Acc<M, N>& acc, const FE& emit) {
+  const int wv = threadIdx.x >> 6, lr = threadIdx.x & 15, lk = (threadIdx.x >> 4) & 3;
 #pragma unroll
-  for (int i = 0; i < M / 16; ++i)
+  for (int r = 0; r < M / 64; ++r)
 #pragma unroll
-    for (int j = 0; j < N / 16; ++j) emit(tm + 16 * i, tn + 16 * j, acc[i][j]);
+    for (int n = 0; n < N / 16; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) emit(16 * (wv + 4 * r) + 4 * lk + i, 16 * n + lr, acc[r][n][i]);
 }
 
 template <int M, int N, int K, typename FA, typename FB, typename FE>
 __device__ __forceinline__ void tile_mm(const FA& a, const FB& b, const FE& emit) {
-  float acc[M / 16][N / 16];
-#pragma unroll
-  for (int i = 0; i < M / 16; ++i)
-#pragma unroll
-    for (int j = 0; j < N / 16; ++j) acc[i][j] = 0.f;
+  Acc<M, N> acc;
+  tile_zero<M, N>(acc);
   tile_acc<M, N, K>(a, b, acc);
   tile_emit<M, N>(acc, emit);
 }
@@ -135,7 +179,6 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
   __shared__ float Qt[D][CP];   // transported queries of the block, column i = query i
   __shared__ float Lam[D][CP];  // their adjoint; also the transport's output
   __shared__ float Kh[C][DP];   // khat rows of key block n
-  __shared__ float Vn[C][DP];   // value rows of key block n
   __shared__ float X[C][CP];    // [key j][query i]: p, then dS
   __shared__ float sD[C], sL[C], sCm[C], sCn[C], sRs[C];
 
@@ -189,9 +232,9 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
     for (int idx = tid; idx < C * D; idx += kT) {
       const int j = idx / D, e = idx % D;
       Kh[j][e] = khat[(hb + j0 + j) * D + e];
-      Vn[j][e] = load_f32(v + (hb + j0 + j) * D + e);
     }
     if (tid < C) sCn[tid] = FOX ? cum[hb + j0 + tid] : 0.f;
+    const T* vn = v + (hb + j0) * D;  // value rows of key block n (a whole block: n < m)
     __syncthreads();
 
     // p_ij
@@ -207,7 +250,8 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
     });
     __syncthreads();
     // dS = p (dO . v - D)
-    tile_mm<C, C, D>([&](int j, int e) { return Vn[j][e]; }, [&](int e, int i) { return dO_at(i, e); },
+    tile_mm<C, C, D>([&](int j, int e) { return load_f32(vn + static_cast<int64_t>(j) * D + e); },
+                     [&](int e, int i) { return dO_at(i, e); },
                      [&](int j, int i, float x) { X[j][i] = X[j][i] * (x - sD[i]); });
     __syncthreads();
     if (FOX) {
@@ -230,11 +274,8 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
       tile_mm<D, D, C>([&](int a, int i) { return Lam[a][i]; }, [&](int i, int b) { return Qt[b][i]; },
                        [&](int a, int b, float x) { unsafeAtomicAdd(dPacc + ((bh * Nb + n) * D + a) * D + b, x); });
     // Lam <- P_n^T Lam + scale Khat_n^T dS
-    float acc[D / 16][C / 16];
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-      for (int j = 0; j < C / 16; ++j) acc[i][j] = 0.f;
+    Acc<D, C> acc;
+    tile_zero<D, C>(acc);
     if (n >= 1) {
       const float* P = pT + (bh * Nb + n) * D * D;
       tile_acc<D, C, D>([&](int a, int b) { return P[a * D + b]; }, [&](int b, int i) { return Lam[b][i]; }, acc);
@@ -252,7 +293,7 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
 }
 
 template <typename T, int D, bool FOX>
-__global__ __launch_bounds__(kT) void bwd_block_kernel(
+__global__ __launch_bounds__(kTB) void bwd_block_kernel(
     int64_t L, int Nb, int64_t BH, float scale, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ w, const float* __restrict__ beta,
     const T* __restrict__ dO, const float* __restrict__ cum, const float* __restrict__ lse,
@@ -273,7 +314,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
   const int64_t hb = bh * L;
   const int64_t rb = (hb + t0) * D;  // first element of the block's rows
 
-  for (int idx = tid; idx < C * D; idx += kT) {
+  for (int idx = tid; idx < C * D; idx += kTB) {
     const int r = idx / D, e = idx % D;
     const bool ok = r < valid;
     Ws[r][e] = ok ? load_f32(w + rb + idx) : 0.f;
@@ -292,14 +333,15 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
     rs[tid] = 0.f;
   }
   const auto dO_at = [&](int r, int e) { return r < valid ? load_f32(dO + rb + static_cast<int64_t>(r) * D + e) : 0.f; };
-  tile_mm<C, C, D>([&](int c, int e) { return c < valid ? load_f32(v + rb + static_cast<int64_t>(c) * D + e) : 0.f; },
-                   [&](int e, int r) { return dO_at(r, e); },
-                   [&](int c, int r, float x) { PD[c][r] = c <= r ? x : 0.f; });  // p = 0 above the causal edge
+  if (wave < kT / 64)  // the tile products run on the first four waves
+    tile_mm<C, C, D>([&](int c, int e) { return c < valid ? load_f32(v + rb + static_cast<int64_t>(c) * D + e) : 0.f; },
+                     [&](int e, int r) { return dO_at(r, e); },
+                     [&](int c, int r, float x) { PD[c][r] = c <= r ? x : 0.f; });  // p = 0 above the causal edge
   __syncthreads();
 
   const bool haveP = n >= 1 && n <= Nb - 2;  // P_n takes part in some transport
   const int nchains = 2 * valid + (haveP ? D : 0);
-  for (int ch = wave; ch < nchains; ch += kT / 64) {
+  for (int ch = wave; ch < nchains; ch += kTB / 64) {
     float x[NE], xb[NE];
     float alph = 0.f;
     if (ch < valid) {
@@ -316,8 +358,8 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
           kx = fmaf(Ks[t][lane + 64 * u], x[u], kx);
           wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
         }
-        kx = wave_sum(kx);
-        wx = wave_sum(wx);
+        kx = wave_sum_dpp(kx);
+        wx = wave_sum_dpp(wx);
         const float sv = scale * kx + (FOX ? cr - sC[t] : 0.f);
         const float p = expf(sv - lr);
         const float ds = p * (PD[t][r] - dr);
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
         for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
       }
       if (FOX) {
-        const float rsv = wave_sum(lane < r ? dsreg : 0.f);
+        const float rsv = wave_sum_dpp(lane < r ? dsreg : 0.f);
         if (lane == 0) rs[r] = rsv;
         if (lane < r) atomicAdd(&cs[lane], dsreg);
       }
@@ -346,7 +388,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
           xn[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
           g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
         }
-        g = wave_sum(g);
+        g = wave_sum_dpp(g);
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
           atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xn[u]));
@@ -368,7 +410,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
         float wx = 0.f;
 #pragma unroll
         for (int u = 0; u < NE; ++u) wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
-        wx = wave_sum(wx);
+        wx = wave_sum_dpp(wx);
         if (lane == t) alph = wx;
         const float bw = sB[t] * wx;
 #pragma unroll
@@ -384,7 +426,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
           xp[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
           g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
         }
-        g = wave_sum(g);
+        g = wave_sum_dpp(g);
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
           atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xp[u]));
@@ -404,7 +446,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
         float wx = 0.f;
 #pragma unroll
         for (int u = 0; u < NE; ++u) wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
-        wx = wave_sum(wx);
+        wx = wave_sum_dpp(wx);
         if (lane == t) alph = wx;
         const float bw = sB[t] * wx;
 #pragma unroll
@@ -421,7 +463,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
           xn[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
           g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
         }
-        g = wave_sum(g);
+        g = wave_sum_dpp(g);
 #pragma unroll
         for (int u = 0; u < NE; ++u) {
           atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xn[u]));
@@ -434,7 +476,7 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
   }
   __syncthreads();
 
-  for (int idx = tid; idx < C * D; idx += kT) {
+  for (int idx = tid; idx < C * D; idx += kTB) {
     const int r = idx / D, e = idx % D;
     if (r < valid) {
       store_f32(dk + rb + idx, gK[r][e]);
@@ -446,9 +488,10 @@ __global__ __launch_bounds__(kT) void bwd_block_kernel(
     if (FOX) dc[hb + t0 + tid] = rsum[hb + t0 + tid] + rs[tid] - csum[hb + t0 + tid] - cs[tid];
   }
   // dv_c = cross-block part + sum_r p_cr dO_r
-  tile_mm<C, D, C>([&](int c, int r) { return PD[c][r]; }, dO_at, [&](int c, int e, float x) {
-    if (c < valid) store_f32(dv + rb + static_cast<int64_t>(c) * D + e, x + dVacc[rb + static_cast<int64_t>(c) * D + e]);
-  });
+  if (wave < kT / 64)
+    tile_mm<C, D, C>([&](int c, int r) { return PD[c][r]; }, dO_at, [&](int c, int e, float x) {
+      if (c < valid) store_f32(dv + rb + static_cast<int64_t>(c) * D + e, x + dVacc[rb + static_cast<int64_t>(c) * D + e]);
+    });
 }
 
 template <typename T, int D, bool FOX>
@@ -468,7 +511,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      a.ws.qhat, a.ws.khat, a.ws.pT, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum,
                      a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.csum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(kT), 0, stream, L, Nb, BH, a.scale,
+  hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(kTB), 0, stream, L, Nb, BH, a.scale,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), v, static_cast<const T*>(a.w), a.beta, dO,
                      a.ws.cum, a.lse, a.ws.Dv, a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum,
                      static_cast<T*>(a.dq), static_cast<T*>(a.dk), static_cast<T*>(a.dv), static_cast<T*>(a.dw),
