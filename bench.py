@@ -36,6 +36,16 @@ gates); the default, 2, is the headline workload above.  The roofline then
 describes that configuration's scan kernel, and its traffic is reported only
 for the default workload, whose counters are recorded.
 
+Last, the backward pass (`path_attn_bwd`: gradients of q, k, v, w, beta and,
+with gates, the log forget gates) runs on the forward workload with a seeded
+incoming gradient dO, 2 untimed and 5 timed launches, reported in `bwd` in
+TFLOP/s under F_bwd = sum over (b,h) of (5 d L^2 + 3 d^2 L^2 / 64): five
+L x L x d products over the causal half (logits recomputed, dV, dO V^T, dK,
+the adjoint of the queries) and three block transports (queries again, their
+adjoint, the transitions' gradient).  The in-block chains earn no FLOPs.  It
+computes in fp32 (matrix cores and vector ALUs), so its peak is MI355X's fp32
+157.3 TFLOP/s.  `--no-bwd` skips it.
+
 `--copy-ref` first runs a plain 1 GiB device copy, whose FETCH_SIZE and
 WRITE_SIZE counters calibrate those of the other kernels in a rocprofv3
 --pmc run of this script.
@@ -56,12 +66,17 @@ from dependent_position_encoding_fwd_amd.profsum import source_hash  # noqa: E40
 
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32, matrix and vector alike
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 COPY_REF_BYTES = 1 << 30
 
 
 def flops_path(B, H, L, d):
     return B * H * (2.0 * d * L * L + d * d * L * L / 64.0)
+
+
+def flops_path_bwd(B, H, L, d):
+    return B * H * (5.0 * d * L * L + 3.0 * d * d * L * L / 64.0)
 
 
 def decode_bytes(B, H, n, d, esize):
@@ -91,6 +106,7 @@ def main():
     ap.add_argument("--precision", default="auto", choices=["auto", "accurate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--fwd-config", type=int, default=2, choices=[2, 3, 4])
     args = ap.parse_args()
     if args.gpus != 1:
@@ -184,6 +200,8 @@ def main():
                 "kernel": f"scan{cf.d}_kernel (right-to-left scan, d={cf.d})", "flops_per_launch": F,
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
+    bwd = None if args.no_bwd else bwd_leg(pa, fargs, gates, cf, o, lse)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cf)
@@ -207,10 +225,40 @@ def main():
         "decode_fox": {"ms": round(fox_ms, 4), "GB_per_s": round(fox_gbs, 1), "bytes_model": fbytes,
                        "frac_hbm_peak": round(fox_gbs / PEAK_HBM_GBS, 4),
                        "what": "gated decode step, same cache, forget-gate prefix cache (fp32)"},
+        "bwd": bwd,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):
+    """Times path_attn_bwd on the forward workload: median of `steps` launches,
+    each bracketed by HIP events on the launch stream."""
+    import torch
+
+    q = fargs[0]
+    gen = torch.Generator().manual_seed(cf.seed + 4242)
+    do = torch.randn(tuple(q.shape), generator=gen).to(q.dtype).to(q.device)
+    nbytes = pa.bwd_workspace_bytes(cf.B, cf.H, cf.L, cf.d, pa.PATH_BF16 if q.dtype == torch.bfloat16 else pa.PATH_F32,
+                                    gates is not None)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(warmup + steps):
+        if k >= warmup:
+            evs[k - warmup][0].record()
+        pa.path_attn_bwd(*fargs, o, lse, do, gates, scale=cf.scale, workspace=ws)
+        if k >= warmup:
+            evs[k - warmup][1].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    F = flops_path_bwd(cf.B, cf.H, cf.L, cf.d)
+    tf = F / (ms * 1e-3) / 1e12
+    print(f"[bench] backward: {ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"ms": round(ms, 3), "TFLOP_per_s": round(tf, 3), "flops_model": F, "bound": "fp32",
+            "peak": PEAK_F32_TFLOPS, "frac_fp32_peak": round(tf / PEAK_F32_TFLOPS, 4),
+            "what": "path_attn_bwd on the forward workload (gradients of q, k, v, w, beta"
+                    f"{', log forget gates' if gates is not None else ''}), seeded dO, median of {steps}"}
 
 
 def cpu_baseline(cf, budget_s=10.0):

@@ -61,7 +61,16 @@ CLASSES = (
 )
 
 
+# the gated decode kernels (template flag true) form classes of their own
+GATED = (("decode_chunk_fox", "decode_chunk_kernel"), ("decode_merge_fox", "decode_merge_kernel"))
+BWD = ("bwd_pair_kernel", "bwd_block_kernel", "prepare_f32_kernel", "bwd_rowdot_kernel", "bwd_zero_kernel",
+       "bwd_suffix_kernel")
+
+
 def classify(name: str):
+    for cls, key in GATED:
+        if key in name and ", true>" in name:
+            return cls
     for cls, key in CLASSES:
         if key in name:
             return cls
@@ -127,7 +136,18 @@ def short(name: str) -> str:
     c = classify(name)
     return {"scan": "scan64_kernel (d=64 scan)", "prepare": "prepare_mfma_kernel<64>",
             "head_reduce": "head_reduce_kernel", "decode_chunk": "decode_chunk_kernel<bf16,64>",
-            "decode_merge": "decode_merge_kernel<bf16,64>", "copy": "__amd_rocclr_copyBuffer"}.get(c, name[:60])
+            "decode_merge": "decode_merge_kernel<bf16,64>", "copy": "__amd_rocclr_copyBuffer",
+            "decode_chunk_fox": "decode_chunk_kernel<bf16,64,gated>",
+            "decode_merge_fox": "decode_merge_kernel<bf16,64,gated>"}.get(c, _short_other(name))
+
+
+def _short_other(name: str) -> str:
+    """A backward kernel's name without its argument list, else the first 60 characters."""
+    for key in BWD:
+        if key in name:
+            head = name.split("(")[0].replace("void ", "").replace("path::", "")
+            return f"{head} (backward)"
+    return name[:60]
 
 
 def scan_algorithmic_bytes(B, H, L, d):
