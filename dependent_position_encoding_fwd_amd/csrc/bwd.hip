@@ -123,6 +123,54 @@ __device__ __forceinline__ void tile_mm(const FA& a, const FB& b, const FE& emit
   tile_emit<M, N>(acc, emit);
 }
 
+// A operands held in registers: af[r][4 c + j] = a(16 (wv + 4 r) + lr, 16 c + 4 lk + j),
+// the values lane (lk, lr) of wave wv feeds to the MFMAs of tile_acc.  Only the
+// wave's own rows are held, so a fragment can be fetched from global memory
+// one iteration ahead of its use.
+template <int M, int K>
+using Frag = float[M / 64][K / 4];
+
+template <int M, int K, typename FA>
+__device__ __forceinline__ void frag_load(const FA& a, Frag<M, K>& af) {
+  const int wv = threadIdx.x >> 6, lr = threadIdx.x & 15, lk = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int r = 0; r < M / 64; ++r)
+#pragma unroll
+    for (int c = 0; c < K / 16; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[r][4 * c + j] = a(16 * (wv + 4 * r) + lr, 16 * c + 4 * lk + j);
+}
+
+template <int M, int N, int K, typename FB>
+__device__ __forceinline__ void tile_acc_ra(const Frag<M, K>& af, const FB& b, Acc<M, N>& acc) {
+  constexpr int R = M / 64, NC = N / 16;
+  const int lr = threadIdx.x & 15, lk = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int c = 0; c < K / 16; ++c) {
+    float bv[4][NC];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int n = 0; n < NC; ++n) bv[j][n] = b(16 * c + 4 * lk + j, 16 * n + lr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+          acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[r][4 * c + j], bv[j][n], acc[r][n], 0, 0, 0);
+  }
+}
+
+// Sum over the 16 lanes of a row (every lane of the row gets it).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return x;
+}
+
 __device__ __forceinline__ float lane_of(float x, int t) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
 }
@@ -168,28 +216,28 @@ __global__ __launch_bounds__(kT) void bwd_suffix_kernel(int64_t L, const float* 
 }
 
 template <typename T, int D, bool FOX>
-__global__ __launch_bounds__(kT) void bwd_pair_kernel(
+__global__ __launch_bounds__(kT, D == 64 ? 2 : 1) void bwd_pair_kernel(
     int64_t L, int Nb, int64_t BH, float scale, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ qhat, const float* __restrict__ khat, const float* __restrict__ pT,
     const float* __restrict__ cum, const float* __restrict__ lse, const float* __restrict__ Dv,
     float* __restrict__ qt_scratch, float* __restrict__ dqh, float* __restrict__ rsum,
     float* __restrict__ dkh, float* __restrict__ dPacc, float* __restrict__ dVacc,
     float* __restrict__ csum) {
-  constexpr int C = kBlk, CP = C + 1, DP = D + 1;
-  __shared__ float Qt[D][CP];   // transported queries of the block, column i = query i
-  __shared__ float Lam[D][CP];  // their adjoint; also the transport's output
-  __shared__ float Kh[C][DP];   // khat rows of key block n
-  __shared__ float X[C][CP];    // [key j][query i]: p, then dS
+  constexpr int C = kBlk, CQ = C + 1, CA = C + 4, DP = D + 1, NQ = D * C / kT;
+  __shared__ float Qt[D][CQ];   // transported queries of the block, column i = query i
+  __shared__ float Lam[D][CA];  // their adjoint; in the first pass the transport's output
+  __shared__ float X[C][CA];    // [key j][query i]: p, then dS
+  __shared__ float dOs[C][DP];  // dO of the query block (rows past the end are 0)
   __shared__ float sD[C], sL[C], sCm[C], sCn[C], sRs[C];
 
   const int tid = threadIdx.x;
+  const int lr = tid & 15, lk = (tid >> 4) & 3, wv = tid >> 6;
   const int m = Nb - 1 - static_cast<int>(blockIdx.x / BH);  // longest query blocks first
   const int64_t bh = blockIdx.x % BH;
   const int64_t i0 = static_cast<int64_t>(m) * C;
   const int valid = static_cast<int>(L - i0 < C ? L - i0 : C);
   const int64_t hb = bh * L;
   const T* dOm = dO + (hb + i0) * D;
-  const auto dO_at = [&](int i, int e) { return i < valid ? load_f32(dOm + static_cast<int64_t>(i) * D + e) : 0.f; };
 
   if (tid < C) {
     const bool ok = tid < valid;
@@ -200,70 +248,125 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
   }
   for (int idx = tid; idx < C * D; idx += kT) {
     const int i = idx / D, e = idx % D;
-    Qt[e][i] = i < valid ? qhat[(hb + i0 + i) * D + e] : 0.f;
-    Lam[e][i] = 0.f;
+    const bool ok = i < valid;
+    Qt[e][i] = ok ? qhat[(hb + i0 + i) * D + e] : 0.f;
+    dOs[i][e] = ok ? load_f32(dOm + idx) : 0.f;
   }
-  __syncthreads();
 
   const int64_t npairs = static_cast<int64_t>(Nb) * (Nb - 1) / 2;
   float* scr = qt_scratch + (bh * npairs + static_cast<int64_t>(m) * (m - 1) / 2) * (D * C);
+  // P_n as stored: pT[(bh Nb + n) D^2 + b D + a] = P_n[a][b]
+  const auto Pblk = [&](int n) { return pT + (bh * Nb + n) * D * D; };
 
-  // Pass 1: Qt^(n) for n = m-1 .. 0.
+  // Pass 1: Qt^(n) for n = m-1 .. 0, each kept in the scratch buffer.
+  Frag<D, D> pf;  // P_n[a][b] for the wave's rows a
+  if (m >= 2) {
+    const float* P = Pblk(m - 1);
+    frag_load<D, D>([&](int a, int b) { return P[b * D + a]; }, pf);
+  }
+  __syncthreads();
   for (int n = m - 1; n >= 0; --n) {
     float* dst = scr + static_cast<int64_t>(n) * (D * C);
     for (int idx = tid; idx < D * C; idx += kT) dst[idx] = Qt[idx / C][idx % C];
     if (n == 0) break;
-    const float* P = pT + (bh * Nb + n) * D * D;  // P^T row-major: P[a][b] = P[b * D + a]
-    tile_mm<D, C, D>([&](int a, int b) { return P[b * D + a]; }, [&](int b, int i) { return Qt[b][i]; },
-                     [&](int a, int i, float x) { Lam[a][i] = x; });
+    Acc<D, C> acc;
+    tile_zero<D, C>(acc);
+    tile_acc_ra<D, C, D>(pf, [&](int b, int i) { return Qt[b][i]; }, acc);
+    if (n >= 2) {
+      const float* P = Pblk(n - 1);
+      frag_load<D, D>([&](int a, int b) { return P[b * D + a]; }, pf);
+    }
+    tile_emit<D, C>(acc, [&](int a, int i, float x) { Lam[a][i] = x; });
     __syncthreads();
     for (int idx = tid; idx < D * C; idx += kT) Qt[idx / C][idx % C] = Lam[idx / C][idx % C];
     __syncthreads();
   }
-  __syncthreads();
-  for (int idx = tid; idx < D * C; idx += kT) Lam[idx / C][idx % C] = 0.f;
 
-  // Pass 2: key blocks left to right.
+  // Pass 2: key blocks left to right.  Operands of block n + 1 are fetched into
+  // registers while block n is computed, each right after its last use:
+  //   qn  - Qt^(n) from the scratch buffer (written to LDS at the top);
+  //   kf  - khat_n rows (A of S = Khat Qt), vf - value rows (A of V dO^T);
+  //   ktf - scale * Khat_n^T and ptf - P_n^T (A operands of the adjoint update).
+  float qn[NQ];
+  Frag<C, D> kf, vf;
+  Frag<D, C> ktf;
+  Frag<D, D> ptf;
+  float cn = 0.f;
+  const auto loadA = [&](int n) {
+    const float* src = scr + static_cast<int64_t>(n) * (D * C);
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) qn[u] = src[tid + kT * u];
+    const float* kb = khat + (hb + static_cast<int64_t>(n) * C) * D;
+    const T* vb = v + (hb + static_cast<int64_t>(n) * C) * D;  // a whole block: n < m
+    frag_load<C, D>([&](int j, int e) { return kb[j * D + e]; }, kf);
+    frag_load<C, D>([&](int j, int e) { return load_f32(vb + j * D + e); }, vf);
+    if (FOX && tid < C) cn = cum[hb + static_cast<int64_t>(n) * C + tid];
+  };
+  const auto loadB = [&](int n) {
+    const float* kb = khat + (hb + static_cast<int64_t>(n) * C) * D;
+    frag_load<D, C>([&](int a, int j) { return scale * kb[j * D + a]; }, ktf);
+    if (n >= 1) {
+      const float* P = Pblk(n);
+      frag_load<D, D>([&](int a, int b) { return P[a * D + b]; }, ptf);
+    }
+  };
+  if (m >= 1) {
+    loadA(0);
+    loadB(0);
+  }
   for (int n = 0; n < m; ++n) {
     const int64_t j0 = static_cast<int64_t>(n) * C;
-    __syncthreads();
-    const float* src = scr + static_cast<int64_t>(n) * (D * C);
-    for (int idx = tid; idx < D * C; idx += kT) Qt[idx / C][idx % C] = src[idx];
-    for (int idx = tid; idx < C * D; idx += kT) {
-      const int j = idx / D, e = idx % D;
-      Kh[j][e] = khat[(hb + j0 + j) * D + e];
+    // Qt's readers of block n - 1 passed the barrier before the adjoint emit
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = tid + kT * u;
+      Qt[idx / C][idx % C] = qn[u];
     }
-    if (tid < C) sCn[tid] = FOX ? cum[hb + j0 + tid] : 0.f;
-    const T* vn = v + (hb + j0) * D;  // value rows of key block n (a whole block: n < m)
+    if (FOX && tid < C) sCn[tid] = cn;
     __syncthreads();
 
-    // p_ij
-    tile_mm<C, C, D>([&](int j, int e) { return Kh[j][e]; }, [&](int e, int i) { return Qt[e][i]; },
-                     [&](int j, int i, float s) {
-                       const float sv = scale * s + (FOX ? sCm[i] - sCn[j] : 0.f);
-                       X[j][i] = i < valid ? expf(sv - sL[i]) : 0.f;
-                     });
-    __syncthreads();
-    // dV_n += p dO_m
-    tile_mm<C, D, C>([&](int j, int i) { return X[j][i]; }, dO_at, [&](int j, int e, float x) {
-      unsafeAtomicAdd(dVacc + (hb + j0 + j) * D + e, x);
-    });
-    __syncthreads();
-    // dS = p (dO . v - D)
-    tile_mm<C, C, D>([&](int j, int e) { return load_f32(vn + static_cast<int64_t>(j) * D + e); },
-                     [&](int e, int i) { return dO_at(i, e); },
-                     [&](int j, int i, float x) { X[j][i] = X[j][i] * (x - sD[i]); });
-    __syncthreads();
+    // p_ij = exp(scale Khat_n Qt + c_i - c_j - lse_i), kept in registers
+    Acc<C, C> ps;
+    tile_zero<C, C>(ps);
+    tile_acc_ra<C, C, D>(kf, [&](int e, int i) { return Qt[e][i]; }, ps);
+    // dP_ij = dO_i . v_j
+    Acc<C, C> pd;
+    tile_zero<C, C>(pd);
+    tile_acc_ra<C, C, D>(vf, [&](int e, int i) { return dOs[i][e]; }, pd);
+    if (n + 1 < m) loadA(n + 1);
+#pragma unroll
+    for (int c = 0; c < C / 16; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = 16 * wv + 4 * lk + t, i = 16 * c + lr;
+        const float sv = scale * ps[0][c][t] + (FOX ? sCm[i] - sCn[j] : 0.f);
+        const float p = i < valid ? expf(sv - sL[i]) : 0.f;
+        ps[0][c][t] = p;
+        X[j][i] = p;
+      }
+    // dV_n += p dO_m (the wave's own rows of X: no barrier)
+    tile_mm<C, D, C>([&](int j, int i) { return X[j][i]; }, [&](int i, int e) { return dOs[i][e]; },
+                     [&](int j, int e, float x) { unsafeAtomicAdd(dVacc + (hb + j0 + j) * D + e, x); });
+    // dS = p (dO . v - D), over the same elements
+    float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C / 16; ++c) {
+      float colp = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = 16 * wv + 4 * lk + t, i = 16 * c + lr;
+        const float ds = ps[0][c][t] * (pd[0][c][t] - sD[i]);
+        X[j][i] = ds;
+        rowp[t] += ds;
+        colp += ds;
+      }
+      if (FOX) atomicAdd(&sRs[16 * c + lr], colp);
+    }
     if (FOX) {
-      if (tid < C) {
-        float r = 0.f;
-        for (int j = 0; j < C; ++j) r += X[j][tid];
-        sRs[tid] += r;
-      } else if (tid < 2 * C) {
-        const int j = tid - C;
-        float c = 0.f;
-        for (int i = 0; i < C; ++i) c += X[j][i];
-        unsafeAtomicAdd(csum + hb + j0 + j, c);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float r = row16_sum(rowp[t]);
+        if (lr == 0) unsafeAtomicAdd(csum + hb + j0 + 16 * wv + 4 * lk + t, r);
       }
     }
     // dKhat_n += scale dS Qt^T
@@ -273,21 +376,21 @@ __global__ __launch_bounds__(kT) void bwd_pair_kernel(
     if (n >= 1)
       tile_mm<D, D, C>([&](int a, int i) { return Lam[a][i]; }, [&](int i, int b) { return Qt[b][i]; },
                        [&](int a, int b, float x) { unsafeAtomicAdd(dPacc + ((bh * Nb + n) * D + a) * D + b, x); });
+    __syncthreads();  // every wave's dS rows are in X
     // Lam <- P_n^T Lam + scale Khat_n^T dS
     Acc<D, C> acc;
     tile_zero<D, C>(acc);
-    if (n >= 1) {
-      const float* P = pT + (bh * Nb + n) * D * D;
-      tile_acc<D, C, D>([&](int a, int b) { return P[a * D + b]; }, [&](int b, int i) { return Lam[b][i]; }, acc);
-    }
-    tile_acc<D, C, C>([&](int a, int j) { return scale * Kh[j][a]; }, [&](int j, int i) { return X[j][i]; }, acc);
+    if (n >= 1) tile_acc_ra<D, C, D>(ptf, [&](int b, int i) { return Lam[b][i]; }, acc);
+    tile_acc_ra<D, C, C>(ktf, [&](int j, int i) { return X[j][i]; }, acc);
+    if (n + 1 < m) loadB(n + 1);
     __syncthreads();
     tile_emit<D, C>(acc, [&](int a, int i, float x) { Lam[a][i] = x; });
   }
   __syncthreads();
   for (int idx = tid; idx < C * D; idx += kT) {
     const int i = idx / D, e = idx % D;
-    if (i < valid) dqh[(hb + i0 + i) * D + e] = Lam[e][i];
+    // the first block has no earlier key blocks: nothing reaches its qhat
+    if (i < valid) dqh[(hb + i0 + i) * D + e] = m > 0 ? Lam[e][i] : 0.f;
   }
   if (FOX && tid < valid) rsum[hb + i0 + tid] = sRs[tid];
 }
