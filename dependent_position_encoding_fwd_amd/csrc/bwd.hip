@@ -33,28 +33,16 @@
 
 #include "common.h"
 #include "launch.h"
-#include "mfma_util.h"
 
 namespace path {
 namespace {
 
 constexpr int kT = 256;    // threads per workgroup: 4 waves
-constexpr int kTB = 1024;  // in-block kernel: 16 waves, one Householder chain per wave at a time
 
-// Sum over the 64 lanes of a wave, the same bits in every lane: pairwise sums
-// within quads, 8-lane halves and 16-lane rows by DPP lane permutations, then
-// across the four rows by the permlane swaps.  Each step adds two partial sums
-// held by two lanes, and addition is commutative, so all lanes agree.
+// DPP lane move within a row of 16 lanes (row_mask and bank_mask full).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x);  // row_half_mirror: the other quad of the 8-lane half
-  x += dpp_mov<0x140>(x);  // row_mirror: the other half of the 16-lane row
-  return mfma::grp_sum(x);
 }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -162,7 +150,9 @@ __device__ __forceinline__ void tile_acc_ra(const Frag<M, K>& af, const FB& b, A
   }
 }
 
-// Sum over the 16 lanes of a row (every lane of the row gets it).
+// Sum over the 16 lanes of a row, the same bits in every lane of the row:
+// pairwise sums within quads, 8-lane halves and the row (each step adds two
+// partial sums held by two lanes, and addition is commutative).
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_mov<0xB1>(x);
   x += dpp_mov<0x4E>(x);
@@ -171,9 +161,6 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float lane_of(float x, int t) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
-}
 
 }  // namespace
 
@@ -395,8 +382,27 @@ __global__ __launch_bounds__(kT, D == 64 ? 2 : 1) void bwd_pair_kernel(
   if (FOX && tid < valid) rsum[hb + i0 + tid] = sRs[tid];
 }
 
+// Reduce-scatter over the four 16-lane rows of a wave: each lane passes four
+// values v[0..3] and receives, in row s, the sum over the four rows of v[s]
+// (lane l16 of every row contributing its own v).  Two permlane32 swaps pair
+// rows s and s ^ 2 (rows 0-1 keep v0, v1; rows 2-3 keep v2, v3), one
+// permlane16 swap pairs rows s and s ^ 1.  Every lane takes part.
+__device__ __forceinline__ float rows_reduce_scatter(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float r02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows 0-1: v0, rows 2-3: v2
+  const float r13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows 0-1: v1, rows 2-3: v3
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(r02), __float_as_uint(r13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Waves of the in-block kernel: 16 at d = 64, 8 at d = 128 (LDS holds the
+// block's w, k rows and their gradient sums, 32 or 64 KB each).
+template <int D>
+constexpr int block_waves() { return D == 64 ? 16 : 8; }
+
 template <typename T, int D, bool FOX>
-__global__ __launch_bounds__(kTB) void bwd_block_kernel(
+__global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
     int64_t L, int Nb, int64_t BH, float scale, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ w, const float* __restrict__ beta,
     const T* __restrict__ dO, const float* __restrict__ cum, const float* __restrict__ lse,
@@ -404,12 +410,15 @@ __global__ __launch_bounds__(kTB) void bwd_block_kernel(
     const float* __restrict__ dPacc, const float* __restrict__ dVacc, const float* __restrict__ rsum,
     const float* __restrict__ csum, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
     T* __restrict__ dw, float* __restrict__ dbeta, float* __restrict__ dc) {
-  constexpr int C = kBlk, CP = C + 1, NE = D / 64;
+  constexpr int C = kBlk, CP = C + 1, NW = block_waves<D>(), NT = 64 * NW;
+  constexpr int NU = D / 16;  // elements of a chain's vector per lane
   __shared__ float Ws[C][D], Ks[C][D], gW[C][D], gK[C][D];
-  __shared__ float PD[C][CP];  // [key c][query r]: dO_r . v_c, then p
+  __shared__ float PD[C][CP];     // [key c][query r]: dO_r . v_c, then p
+  __shared__ float sA[NW][4][C];  // a_t = w_t . x^(t+1) of each chain a wave runs
   __shared__ float sB[C], sL[C], sD[C], sC[C], gB[C], cs[C], rs[C];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int sub = (tid >> 4) & 3, l16 = tid & 15;  // chain of the wave, lane in the chain
   const int n = static_cast<int>(blockIdx.x / BH);
   const int64_t bh = blockIdx.x % BH;
   const int64_t t0 = static_cast<int64_t>(n) * C;
@@ -417,7 +426,7 @@ __global__ __launch_bounds__(kTB) void bwd_block_kernel(
   const int64_t hb = bh * L;
   const int64_t rb = (hb + t0) * D;  // first element of the block's rows
 
-  for (int idx = tid; idx < C * D; idx += kTB) {
+  for (int idx = tid; idx < C * D; idx += NT) {
     const int r = idx / D, e = idx % D;
     const bool ok = r < valid;
     Ws[r][e] = ok ? load_f32(w + rb + idx) : 0.f;
@@ -442,144 +451,184 @@ __global__ __launch_bounds__(kTB) void bwd_block_kernel(
                      [&](int c, int r, float x) { PD[c][r] = c <= r ? x : 0.f; });  // p = 0 above the causal edge
   __syncthreads();
 
-  const bool haveP = n >= 1 && n <= Nb - 2;  // P_n takes part in some transport
-  const int nchains = 2 * valid + (haveP ? D : 0);
-  for (int ch = wave; ch < nchains; ch += kTB / 64) {
-    float x[NE], xb[NE];
-    float alph = 0.f;
-    if (ch < valid) {
-      // Query chain r: x = H_{t+1}...H_r q_r meets key t, then takes H_t.
-      const int r = ch;
-      const float lr = sL[r], dr = sD[r], cr = sC[r];
-      float Ereg = 0.f, dsreg = 0.f;
+  // Householder chains, four per wave: chain `sub` owns lanes 16 sub .. 16 sub + 15,
+  // each holding elements e = l16 + 16 u of the chain's vector.  Dot products are
+  // sums over the chain's 16 lanes (DPP moves within a row, so chains never mix).
+  // A chain's earlier state is rebuilt from the next as x^(t+1) = x^(t) + beta_t a_t w_t.
+  // Chains run in groups of four consecutive indices: query chains r, key chains c,
+  // then (when P_n takes part in a transport) columns of P_n.  The four chains'
+  // contributions to a gradient row are summed across the wave's rows before the
+  // LDS atomic (the atomic rate, not the arithmetic, bounds this kernel).
+  const auto dotw = [&](int t, const float (&x)[NU]) {
+    float s = 0.f;
 #pragma unroll
-      for (int u = 0; u < NE; ++u) x[u] = load_f32(q + rb + static_cast<int64_t>(r) * D + lane + 64 * u);
-      for (int t = r; t >= 0; --t) {
-        float kx = 0.f, wx = 0.f;
+    for (int u = 0; u < NU; ++u) s = fmaf(Ws[t][l16 + 16 * u], x[u], s);
+    return row16_sum(s);
+  };
+  float* myA = sA[wave][sub];
+  const int ngq = (valid + 3) / 4;
+  const bool haveP = n >= 1 && n <= Nb - 2;
+  const int ngroups = 2 * ngq + (haveP ? D / 4 : 0);
+  for (int grp = wave; grp < ngroups; grp += NW) {
+    float x[NU], xb[NU];
+    if (grp < ngq) {
+      // Query chain r: x^(t+1) = H_{t+1}...H_r q_r meets key t, then takes H_t.
+      const int r = 4 * grp + sub;
+      const bool live = r < valid;
+      const int tmax = min(4 * grp + 3, valid - 1);
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          kx = fmaf(Ks[t][lane + 64 * u], x[u], kx);
-          wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
-        }
-        kx = wave_sum_dpp(kx);
-        wx = wave_sum_dpp(wx);
+      for (int u = 0; u < NU; ++u)
+        x[u] = live ? load_f32(q + rb + static_cast<int64_t>(r) * D + l16 + 16 * u) : 0.f;
+      for (int t = tmax; t >= 0; --t) {
+        const bool act = live && t <= r;
+        const float a = dotw(t, x);
+        if (act && l16 == 0) myA[t] = a;
+        const float ba = act ? sB[t] * a : 0.f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) x[u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) xb[u] = live ? dqh[rb + static_cast<int64_t>(r) * D + l16 + 16 * u] : 0.f;
+      const float lr = live ? sL[r] : 0.f, dr = live ? sD[r] : 0.f, cr = live ? sC[r] : 0.f;
+      float rsum_r = 0.f;
+      for (int t = 0; t <= tmax; ++t) {
+        const bool act = live && t <= r;
+        const float bt = sB[t];
+        const float a = act ? myA[t] : 0.f;
+        float xn[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) xn[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[u]);
+        float kx = 0.f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) kx = fmaf(Ks[t][l16 + 16 * u], xn[u], kx);
+        kx = row16_sum(kx);
+        const float g = dotw(t, xb);
         const float sv = scale * kx + (FOX ? cr - sC[t] : 0.f);
-        const float p = expf(sv - lr);
-        const float ds = p * (PD[t][r] - dr);
-        if (lane == t) {
-          Ereg = scale * ds;
-          dsreg = ds;
-          alph = wx;
+        const float p = act ? expf(sv - lr) : 0.f;
+        const float ds = act ? p * (PD[t][r] - dr) : 0.f;
+        const float E = scale * ds;
+        const float bta = act ? bt : 0.f;  // an idle chain adds exact zeros
+        float cw[NU], ck[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          cw[u] = -bta * (a * xb[u] + g * xn[u]);
+          ck[u] = E * xn[u];
         }
-        if (lane == 0) PD[t][r] = p;
-        const float bw = sB[t] * wx;
 #pragma unroll
-        for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
-      }
-      if (FOX) {
-        const float rsv = wave_sum_dpp(lane < r ? dsreg : 0.f);
-        if (lane == 0) rs[r] = rsv;
-        if (lane < r) atomicAdd(&cs[lane], dsreg);
-      }
-#pragma unroll
-      for (int u = 0; u < NE; ++u) xb[u] = dqh[rb + static_cast<int64_t>(r) * D + lane + 64 * u];
-      for (int t = 0; t <= r; ++t) {
-        const float a = lane_of(alph, t), E = lane_of(Ereg, t), bt = sB[t];
-        float xn[NE], g = 0.f;
-#pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          xn[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
-          g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
+        for (int h = 0; h < NU / 4; ++h) {
+          const int e = l16 + 16 * (4 * h + sub);
+          atomicAdd(&gW[t][e], rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
+          atomicAdd(&gK[t][e], rows_reduce_scatter(ck[4 * h], ck[4 * h + 1], ck[4 * h + 2], ck[4 * h + 3]));
         }
-        g = wave_sum_dpp(g);
+        if (act) {
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xn[u]));
-          xb[u] = fmaf(-bt * g, Ws[t][lane + 64 * u], xb[u]);
-          xb[u] = fmaf(E, Ks[t][lane + 64 * u], xb[u]);
-          atomicAdd(&gK[t][lane + 64 * u], E * xn[u]);
-          x[u] = xn[u];
+          for (int u = 0; u < NU; ++u) {
+            xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
+            xb[u] = fmaf(E, Ks[t][l16 + 16 * u], xb[u]);
+            x[u] = xn[u];
+          }
+          if (l16 == 0) {
+            PD[t][r] = p;
+            atomicAdd(&gB[t], -g * a);
+            if (FOX && t < r) {
+              rsum_r += ds;
+              atomicAdd(&cs[t], ds);
+            }
+          }
         }
-        if (lane == 0) atomicAdd(&gB[t], -g * a);
       }
+      if (live) {
 #pragma unroll
-      for (int u = 0; u < NE; ++u) store_f32(dq + rb + static_cast<int64_t>(r) * D + lane + 64 * u, xb[u]);
-    } else if (ch < 2 * valid) {
+        for (int u = 0; u < NU; ++u) store_f32(dq + rb + static_cast<int64_t>(r) * D + l16 + 16 * u, xb[u]);
+        if (FOX && l16 == 0) rs[r] = rsum_r;
+      }
+    } else if (grp < 2 * ngq) {
       // Key chain c: y = H_t...H_{c+1} k_c, from k_c up to khat_c.
-      const int c = ch - valid;
+      const int c = 4 * (grp - ngq) + sub;
+      const bool live = c < valid;
+      const int tmin = 4 * (grp - ngq) + 1;  // smallest c + 1 of the group
 #pragma unroll
-      for (int u = 0; u < NE; ++u) x[u] = Ks[c][lane + 64 * u];
-      for (int t = c + 1; t < valid; ++t) {
-        float wx = 0.f;
+      for (int u = 0; u < NU; ++u) x[u] = live ? Ks[c][l16 + 16 * u] : 0.f;
+      for (int t = tmin; t < valid; ++t) {
+        const bool act = live && t > c;
+        const float a = dotw(t, x);
+        if (act && l16 == 0) myA[t] = a;
+        const float ba = act ? sB[t] * a : 0.f;
 #pragma unroll
-        for (int u = 0; u < NE; ++u) wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
-        wx = wave_sum_dpp(wx);
-        if (lane == t) alph = wx;
-        const float bw = sB[t] * wx;
-#pragma unroll
-        for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
+        for (int u = 0; u < NU; ++u) x[u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[u]);
       }
 #pragma unroll
-      for (int u = 0; u < NE; ++u) xb[u] = dkh[rb + static_cast<int64_t>(c) * D + lane + 64 * u];
-      for (int t = valid - 1; t > c; --t) {
-        const float a = lane_of(alph, t), bt = sB[t];
-        float xp[NE], g = 0.f;
+      for (int u = 0; u < NU; ++u) xb[u] = live ? dkh[rb + static_cast<int64_t>(c) * D + l16 + 16 * u] : 0.f;
+      for (int t = valid - 1; t >= tmin; --t) {
+        const bool act = live && t > c;
+        const float bt = sB[t];
+        const float a = act ? myA[t] : 0.f;
+        float xp[NU];
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          xp[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
-          g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
-        }
-        g = wave_sum_dpp(g);
+        for (int u = 0; u < NU; ++u) xp[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[u]);
+        const float g = dotw(t, xb);
+        const float bta = act ? bt : 0.f;
+        float cw[NU];
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xp[u]));
-          xb[u] = fmaf(-bt * g, Ws[t][lane + 64 * u], xb[u]);
-          x[u] = xp[u];
+        for (int u = 0; u < NU; ++u) cw[u] = -bta * (a * xb[u] + g * xp[u]);
+#pragma unroll
+        for (int h = 0; h < NU / 4; ++h)
+          atomicAdd(&gW[t][l16 + 16 * (4 * h + sub)],
+                    rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
+        if (act) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
+            x[u] = xp[u];
+          }
+          if (l16 == 0) atomicAdd(&gB[t], -g * a);
         }
-        if (lane == 0) atomicAdd(&gB[t], -g * a);
       }
+      if (live) {
 #pragma unroll
-      for (int u = 0; u < NE; ++u) atomicAdd(&gK[c][lane + 64 * u], xb[u]);
+        for (int u = 0; u < NU; ++u) atomicAdd(&gK[c][l16 + 16 * u], xb[u]);
+      }
     } else {
       // Column col of P_n = H_0 ... H_63: x = H_t...H_63 e_col.
-      const int col = ch - 2 * valid;
+      const int col = 4 * (grp - 2 * ngq) + sub;
 #pragma unroll
-      for (int u = 0; u < NE; ++u) x[u] = (lane + 64 * u == col) ? 1.f : 0.f;
+      for (int u = 0; u < NU; ++u) x[u] = (l16 + 16 * u == col) ? 1.f : 0.f;
       for (int t = valid - 1; t >= 0; --t) {
-        float wx = 0.f;
+        const float a = dotw(t, x);
+        if (l16 == 0) myA[t] = a;
+        const float ba = sB[t] * a;
 #pragma unroll
-        for (int u = 0; u < NE; ++u) wx = fmaf(Ws[t][lane + 64 * u], x[u], wx);
-        wx = wave_sum_dpp(wx);
-        if (lane == t) alph = wx;
-        const float bw = sB[t] * wx;
-#pragma unroll
-        for (int u = 0; u < NE; ++u) x[u] = fmaf(-bw, Ws[t][lane + 64 * u], x[u]);
+        for (int u = 0; u < NU; ++u) x[u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[u]);
       }
       const float* gP = dPacc + (bh * Nb + n) * D * D;
 #pragma unroll
-      for (int u = 0; u < NE; ++u) xb[u] = gP[(lane + 64 * u) * D + col];
+      for (int u = 0; u < NU; ++u) xb[u] = gP[(l16 + 16 * u) * D + col];
       for (int t = 0; t < valid; ++t) {
-        const float a = lane_of(alph, t), bt = sB[t];
-        float xn[NE], g = 0.f;
+        const float bt = sB[t];
+        const float a = myA[t];
+        float xn[NU];
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          xn[u] = fmaf(bt * a, Ws[t][lane + 64 * u], x[u]);
-          g = fmaf(Ws[t][lane + 64 * u], xb[u], g);
-        }
-        g = wave_sum_dpp(g);
+        for (int u = 0; u < NU; ++u) xn[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[u]);
+        const float g = dotw(t, xb);
+        float cw[NU];
 #pragma unroll
-        for (int u = 0; u < NE; ++u) {
-          atomicAdd(&gW[t][lane + 64 * u], -bt * (a * xb[u] + g * xn[u]));
-          xb[u] = fmaf(-bt * g, Ws[t][lane + 64 * u], xb[u]);
+        for (int u = 0; u < NU; ++u) cw[u] = -bt * (a * xb[u] + g * xn[u]);
+#pragma unroll
+        for (int h = 0; h < NU / 4; ++h)
+          atomicAdd(&gW[t][l16 + 16 * (4 * h + sub)],
+                    rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
           x[u] = xn[u];
         }
-        if (lane == 0) atomicAdd(&gB[t], -g * a);
+        if (l16 == 0) atomicAdd(&gB[t], -g * a);
       }
     }
   }
   __syncthreads();
 
-  for (int idx = tid; idx < C * D; idx += kTB) {
+  for (int idx = tid; idx < C * D; idx += NT) {
     const int r = idx / D, e = idx % D;
     if (r < valid) {
       store_f32(dk + rb + idx, gK[r][e]);
@@ -614,7 +663,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      a.ws.qhat, a.ws.khat, a.ws.pT, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum,
                      a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.csum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(kTB), 0, stream, L, Nb, BH, a.scale,
+  hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(64 * block_waves<D>()), 0, stream, L, Nb, BH, a.scale,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), v, static_cast<const T*>(a.w), a.beta, dO,
                      a.ws.cum, a.lse, a.ws.Dv, a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum,
                      static_cast<T*>(a.dq), static_cast<T*>(a.dk), static_cast<T*>(a.dv), static_cast<T*>(a.dw),
