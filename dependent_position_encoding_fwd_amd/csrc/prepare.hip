@@ -1,4 +1,5 @@
-// Per-block UT transform for PaTH attention, fp32 on the vector ALUs.
+// Per-block UT transform for PaTH attention in fp32: products on the fp32
+// matrix cores, the triangular solve on the vector ALUs.
 //
 // [PaTH Attention summary (gist.science 2505.16381), §3 "Representação de
 // Transformação UT"]: the product of the transitions of one block,
@@ -17,6 +18,7 @@
 // transition is also produced in row-update form, pT = P^T = I - W^T T^{-T} W.
 #include "common.h"
 #include "launch.h"
+#include "tile_f32.h"
 
 namespace path {
 
@@ -49,14 +51,10 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
   if (tid < C) bs[tid] = tid < valid ? beta[bh * L + t0 + tid] : 0.f;
   __syncthreads();
 
-  for (int idx = tid; idx < C * C; idx += 256) {
-    int r = idx / C, t = idx % C;
-    float g = 0.f;
-    if (t > r) {
-      for (int e = 0; e < D; ++e) g += Ws[r][e] * Ws[t][e];
-    }
-    Gs[r][t] = g;
-  }
+  using f32tile::tile_mm;
+  // G = strict_upper(W W^T)
+  tile_mm<C, C, D>([&](int r, int e) { return Ws[r][e]; }, [&](int e, int t) { return Ws[t][e]; },
+                   [&](int r, int t, float x) { Gs[r][t] = t > r ? x : 0.f; });
   __syncthreads();
 
   // Back substitution, one column of X = T^{-1} per thread, last row first:
@@ -86,30 +84,20 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       Xs[r][e] = r < valid ? load_f32(k + base + (t0 + r) * D + e) : 0.f;
     }
     __syncthreads();
-    // Z[c][s] = (w_s . k_c) for s > c
-    for (int idx = tid; idx < C * C; idx += 256) {
-      int c = idx / C, s = idx % C;
-      float z = 0.f;
-      if (s > c) {
-        for (int e = 0; e < D; ++e) z += Ws[s][e] * Xs[c][e];
-      }
-      Gs[c][s] = z;
-    }
+    // Z[c][s] = (w_s . k_c) for s > c, else 0
+    tile_mm<C, C, D>([&](int c, int e) { return Xs[c][e]; }, [&](int e, int s2) { return Ws[s2][e]; },
+                     [&](int c, int s2, float x) { Gs[c][s2] = s2 > c ? x : 0.f; });
     __syncthreads();
-    // Y[c][a] = sum_s Z[c][s] T^{-1}[s][a]   (= (T^{-T} z_c)_a)
-    for (int idx = tid; idx < C * C; idx += 256) {
-      int c = idx / C, a = idx % C;
-      float y = 0.f;
-      for (int s = c + 1; s <= a; ++s) y += Gs[c][s] * Ts[s][a];
-      Ys[c][a] = y;
-    }
+    // Y = Z T^{-1}: Y[c][a] = sum_{c<s<=a} Z[c][s] T^{-1}[s][a] (= (T^{-T} z_c)_a; both factors
+    // vanish outside that range, so the full product is the same sum)
+    tile_mm<C, C, C>([&](int c, int s2) { return Gs[c][s2]; }, [&](int s2, int a) { return Ts[s2][a]; },
+                     [&](int c, int a, float x) { Ys[c][a] = x; });
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) {
-      int c = idx / D, e = idx % D;
-      float x = Xs[c][e];
-      for (int a = c + 1; a < C; ++a) x -= Ys[c][a] * Ws[a][e];
-      if (c < valid) khat_out[base + (t0 + c) * D + e] = x;
-    }
+    // khat = K - Y W  (Y[c][a] = 0 for a <= c)
+    tile_mm<C, D, C>([&](int c, int a) { return Ys[c][a]; }, [&](int a, int e) { return Ws[a][e]; },
+                     [&](int c, int e, float x) {
+                       if (c < valid) khat_out[base + (t0 + c) * D + e] = Xs[c][e] - x;
+                     });
     __syncthreads();
   }
 
@@ -119,52 +107,31 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
       Xs[r][e] = r < valid ? load_f32(q + base + (t0 + r) * D + e) : 0.f;
     }
     __syncthreads();
-    // A[r][t] = (w_t . q_r) for t <= r
-    for (int idx = tid; idx < C * C; idx += 256) {
-      int r = idx / C, t = idx % C;
-      float z = 0.f;
-      if (t <= r) {
-        for (int e = 0; e < D; ++e) z += Ws[t][e] * Xs[r][e];
-      }
-      Gs[r][t] = z;
-    }
+    // A[r][t] = (w_t . q_r) for t <= r, else 0
+    tile_mm<C, C, D>([&](int r, int e) { return Xs[r][e]; }, [&](int e, int t) { return Ws[t][e]; },
+                     [&](int r, int t, float x) { Gs[r][t] = t <= r ? x : 0.f; });
     __syncthreads();
-    // Y[r][a] = sum_t T^{-1}[a][t] A[r][t]   (= (T^{-1} a_r)_a, nonzero for a <= r)
-    for (int idx = tid; idx < C * C; idx += 256) {
-      int r = idx / C, a = idx % C;
-      float y = 0.f;
-      for (int t = a; t <= r; ++t) y += Ts[a][t] * Gs[r][t];
-      Ys[r][a] = y;
-    }
+    // Y = A T^{-T}: Y[r][a] = sum_{a<=t<=r} T^{-1}[a][t] A[r][t] (= (T^{-1} a_r)_a, 0 for a > r)
+    tile_mm<C, C, C>([&](int r, int t) { return Gs[r][t]; }, [&](int t, int a) { return Ts[a][t]; },
+                     [&](int r, int a, float x) { Ys[r][a] = x; });
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) {
-      int r = idx / D, e = idx % D;
-      float x = 0.f;
-      if (r < valid) {
-        x = Xs[r][e];
-        for (int a = 0; a <= r; ++a) x -= Ys[r][a] * Ws[a][e];
-        qhat_out[base + (t0 + r) * D + e] = x;
-      }
-    }
+    // qhat = Q - Y W
+    tile_mm<C, D, C>([&](int r, int a) { return Ys[r][a]; }, [&](int a, int e) { return Ws[a][e]; },
+                     [&](int r, int e, float x) {
+                       if (r < valid) qhat_out[base + (t0 + r) * D + e] = Xs[r][e] - x;
+                     });
     __syncthreads();
   }
 
   if (pT_out) {
-    // F[s][e] = sum_t T^{-1}[t][s] W[t][e]   (F = T^{-T} W)
-    for (int idx = tid; idx < C * D; idx += 256) {
-      int s = idx / D, e = idx % D;
-      float f = 0.f;
-      for (int t = 0; t <= s; ++t) f += Ts[t][s] * Ws[t][e];
-      Xs[s][e] = f;
-    }
+    // F = T^{-T} W: F[s][e] = sum_{t<=s} T^{-1}[t][s] W[t][e]
+    tile_mm<C, D, C>([&](int s2, int t) { return Ts[t][s2]; }, [&](int t, int e) { return Ws[t][e]; },
+                     [&](int s2, int e, float x) { Xs[s2][e] = x; });
     __syncthreads();
+    // P^T = I - W^T F
     float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
-    for (int idx = tid; idx < D * D; idx += 256) {
-      int a = idx / D, b = idx % D;
-      float x = (a == b) ? 1.f : 0.f;
-      for (int s = 0; s < C; ++s) x -= Ws[s][a] * Xs[s][b];
-      dst[idx] = x;
-    }
+    tile_mm<D, D, C>([&](int a, int s2) { return Ws[s2][a]; }, [&](int s2, int b) { return Xs[s2][b]; },
+                     [&](int a, int b, float x) { dst[a * D + b] = (a == b ? 1.f : 0.f) - x; });
   }
 }
 
