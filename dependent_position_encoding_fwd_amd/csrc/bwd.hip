@@ -338,6 +338,15 @@ __device__ __forceinline__ float rows_reduce_scatter(float v0, float v1, float v
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// the same bits in every lane.
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Waves of the in-block kernel: 16 at d = 64, 8 at d = 128 (LDS holds the
 // block's w, k rows and their gradient sums, 32 or 64 KB each).
 template <int D>
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
   __shared__ float sA[NW][4][C];  // a_t = w_t . x^(t+1) of each chain a wave runs
   __shared__ float sB[C], sL[C], sD[C], sC[C], gB[C], cs[C], rs[C];
 
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = (tid >> 4) & 3, l16 = tid & 15;  // chain of the wave, lane in the chain
   const int n = static_cast<int>(blockIdx.x / BH);
   const int64_t bh = blockIdx.x % BH;
@@ -462,6 +471,13 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
           atomicAdd(&gW[t][e], rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
           atomicAdd(&gK[t][e], rows_reduce_scatter(ck[4 * h], ck[4 * h + 1], ck[4 * h + 2], ck[4 * h + 3]));
         }
+        // dbeta_t and gate terms of the four chains (idle chains give 0), one lane adds
+        const float gbt = rows_sum(-g * a);
+        const float cst = FOX ? rows_sum(t < r ? ds : 0.f) : 0.f;
+        if (lane == 0) {
+          atomicAdd(&gB[t], gbt);
+          if (FOX) atomicAdd(&cs[t], cst);
+        }
         if (act) {
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
@@ -471,11 +487,7 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
           }
           if (l16 == 0) {
             PD[t][r] = p;
-            atomicAdd(&gB[t], -g * a);
-            if (FOX && t < r) {
-              rsum_r += ds;
-              atomicAdd(&cs[t], ds);
-            }
+            if (FOX && t < r) rsum_r += ds;
           }
         }
       }
@@ -517,13 +529,14 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
         for (int h = 0; h < NU / 4; ++h)
           atomicAdd(&gW[t][l16 + 16 * (4 * h + sub)],
                     rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
+        const float gbt = rows_sum(-g * a);
+        if (lane == 0) atomicAdd(&gB[t], gbt);
         if (act) {
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
             xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
             x[u] = xp[u];
           }
-          if (l16 == 0) atomicAdd(&gB[t], -g * a);
         }
       }
       if (live) {
@@ -564,7 +577,8 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
           xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
           x[u] = xn[u];
         }
-        if (l16 == 0) atomicAdd(&gB[t], -g * a);
+        const float gbt = rows_sum(-g * a);
+        if (lane == 0) atomicAdd(&gB[t], gbt);
       }
     }
   }
