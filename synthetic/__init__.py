@@ -185,3 +185,15 @@ def config_inputs(cfg_id: int, heads=None, small=None):
     if isinstance(c, DecodeConfig):
         return decode_inputs(c.B, c.H, c.d, c.cache_len, c.capacity, c.dtype, c.seed, heads)
     return fwd_inputs(c.B, c.H, c.L, c.d, c.dtype, c.seed, c.near2_frac, c.fox, heads)
+
+
+def project_inputs(B: int, L: int, Dm: int, H: int, d: int, seed: int):
+    """Inputs of the projection prologue: tokens x [B, L, Dm] ~ N(0,1) (bf16),
+    per-head maps Ww [H, d, Dm] and gate vectors u [H, Dm] ~ N(0, 1/Dm) (bf16,
+    so projections are O(1)), biases b [H] ~ N(0,1) (fp32).  Random weights
+    stand in for trained ones."""
+    x = torch.randn(B, L, Dm, generator=_gen("proj", seed, "x")).to(torch.bfloat16)
+    Ww = (torch.randn(H, d, Dm, generator=_gen("proj", seed, "Ww")) / Dm ** 0.5).to(torch.bfloat16)
+    u = (torch.randn(H, Dm, generator=_gen("proj", seed, "u")) / Dm ** 0.5).to(torch.bfloat16)
+    bias = torch.randn(H, generator=_gen("proj", seed, "b"))
+    return {"x": x, "Ww": Ww, "u": u, "b": bias}
