@@ -29,7 +29,7 @@ STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UN
 EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
            "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
            "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox",
-           "path_bwd_workspace_bytes", "path_attn_bwd"]
+           "path_bwd_workspace_bytes", "path_attn_bwd", "path_project"]
 
 _lib = None
 _I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.path_bwd_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _INT, _INT]
         L.path_attn_bwd.restype = _INT
         L.path_attn_bwd.argtypes = [_I64, _I64, _I64, _I64, _INT, _F] + [_VP] * 15 + [_VP, _SZ, _VP]
+        L.path_project.restype = _INT
+        L.path_project.argtypes = [_I64] * 5 + [_VP] * 4 + [_F] + [_VP, _VP, _VP]
         L.path_decode_step_fox.restype = _INT
         L.path_decode_step_fox.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 9 + [_I64, _I64] +
                                            [_VP, _VP, _VP, _SZ, _VP])
@@ -279,3 +281,25 @@ def _decode(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, ca
         st = lib().path_decode_step(*head, _ptr(k_cache), _ptr(v_cache), *tail)
         _raise(st, "path_decode_step")
     return o, lse
+
+
+def path_project(x, Ww, u, bias, beta_max=None, out=None):
+    """Projection prologue: x [B,L,Dm], Ww [H,d,Dm], u [H,Dm] (bf16), bias [H] fp32.
+
+    Returns (w [B,H,L,d] bf16, unit length per (b,h,l); beta [B,H,L] fp32 =
+    2 sigmoid(u_h . x + bias_h), capped at beta_max when given)."""
+    B, L, Dm = x.shape
+    H, d, _ = Ww.shape
+    _check(x, "x", torch.bfloat16, (B, L, Dm))
+    _check(Ww, "Ww", torch.bfloat16, (H, d, Dm))
+    _check(u, "u", torch.bfloat16, (H, Dm))
+    _check(bias, "bias", torch.float32, (H,))
+    w, beta = out if out is not None else (torch.empty((B, H, L, d), dtype=torch.bfloat16, device=x.device),
+                                           torch.empty((B, H, L), dtype=torch.float32, device=x.device))
+    _check(w, "w", torch.bfloat16, (B, H, L, d))
+    _check(beta, "beta", torch.float32, (B, H, L))
+    bm = 0.0 if beta_max is None else float(beta_max)
+    st = lib().path_project(B, L, Dm, H, d, _ptr(x), _ptr(Ww), _ptr(u), _ptr(bias), bm, _ptr(w), _ptr(beta),
+                            _stream(x))
+    _raise(st, "path_project")
+    return w, beta

@@ -415,3 +415,22 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
 }
 
 }  // extern "C"
+
+extern "C" int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d, const void* x,
+                            const void* Ww, const void* u, const float* bias, float beta_max, void* w,
+                            float* beta, hipStream_t stream) {
+  if (B < 1 || L < 1 || H < 1 || Dm < 1 || Dm % 64 != 0) return PATH_ERR_SHAPE;
+  int st = check_d(d);
+  if (st) return st;
+  int64_t T, xe, we, oe, tiles_cols;
+  if (!mul_ok(B, L, &T) || !mul_ok(T, Dm, &xe) || !mul_ok(H * d, Dm, &we) || !mul_ok(T * H, d, &oe))
+    return PATH_ERR_SHAPE;
+  // 128-token tiles times column groups (one per head, plus the beta groups) must fit a 32-bit grid
+  const int64_t ncol = H + (H + d - 1) / d;
+  if (!mul_ok(((T + 127) / 128 + 7) / 8 * 8, ncol, &tiles_cols) || tiles_cols > (int64_t(1) << 31) - 1)
+    return PATH_ERR_SHAPE;
+  if (!x || !Ww || !u || !bias || !w || !beta) return PATH_ERR_NULL;
+  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(x) || misaligned(Ww) || misaligned(u)) return PATH_ERR_UNSUPPORTED;
+  return hip_status(path::launch_project(B, L, Dm, H, d, x, Ww, u, bias, beta_max, w, beta, stream));
+}

@@ -60,6 +60,12 @@ hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const vo
                          int64_t cache_len, int64_t capacity, void* o, float* lse, float* partials,
                          hipStream_t stream);
 
+// Projection prologue (bf16 matrix cores): w [B,H,L,d] bf16 and beta [B,H,L]
+// fp32 from tokens x [B,L,Dm], Ww [H,d,Dm], u [H,Dm] (bf16) and bias [H].
+hipError_t launch_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d, const void* x, const void* Ww,
+                          const void* u, const float* bias, float beta_max, void* w_out, float* beta_out,
+                          hipStream_t stream);
+
 // Backward pass (fp32 arithmetic).  Workspace regions, all fp32; the run from
 // zero_begin over zero_count floats (dkh, dP, dV, csum) is cleared first.
 struct BwdWs {

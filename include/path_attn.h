@@ -204,6 +204,30 @@ int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale
                          int64_t cache_len, int64_t capacity, void* o, float* lse, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * path_project - projection prologue [PaTH summary §2 "Mecanismo Central":
+ * w_s and beta_s are functions of the input token x_s, beta_s =
+ * 2 sigmoid(u^T x_s + b); §6 "Limitações" mentions clipping beta]: for every
+ * token s = (b, l) and head h,
+ *   w[b,h,l,:] = W_h x_s / max(|W_h x_s|_2, 1e-12)       (bf16, rounded to nearest even)
+ *   beta[b,h,l] = min(2 sigmoid(u_h . x_s + bias_h), beta_max)   (fp32; no bound
+ *                 when beta_max <= 0 or NaN)
+ * computed on the bf16 matrix cores with fp32 accumulation.  The pages give no
+ * formula for w_s; a per-head linear map scaled to unit length is the reading
+ * taken (the attention workloads use unit-norm w).
+ * Inputs (bf16): x [B,L,Dm] tokens; Ww [H,d,Dm] (row e of head h maps x to
+ *   component e); u [H,Dm]; bias [H] fp32.  Dm must be a positive multiple of
+ *   64 and d is 64 or 128.  x, Ww and u must be 16-byte aligned.
+ * Outputs (caller-allocated): w [B,H,L,d] bf16, beta [B,H,L] fp32, in the
+ *   layouts path_attn_fwd takes.
+ * Errors: PATH_ERR_NULL for a null pointer, PATH_ERR_SHAPE for non-positive
+ *   or overflowing sizes or Dm not a multiple of 64, PATH_ERR_UNSUPPORTED for
+ *   another d or misaligned inputs; nothing is launched then.  PATH_ERR_HIP if
+ *   the launch fails.  Asynchronous on `stream`; allocates nothing.
+ */
+int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d, const void* x, const void* Ww,
+                 const void* u, const float* bias, float beta_max, void* w, float* beta, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -115,3 +115,20 @@ def test_python_binding_rejects_cpu_tensors():
     b = torch.zeros(1, 1, 64)
     with pytest.raises(ValueError):
         pa.path_attn_fwd(x, x, x, x, b)
+
+
+def _proj(B=1, L=128, Dm=256, H=2, d=64, ptr=FAKE, x=None, bias=FAKE):
+    xp = ptr if x is None else x
+    return pa.lib().path_project(B, L, Dm, H, d, xp, ptr, ptr, bias, 0.0, ptr, ptr, None)
+
+
+def test_project_validation():
+    assert _proj(d=96) == UNSUP
+    assert _proj(Dm=96) == SHAPE          # not a multiple of 64
+    assert _proj(Dm=0) == SHAPE
+    assert _proj(B=0) == SHAPE
+    assert _proj(H=0) == SHAPE
+    assert _proj(B=1 << 40, L=1 << 20) == SHAPE
+    assert _proj(ptr=None) == NULL
+    assert _proj(bias=None) == NULL
+    assert _proj(x=ctypes.c_void_p(0x1008)) == UNSUP   # not 16-byte aligned
