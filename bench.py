@@ -46,6 +46,11 @@ adjoint, the transitions' gradient).  The in-block chains earn no FLOPs.  It
 computes in fp32 (matrix cores and vector ALUs), so its peak is MI355X's fp32
 157.3 TFLOP/s.  `--no-bwd` skips it.
 
+The projection prologue (`path_project`: w and beta of every head from the
+tokens, model width Dm = H d) runs on the forward workload's tokens and is
+reported in `project`: TFLOP/s on 2 T Dm (H d + H) FLOP (T = B L tokens)
+against the 2.5 PFLOP/s bf16 matrix peak, median of 50 launches after 20.
+
 `--copy-ref` first runs a plain 1 GiB device copy, whose FETCH_SIZE and
 WRITE_SIZE counters calibrate those of the other kernels in a rocprofv3
 --pmc run of this script.
@@ -201,6 +206,7 @@ def main():
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
     bwd = None if args.no_bwd else bwd_leg(pa, fargs, gates, cf, o, lse)
+    proj = project_leg(pa, cf)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,6 +232,7 @@ def main():
                        "frac_hbm_peak": round(fox_gbs / PEAK_HBM_GBS, 4),
                        "what": "gated decode step, same cache, forget-gate prefix cache (fp32)"},
         "bwd": bwd,
+        "project": proj,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -259,6 +266,33 @@ def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):
             "peak": PEAK_F32_TFLOPS, "frac_fp32_peak": round(tf / PEAK_F32_TFLOPS, 4),
             "what": "path_attn_bwd on the forward workload (gradients of q, k, v, w, beta"
                     f"{', log forget gates' if gates is not None else ''}), seeded dO, median of {steps}"}
+
+
+def project_leg(pa, cf, warmup=20, steps=50):
+    """Times path_project on the forward workload's tokens (Dm = H d)."""
+    import torch
+
+    import synthetic
+
+    Dm = cf.H * cf.d
+    x = {n: t.to("cuda:0") for n, t in synthetic.project_inputs(cf.B, cf.L, Dm, cf.H, cf.d, cf.seed).items()}
+    out = (torch.empty((cf.B, cf.H, cf.L, cf.d), dtype=torch.bfloat16, device="cuda:0"),
+           torch.empty((cf.B, cf.H, cf.L), dtype=torch.float32, device="cuda:0"))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(warmup + steps):
+        if k >= warmup:
+            evs[k - warmup][0].record()
+        pa.path_project(x["x"], x["Ww"], x["u"], x["b"], out=out)
+        if k >= warmup:
+            evs[k - warmup][1].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    T = cf.B * cf.L
+    F = 2.0 * T * Dm * (cf.H * cf.d + cf.H)
+    tf = F / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP_per_s": round(tf, 3), "flops_model": F, "bound": "mfma",
+            "peak": PEAK_MFMA_F16_TFLOPS, "frac_bf16_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4),
+            "what": f"path_project, T={T} tokens, Dm={Dm}, H={cf.H}, d={cf.d} (bf16 in, w bf16 + beta fp32 out)"}
 
 
 def cpu_baseline(cf, budget_s=10.0):
