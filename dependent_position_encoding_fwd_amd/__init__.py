@@ -29,7 +29,7 @@ STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UN
 EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
            "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
            "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox",
-           "path_bwd_workspace_bytes", "path_attn_bwd", "path_project"]
+           "path_bwd_workspace_bytes", "path_attn_bwd", "path_project", "path_decode_step_paged"]
 
 _lib = None
 _I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.path_bwd_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _INT, _INT]
         L.path_attn_bwd.restype = _INT
         L.path_attn_bwd.argtypes = [_I64, _I64, _I64, _I64, _INT, _F] + [_VP] * 15 + [_VP, _SZ, _VP]
+        L.path_decode_step_paged.restype = _INT
+        L.path_decode_step_paged.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 7 + [_I64, _I64, _VP, _I64, _VP,
+                                             _I64, _VP, _VP, _VP, _SZ, _VP])
         L.path_project.restype = _INT
         L.path_project.argtypes = [_I64] * 5 + [_VP] * 4 + [_F] + [_VP, _VP, _VP]
         L.path_decode_step_fox.restype = _INT
@@ -303,3 +306,34 @@ def path_project(x, Ww, u, bias, beta_max=None, out=None):
                             _stream(x))
     _raise(st, "path_project")
     return w, beta
+
+
+def path_decode_step_paged(q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, page_table, cache_lens, max_cache_len,
+                           scale=1.0, workspace=None):
+    """Decode step over a paged cache.  q_t, k_t, v_t, w_t [B,H,d]; beta_t [B,H] fp32;
+    k_pages, v_pages [num_pages,H,page_size,d] (updated in place, new token appended);
+    page_table [B,max_pages] int32 and cache_lens [B] int32 on the device; max_cache_len
+    (host int) bounds every cache_lens[b].  Returns (o [B,H,d], lse [B,H] fp32)."""
+    B, H, d = q_t.shape
+    num_pages, _, page_size, _ = k_pages.shape
+    max_pages = page_table.shape[1]
+    dt = q_t.dtype
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _check(t, name, dt, (B, H, d))
+    _check(beta_t, "beta_t", torch.float32, (B, H))
+    _check(k_pages, "k_pages", dt, (num_pages, H, page_size, d))
+    _check(v_pages, "v_pages", dt, (num_pages, H, page_size, d))
+    _check(page_table, "page_table", torch.int32, (B, max_pages))
+    _check(cache_lens, "cache_lens", torch.int32, (B,))
+    o = torch.empty_like(q_t)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_t.device)
+    nbytes = decode_workspace_bytes(B, H, d, max_cache_len)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q_t.device)
+    st = lib().path_decode_step_paged(B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+                                      _ptr(w_t), _ptr(beta_t), _ptr(k_pages), _ptr(v_pages), int(num_pages),
+                                      int(page_size), _ptr(page_table), int(max_pages), _ptr(cache_lens),
+                                      int(max_cache_len), _ptr(o), _ptr(lse), _ptr(workspace),
+                                      int(workspace.numel()), _stream(q_t))
+    _raise(st, "path_decode_step_paged")
+    return o, lse

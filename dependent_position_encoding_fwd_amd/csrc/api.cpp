@@ -434,3 +434,32 @@ extern "C" int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t
   if (misaligned(x) || misaligned(Ww) || misaligned(u)) return PATH_ERR_UNSUPPORTED;
   return hip_status(path::launch_project(B, L, Dm, H, d, x, Ww, u, bias, beta_max, w, beta, stream));
 }
+
+extern "C" int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                                      const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                                      void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
+                                      const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
+                                      int64_t max_cache_len, void* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_d(d))) return st;
+  if (B < 1 || H < 1 || page_size < 1 || num_pages < 1 || max_pages < 1 || max_cache_len < 0)
+    return PATH_ERR_SHAPE;
+  int64_t BH, n, tbl, slots;
+  if (!mul_ok(B, H, &BH) || !mul_ok(num_pages, H, &n) || !mul_ok(n, page_size, &n) || !mul_ok(n, d, &n) ||
+      !mul_ok(B, max_pages, &tbl) || !mul_ok(max_pages, page_size, &slots))
+    return PATH_ERR_SHAPE;
+  // page ids are int32 and rows are (page * H + h) * page_size + slot
+  if (num_pages > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
+  if (max_cache_len >= slots) return PATH_ERR_CAPACITY;
+  if (BH * path::decode_num_chunks(max_cache_len) > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
+  if (!q_t || !k_t || !v_t || !w_t || !beta_t || !k_pages || !v_pages || !page_table || !cache_lens || !o || !lse)
+    return PATH_ERR_NULL;
+  const size_t need = path_decode_workspace_bytes(B, H, d, max_cache_len);
+  if (!workspace || need == 0 || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return PATH_ERR_WORKSPACE;
+  return hip_status(path::launch_decode_paged(dtype, B, H, d, scale, q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages,
+                                              num_pages, page_size, page_table, max_pages, cache_lens,
+                                              max_cache_len, o, lse, static_cast<float*>(workspace), stream));
+}

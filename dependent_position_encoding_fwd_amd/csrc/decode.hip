@@ -14,6 +14,11 @@
 // The chunk loop is software-pipelined: the loads of the next group of 8 rows
 // per lane are issued before the current group is updated and attended to.
 //
+// Paged variant (FlashDecoding/paged-KV layout, which the same bullet says the
+// method stays compatible with): the same kernels with another row map, pages
+// [num_pages, H, page, d] addressed through a per-sequence page table, and one
+// cache length per sequence read on the device.
+//
 // Gated variant (FOX) [same summary, §2 "Extensões: PaTH-FoX"]: the logit of
 // cached key j gains the forget-gate sum over j < s <= t, kept as a difference
 // of running prefixes c_t - c_j.  The prefix of every cached key sits in an
@@ -86,10 +91,36 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Where cached key j of head bh lives, in rows of d elements.
+// ContigRows: caches [B*H, capacity, d], one length for every head.
+struct ContigRows {
+  int64_t capacity, len;
+  __device__ int64_t length(int64_t) const { return len; }
+  __device__ int64_t row(int64_t bh, int64_t j) const { return bh * capacity + j; }
+  __device__ static constexpr bool ok(int64_t) { return true; }
+};
+// PagedRows: pages [num_pages, H, page, d]; sequence b's logical page lp is
+// table[b * max_pages + lp] and its length lens[b].  A slot whose page is not
+// mapped (outside the table or the pool) is reported as row -1 and skipped.
+struct PagedRows {
+  const int32_t* table;
+  const int32_t* lens;
+  int64_t H, max_pages, num_pages, page;
+  __device__ int64_t length(int64_t bh) const { return lens[bh / H]; }
+  __device__ int64_t row(int64_t bh, int64_t j) const {
+    const int64_t lp = j / page;
+    if (j < 0 || lp >= max_pages) return -1;
+    const int64_t pg = table[(bh / H) * max_pages + lp];
+    if (pg < 0 || pg >= num_pages) return -1;
+    return (pg * H + bh % H) * page + (j - lp * page);
+  }
+  __device__ static bool ok(int64_t r) { return r >= 0; }
+};
+
 // partial layout per (bh, chunk): [m, l, acc[D]]
-template <typename T, int D, bool FOX>
+template <typename T, int D, bool FOX, class Rows>
 __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
-    int64_t cache_len, int64_t capacity, int nchunks, float scale, const T* __restrict__ q_t,
+    Rows rows, int nchunks, float scale, const T* __restrict__ q_t,
     const T* __restrict__ w_t, const float* __restrict__ beta_t, const float* __restrict__ log_f_t,
     T* __restrict__ k_cache, const T* __restrict__ v_cache, const float* __restrict__ cum_cache,
     float* __restrict__ partials) {
@@ -121,15 +152,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   const float bt = beta_t[bh];
   constexpr float kLog2e = 1.4426950408889634f;
   const float scale2 = scale * kLog2e;  // logits in log2 units
-  const float* cbase = FOX ? cum_cache + bh * capacity : nullptr;
-  // c_t of the new query; this kernel only runs with cache_len >= 1.
-  const float ct = FOX ? cbase[cache_len - 1] + log_f_t[bh] : 0.f;
+  const int64_t len = rows.length(bh);
+  const float* cbase = nullptr;
+  float ct = 0.f;
+  if constexpr (FOX) {
+    // c_t of the new query; the gated kernel only runs with cache_len >= 1
+    cbase = cum_cache + bh * rows.capacity;
+    ct = cbase[len - 1] + log_f_t[bh];
+  }
 
   const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
-  const int64_t j1 = j0 + kDecChunk < cache_len ? j0 + kDecChunk : cache_len;
-  typename V::raw* kbase = reinterpret_cast<typename V::raw*>(k_cache + bh * capacity * D);
-  const typename V::raw* vbase =
-      reinterpret_cast<const typename V::raw*>(v_cache + bh * capacity * D);
+  const int64_t j1 = j0 + kDecChunk < len ? j0 + kDecChunk : len;
+  typename V::raw* kraw = reinterpret_cast<typename V::raw*>(k_cache);
+  const typename V::raw* vraw = reinterpret_cast<const typename V::raw*>(v_cache);
 
   float mrun = -INFINITY, lrun = 0.f;
   float acc[EPV];
@@ -147,9 +182,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       vr[u] = kr[u];
       cr[u] = 0.f;
       if (j < j1) {
-        kr[u] = __builtin_nontemporal_load(&kbase[j * LPK + sub]);
-        vr[u] = __builtin_nontemporal_load(&vbase[j * LPK + sub]);
-        if constexpr (FOX) cr[u] = cbase[j];
+        const int64_t rw = rows.row(bh, j);
+        if (rows.ok(rw)) {
+          kr[u] = __builtin_nontemporal_load(&kraw[rw * LPK + sub]);
+          vr[u] = __builtin_nontemporal_load(&vraw[rw * LPK + sub]);
+          if constexpr (FOX) cr[u] = cbase[j];
+        }
       }
     }
   };
@@ -169,7 +207,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
-      const bool live = j < j1;
+      const int64_t rw = j < j1 ? rows.row(bh, j) : -1;
+      const bool live = j < j1 && rows.ok(rw);
       float kf[EPV];
       V::unpack(kc[u], kf);
       float a = 0.f, b = 0.f;
@@ -183,7 +222,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       const float ba = bt * a;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) kf[e] -= ba * wv[e];
-      if (live) __builtin_nontemporal_store(V::pack(kf), &kbase[j * LPK + sub]);
+      if (live) __builtin_nontemporal_store(V::pack(kf), &kraw[rw * LPK + sub]);
       float su = scale2 * (b - ba * wq);
       if constexpr (FOX) su += kLog2e * (ct - cc[u]);
       sv[u] = live ? su : -INFINITY;
@@ -261,9 +300,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 
 // One wave per (b,h): merge chunk partials with the new key, write o and lse,
 // then append k_t, v_t (and, gated, c_t) at slot cache_len.
-template <typename T, int D, bool FOX>
+template <typename T, int D, bool FOX, class Rows>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
-    int64_t cache_len, int64_t capacity, int nchunks, float scale, const T* __restrict__ q_t,
+    Rows rows, int nchunks, float scale, const T* __restrict__ q_t,
     const T* __restrict__ k_t, const T* __restrict__ v_t, const float* __restrict__ log_f_t,
     T* __restrict__ k_cache, T* __restrict__ v_cache, float* __restrict__ cum_cache,
     const float* __restrict__ partials, T* __restrict__ o, float* __restrict__ lse) {
@@ -299,18 +338,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     for (int t = 0; t < PER; ++t) oo[t] += a * p[2 + lane + 64 * t];
   }
   const float inv = 1.f / ll;
+  const int64_t len = rows.length(bh);
+  const int64_t slot = rows.row(bh, len);  // the new key's row (skipped when not mapped)
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
     const int e = lane + 64 * t;
     store_f32(o + bh * D + e, oo[t] * inv);
-    k_cache[(bh * capacity + cache_len) * D + e] = k_t[bh * D + e];
-    v_cache[(bh * capacity + cache_len) * D + e] = v_t[bh * D + e];
+    if (rows.ok(slot)) {
+      k_cache[slot * D + e] = k_t[bh * D + e];
+      v_cache[slot * D + e] = v_t[bh * D + e];
+    }
   }
   if (lane == 0) {
     lse[bh] = (mm + __log2f(ll)) * 0.69314718055994531f;
     if constexpr (FOX) {
-      float* cbase = cum_cache + bh * capacity;
-      cbase[cache_len] = (cache_len > 0 ? cbase[cache_len - 1] : 0.f) + log_f_t[bh];
+      float* cbase = cum_cache + bh * rows.capacity;
+      cbase[len] = (len > 0 ? cbase[len - 1] : 0.f) + log_f_t[bh];
     }
   }
 }
@@ -324,16 +367,17 @@ static hipError_t launch_dec_t(int64_t BH, float scale, const void* q_t, const v
                                int64_t cache_len, int64_t capacity, void* o, float* lse,
                                float* partials, hipStream_t stream) {
   const int nchunks = static_cast<int>(decode_num_chunks(cache_len));
+  const ContigRows rows{capacity, cache_len};
   if (nchunks > 0) {
-    hipLaunchKernelGGL((decode_chunk_kernel<T, D, FOX>), dim3(static_cast<unsigned>(BH * nchunks)),
-                       dim3(kDecThreads), 0, stream, cache_len, capacity, nchunks, scale,
+    hipLaunchKernelGGL((decode_chunk_kernel<T, D, FOX, ContigRows>), dim3(static_cast<unsigned>(BH * nchunks)),
+                       dim3(kDecThreads), 0, stream, rows, nchunks, scale,
                        static_cast<const T*>(q_t), static_cast<const T*>(w_t), beta_t, log_f_t,
                        static_cast<T*>(k_cache), static_cast<const T*>(v_cache), cum_cache, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, FOX>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
-                     stream, cache_len, capacity, nchunks, scale, static_cast<const T*>(q_t),
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, FOX, ContigRows>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+                     stream, rows, nchunks, scale, static_cast<const T*>(q_t),
                      static_cast<const T*>(k_t), static_cast<const T*>(v_t), log_f_t,
                      static_cast<T*>(k_cache), static_cast<T*>(v_cache), cum_cache, partials,
                      static_cast<T*>(o), lse);
@@ -364,6 +408,42 @@ hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const vo
                                 v_cache, cum_cache, cache_len, capacity, o, lse, partials, stream);
   return launch_dec_fox<false>(dtype, BH, d, scale, q_t, k_t, v_t, w_t, beta_t, nullptr, k_cache, v_cache,
                                nullptr, cache_len, capacity, o, lse, partials, stream);
+}
+
+template <typename T, int D>
+static hipError_t launch_dec_paged_t(int64_t BH, float scale, const void* q_t, const void* k_t, const void* v_t,
+                                     const void* w_t, const float* beta_t, void* k_pages, void* v_pages,
+                                     const PagedRows& rows, int64_t max_len, void* o, float* lse, float* partials,
+                                     hipStream_t stream) {
+  const int nchunks = static_cast<int>(decode_num_chunks(max_len));
+  if (nchunks > 0) {
+    hipLaunchKernelGGL((decode_chunk_kernel<T, D, false, PagedRows>), dim3(static_cast<unsigned>(BH * nchunks)),
+                       dim3(kDecThreads), 0, stream, rows, nchunks, scale, static_cast<const T*>(q_t),
+                       static_cast<const T*>(w_t), beta_t, nullptr, static_cast<T*>(k_pages),
+                       static_cast<const T*>(v_pages), nullptr, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, false, PagedRows>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+                     stream, rows, nchunks, scale, static_cast<const T*>(q_t), static_cast<const T*>(k_t),
+                     static_cast<const T*>(v_t), nullptr, static_cast<T*>(k_pages), static_cast<T*>(v_pages),
+                     nullptr, partials, static_cast<T*>(o), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_paged(int dtype, int64_t B, int64_t H, int64_t d, float scale, const void* q_t,
+                               const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                               void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
+                               const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
+                               int64_t max_len, void* o, float* lse, float* partials, hipStream_t stream) {
+  const PagedRows rows{page_table, cache_lens, H, max_pages, num_pages, page_size};
+  const int64_t BH = B * H;
+  auto go = [&](auto launch) {
+    return launch(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, rows, max_len, o, lse, partials,
+                  stream);
+  };
+  if (dtype == 0) return d == 64 ? go(launch_dec_paged_t<float, 64>) : go(launch_dec_paged_t<float, 128>);
+  return d == 64 ? go(launch_dec_paged_t<bf16_t, 64>) : go(launch_dec_paged_t<bf16_t, 128>);
 }
 
 }  // namespace path

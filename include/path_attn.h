@@ -205,6 +205,38 @@ int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * path_decode_step_paged - path_decode_step over a paged key/value cache
+ * with one length per sequence [PaTH summary §3 "Inferência": the in-place
+ * update k_j <- H_t k_j keeps the method compatible with FlashDecoding-style
+ * caches].  For every sequence b and head h, with len = cache_lens[b]:
+ *   keys j < len are updated in place, k_j <- H_t k_j (stored in dtype),
+ *   o, lse = single-query softmax attention over those len keys and k_t
+ *            (exactly path_decode_step with cache_len = len),
+ *   then k_t, v_t are written at logical slot len.
+ * Cache layout: k_pages, v_pages [num_pages, H, page_size, d] (dtype); slot j
+ *   of sequence b is row j % page_size of page page_table[b * max_pages +
+ *   j / page_size], head h.  page_table [B, max_pages] and cache_lens [B] are
+ *   int32 in device memory, owned by the caller; pages no sequence maps are
+ *   not touched.
+ * max_cache_len (host): an upper bound on every cache_lens[b]; it sizes the
+ *   launch (keys beyond it are not visited) and must be < max_pages * page_size.
+ * The device-side values are not checked on the host: a slot whose page id
+ *   is outside [0, num_pages) or whose logical page is >= max_pages is skipped
+ *   (never read or written), so a bad table gives wrong results, not an
+ *   out-of-bounds access.
+ * Workspace: path_decode_workspace_bytes(B, H, d, max_cache_len).
+ * Errors: as path_decode_step (PATH_ERR_CAPACITY when max_cache_len >=
+ *   max_pages * page_size); PATH_ERR_SHAPE for page_size < 1, num_pages < 1 or
+ *   max_pages < 1.
+ */
+int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                           const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                           void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
+                           const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
+                           int64_t max_cache_len, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * path_project - projection prologue [PaTH summary §2 "Mecanismo Central":
  * w_s and beta_s are functions of the input token x_s, beta_s =
  * 2 sigmoid(u^T x_s + b); §6 "Limitações" mentions clipping beta]: for every

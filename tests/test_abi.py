@@ -132,3 +132,23 @@ def test_project_validation():
     assert _proj(ptr=None) == NULL
     assert _proj(bias=None) == NULL
     assert _proj(x=ctypes.c_void_p(0x1008)) == UNSUP   # not 16-byte aligned
+
+
+def _paged(B=2, H=2, d=64, dtype=1, npages=8, page=16, mp=4, maxlen=20, ptr=FAKE, ws=FAKE, wsb=1 << 30,
+           table=FAKE):
+    return pa.lib().path_decode_step_paged(B, H, d, dtype, 1.0, ptr, ptr, ptr, ptr, ptr, ptr, ptr, npages, page,
+                                           table, mp, ptr, maxlen, ptr, ptr, ws, wsb, None)
+
+
+def test_decode_paged_validation():
+    assert _paged(d=80) == UNSUP
+    assert _paged(dtype=4) == UNSUP
+    assert _paged(page=0) == SHAPE
+    assert _paged(npages=0) == SHAPE
+    assert _paged(mp=0) == SHAPE
+    assert _paged(maxlen=-1) == SHAPE
+    assert _paged(maxlen=64) == CAP         # 4 pages of 16 slots hold keys 0..63, the new key needs slot maxlen
+    assert _paged(ptr=None) == NULL
+    assert _paged(table=None) == NULL
+    assert _paged(ws=None) == WS
+    assert _paged(wsb=8) == WS
