@@ -46,6 +46,11 @@ adjoint, the transitions' gradient).  The in-block chains earn no FLOPs.  It
 computes in fp32 (matrix cores and vector ALUs), so its peak is MI355X's fp32
 157.3 TFLOP/s.  `--no-bwd` skips it.
 
+The paged decode step (`path_decode_step_paged`) runs on the same caches
+scattered into 256-slot pages in a seeded random page order, every sequence at
+length 8192, and is reported in `decode_paged` on the decode's bytes (the page
+table adds 132 bytes per head), median of 50 launches after 20.
+
 The projection prologue (`path_project`: w and beta of every head from the
 tokens, model width Dm = H d) runs on the forward workload's tokens and is
 reported in `project`: TFLOP/s on 2 T Dm (H d + H) FLOP (T = B L tokens)
@@ -205,6 +210,7 @@ def main():
                 "kernel": f"scan{cf.d}_kernel (right-to-left scan, d={cf.d})", "flops_per_launch": F,
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
+    paged = paged_leg(pa, xd, cd, dbytes)
     bwd = None if args.no_bwd else bwd_leg(pa, fargs, gates, cf, o, lse)
     proj = project_leg(pa, cf)
 
@@ -231,6 +237,7 @@ def main():
         "decode_fox": {"ms": round(fox_ms, 4), "GB_per_s": round(fox_gbs, 1), "bytes_model": fbytes,
                        "frac_hbm_peak": round(fox_gbs / PEAK_HBM_GBS, 4),
                        "what": "gated decode step, same cache, forget-gate prefix cache (fp32)"},
+        "decode_paged": paged,
         "bwd": bwd,
         "project": proj,
         "roofline": roofline,
@@ -266,6 +273,45 @@ def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):
             "peak": PEAK_F32_TFLOPS, "frac_fp32_peak": round(tf / PEAK_F32_TFLOPS, 4),
             "what": "path_attn_bwd on the forward workload (gradients of q, k, v, w, beta"
                     f"{', log forget gates' if gates is not None else ''}), seeded dO, median of {steps}"}
+
+
+def paged_leg(pa, xd, cd, dbytes, page=256, warmup=20, steps=50):
+    """Times path_decode_step_paged on the decode workload's caches, scattered
+    into `page`-slot pages in a seeded random order (lengths all cache_len)."""
+    import torch
+
+    B, H, n, d = cd.B, cd.H, cd.cache_len, cd.d
+    mp = (n + 1 + page - 1) // page
+    npg = B * mp
+    perm = torch.randperm(npg, generator=torch.Generator().manual_seed(cd.seed)).to("cuda:0")
+    table = perm.view(B, mp).to(torch.int32)
+
+    def scatter(c):
+        padded = torch.zeros(B, H, mp * page, d, dtype=c.dtype, device=c.device)
+        padded[:, :, : c.shape[2]] = c
+        logical = padded.view(B, H, mp, page, d).permute(0, 2, 1, 3, 4).reshape(npg, H, page, d)
+        pages = torch.empty_like(logical)
+        pages[perm] = logical
+        return pages
+
+    kp, vp = scatter(xd["k_cache"]), scatter(xd["v_cache"])
+    lens = torch.full((B,), n, dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(max(256, pa.decode_workspace_bytes(B, H, d, n)), dtype=torch.uint8, device="cuda:0")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(warmup + steps):
+        if k >= warmup:
+            evs[k - warmup][0].record()
+        pa.path_decode_step_paged(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], kp, vp, table, lens, n,
+                                  scale=cd.scale, workspace=ws)
+        if k >= warmup:
+            evs[k - warmup][1].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    gbs = dbytes / (ms * 1e-3) / 1e9
+    del kp, vp
+    return {"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "bytes_model": dbytes,
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "what": f"paged decode step, same caches in {page}-slot pages (random page order), length {n} each"}
 
 
 def project_leg(pa, cf, warmup=20, steps=50):

@@ -450,8 +450,9 @@ extern "C" int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype
   if (!mul_ok(B, H, &BH) || !mul_ok(num_pages, H, &n) || !mul_ok(n, page_size, &n) || !mul_ok(n, d, &n) ||
       !mul_ok(B, max_pages, &tbl) || !mul_ok(max_pages, page_size, &slots))
     return PATH_ERR_SHAPE;
-  // page ids are int32 and rows are (page * H + h) * page_size + slot
-  if (num_pages > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
+  // page ids are int32, rows are (page * H + h) * page_size + slot, and key
+  // indices stay below 2^31 (the kernels map them with 32-bit arithmetic)
+  if (num_pages > (int64_t(1) << 31) - 1 || slots > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
   if (max_cache_len >= slots) return PATH_ERR_CAPACITY;
   if (BH * path::decode_num_chunks(max_cache_len) > (int64_t(1) << 31) - 1) return PATH_ERR_SHAPE;
   if (!q_t || !k_t || !v_t || !w_t || !beta_t || !k_pages || !v_pages || !page_table || !cache_lens || !o || !lse)

@@ -91,30 +91,74 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Where cached key j of head bh lives, in rows of d elements.
+// Where cached key j of head bh lives, in rows of d elements.  row() maps one
+// key (the appended one); chunk_map() gives the map of one workgroup's chunk
+// of keys [j0, j1), which every thread of the workgroup builds together.
 // ContigRows: caches [B*H, capacity, d], one length for every head.
 struct ContigRows {
+  static constexpr int kMapSlots = 1;
   int64_t capacity, len;
   __device__ int64_t length(int64_t) const { return len; }
   __device__ int64_t row(int64_t bh, int64_t j) const { return bh * capacity + j; }
   __device__ static constexpr bool ok(int64_t) { return true; }
+  struct Map {
+    int64_t base;
+    __device__ int64_t row(int64_t j) const { return base + j; }
+  };
+  __device__ Map chunk_map(int64_t bh, int64_t, int64_t, int32_t*) const { return Map{bh * capacity}; }
 };
 // PagedRows: pages [num_pages, H, page, d]; sequence b's logical page lp is
 // table[b * max_pages + lp] and its length lens[b].  A slot whose page is not
 // mapped (outside the table or the pool) is reported as row -1 and skipped.
+// Keys are below 2^31 (the host checks max_pages * page), so logical pages come
+// from a shift when page is a power of two (shift >= 0), else a 32-bit division.
 struct PagedRows {
+  static constexpr int kMapSlots = kDecChunk;
   const int32_t* table;
   const int32_t* lens;
   int64_t H, max_pages, num_pages, page;
+  int shift;
+  __device__ int64_t lpage(int64_t j) const {
+    return shift >= 0 ? (j >> shift)
+                      : static_cast<int64_t>(static_cast<uint32_t>(j) / static_cast<uint32_t>(page));
+  }
   __device__ int64_t length(int64_t bh) const { return lens[bh / H]; }
   __device__ int64_t row(int64_t bh, int64_t j) const {
-    const int64_t lp = j / page;
-    if (j < 0 || lp >= max_pages) return -1;
+    if (j < 0) return -1;
+    const int64_t lp = lpage(j);
+    if (lp >= max_pages) return -1;
     const int64_t pg = table[(bh / H) * max_pages + lp];
     if (pg < 0 || pg >= num_pages) return -1;
     return (pg * H + bh % H) * page + (j - lp * page);
   }
   __device__ static bool ok(int64_t r) { return r >= 0; }
+  struct Map {
+    const int32_t* spg;  // validated page ids of the chunk's logical pages, from lp0
+    int64_t lp0, h, H, page;
+    int shift;
+    __device__ int64_t row(int64_t j) const {
+      const int64_t lp = shift >= 0 ? (j >> shift)
+                                    : static_cast<int64_t>(static_cast<uint32_t>(j) / static_cast<uint32_t>(page));
+      const int32_t pg = spg[lp - lp0];
+      return pg < 0 ? -1 : (pg * H + h) * page + (j - lp * page);
+    }
+  };
+  __device__ Map chunk_map(int64_t bh, int64_t j0, int64_t j1, int32_t* spg) const {
+    const int64_t b = bh / H;
+    const int64_t lp0 = j1 > j0 ? lpage(j0) : 0;
+    const int64_t cnt = j1 > j0 ? lpage(j1 - 1) - lp0 + 1 : 0;  // <= j1 - j0 <= kDecChunk
+    for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+      const int64_t lp = lp0 + i;
+      int32_t pg = -1;
+      if (lp < max_pages) {
+        const int32_t t = table[b * max_pages + lp];
+        if (t >= 0 && t < num_pages) pg = t;
+      }
+      spg[i] = pg;
+    }
+    __syncthreads();
+    return Map{spg, lp0, bh % H, H, page, shift};
+  }
 };
 
 // partial layout per (bh, chunk): [m, l, acc[D]]
@@ -163,6 +207,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 
   const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
   const int64_t j1 = j0 + kDecChunk < len ? j0 + kDecChunk : len;
+  __shared__ int32_t spg[Rows::kMapSlots];
+  const auto map = rows.chunk_map(bh, j0, j1, spg);
   typename V::raw* kraw = reinterpret_cast<typename V::raw*>(k_cache);
   const typename V::raw* vraw = reinterpret_cast<const typename V::raw*>(v_cache);
 
@@ -182,7 +228,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       vr[u] = kr[u];
       cr[u] = 0.f;
       if (j < j1) {
-        const int64_t rw = rows.row(bh, j);
+        const int64_t rw = map.row(j);
         if (rows.ok(rw)) {
           kr[u] = __builtin_nontemporal_load(&kraw[rw * LPK + sub]);
           vr[u] = __builtin_nontemporal_load(&vraw[rw * LPK + sub]);
@@ -207,7 +253,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
-      const int64_t rw = j < j1 ? rows.row(bh, j) : -1;
+      const int64_t rw = j < j1 ? map.row(j) : -1;
       const bool live = j < j1 && rows.ok(rw);
       float kf[EPV];
       V::unpack(kc[u], kf);
@@ -436,7 +482,11 @@ hipError_t launch_decode_paged(int dtype, int64_t B, int64_t H, int64_t d, float
                                void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
                                const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
                                int64_t max_len, void* o, float* lse, float* partials, hipStream_t stream) {
-  const PagedRows rows{page_table, cache_lens, H, max_pages, num_pages, page_size};
+  int shift = -1;
+  if ((page_size & (page_size - 1)) == 0)
+    for (shift = 0; (int64_t(1) << shift) < page_size; ++shift) {
+    }
+  const PagedRows rows{page_table, cache_lens, H, max_pages, num_pages, page_size, shift};
   const int64_t BH = B * H;
   auto go = [&](auto launch) {
     return launch(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, rows, max_len, o, lse, partials,

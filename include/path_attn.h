@@ -226,8 +226,9 @@ int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale
  *   out-of-bounds access.
  * Workspace: path_decode_workspace_bytes(B, H, d, max_cache_len).
  * Errors: as path_decode_step (PATH_ERR_CAPACITY when max_cache_len >=
- *   max_pages * page_size); PATH_ERR_SHAPE for page_size < 1, num_pages < 1 or
- *   max_pages < 1.
+ *   max_pages * page_size); PATH_ERR_SHAPE for page_size < 1, num_pages < 1,
+ *   max_pages < 1 or max_pages * page_size >= 2^31.  Any page_size >= 1 works;
+ *   a power of two saves a division per key.
  */
 int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
                            const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
