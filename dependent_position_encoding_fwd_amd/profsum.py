@@ -67,9 +67,16 @@ BWD = ("bwd_pair_kernel", "bwd_block_kernel", "prepare_f32_kernel", "bwd_rowdot_
        "bwd_suffix_kernel")
 
 
+# the paged decode kernels (row map PagedRows) too
+PAGED = (("decode_chunk_paged", "decode_chunk_kernel"), ("decode_merge_paged", "decode_merge_kernel"))
+
+
 def classify(name: str):
+    for cls, key in PAGED:
+        if key in name and "PagedRows" in name:
+            return cls
     for cls, key in GATED:
-        if key in name and ", true>" in name:
+        if key in name and (", true>" in name or ", true," in name):
             return cls
     for cls, key in CLASSES:
         if key in name:
@@ -138,11 +145,15 @@ def short(name: str) -> str:
             "head_reduce": "head_reduce_kernel", "decode_chunk": "decode_chunk_kernel<bf16,64>",
             "decode_merge": "decode_merge_kernel<bf16,64>", "copy": "__amd_rocclr_copyBuffer",
             "decode_chunk_fox": "decode_chunk_kernel<bf16,64,gated>",
-            "decode_merge_fox": "decode_merge_kernel<bf16,64,gated>"}.get(c, _short_other(name))
+            "decode_merge_fox": "decode_merge_kernel<bf16,64,gated>",
+            "decode_chunk_paged": "decode_chunk_kernel<bf16,64,paged>",
+            "decode_merge_paged": "decode_merge_kernel<bf16,64,paged>"}.get(c, _short_other(name))
 
 
 def _short_other(name: str) -> str:
     """A backward kernel's name without its argument list, else the first 60 characters."""
+    if "project_kernel" in name:
+        return "project_kernel (projection)"
     for key in BWD:
         if key in name:
             head = name.split("(")[0].replace("void ", "").replace("path::", "")
