@@ -363,9 +363,10 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
     T* __restrict__ dw, float* __restrict__ dbeta, float* __restrict__ dc) {
   constexpr int C = kBlk, CP = C + 1, NW = block_waves<D>(), NT = 64 * NW;
   constexpr int NU = D / 16;  // elements of a chain's vector per lane
+  constexpr int G = D == 64 ? 2 : 1;  // groups of four chains a wave runs in lockstep
   __shared__ float Ws[C][D], Ks[C][D], gW[C][D], gK[C][D];
   __shared__ float PD[C][CP];     // [key c][query r]: dO_r . v_c, then p
-  __shared__ float sA[NW][4][C];  // a_t = w_t . x^(t+1) of each chain a wave runs
+  __shared__ float sA[NW][G][4][C];  // a_t = w_t . x^(t+1) of each chain a wave runs
   __shared__ float sB[C], sL[C], sD[C], sC[C], gB[C], cs[C], rs[C];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -402,182 +403,243 @@ __global__ __launch_bounds__(64 * block_waves<D>()) void bwd_block_kernel(
                      [&](int c, int r, float x) { PD[c][r] = c <= r ? x : 0.f; });  // p = 0 above the causal edge
   __syncthreads();
 
-  // Householder chains, four per wave: chain `sub` owns lanes 16 sub .. 16 sub + 15,
-  // each holding elements e = l16 + 16 u of the chain's vector.  Dot products are
-  // sums over the chain's 16 lanes (DPP moves within a row, so chains never mix).
-  // A chain's earlier state is rebuilt from the next as x^(t+1) = x^(t) + beta_t a_t w_t.
-  // Chains run in groups of four consecutive indices: query chains r, key chains c,
-  // then (when P_n takes part in a transport) columns of P_n.  The four chains'
-  // contributions to a gradient row are summed across the wave's rows before the
-  // LDS atomic (the atomic rate, not the arithmetic, bounds this kernel).
+  // Householder chains, four per wave and G groups of four in lockstep: chain
+  // `sub` of group gi owns lanes 16 sub .. 16 sub + 15, each holding elements
+  // e = l16 + 16 u of the chain's vector.  Dot products are sums over the
+  // chain's 16 lanes (DPP moves within a row, so chains never mix).  A chain's
+  // earlier state is rebuilt from the next as x^(t+1) = x^(t) + beta_t a_t w_t.
+  // Groups hold four consecutive indices: query chains r, key chains c, then
+  // (when P_n takes part in a transport) columns of P_n.  The contributions of
+  // the G x 4 chains to a gradient row are summed in registers over the groups
+  // and across the wave's rows (reduce-scatter) before one LDS atomic per lane:
+  // the atomic rate, not the arithmetic, bounds this kernel.
   const auto dotw = [&](int t, const float (&x)[NU]) {
     float s = 0.f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) s = fmaf(Ws[t][l16 + 16 * u], x[u], s);
     return row16_sum(s);
   };
-  float* myA = sA[wave][sub];
+  const auto add_rows = [&](float (*dst)[D], int t, const float (&c)[NU]) {
+#pragma unroll
+    for (int h = 0; h < NU / 4; ++h)
+      atomicAdd(&dst[t][l16 + 16 * (4 * h + sub)],
+                rows_reduce_scatter(c[4 * h], c[4 * h + 1], c[4 * h + 2], c[4 * h + 3]));
+  };
   const int ngq = (valid + 3) / 4;
+  const int nsq = (ngq + G - 1) / G;  // lockstep sets of query (and of key) groups
   const bool haveP = n >= 1 && n <= Nb - 2;
-  const int ngroups = 2 * ngq + (haveP ? D / 4 : 0);
-  for (int grp = wave; grp < ngroups; grp += NW) {
-    float x[NU], xb[NU];
-    if (grp < ngq) {
+  const int nsets = 2 * nsq + (haveP ? D / 4 / G : 0);
+  for (int set = wave; set < nsets; set += NW) {
+    float x[G][NU], xb[G][NU];
+    if (set < nsq) {
       // Query chain r: x^(t+1) = H_{t+1}...H_r q_r meets key t, then takes H_t.
-      const int r = 4 * grp + sub;
-      const bool live = r < valid;
-      const int tmax = min(4 * grp + 3, valid - 1);
+      int r[G];
+      bool live[G];
+      float lr[G], dr[G], cr[G], rsum_r[G];
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
-        x[u] = live ? load_f32(q + rb + static_cast<int64_t>(r) * D + l16 + 16 * u) : 0.f;
+      for (int gi = 0; gi < G; ++gi) {
+        r[gi] = 4 * (G * set + gi) + sub;  // < 64: G nsq <= 16 groups
+        live[gi] = r[gi] < valid;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          x[gi][u] = live[gi] ? load_f32(q + rb + static_cast<int64_t>(r[gi]) * D + l16 + 16 * u) : 0.f;
+      }
+      const int tmax = min(4 * (G * set + G - 1) + 3, valid - 1);
       for (int t = tmax; t >= 0; --t) {
-        const bool act = live && t <= r;
-        const float a = dotw(t, x);
-        if (act && l16 == 0) myA[t] = a;
-        const float ba = act ? sB[t] * a : 0.f;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) x[u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[u]);
+        for (int gi = 0; gi < G; ++gi) {
+          const bool act = live[gi] && t <= r[gi];
+          const float a = dotw(t, x[gi]);
+          if (act && l16 == 0) sA[wave][gi][sub][t] = a;
+          const float ba = act ? sB[t] * a : 0.f;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) x[gi][u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[gi][u]);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < NU; ++u) xb[u] = live ? dqh[rb + static_cast<int64_t>(r) * D + l16 + 16 * u] : 0.f;
-      const float lr = live ? sL[r] : 0.f, dr = live ? sD[r] : 0.f, cr = live ? sC[r] : 0.f;
-      float rsum_r = 0.f;
+      for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          xb[gi][u] = live[gi] ? dqh[rb + static_cast<int64_t>(r[gi]) * D + l16 + 16 * u] : 0.f;
+        lr[gi] = live[gi] ? sL[r[gi]] : 0.f;
+        dr[gi] = live[gi] ? sD[r[gi]] : 0.f;
+        cr[gi] = live[gi] ? sC[r[gi]] : 0.f;
+        rsum_r[gi] = 0.f;
+      }
       for (int t = 0; t <= tmax; ++t) {
-        const bool act = live && t <= r;
         const float bt = sB[t];
-        const float a = act ? myA[t] : 0.f;
-        float xn[NU];
-#pragma unroll
-        for (int u = 0; u < NU; ++u) xn[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[u]);
-        float kx = 0.f;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) kx = fmaf(Ks[t][l16 + 16 * u], xn[u], kx);
-        kx = row16_sum(kx);
-        const float g = dotw(t, xb);
-        const float sv = scale * kx + (FOX ? cr - sC[t] : 0.f);
-        const float p = act ? expf(sv - lr) : 0.f;
-        const float ds = act ? p * (PD[t][r] - dr) : 0.f;
-        const float E = scale * ds;
-        const float bta = act ? bt : 0.f;  // an idle chain adds exact zeros
         float cw[NU], ck[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          cw[u] = -bta * (a * xb[u] + g * xn[u]);
-          ck[u] = E * xn[u];
-        }
+        for (int u = 0; u < NU; ++u) cw[u] = ck[u] = 0.f;
+        float gb = 0.f, cst = 0.f;
 #pragma unroll
-        for (int h = 0; h < NU / 4; ++h) {
-          const int e = l16 + 16 * (4 * h + sub);
-          atomicAdd(&gW[t][e], rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
-          atomicAdd(&gK[t][e], rows_reduce_scatter(ck[4 * h], ck[4 * h + 1], ck[4 * h + 2], ck[4 * h + 3]));
+        for (int gi = 0; gi < G; ++gi) {
+          const bool act = live[gi] && t <= r[gi];
+          const float a = act ? sA[wave][gi][sub][t] : 0.f;
+          float xn[NU];
+#pragma unroll
+          for (int u = 0; u < NU; ++u) xn[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[gi][u]);
+          float kx = 0.f;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) kx = fmaf(Ks[t][l16 + 16 * u], xn[u], kx);
+          kx = row16_sum(kx);
+          const float g = dotw(t, xb[gi]);
+          const float sv = scale * kx + (FOX ? cr[gi] - sC[t] : 0.f);
+          const float p = act ? expf(sv - lr[gi]) : 0.f;
+          const float ds = act ? p * (PD[t][r[gi]] - dr[gi]) : 0.f;
+          const float E = scale * ds;
+          const float bta = act ? bt : 0.f;  // an idle chain adds exact zeros
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            cw[u] = fmaf(-bta, fmaf(a, xb[gi][u], g * xn[u]), cw[u]);
+            ck[u] = fmaf(E, xn[u], ck[u]);
+          }
+          gb -= g * a;
+          if (FOX && t < r[gi]) cst += ds;
+          if (act) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              xb[gi][u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[gi][u]);
+              xb[gi][u] = fmaf(E, Ks[t][l16 + 16 * u], xb[gi][u]);
+              x[gi][u] = xn[u];
+            }
+            if (l16 == 0) {
+              PD[t][r[gi]] = p;
+              if (FOX && t < r[gi]) rsum_r[gi] += ds;
+            }
+          }
         }
-        // dbeta_t and gate terms of the four chains (idle chains give 0), one lane adds
-        const float gbt = rows_sum(-g * a);
-        const float cst = FOX ? rows_sum(t < r ? ds : 0.f) : 0.f;
+        add_rows(gW, t, cw);
+        add_rows(gK, t, ck);
+        // dbeta_t and gate terms of the chains (idle chains give 0), one lane adds
+        const float gbt = rows_sum(gb);
+        const float cs4 = FOX ? rows_sum(cst) : 0.f;
         if (lane == 0) {
           atomicAdd(&gB[t], gbt);
-          if (FOX) atomicAdd(&cs[t], cst);
-        }
-        if (act) {
-#pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
-            xb[u] = fmaf(E, Ks[t][l16 + 16 * u], xb[u]);
-            x[u] = xn[u];
-          }
-          if (l16 == 0) {
-            PD[t][r] = p;
-            if (FOX && t < r) rsum_r += ds;
-          }
+          if (FOX) atomicAdd(&cs[t], cs4);
         }
       }
-      if (live) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) store_f32(dq + rb + static_cast<int64_t>(r) * D + l16 + 16 * u, xb[u]);
-        if (FOX && l16 == 0) rs[r] = rsum_r;
-      }
-    } else if (grp < 2 * ngq) {
+      for (int gi = 0; gi < G; ++gi)
+        if (live[gi]) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            store_f32(dq + rb + static_cast<int64_t>(r[gi]) * D + l16 + 16 * u, xb[gi][u]);
+          if (FOX && l16 == 0) rs[r[gi]] = rsum_r[gi];
+        }
+    } else if (set < 2 * nsq) {
       // Key chain c: y = H_t...H_{c+1} k_c, from k_c up to khat_c.
-      const int c = 4 * (grp - ngq) + sub;
-      const bool live = c < valid;
-      const int tmin = 4 * (grp - ngq) + 1;  // smallest c + 1 of the group
+      const int s0 = set - nsq;
+      int c[G];
+      bool live[G];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) x[u] = live ? Ks[c][l16 + 16 * u] : 0.f;
+      for (int gi = 0; gi < G; ++gi) {
+        c[gi] = 4 * (G * s0 + gi) + sub;
+        live[gi] = c[gi] < valid;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) x[gi][u] = live[gi] ? Ks[c[gi]][l16 + 16 * u] : 0.f;
+      }
+      const int tmin = 4 * G * s0 + 1;  // smallest c + 1 of the set
       for (int t = tmin; t < valid; ++t) {
-        const bool act = live && t > c;
-        const float a = dotw(t, x);
-        if (act && l16 == 0) myA[t] = a;
-        const float ba = act ? sB[t] * a : 0.f;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) x[u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[u]);
+        for (int gi = 0; gi < G; ++gi) {
+          const bool act = live[gi] && t > c[gi];
+          const float a = dotw(t, x[gi]);
+          if (act && l16 == 0) sA[wave][gi][sub][t] = a;
+          const float ba = act ? sB[t] * a : 0.f;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) x[gi][u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[gi][u]);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < NU; ++u) xb[u] = live ? dkh[rb + static_cast<int64_t>(c) * D + l16 + 16 * u] : 0.f;
-      for (int t = valid - 1; t >= tmin; --t) {
-        const bool act = live && t > c;
-        const float bt = sB[t];
-        const float a = act ? myA[t] : 0.f;
-        float xp[NU];
+      for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-        for (int u = 0; u < NU; ++u) xp[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[u]);
-        const float g = dotw(t, xb);
-        const float bta = act ? bt : 0.f;
+        for (int u = 0; u < NU; ++u)
+          xb[gi][u] = live[gi] ? dkh[rb + static_cast<int64_t>(c[gi]) * D + l16 + 16 * u] : 0.f;
+      for (int t = valid - 1; t >= tmin; --t) {
+        const float bt = sB[t];
         float cw[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) cw[u] = -bta * (a * xb[u] + g * xp[u]);
+        for (int u = 0; u < NU; ++u) cw[u] = 0.f;
+        float gb = 0.f;
 #pragma unroll
-        for (int h = 0; h < NU / 4; ++h)
-          atomicAdd(&gW[t][l16 + 16 * (4 * h + sub)],
-                    rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
-        const float gbt = rows_sum(-g * a);
-        if (lane == 0) atomicAdd(&gB[t], gbt);
-        if (act) {
+        for (int gi = 0; gi < G; ++gi) {
+          const bool act = live[gi] && t > c[gi];
+          const float a = act ? sA[wave][gi][sub][t] : 0.f;
+          float xp[NU];
 #pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
-            x[u] = xp[u];
+          for (int u = 0; u < NU; ++u) xp[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[gi][u]);
+          const float g = dotw(t, xb[gi]);
+          const float bta = act ? bt : 0.f;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) cw[u] = fmaf(-bta, fmaf(a, xb[gi][u], g * xp[u]), cw[u]);
+          gb -= g * a;
+          if (act) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              xb[gi][u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[gi][u]);
+              x[gi][u] = xp[u];
+            }
           }
         }
+        add_rows(gW, t, cw);
+        const float gbt = rows_sum(gb);
+        if (lane == 0) atomicAdd(&gB[t], gbt);
       }
-      if (live) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) atomicAdd(&gK[c][l16 + 16 * u], xb[u]);
-      }
+      for (int gi = 0; gi < G; ++gi)
+        if (live[gi]) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) atomicAdd(&gK[c[gi]][l16 + 16 * u], xb[gi][u]);
+        }
     } else {
       // Column col of P_n = H_0 ... H_63: x = H_t...H_63 e_col.
-      const int col = 4 * (grp - 2 * ngq) + sub;
+      const int s0 = set - 2 * nsq;
+      int col[G];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) x[u] = (l16 + 16 * u == col) ? 1.f : 0.f;
+      for (int gi = 0; gi < G; ++gi) {
+        col[gi] = 4 * (G * s0 + gi) + sub;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) x[gi][u] = (l16 + 16 * u == col[gi]) ? 1.f : 0.f;
+      }
       for (int t = valid - 1; t >= 0; --t) {
-        const float a = dotw(t, x);
-        if (l16 == 0) myA[t] = a;
-        const float ba = sB[t] * a;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) x[u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[u]);
+        for (int gi = 0; gi < G; ++gi) {
+          const float a = dotw(t, x[gi]);
+          if (l16 == 0) sA[wave][gi][sub][t] = a;
+          const float ba = sB[t] * a;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) x[gi][u] = fmaf(-ba, Ws[t][l16 + 16 * u], x[gi][u]);
+        }
       }
       const float* gP = dPacc + (bh * Nb + n) * D * D;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) xb[u] = gP[(l16 + 16 * u) * D + col];
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) xb[gi][u] = gP[(l16 + 16 * u) * D + col[gi]];
       for (int t = 0; t < valid; ++t) {
         const float bt = sB[t];
-        const float a = myA[t];
-        float xn[NU];
-#pragma unroll
-        for (int u = 0; u < NU; ++u) xn[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[u]);
-        const float g = dotw(t, xb);
         float cw[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) cw[u] = -bt * (a * xb[u] + g * xn[u]);
+        for (int u = 0; u < NU; ++u) cw[u] = 0.f;
+        float gb = 0.f;
 #pragma unroll
-        for (int h = 0; h < NU / 4; ++h)
-          atomicAdd(&gW[t][l16 + 16 * (4 * h + sub)],
-                    rows_reduce_scatter(cw[4 * h], cw[4 * h + 1], cw[4 * h + 2], cw[4 * h + 3]));
+        for (int gi = 0; gi < G; ++gi) {
+          const float a = sA[wave][gi][sub][t];
+          float xn[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          xb[u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[u]);
-          x[u] = xn[u];
+          for (int u = 0; u < NU; ++u) xn[u] = fmaf(bt * a, Ws[t][l16 + 16 * u], x[gi][u]);
+          const float g = dotw(t, xb[gi]);
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            cw[u] = fmaf(-bt, fmaf(a, xb[gi][u], g * xn[u]), cw[u]);
+            xb[gi][u] = fmaf(-bt * g, Ws[t][l16 + 16 * u], xb[gi][u]);
+            x[gi][u] = xn[u];
+          }
+          gb -= g * a;
         }
-        const float gbt = rows_sum(-g * a);
+        add_rows(gW, t, cw);
+        const float gbt = rows_sum(gb);
         if (lane == 0) atomicAdd(&gB[t], gbt);
       }
     }
