@@ -110,3 +110,34 @@ def test_bwd_deterministic_up_to_atomics():
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.allclose(a, b, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_full_length_directional(fox):
+    """At the L = 4096 workload length (64 blocks, 2016 block pairs per head),
+    where the fp64 gradient oracle is too slow, the gradients must give the
+    directional derivative of f = sum(dO * o) along a random direction of all
+    inputs: sum_x <grad_x, v_x> against the central difference
+    (f(x + v) - f(x - v)) / 2 of the GPU forward (fp32).  The O(|v|^3) error and
+    fp32 rounding of f keep the two within 1 % of each other."""
+    B, H, L, d, scale = 1, 2, 4096, 64, 0.125
+    x = synthetic.fwd_inputs(B, H, L, d, "f32", 4096 + fox, fox=fox)
+    gen = torch.Generator().manual_seed(77 + fox)
+    names = ["q", "k", "v", "w", "beta"] + (["log_forget"] if fox else [])
+    g = {n: x[n].to(DEV) for n in names}
+    do = torch.randn(B, H, L, d, generator=gen).to(DEV)
+    step = {n: (1e-3 * torch.randn(g[n].shape, generator=gen)).to(DEV) for n in names}
+
+    def f(sign):
+        y = {n: g[n] + sign * step[n] for n in names}
+        o, _ = pa.path_attn_fwd(y["q"], y["k"], y["v"], y["w"], y["beta"], y.get("log_forget"), scale=scale)
+        return float((o.double() * do.double()).sum())
+
+    o, lse = pa.path_attn_fwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g.get("log_forget"), scale=scale)
+    grads = pa.path_attn_bwd(g["q"], g["k"], g["v"], g["w"], g["beta"], o, lse, do, g.get("log_forget"), scale=scale)
+    torch.cuda.synchronize()
+    gmap = dict(zip(["q", "k", "v", "w", "beta", "log_forget"], grads))
+    dirder = sum(float((gmap[n].double() * step[n].double()).sum()) for n in names)
+    fd = (f(1.0) - f(-1.0)) / 2.0
+    print(f"  L={L} fox={fox}: <grad, v> = {dirder:.6e}, central difference = {fd:.6e}", flush=True)
+    assert abs(dirder - fd) <= 1e-2 * abs(fd), (dirder, fd)
