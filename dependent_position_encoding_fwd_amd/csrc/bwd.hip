@@ -1,5 +1,6 @@
 // Backward pass of PaTH attention: gradients of <dO, o> with respect to q, k,
-// v, w, beta and the log forget gates, in fp32 arithmetic on the vector ALUs.
+// v, w, beta and the log forget gates, in fp32 arithmetic: tile products on
+// the fp32 matrix cores, Householder chains on the vector ALUs.
 //
 // The forward [PaTH Attention summary (gist.science 2505.16381), §2 "Mecanismo
 // Central", §2 "Extensões: PaTH-FoX"; blockwise as in §3 "Representação de
@@ -19,7 +20,8 @@
 //     Khat_n receives scale dS_n Qt^(n)^T and V_n receives p_n dO_m; the last
 //     three are summed over query blocks with fp32 atomics.
 // In-block part (bwd_block_kernel, one workgroup per block): every Householder
-// chain of the block is replayed by one wave and then differentiated in reverse:
+// chain of the block is replayed by 16 lanes of a wave (four chains per wave)
+// and then differentiated in reverse:
 // query chains x <- H_t x from q_r down to qhat_r (they meet the in-block keys
 // on the way), key chains from k_c up to khat_c, and one chain per column of
 // P_n.  Running a chain backwards needs its states in the opposite order; each

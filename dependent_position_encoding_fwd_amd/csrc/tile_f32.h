@@ -1,14 +1,12 @@
 // Tile products on the fp32 matrix cores (16x16x4 MFMA, fp32 in and out) for
-// 256-thread workgroups: the shared building block of the fp32 kernels (block
-// prepare, backward).
+// workgroups whose first four waves compute them: the shared building block of
+// the fp32 kernels (block prepare, backward).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace path {
 namespace f32tile {
-
-constexpr int kThreads = 256;  // four waves
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
