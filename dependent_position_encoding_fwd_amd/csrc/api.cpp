@@ -264,7 +264,8 @@ size_t path_decode_workspace_bytes(int64_t B, int64_t H, int64_t d, int64_t cach
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, path::decode_num_chunks(cache_len), &n) ||
       !mul_ok(n, d + 2, &n))
     return 0;
-  return align_up(sizeof(float) * size_t(n > 0 ? n : 1));
+  // a 512-byte slot for the key loop's stores past a chunk's end, then the partials
+  return 512 + align_up(sizeof(float) * size_t(n > 0 ? n : 1));
 }
 
 }  // extern "C"

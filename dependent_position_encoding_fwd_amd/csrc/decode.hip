@@ -36,6 +36,10 @@ namespace path {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecChunk = 1024;  // keys per workgroup
+// The decode workspace starts with a 512-byte slot that takes the stores of key
+// slots past the end of a chunk (contiguous caches), so that every load and
+// store of the key loop is unconditional; the chunk partials follow it.
+constexpr int kDecTrashFloats = 128;
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
     Rows rows, int nchunks, float scale, const T* __restrict__ q_t,
     const T* __restrict__ w_t, const float* __restrict__ beta_t, const float* __restrict__ log_f_t,
     T* __restrict__ k_cache, const T* __restrict__ v_cache, const float* __restrict__ cum_cache,
-    float* __restrict__ partials) {
+    float* __restrict__ trash, float* __restrict__ partials) {
   using V = Vec16<T>;
   constexpr int EPV = V::N;          // elements per 16-byte access
   constexpr int LPK = D / EPV;       // lanes per key row
@@ -220,26 +224,38 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   constexpr int STRIDE = NW * KPW;  // key rows per workgroup pass
   typename V::raw kr[UNR], vr[UNR];
   float cr[UNR];
+  // The loop's loads and stores carry no conditions, so the compiler can keep
+  // the next group's loads and this group's stores in flight together.  A slot
+  // past j1 (or, paged, on an unmapped page) stores into the trash slot and is
+  // kept out of the softmax; it loads row j1 - 1 of a contiguous cache (finite
+  // data) or, paged, the trash slot, whose value row is then zeroed.
+  constexpr bool kDense = std::is_same_v<Rows, ContigRows>;
+  typename V::raw* trash_slot = reinterpret_cast<typename V::raw*>(trash) + sub;
   auto fetch = [&](int64_t jb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
-      kr[u] = typename V::raw{0u, 0u, 0u, 0u};
-      vr[u] = kr[u];
-      cr[u] = 0.f;
-      if (j < j1) {
-        const int64_t rw = map.row(j);
-        if (rows.ok(rw)) {
-          kr[u] = __builtin_nontemporal_load(&kraw[rw * LPK + sub]);
-          vr[u] = __builtin_nontemporal_load(&vraw[rw * LPK + sub]);
-          if constexpr (FOX) cr[u] = cbase[j];
-        }
+      if constexpr (kDense) {
+        const int64_t jc = j < j1 ? j : j1 - 1;
+        const int64_t rw = map.row(jc);
+        kr[u] = __builtin_nontemporal_load(&kraw[rw * LPK + sub]);
+        vr[u] = __builtin_nontemporal_load(&vraw[rw * LPK + sub]);
+        if constexpr (FOX) cr[u] = cbase[jc];
+      } else {
+        const int64_t rw = j < j1 ? map.row(j) : -1;
+        const bool ok = rows.ok(rw);
+        kr[u] = __builtin_nontemporal_load(ok ? &kraw[rw * LPK + sub] : trash_slot);
+        vr[u] = __builtin_nontemporal_load(ok ? &vraw[rw * LPK + sub] : trash_slot);
+        cr[u] = 0.f;
       }
     }
   };
-  const int64_t jstart = j0 + wave * KPW + slot;
-  if (jstart < j1) fetch(jstart);
-  for (int64_t jb = jstart; jb < j1; jb += STRIDE * UNR) {
+  // The wave walks rows jw + slot + u STRIDE from its base row jw, the same trip
+  // count in every lane; a group entirely past j1 is only fetched, never used.
+  const int64_t jw0 = j0 + wave * KPW;
+  if (jw0 < j1) fetch(jw0 + slot);
+  for (int64_t jw = jw0; jw < j1; jw += STRIDE * UNR) {
+    const int64_t jb = jw + slot;
     typename V::raw kc[UNR], vc[UNR];
     float cc[UNR];
 #pragma unroll
@@ -248,13 +264,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       vc[u] = vr[u];
       cc[u] = cr[u];
     }
-    if (jb + STRIDE * UNR < j1) fetch(jb + STRIDE * UNR);
+    fetch(jb + STRIDE * UNR);
     float sv[UNR];
+    bool lv[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t j = jb + static_cast<int64_t>(u) * STRIDE;
-      const int64_t rw = j < j1 ? map.row(j) : -1;
+      const int64_t rw = kDense ? map.row(j < j1 ? j : j1 - 1) : (j < j1 ? map.row(j) : -1);
       const bool live = j < j1 && rows.ok(rw);
+      lv[u] = live;
       float kf[EPV];
       V::unpack(kc[u], kf);
       float a = 0.f, b = 0.f;
@@ -268,7 +286,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
       const float ba = bt * a;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) kf[e] -= ba * wv[e];
-      if (live) __builtin_nontemporal_store(V::pack(kf), &kraw[rw * LPK + sub]);
+      __builtin_nontemporal_store(V::pack(kf), live ? &kraw[rw * LPK + sub] : trash_slot);
       float su = scale2 * (b - ba * wq);
       if constexpr (FOX) su += kLog2e * (ct - cc[u]);
       sv[u] = live ? su : -INFINITY;
@@ -287,6 +305,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
         const float p = __builtin_amdgcn_exp2f(sv[u] - mnew);
         float vf[EPV];
         V::unpack(vc[u], vf);
+        if constexpr (!kDense) {
+          if (!lv[u]) {  // a slot that is not a key: its value row may hold anything
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) vf[e] = 0.f;
+          }
+        }
         lrun += p;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[e] += p * vf[e];
@@ -414,11 +438,13 @@ static hipError_t launch_dec_t(int64_t BH, float scale, const void* q_t, const v
                                float* partials, hipStream_t stream) {
   const int nchunks = static_cast<int>(decode_num_chunks(cache_len));
   const ContigRows rows{capacity, cache_len};
+  float* trash = partials;
+  partials += kDecTrashFloats;
   if (nchunks > 0) {
     hipLaunchKernelGGL((decode_chunk_kernel<T, D, FOX, ContigRows>), dim3(static_cast<unsigned>(BH * nchunks)),
                        dim3(kDecThreads), 0, stream, rows, nchunks, scale,
                        static_cast<const T*>(q_t), static_cast<const T*>(w_t), beta_t, log_f_t,
-                       static_cast<T*>(k_cache), static_cast<const T*>(v_cache), cum_cache, partials);
+                       static_cast<T*>(k_cache), static_cast<const T*>(v_cache), cum_cache, trash, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -462,11 +488,13 @@ static hipError_t launch_dec_paged_t(int64_t BH, float scale, const void* q_t, c
                                      const PagedRows& rows, int64_t max_len, void* o, float* lse, float* partials,
                                      hipStream_t stream) {
   const int nchunks = static_cast<int>(decode_num_chunks(max_len));
+  float* trash = partials;
+  partials += kDecTrashFloats;
   if (nchunks > 0) {
     hipLaunchKernelGGL((decode_chunk_kernel<T, D, false, PagedRows>), dim3(static_cast<unsigned>(BH * nchunks)),
                        dim3(kDecThreads), 0, stream, rows, nchunks, scale, static_cast<const T*>(q_t),
                        static_cast<const T*>(w_t), beta_t, nullptr, static_cast<T*>(k_pages),
-                       static_cast<const T*>(v_pages), nullptr, partials);
+                       static_cast<const T*>(v_pages), nullptr, trash, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

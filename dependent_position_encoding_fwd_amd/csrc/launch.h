@@ -50,7 +50,8 @@ hipError_t launch_fwd_scan_f32(int dtype, int64_t B, int64_t H, int64_t L, int64
                                const float* beta, const float* cum, const float* khat,
                                const float* pT, void* o, float* lse, hipStream_t stream);
 
-// Decode: number of key chunks and partial-result floats per (b,h).  With
+// Decode: number of key chunks and partial-result floats per (b,h).  `partials`
+// is the whole decode workspace: 128 floats of store slot, then the partials.  With
 // log_f_t != null the step is gated: cum_cache [BH, capacity] holds the gate
 // prefixes of the cached keys and receives c_t at slot cache_len.
 int64_t decode_num_chunks(int64_t cache_len);
