@@ -377,8 +377,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     T* __restrict__ k_cache, T* __restrict__ v_cache, float* __restrict__ cum_cache,
     const float* __restrict__ partials, T* __restrict__ o, float* __restrict__ lse) {
   constexpr int PER = D / 64;
+  constexpr int kPre = 8;  // chunks whose partials are fetched with the new token
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
+  const float* pb = partials + bh * nchunks * (D + 2);
+  // Every load is issued before any is used (one memory round trip): the new
+  // token, and the partials of the first kPre chunks (a chunk past the last
+  // re-reads the last; there is none to read when the cache is empty).
   float qf[PER], kf[PER], vf[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
@@ -387,20 +392,43 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     kf[t] = load_f32(k_t + bh * D + e);
     vf[t] = load_f32(v_t + bh * D + e);
   }
+  const int npre = nchunks < kPre ? nchunks : kPre;
+  float pm[kPre], pl[kPre], pa[kPre][PER];
+  if (nchunks > 0) {
+#pragma unroll
+    for (int c = 0; c < kPre; ++c) {
+      const float* p = pb + (c < nchunks ? c : nchunks - 1) * (D + 2);
+      pm[c] = p[0];
+      pl[c] = p[1];
+#pragma unroll
+      for (int t = 0; t < PER; ++t) pa[c][t] = p[2 + lane + 64 * t];
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int t = 0; t < PER; ++t) s += qf[t] * kf[t];
   s = scale * 1.4426950408889634f * wave_sum(s);  // log2 units, like the partials
 
   float mm = s;
-  const float* pb = partials + bh * nchunks * (D + 2);
-  for (int c = 0; c < nchunks; ++c) mm = fmaxf(mm, pb[c * (D + 2)]);
+#pragma unroll
+  for (int c = 0; c < kPre; ++c)
+    if (c < npre) mm = fmaxf(mm, pm[c]);
+  for (int c = kPre; c < nchunks; ++c) mm = fmaxf(mm, pb[c * (D + 2)]);
   const float es = __builtin_amdgcn_exp2f(s - mm);
   float ll = es;
   float oo[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) oo[t] = es * vf[t];
-  for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+  for (int c = 0; c < kPre; ++c) {
+    if (c < npre) {
+      const float a = __builtin_amdgcn_exp2f(pm[c] - mm);
+      ll += a * pl[c];
+#pragma unroll
+      for (int t = 0; t < PER; ++t) oo[t] += a * pa[c][t];
+    }
+  }
+  for (int c = kPre; c < nchunks; ++c) {
     const float* p = pb + c * (D + 2);
     const float a = __builtin_amdgcn_exp2f(p[0] - mm);
     ll += a * p[1];
