@@ -32,10 +32,9 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
   constexpr int DP = D + 1;
   __shared__ float Ws[C][DP];  // rows w_s of the block (zero past L)
   __shared__ float Xs[C][DP];  // k rows, then q rows, then F = T^{-T} W
-  __shared__ float Gs[C][CP];  // strict_upper(W W^T), then masked W k / W q products
+  __shared__ float Gs[C][CP];  // strict_upper(W W^T), then masked W k / W q products, then Y
   __shared__ float Ts[C][CP];  // T^{-1}
-  __shared__ float Ys[C][CP];  // coefficient rows
-  __shared__ float bs[C];
+  __shared__ float bs[C];      // (67 KB at d = 64: two workgroups per CU)
 
   const int tid = threadIdx.x;
   const int n = blockIdx.x % Nb;
@@ -51,7 +50,19 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
   if (tid < C) bs[tid] = tid < valid ? beta[bh * L + t0 + tid] : 0.f;
   __syncthreads();
 
+  using f32tile::Acc;
+  using f32tile::tile_acc;
+  using f32tile::tile_emit;
   using f32tile::tile_mm;
+  using f32tile::tile_zero;
+  // Y = Z M, written over Z in Gs once every wave has read Z
+  const auto gs_times = [&](const auto& b) {
+    Acc<C, C> acc;
+    tile_zero<C, C>(acc);
+    tile_acc<C, C, C>([&](int r, int t) { return Gs[r][t]; }, b, acc);
+    __syncthreads();
+    tile_emit<C, C>(acc, [&](int r, int a, float x) { Gs[r][a] = x; });
+  };
   // G = strict_upper(W W^T)
   tile_mm<C, C, D>([&](int r, int e) { return Ws[r][e]; }, [&](int e, int t) { return Ws[t][e]; },
                    [&](int r, int t, float x) { Gs[r][t] = t > r ? x : 0.f; });
@@ -89,12 +100,11 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
                      [&](int c, int s2, float x) { Gs[c][s2] = s2 > c ? x : 0.f; });
     __syncthreads();
     // Y = Z T^{-1}: Y[c][a] = sum_{c<s<=a} Z[c][s] T^{-1}[s][a] (= (T^{-T} z_c)_a; both factors
-    // vanish outside that range, so the full product is the same sum)
-    tile_mm<C, C, C>([&](int c, int s2) { return Gs[c][s2]; }, [&](int s2, int a) { return Ts[s2][a]; },
-                     [&](int c, int a, float x) { Ys[c][a] = x; });
+    // vanish outside that range, so the full product is the same sum), into Gs
+    gs_times([&](int s2, int a) { return Ts[s2][a]; });
     __syncthreads();
     // khat = K - Y W  (Y[c][a] = 0 for a <= c)
-    tile_mm<C, D, C>([&](int c, int a) { return Ys[c][a]; }, [&](int a, int e) { return Ws[a][e]; },
+    tile_mm<C, D, C>([&](int c, int a) { return Gs[c][a]; }, [&](int a, int e) { return Ws[a][e]; },
                      [&](int c, int e, float x) {
                        if (c < valid) khat_out[base + (t0 + c) * D + e] = Xs[c][e] - x;
                      });
@@ -111,12 +121,11 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     tile_mm<C, C, D>([&](int r, int e) { return Xs[r][e]; }, [&](int e, int t) { return Ws[t][e]; },
                      [&](int r, int t, float x) { Gs[r][t] = t <= r ? x : 0.f; });
     __syncthreads();
-    // Y = A T^{-T}: Y[r][a] = sum_{a<=t<=r} T^{-1}[a][t] A[r][t] (= (T^{-1} a_r)_a, 0 for a > r)
-    tile_mm<C, C, C>([&](int r, int t) { return Gs[r][t]; }, [&](int t, int a) { return Ts[a][t]; },
-                     [&](int r, int a, float x) { Ys[r][a] = x; });
+    // Y = A T^{-T}: Y[r][a] = sum_{a<=t<=r} T^{-1}[a][t] A[r][t] (= (T^{-1} a_r)_a, 0 for a > r), into Gs
+    gs_times([&](int t, int a) { return Ts[a][t]; });
     __syncthreads();
     // qhat = Q - Y W
-    tile_mm<C, D, C>([&](int r, int a) { return Ys[r][a]; }, [&](int a, int e) { return Ws[a][e]; },
+    tile_mm<C, D, C>([&](int r, int a) { return Gs[r][a]; }, [&](int a, int e) { return Ws[a][e]; },
                      [&](int r, int e, float x) {
                        if (r < valid) qhat_out[base + (t0 + r) * D + e] = Xs[r][e] - x;
                      });
