@@ -426,7 +426,8 @@ extern "C" int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t
   int64_t T, xe, we, oe, tiles_cols;
   if (!mul_ok(B, L, &T) || !mul_ok(T, Dm, &xe) || !mul_ok(H * d, Dm, &we) || !mul_ok(T * H, d, &oe))
     return PATH_ERR_SHAPE;
-  // 128-token tiles times 128-column groups (w of whole heads, then beta logits) must fit a 32-bit grid
+  // token tiles (256 tokens; 128 bounds them) times 128-column groups (w of whole heads, then beta
+  // logits) must fit a 32-bit grid
   const int64_t ncol = (H * d + 127) / 128 + (H + 127) / 128;
   if (!mul_ok(((T + 127) / 128 + 7) / 8 * 8, ncol, &tiles_cols) || tiles_cols > (int64_t(1) << 31) - 1)
     return PATH_ERR_SHAPE;

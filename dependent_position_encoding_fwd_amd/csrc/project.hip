@@ -9,16 +9,24 @@
 //
 // One GEMM over all heads: tokens x [T, Dm] (T = B L, bf16) against the rows
 // of Ww [H d, Dm] (head h owns rows h d .. h d + d - 1) and of u [H, Dm].  A
-// workgroup takes 128 tokens and one group of 128 columns: either the rows of
+// workgroup takes 256 tokens and one group of 128 columns: either the rows of
 // 128 / d whole heads (so each head's vector w_s is in the tile and is
 // normalised in the epilogue) or the u rows of 128 consecutive heads (their
-// beta logits).
-// Products are 16x16x32 bf16 MFMAs with fp32 accumulation; the reduction over
-// Dm runs in chunks of 64 through two LDS stages, fed from registers that hold
-// the next 3 chunks' global loads.
+// beta logits).  Eight waves, each 32 tokens x 128 columns.
+// Products are 16x16x32 bf16 MFMAs with fp32 accumulation.  Dm is reduced in
+// chunks of 64 that travel global -> LDS with direct-to-LDS loads through a
+// ring of three stages: chunk c + 2 is in flight while chunk c is multiplied,
+// and one barrier per chunk both publishes the next stage and frees the oldest.
+// Every load is unconditional: rows past the tokens or the weight rows read a
+// clamped row, whose products land only in outputs that are not written.
+// Tiles are unpadded 128-byte rows; 16-byte chunk j of row r sits at slot
+// j ^ (r & 7), so the operand reads (16 rows, one chunk column) hit distinct
+// banks.
 // Workgroup ids are dealt to the 8 XCDs round robin; all column groups of a
 // token tile are given ids on one XCD, so its L2 fetches the tile once.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -28,11 +36,14 @@ namespace path {
 
 namespace {
 
-constexpr int kPT = 256;     // threads: four waves
-constexpr int kPM = 128;     // tokens per workgroup (32 per wave)
-constexpr int kPK = 64;      // reduction chunk
-constexpr int kPKP = kPK + 8;  // LDS row pitch (bf16 elements): 144 bytes, spreads the 16-byte reads
-constexpr int kPN = 128;     // columns per workgroup
+constexpr int kPW = 8;             // waves
+constexpr int kPT = 64 * kPW;      // threads
+constexpr int kPM = 32 * kPW;      // tokens per workgroup (32 per wave)
+constexpr int kPK = 64;            // reduction chunk (bf16 elements: one 128-byte row)
+constexpr int kPN = 128;           // columns per workgroup
+constexpr int kALd = kPM * kPK / 8 / kPT;  // direct-to-LDS loads per thread per chunk, tokens
+constexpr int kBLd = kPN * kPK / 8 / kPT;  // the same, weight rows
+static_assert(kALd * kPT * 8 == kPM * kPK && kBLd * kPT * 8 == kPN * kPK, "whole 16-byte chunks per thread");
 
 using mfma::b8;
 using mfma::f4;
@@ -50,20 +61,43 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// s_waitcnt with expcnt and lgkmcnt left open and vmcnt = N (N < 16).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Calls f(integral_constant<int, I>) for each I of the sequence, in order.
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(kPT, 2) void project_kernel(
+// NCH > 0: Dm = 64 NCH, the chunk loop fully unrolled, so every wait is a
+// constant and the compiler keeps track of which stage each load in flight
+// writes (a loop merges that knowledge away and drains all loads before the
+// operand reads).  NCH = 0: any Dm, a loop over chunks.
+template <int D, int NCH>
+__global__ __launch_bounds__(kPT, 1) void project_kernel(
     int64_t T, int64_t L, int64_t H, int64_t Dm, int ntiles, int ncol, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ Ww, const uint16_t* __restrict__ u, const float* __restrict__ bias,
     float beta_max, uint16_t* __restrict__ w_out, float* __restrict__ beta_out) {
   constexpr int NC = kPN / 16;         // column tiles
   constexpr int HT = D / 16;           // column tiles per head
-  constexpr int P = 3;                 // chunks of global loads in flight
-  constexpr int BL = kPN * kPK / 8 / kPT;  // 16-byte weight loads per thread per chunk
-  constexpr int AL = kPM * kPK / 8 / kPT;  // 16-byte token loads per thread per chunk
-  __shared__ __align__(16) uint16_t As[2][kPM][kPKP];
-  __shared__ __align__(16) uint16_t Bs[2][kPN][kPKP];
+  constexpr int NLD = kALd + kBLd;     // loads per thread per chunk
+  // Three stages of the ring, each its own LDS object so that the compiler can
+  // tell reads of one stage from loads still landing in another.
+  // Stage s holds the token tile (kPM rows) followed by the weight tile (kPN rows).
+  __shared__ __attribute__((aligned(1024))) uint16_t sT0[(kPM + kPN) * kPK], sT1[(kPM + kPN) * kPK],
+      sT2[(kPM + kPN) * kPK];
+  auto stageA = [&](auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return sT0; else if constexpr (S == 1) return sT1; else return sT2;
+  };
+  auto stageB = [&](auto st) __attribute__((always_inline)) { return stageA(st) + kPM * kPK; };
 
   // XCD-aware map: ids i, i + 8, i + 16, ... run on one XCD; consecutive ids of
   // that stream walk the column groups of one token tile.
@@ -78,41 +112,39 @@ __global__ __launch_bounds__(kPT, 2) void project_kernel(
   const int64_t nrows = beta_group ? H : H * D;  // rows of the matrix this group reads
   const uint16_t* Wm = beta_group ? u : Ww;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
 
-  uint4 ra[P][AL], rb[P][BL];  // chunk c is held in set c % P
-  const int nchunks = static_cast<int>(Dm / kPK);
-  auto gload = [&](int c, uint4 (&a)[AL], uint4 (&b)[BL]) {
+  // Direct-to-LDS sources.  Load i of this wave fills the 64 consecutive
+  // 16-byte LDS slots (i * kPW + wv) * 64 + lane of a tile; the lane fetches
+  // the logical chunk that belongs in its slot, from a clamped row.
+  const char* asrc[kALd];
+  const char* bsrc[kBLd];
 #pragma unroll
-    for (int p = 0; p < AL; ++p) {
-      const int idx = tid + kPT * p;
-      const int row = idx >> 3, seg = idx & 7;
-      const int64_t t = t0 + row;
-      a[p] = make_uint4(0u, 0u, 0u, 0u);
-      if (t < T) a[p] = *reinterpret_cast<const uint4*>(x + t * Dm + c * kPK + 8 * seg);
-    }
+  for (int i = 0; i < kALd; ++i) {
+    const int pos = (i * kPW + wv) * 64 + lane;
+    const int r = pos >> 3, jc = (pos & 7) ^ (r & 7);
+    const int64_t t = t0 + r < T ? t0 + r : T - 1;
+    asrc[i] = reinterpret_cast<const char*>(x + t * Dm) + 16 * jc;
+  }
 #pragma unroll
-    for (int p = 0; p < BL; ++p) {
-      const int idx = tid + kPT * p;
-      const int row = idx >> 3, seg = idx & 7;
-      const int64_t r = r0 + row;
-      b[p] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nrows) b[p] = *reinterpret_cast<const uint4*>(Wm + r * Dm + c * kPK + 8 * seg);
-    }
+  for (int i = 0; i < kBLd; ++i) {
+    const int pos = (i * kPW + wv) * 64 + lane;
+    const int r = pos >> 3, jc = (pos & 7) ^ (r & 7);
+    const int64_t rr = r0 + r < nrows ? r0 + r : nrows - 1;
+    bsrc[i] = reinterpret_cast<const char*>(Wm + rr * Dm) + 16 * jc;
+  }
+  auto dma_to = [&](int c, uint16_t* adst, uint16_t* bdst) __attribute__((always_inline)) {
+    const int64_t off = static_cast<int64_t>(c) * (kPK * 2);
+#pragma unroll
+    for (int i = 0; i < kALd; ++i)
+      __builtin_amdgcn_global_load_lds(asrc[i] + off, adst + (i * kPW + wv) * 512, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kBLd; ++i)
+      __builtin_amdgcn_global_load_lds(bsrc[i] + off, bdst + (i * kPW + wv) * 512, 16, 0, 0);
   };
-  auto lstore = [&](int s, const uint4 (&a)[AL], const uint4 (&b)[BL]) {
-#pragma unroll
-    for (int p = 0; p < AL; ++p) {
-      const int idx = tid + kPT * p;
-      *reinterpret_cast<uint4*>(&As[s][idx >> 3][8 * (idx & 7)]) = a[p];
-    }
-#pragma unroll
-    for (int p = 0; p < BL; ++p) {
-      const int idx = tid + kPT * p;
-      *reinterpret_cast<uint4*>(&Bs[s][idx >> 3][8 * (idx & 7)]) = b[p];
-    }
-  };
+  auto dma = [&](int c, auto st) __attribute__((always_inline)) { dma_to(c, stageA(st), stageB(st)); };
 
   f4 acc[2][NC];
 #pragma unroll
@@ -120,36 +152,63 @@ __global__ __launch_bounds__(kPT, 2) void project_kernel(
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // LDS element offsets of this lane's operand chunks: row 16 tile + lr, logical
+  // chunk 4 ks + lg at its swizzled slot (row & 7 == lr & 7 for every tile).
+  int aoff[2][2], boff[2];
 #pragma unroll
-  for (int q = 0; q < P; ++q)
-    if (q < nchunks) gload(q, ra[q], rb[q]);
-  lstore(0, ra[0], rb[0]);
-  __syncthreads();
-  for (int c0 = 0; c0 < nchunks; c0 += P) {
+  for (int ks = 0; ks < 2; ++ks) {
+    const int slot = ((4 * ks + lg) ^ (lr & 7)) * 8;
 #pragma unroll
-    for (int q = 0; q < P; ++q) {
-      const int c = c0 + q;
-      if (c >= nchunks) break;
-      const int s = c & 1;
-      // set q was written to LDS one step ago: it takes chunk c + P
-      if (c + P < nchunks) gload(c + P, ra[q], rb[q]);
+    for (int rt = 0; rt < 2; ++rt) aoff[rt][ks] = (32 * wv + 16 * rt + lr) * kPK + slot;
+    boff[ks] = lr * kPK + slot;
+  }
+
+  const int nchunks = NCH > 0 ? NCH : static_cast<int>(Dm / kPK);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  // One chunk: wait for its loads, publish it (and free the stage the chunk
+  // c + 2 loads go to), start those loads, multiply.
+  auto step = [&](int c, auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    if (c + 1 < nchunks)
+      wait_vm<NLD>();  // chunk c + 1's loads may still be in flight
+    else
+      wait_vm<0>();
+    asm volatile("s_barrier" ::: "memory");
+    if (c + 2 < nchunks) dma(c + 2, std::integral_constant<int, (S + 2) % 3>{});
+    const uint16_t* As = stageA(st);
+    const uint16_t* Bs = stageB(st);
 #pragma unroll
-      for (int ks = 0; ks < kPK / 32; ++ks) {
-        // lane (lg, lr): row lr of each 16-row tile, reduction elements 32 ks + 8 lg .. + 7
-        b8 af[2], bf[NC];
+    for (int ks = 0; ks < 2; ++ks) {
+      b8 af[2], bf[NC];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          af[rt] = *reinterpret_cast<const b8*>(&As[s][32 * wv + 16 * rt + lr][32 * ks + 8 * lg]);
+      for (int rt = 0; rt < 2; ++rt) af[rt] = *reinterpret_cast<const b8*>(As + aoff[rt][ks]);
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) bf[ct] = *reinterpret_cast<const b8*>(&Bs[s][16 * ct + lr][32 * ks + 8 * lg]);
+      for (int ct = 0; ct < NC; ++ct) bf[ct] = *reinterpret_cast<const b8*>(Bs + boff[ks] + 16 * ct * kPK);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-          for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = mfma::mmb16(af[rt], bf[ct], acc[rt][ct]);
-      }
-      if (c + 1 < nchunks) lstore(s ^ 1, ra[(q + 1) % P], rb[(q + 1) % P]);
-      __syncthreads();
+        for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = mfma::mmb16(af[rt], bf[ct], acc[rt][ct]);
     }
+  };
+
+  dma(0, S0{});
+  if (nchunks > 1) dma(1, S1{});
+  if constexpr (NCH > 0) {
+    static_for(std::make_integer_sequence<int, NCH>{}, [&](auto ic) __attribute__((always_inline)) {
+      constexpr int c = decltype(ic)::value;
+      step(c, std::integral_constant<int, c % 3>{});
+    });
+  } else {
+    int c0 = 0;
+    for (; c0 + 3 <= nchunks; c0 += 3) {
+      step(c0, S0{});
+      step(c0 + 1, S1{});
+      step(c0 + 2, S2{});
+    }
+    if (c0 < nchunks) step(c0, S0{});
+    if (c0 + 1 < nchunks) step(c0 + 1, S1{});
   }
 
   // Epilogue.  acc[rt][ct][i] is token 32 wv + 16 rt + 4 lg + i, column 16 ct + lr.
@@ -204,12 +263,24 @@ hipError_t launch_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d
   const auto* ws = static_cast<const uint16_t*>(Ww);
   const auto* us = static_cast<const uint16_t*>(u);
   auto* wo = static_cast<uint16_t*>(w_out);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kPT), 0, stream, T, L, H, Dm, ntiles, ncol, xs, ws, us, bias, beta_max,
+                       wo, beta_out);
+  };
+  auto pick = [&](auto dc) {
+    constexpr int DD = decltype(dc)::value;
+    switch (Dm) {
+      case 512: go(project_kernel<DD, 8>); break;
+      case 1024: go(project_kernel<DD, 16>); break;
+      case 2048: go(project_kernel<DD, 32>); break;
+      case 4096: go(project_kernel<DD, 64>); break;
+      default: go(project_kernel<DD, 0>); break;
+    }
+  };
   if (d == 64)
-    hipLaunchKernelGGL(project_kernel<64>, grid, dim3(kPT), 0, stream, T, L, H, Dm, ntiles, ncol, xs, ws, us, bias,
-                       beta_max, wo, beta_out);
+    pick(std::integral_constant<int, 64>{});
   else
-    hipLaunchKernelGGL(project_kernel<128>, grid, dim3(kPT), 0, stream, T, L, H, Dm, ntiles, ncol, xs, ws, us, bias,
-                       beta_max, wo, beta_out);
+    pick(std::integral_constant<int, 128>{});
   return hipGetLastError();
 }
 
