@@ -37,8 +37,11 @@ namespace path {
 namespace {
 
 constexpr int kPW = 8;             // waves
+constexpr int kRT = 256 / 16 / kPW;  // 16-token row tiles per wave
+constexpr int kNS = 3;             // LDS stages of the ring
+constexpr int kOcc = kPW * kNS > 16 ? 1 : 2;  // workgroups per CU that the LDS allows
 constexpr int kPT = 64 * kPW;      // threads
-constexpr int kPM = 32 * kPW;      // tokens per workgroup (32 per wave)
+constexpr int kPM = 16 * kRT * kPW;  // tokens per workgroup
 constexpr int kPK = 64;            // reduction chunk (bf16 elements: one 128-byte row)
 constexpr int kPN = 128;           // columns per workgroup
 constexpr int kALd = kPM * kPK / 8 / kPT;  // direct-to-LDS loads per thread per chunk, tokens
@@ -81,7 +84,7 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&&
 // writes (a loop merges that knowledge away and drains all loads before the
 // operand reads).  NCH = 0: any Dm, a loop over chunks.
 template <int D, int NCH>
-__global__ __launch_bounds__(kPT, 1) void project_kernel(
+__global__ __launch_bounds__(kPT, kOcc) void project_kernel(
     int64_t T, int64_t L, int64_t H, int64_t Dm, int ntiles, int ncol, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ Ww, const uint16_t* __restrict__ u, const float* __restrict__ bias,
     float beta_max, uint16_t* __restrict__ w_out, float* __restrict__ beta_out) {
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(kPT, 1) void project_kernel(
   // tell reads of one stage from loads still landing in another.
   // Stage s holds the token tile (kPM rows) followed by the weight tile (kPN rows).
   __shared__ __attribute__((aligned(1024))) uint16_t sT0[(kPM + kPN) * kPK], sT1[(kPM + kPN) * kPK],
-      sT2[(kPM + kPN) * kPK];
+      sT2[kNS > 2 ? (kPM + kPN) * kPK : 8];
   auto stageA = [&](auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     if constexpr (S == 0) return sT0; else if constexpr (S == 1) return sT1; else return sT2;
@@ -146,77 +149,76 @@ __global__ __launch_bounds__(kPT, 1) void project_kernel(
   };
   auto dma = [&](int c, auto st) __attribute__((always_inline)) { dma_to(c, stageA(st), stageB(st)); };
 
-  f4 acc[2][NC];
+  f4 acc[kRT][NC];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
 
   // LDS element offsets of this lane's operand chunks: row 16 tile + lr, logical
   // chunk 4 ks + lg at its swizzled slot (row & 7 == lr & 7 for every tile).
-  int aoff[2][2], boff[2];
+  int aoff[kRT][2], boff[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int slot = ((4 * ks + lg) ^ (lr & 7)) * 8;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) aoff[rt][ks] = (32 * wv + 16 * rt + lr) * kPK + slot;
+    for (int rt = 0; rt < kRT; ++rt) aoff[rt][ks] = (16 * kRT * wv + 16 * rt + lr) * kPK + slot;
     boff[ks] = lr * kPK + slot;
   }
 
   const int nchunks = NCH > 0 ? NCH : static_cast<int>(Dm / kPK);
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
   // One chunk: wait for its loads, publish it (and free the stage the chunk
   // c + 2 loads go to), start those loads, multiply.
   auto step = [&](int c, auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
-    if (c + 1 < nchunks)
+    if (kNS == 3 && c + 1 < nchunks)
       wait_vm<NLD>();  // chunk c + 1's loads may still be in flight
     else
       wait_vm<0>();
     asm volatile("s_barrier" ::: "memory");
-    if (c + 2 < nchunks) dma(c + 2, std::integral_constant<int, (S + 2) % 3>{});
+    if (c + kNS - 1 < nchunks) dma(c + kNS - 1, std::integral_constant<int, (S + kNS - 1) % kNS>{});
     const uint16_t* As = stageA(st);
     const uint16_t* Bs = stageB(st);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      b8 af[2], bf[NC];
+      b8 af[kRT], bf[NC];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) af[rt] = *reinterpret_cast<const b8*>(As + aoff[rt][ks]);
+      for (int rt = 0; rt < kRT; ++rt) af[rt] = *reinterpret_cast<const b8*>(As + aoff[rt][ks]);
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) bf[ct] = *reinterpret_cast<const b8*>(Bs + boff[ks] + 16 * ct * kPK);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) acc[rt][ct] = mfma::mmb16(af[rt], bf[ct], acc[rt][ct]);
     }
   };
 
   dma(0, S0{});
-  if (nchunks > 1) dma(1, S1{});
+  if (kNS == 3 && nchunks > 1) dma(1, S1{});
   if constexpr (NCH > 0) {
     static_for(std::make_integer_sequence<int, NCH>{}, [&](auto ic) __attribute__((always_inline)) {
       constexpr int c = decltype(ic)::value;
-      step(c, std::integral_constant<int, c % 3>{});
+      step(c, std::integral_constant<int, c % kNS>{});
     });
   } else {
     int c0 = 0;
-    for (; c0 + 3 <= nchunks; c0 += 3) {
-      step(c0, S0{});
-      step(c0 + 1, S1{});
-      step(c0 + 2, S2{});
-    }
-    if (c0 < nchunks) step(c0, S0{});
-    if (c0 + 1 < nchunks) step(c0 + 1, S1{});
+    for (; c0 + kNS <= nchunks; c0 += kNS)
+      static_for(std::make_integer_sequence<int, kNS>{}, [&](auto ic) __attribute__((always_inline)) {
+        step(c0 + decltype(ic)::value, ic);
+      });
+    static_for(std::make_integer_sequence<int, kNS - 1>{}, [&](auto ic) __attribute__((always_inline)) {
+      if (c0 + decltype(ic)::value < nchunks) step(c0 + decltype(ic)::value, ic);
+    });
   }
 
-  // Epilogue.  acc[rt][ct][i] is token 32 wv + 16 rt + 4 lg + i, column 16 ct + lr.
+  // Epilogue.  acc[rt][ct][i] is token 16 (kRT wv + rt) + 4 lg + i, column 16 ct + lr.
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 32 * wv + 16 * rt + 4 * lg + i;
+      const int64_t t = t0 + 16 * (kRT * wv + rt) + 4 * lg + i;
       const bool live = t < T;
       const int64_t bi = t / L, li = t - bi * L;
       if (!beta_group) {
