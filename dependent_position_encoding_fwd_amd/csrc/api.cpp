@@ -433,7 +433,7 @@ extern "C" int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t
     return PATH_ERR_SHAPE;
   if (!x || !Ww || !u || !bias || !w || !beta) return PATH_ERR_NULL;
   const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
-  if (misaligned(x) || misaligned(Ww) || misaligned(u)) return PATH_ERR_UNSUPPORTED;
+  if (misaligned(x) || misaligned(Ww) || misaligned(u) || misaligned(w)) return PATH_ERR_UNSUPPORTED;
   return hip_status(path::launch_project(B, L, Dm, H, d, x, Ww, u, bias, beta_max, w, beta, stream));
 }
 

@@ -46,6 +46,7 @@ constexpr int kPK = 64;            // reduction chunk (bf16 elements: one 128-by
 constexpr int kPN = 128;           // columns per workgroup
 constexpr int kALd = kPM * kPK / 8 / kPT;  // direct-to-LDS loads per thread per chunk, tokens
 constexpr int kBLd = kPN * kPK / 8 / kPT;  // the same, weight rows
+constexpr int kOP = 72;            // output staging row pitch (bf16): 144 bytes, 16-byte aligned rows
 static_assert(kALd * kPT * 8 == kPM * kPK && kBLd * kPT * 8 == kPN * kPK, "whole 16-byte chunks per thread");
 
 using mfma::b8;
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kPT, kOcc) void project_kernel(
     if constexpr (S == 0) return sT0; else if constexpr (S == 1) return sT1; else return sT2;
   };
   auto stageB = [&](auto st) __attribute__((always_inline)) { return stageA(st) + kPM * kPK; };
+  __shared__ __attribute__((aligned(16))) uint16_t sOut[kPW * 8 * kOP];  // output staging, 8 rows per wave
 
   // XCD-aware map: ids i, i + 8, i + 16, ... run on one XCD; consecutive ids of
   // that stream walk the column groups of one token tile.
@@ -214,38 +216,69 @@ __global__ __launch_bounds__(kPT, kOcc) void project_kernel(
   }
 
   // Epilogue.  acc[rt][ct][i] is token 16 (kRT wv + rt) + 4 lg + i, column 16 ct + lr.
+  if (!beta_group) {
+    // w: each head's row is scaled to unit length, rounded to bf16 and passed
+    // through this wave's slice of sOut (8 tokens x 64 columns at a time), so
+    // that every lane stores 16 contiguous bytes of one token's row.  The
+    // slice is private to the wave, whose LDS operations run in order.
+    uint16_t* so = sOut + wv * (8 * kOP);
+    const int rr = lane >> 3, seg = lane & 7;  // read-back: staged row, 16-byte segment
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
+    for (int rt = 0; rt < kRT; ++rt) {
+      float inv[kPN / D][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 16 * (kRT * wv + rt) + 4 * lg + i;
-      const bool live = t < T;
-      const int64_t bi = t / L, li = t - bi * L;
-      if (!beta_group) {
+      for (int hh = 0; hh < kPN / D; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < kPN / D; ++hh) {  // the heads of the group
+        for (int i = 0; i < 4; ++i) {
           float n2 = 0.f;
 #pragma unroll
           for (int ct = HT * hh; ct < HT * (hh + 1); ++ct) n2 = fmaf(acc[rt][ct][i], acc[rt][ct][i], n2);
-          n2 = sum16(n2);
-          const float inv = 1.f / fmaxf(sqrtf(n2), 1e-12f);
-          const int64_t h = r0 / D + hh;
-          if (live && h < H) {
-            uint16_t* dst = w_out + ((bi * H + h) * L + li) * D;
-#pragma unroll
-            for (int ct = HT * hh; ct < HT * (hh + 1); ++ct)
-              dst[16 * (ct - HT * hh) + lr] = f32_to_bf16(acc[rt][ct][i] * inv);
-          }
+          inv[hh][i] = 1.f / fmaxf(sqrtf(sum16(n2)), 1e-12f);
         }
-      } else if (live) {
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-          const int64_t h = r0 + 16 * ct + lr;
-          if (h < H) {
-            const float z = acc[rt][ct][i] + bias[h];
-            float beta = 2.f / (1.f + expf(-z));
-            if (beta_max > 0.f) beta = fminf(beta, beta_max);
-            beta_out[(bi * H + h) * L + li] = beta;
+      for (int half = 0; half < 2; ++half) {  // columns 64 half .. 64 half + 63 of the group
+        constexpr int QT = 4;                   // column tiles per half
+        const int hh = (64 * half) / D;         // head of the group these columns belong to
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {        // tokens 4 lg + 2 ip + {0, 1} of each lane group
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int q = 0; q < QT; ++q) {
+              const int i = 2 * ip + i2;
+              so[(2 * lg + i2) * kOP + 16 * q + lr] = f32_to_bf16(acc[rt][QT * half + q][i] * inv[hh][i]);
+            }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const uint4 v = *reinterpret_cast<const uint4*>(so + rr * kOP + 8 * seg);
+          const int64_t t = t0 + 16 * (kRT * wv + rt) + 4 * (rr >> 1) + 2 * ip + (rr & 1);
+          const int64_t h = r0 / D + hh;
+          if (t < T && h < H) {
+            const int64_t bi = t / L, li = t - bi * L;
+            *reinterpret_cast<uint4*>(w_out + ((bi * H + h) * L + li) * D + (64 * half) % D + 8 * seg) = v;
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 16 * (kRT * wv + rt) + 4 * lg + i;
+        if (t < T) {
+          const int64_t bi = t / L, li = t - bi * L;
+#pragma unroll
+          for (int ct = 0; ct < NC; ++ct) {
+            const int64_t h = r0 + 16 * ct + lr;
+            if (h < H) {
+              const float z = acc[rt][ct][i] + bias[h];
+              float beta = 2.f / (1.f + expf(-z));
+              if (beta_max > 0.f) beta = fminf(beta, beta_max);
+              beta_out[(bi * H + h) * L + li] = beta;
+            }
           }
         }
       }

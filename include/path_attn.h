@@ -250,12 +250,12 @@ int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float sca
  * taken (the attention workloads use unit-norm w).
  * Inputs (bf16): x [B,L,Dm] tokens; Ww [H,d,Dm] (row e of head h maps x to
  *   component e); u [H,Dm]; bias [H] fp32.  Dm must be a positive multiple of
- *   64 and d is 64 or 128.  x, Ww and u must be 16-byte aligned.
+ *   64 and d is 64 or 128.  x, Ww, u and w must be 16-byte aligned.
  * Outputs (caller-allocated): w [B,H,L,d] bf16, beta [B,H,L] fp32, in the
  *   layouts path_attn_fwd takes.
  * Errors: PATH_ERR_NULL for a null pointer, PATH_ERR_SHAPE for non-positive
  *   or overflowing sizes or Dm not a multiple of 64, PATH_ERR_UNSUPPORTED for
- *   another d or misaligned inputs; nothing is launched then.  PATH_ERR_HIP if
+ * *   another d or a misaligned pointer; nothing is launched then.  PATH_ERR_HIP if
  *   the launch fails.  Asynchronous on `stream`; allocates nothing.
  */
 int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d, const void* x, const void* Ww,

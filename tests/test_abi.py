@@ -117,9 +117,10 @@ def test_python_binding_rejects_cpu_tensors():
         pa.path_attn_fwd(x, x, x, x, b)
 
 
-def _proj(B=1, L=128, Dm=256, H=2, d=64, ptr=FAKE, x=None, bias=FAKE):
+def _proj(B=1, L=128, Dm=256, H=2, d=64, ptr=FAKE, x=None, bias=FAKE, w=None):
     xp = ptr if x is None else x
-    return pa.lib().path_project(B, L, Dm, H, d, xp, ptr, ptr, bias, 0.0, ptr, ptr, None)
+    wp = ptr if w is None else w
+    return pa.lib().path_project(B, L, Dm, H, d, xp, ptr, ptr, bias, 0.0, wp, ptr, None)
 
 
 def test_project_validation():
@@ -132,6 +133,7 @@ def test_project_validation():
     assert _proj(ptr=None) == NULL
     assert _proj(bias=None) == NULL
     assert _proj(x=ctypes.c_void_p(0x1008)) == UNSUP   # not 16-byte aligned
+    assert _proj(w=ctypes.c_void_p(0x1008)) == UNSUP   # w is written in 16-byte segments
 
 
 def _paged(B=2, H=2, d=64, dtype=1, npages=8, page=16, mp=4, maxlen=20, ptr=FAKE, ws=FAKE, wsb=1 << 30,
