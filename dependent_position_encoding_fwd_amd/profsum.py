@@ -294,7 +294,7 @@ def main():
         "| kernel | calls | avg us | share |",
         "|---|---|---|---|",
     ]
-    for name, calls, avg, pct in stats[:8]:
+    for name, calls, avg, pct in stats[:12]:
         lines.append(f"| {short(name)} | {calls} | {avg / 1e3:.1f} | {pct:.1f} % |")
     r = bs["roofline"]
     lines += [
