@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   uint16_t* Wb = WK;
   uint16_t* Kb = WK + C * RP;
   _Float16* NY = reinterpret_cast<_Float16*>(GY);  // [2][C*TP]
-  _Float16* NFT = reinterpret_cast<_Float16*>(WK); // [2][D*64] (pitch 64, no pad)
+  _Float16* NFT = reinterpret_cast<_Float16*>(WK); // [2][D*64] (pitch 64, no pad, swizzled chunks)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -430,14 +430,16 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     *reinterpret_cast<h8*>(&NY[off]) = -yb[kc].hi;
     *reinterpret_cast<h8*>(&NY[C * TP + off]) = -yb[kc].lo;
   }
-  // lane holds F[b = 16mt+4lg+i][e = 16et+ln] = F^T[e][b] -> -F^T rows (pitch 64, perm b)
+  // lane holds F[b = 16mt+4lg+i][e = 16et+ln] = F^T[e][b] -> -F^T rows (pitch 64, perm b;
+  // unpadded, so the 16-byte chunks of a row are swizzled to keep 16-row reads off one bank)
   HL fb[ET][2];
 #pragma unroll
   for (int j = 0; j < ET; ++j)
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       fb[j][kc] = split8(ft[j][2 * kc], ft[j][2 * kc + 1]);
-      const int off = (16 * (ET * wave + j) + ln) * 64 + 32 * kc + 8 * lg;
+      const int row = 16 * (ET * wave + j) + ln;
+      const int off = row * 64 + (((4 * kc + lg) ^ (row & 7)) << 3);  // 16-byte chunk j at slot j ^ (row & 7)
       *reinterpret_cast<h8*>(&NFT[off]) = -fb[j][kc].hi;
       *reinterpret_cast<h8*>(&NFT[D * 64 + off]) = -fb[j][kc].lo;
     }
@@ -571,7 +573,8 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
           sl = *reinterpret_cast<const h8*>(&NY[C * TP + off]);
         }
         if (x < DT) {
-          const int off = (16 * x + ln) * 64 + 32 * kc + 8 * lg;
+          const int row = 16 * x + ln;
+          const int off = row * 64 + (((4 * kc + lg) ^ (row & 7)) << 3);
           qh = *reinterpret_cast<const h8*>(&NFT[off]);
           ql = *reinterpret_cast<const h8*>(&NFT[D * 64 + off]);
         }
