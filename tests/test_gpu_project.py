@@ -40,7 +40,7 @@ def _check(x, Ww, u, b, w, beta, beta_max=None, tokens=None):
 
 @pytest.mark.parametrize("B,L,Dm,H,d", [(1, 200, 128, 3, 64), (2, 77, 256, 5, 128), (1, 1, 64, 1, 64),
                                         (1, 300, 192, 65, 64), (3, 128, 512, 16, 64), (1, 513, 320, 4, 64),
-                                        (2, 130, 2048, 16, 128)])
+                                        (2, 130, 2048, 16, 128), (1, 70, 4096, 2, 64)])
 def test_project_small(B, L, Dm, H, d):
     print(f"[project] B={B} L={L} Dm={Dm} H={H} d={d}", flush=True)
     x = synthetic.project_inputs(B, L, Dm, H, d, seed=B * 1000 + L + H)
