@@ -38,8 +38,7 @@ namespace {
 
 constexpr int kPW = 8;             // waves
 constexpr int kRT = 256 / 16 / kPW;  // 16-token row tiles per wave
-constexpr int kNS = 3;             // LDS stages of the ring
-constexpr int kOcc = kPW * kNS > 16 ? 1 : 2;  // workgroups per CU that the LDS allows
+constexpr int kNS = 3;             // LDS stages of the ring (2 or 3)
 constexpr int kPT = 64 * kPW;      // threads
 constexpr int kPM = 16 * kRT * kPW;  // tokens per workgroup
 constexpr int kPK = 64;            // reduction chunk (bf16 elements: one 128-byte row)
@@ -47,6 +46,12 @@ constexpr int kPN = 128;           // columns per workgroup
 constexpr int kALd = kPM * kPK / 8 / kPT;  // direct-to-LDS loads per thread per chunk, tokens
 constexpr int kBLd = kPN * kPK / 8 / kPT;  // the same, weight rows
 constexpr int kOP = 72;            // output staging row pitch (bf16): 144 bytes, 16-byte aligned rows
+// LDS bytes of a workgroup (ring stages, output staging) and the workgroups
+// per CU they leave room for in 160 KB: one, for the configuration above.
+constexpr int kLdsBytes = kNS * (kPM + kPN) * kPK * 2 + kPW * 8 * kOP * 2;
+constexpr int kOcc = 163840 / kLdsBytes;
+static_assert(kNS == 2 || kNS == 3, "ring depth");
+static_assert(kOcc >= 1, "the LDS of one workgroup must fit a CU");
 static_assert(kALd * kPT * 8 == kPM * kPK && kBLd * kPT * 8 == kPN * kPK, "whole 16-byte chunks per thread");
 
 using mfma::b8;
