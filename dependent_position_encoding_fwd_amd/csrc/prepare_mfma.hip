@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     _Float16* __restrict__ vt) {
   using G = PGeo<D>;
   constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
+  constexpr int GP = 68;  // row pitch (floats) of G in GY; 64 rows of it fit the C x TP floats
 
   // LDS (halfs unless noted).  WK holds W rows then K rows; it is reused for
   // -F^T rows once the products that read W and K rows are done.
@@ -254,7 +255,8 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     }
   }
   // Diagonal 16x16 blocks of G by columns in the quarter layout
-  // GY[t*64 + q*16 + u] = G[4u+q][t] (rows above t only); wave w holds block (w, w).
+  // GY[t*GP + q*16 + u] = G[4u+q][t] (rows above t only); wave w holds block (w, w).
+  // The row pitch GP = 68 (not 64) spreads the 64 lanes of a store over distinct banks.
   {
     const int t = 16 * wave + ln;
 #pragma unroll
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * mt + 4 * lg + i;
-          GY[t * 64 + (s & 3) * 16 + (s >> 2)] = (s < t) ? gt[mt][i] : 0.f;
+          GY[t * GP + (s & 3) * 16 + (s >> 2)] = (s < t) ? gt[mt][i] : 0.f;
         }
       }
   }
@@ -278,8 +280,12 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   // The block products are fp32 16x16x4 MFMAs.  Their operand B is the accumulator
   // layout of a 16x16 tile (lane (g, j) holds rows 4g..4g+3 of column j); the
   // reduction index of MFMA kc is then 4g + kc, which operand A (from LDS) follows.
-  constexpr int BP = 17;       // pitch (floats) of a 16x16 block in LDS
+  // A 16x16 block in LDS: element (r, c) at r * BP + (c ^ (r & 3)).  Pitch 20
+  // and the swizzle keep both operand orientations of the 16x16x4 products
+  // (16 rows x 4 columns a step apart, and its transpose) on 64 distinct banks.
+  constexpr int BP = 20;       // pitch (floats) of a 16x16 block in LDS
   constexpr int BS = 16 * BP;  // floats per block
+  auto bx = [](int r, int c) { return r * BP + (c ^ (r & 3)); };
   // The W and K rows are dead once the products are formed (the adjusted keys
   // read K again from global memory), so the blocks live in their space.
   float* SD = reinterpret_cast<float*>(WK);  // D_0..D_3
@@ -293,12 +299,12 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       bq[u] = bs[16 * I + 4 * u + qq];
       acc[u] = d[u] = 0.f;
     }
-    const float* gcol = GY + 16 * I * 64 + qq * 16 + 4 * I;  // + r*64: G[16I+4u+qq][16I+r], u = 0..3
-    f4 gc = *reinterpret_cast<const f4*>(gcol + 15 * 64), gn = *reinterpret_cast<const f4*>(gcol + 14 * 64);
+    const float* gcol = GY + 16 * I * GP + qq * 16 + 4 * I;  // + r*GP: G[16I+4u+qq][16I+r], u = 0..3
+    f4 gc = *reinterpret_cast<const f4*>(gcol + 15 * GP), gn = *reinterpret_cast<const f4*>(gcol + 14 * GP);
 #pragma unroll
     for (int r = 15; r >= 0; --r) {
       f4 gnn = gn;
-      if (r > 1) gnn = *reinterpret_cast<const f4*>(gcol + (r - 2) * 64);
+      if (r > 1) gnn = *reinterpret_cast<const f4*>(gcol + (r - 2) * GP);
       const int ur = r >> 2;
       float x = (r == c ? 1.f : 0.f) - bq[ur] * acc[ur];  // right on lanes qq == r % 4
       x = quad_bcast(x, r & 3);
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       gn = gnn;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) SD[I * BS + (4 * u + qq) * BP + c] = d[u];
+    for (int u = 0; u < 4; ++u) SD[I * BS + bx(4 * u + qq, c)] = d[u];
   }
   __syncthreads();
   const int K = wave;
@@ -322,12 +328,12 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
           const float b = bs[16 * I + 4 * lg + kc] * gt[I][kc];
-          const float av = SD[I * BS + ln * BP + 4 * lg + kc];
+          const float av = SD[I * BS + bx(ln, 4 * lg + kc)];
           e = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b, e, 0, 0, 0);
         }
         float* dst = SE + (I * (7 - I) / 2 + K - I - 1) * BS;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(4 * lg + i) * BP + ln] = -e[i];
+        for (int i = 0; i < 4; ++i) dst[bx(4 * lg + i, ln)] = -e[i];
       }
     }
   }
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     for (int I = 0; I < 4; ++I)
       if (I == J) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tc[I][i] = SD[J * BS + (4 * lg + i) * BP + ln];
+        for (int i = 0; i < 4; ++i) tc[I][i] = SD[J * BS + bx(4 * lg + i, ln)];
       }
 #pragma unroll
     for (int I = 2; I >= 0; --I) {
@@ -351,10 +357,10 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
         for (int Kb2 = I + 1; Kb2 < 4; ++Kb2) {
           if (Kb2 <= J) {
-            const float* ea = SE + (I * (7 - I) / 2 + Kb2 - I - 1) * BS + ln * BP + 4 * lg;
+            const float* ea = SE + (I * (7 - I) / 2 + Kb2 - I - 1) * BS;
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kc], tc[Kb2][kc], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[bx(ln, 4 * lg + kc)], tc[Kb2][kc], acc, 0, 0, 0);
           }
         }
         tc[I] = acc;
