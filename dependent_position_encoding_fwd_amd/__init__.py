@@ -115,6 +115,31 @@ def _check(t: torch.Tensor, name: str, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _outputs(q, out):
+    """(o, lse) for a forward on q: new tensors, or the caller's `out` after the
+    checks the C side cannot make (it only sees raw pointers)."""
+    B, H, L, d = q.shape
+    if out is None:
+        return torch.empty_like(q), torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    o, lse = out
+    _check(o, "o", q.dtype, (B, H, L, d))
+    _check(lse, "lse", torch.float32, (B, H, L))
+    if o.device != q.device or lse.device != q.device:
+        raise ValueError("o and lse must be on q's device")
+    return o, lse
+
+
+def _check_workspace(ws, q, nbytes=None):
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise TypeError("workspace must be a 1-D torch.uint8 tensor")
+    if ws.device != q.device:
+        raise ValueError("workspace must be on the inputs' device")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if nbytes is not None and ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} needed")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -154,10 +179,10 @@ def path_attn_fwd(q, k, v, w, beta, log_forget=None, scale=1.0, precision="auto"
 
     Returns (o [B,H,L,d] in the input dtype, lse [B,H,L] fp32)."""
     B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
-    o, lse = out if out is not None else (torch.empty_like(q),
-                                          torch.empty((B, H, L), dtype=torch.float32, device=q.device))
+    o, lse = _outputs(q, out)
     if workspace is None:
         workspace = fwd_workspace(q, log_forget)
+    _check_workspace(workspace, q)
     st = lib().path_attn_fwd(B, H, L, d, code, float(scale), PRECISION[precision], _ptr(q), _ptr(k), _ptr(v),
                              _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(o), _ptr(lse), _ptr(workspace),
                              int(workspace.numel()), _stream(q))
@@ -184,6 +209,7 @@ def path_attn_bwd(q, k, v, w, beta, o, lse, do, log_forget=None, scale=1.0, work
     nbytes = bwd_workspace_bytes(B, H, L, d, code, log_forget is not None)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q)
     st = lib().path_attn_bwd(B, H, L, d, code, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
                              _ptr(log_forget), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw),
                              _ptr(dbeta), _ptr(dlf), _ptr(workspace), int(workspace.numel()), _stream(q))
@@ -196,6 +222,7 @@ def path_fwd_stage_prepare(q, k, v, w, beta, log_forget=None, scale=1.0, precisi
     B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
     if workspace is None:
         workspace = fwd_workspace(q, log_forget)
+    _check_workspace(workspace, q)
     st = lib().path_fwd_stage_prepare(B, H, L, d, code, float(scale), PRECISION[precision], _ptr(q), _ptr(k),
                                       _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(workspace),
                                       int(workspace.numel()), _stream(q))
@@ -206,8 +233,8 @@ def path_fwd_stage_prepare(q, k, v, w, beta, log_forget=None, scale=1.0, precisi
 def path_fwd_stage_scan(q, k, v, w, beta, workspace, log_forget=None, scale=1.0, precision="auto", out=None):
     """Second stage of path_attn_fwd: the right-to-left scan from a prepared workspace."""
     B, H, L, d, code = _fwd_args(q, k, v, w, beta, log_forget)
-    o, lse = out if out is not None else (torch.empty_like(q),
-                                          torch.empty((B, H, L), dtype=torch.float32, device=q.device))
+    o, lse = _outputs(q, out)
+    _check_workspace(workspace, q)
     st = lib().path_fwd_stage_scan(B, H, L, d, code, float(scale), PRECISION[precision], _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(w), _ptr(beta), _ptr(log_forget), _ptr(o), _ptr(lse),
                                    _ptr(workspace), int(workspace.numel()), _stream(q))
@@ -275,6 +302,7 @@ def _decode(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, ca
     nbytes = decode_workspace_bytes(B, H, d, cache_len)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q_t.device)
+    _check_workspace(workspace, q_t)
     head = (B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t))
     tail = (int(cache_len), int(cap), _ptr(o), _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream(q_t))
     if fox:
@@ -330,6 +358,7 @@ def path_decode_step_paged(q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, page_ta
     nbytes = decode_workspace_bytes(B, H, d, max_cache_len)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q_t.device)
+    _check_workspace(workspace, q_t)
     st = lib().path_decode_step_paged(B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t),
                                       _ptr(w_t), _ptr(beta_t), _ptr(k_pages), _ptr(v_pages), int(num_pages),
                                       int(page_size), _ptr(page_table), int(max_pages), _ptr(cache_lens),

@@ -4,6 +4,7 @@
 #include "../../include/path_attn.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "launch.h"
@@ -48,10 +49,21 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t d, int64_t* BH, int64_t
   return PATH_OK;
 }
 
-// Logit budget (log2 units) under which the bf16 forward drops the lo terms
-// of a key block: |Qt|_max * |khat|_max * 2^-10 <= kAutoTau.
-constexpr float kAutoTau = 2e-3f;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Precision switch of the bf16 forward (AUTO).  With plain fp16 operands a
+// logit k.q takes d rounding errors of at most 2^-11 relative on each operand.
+// Modelled as independent and uniform, their sum has the rms
+//     2^-11 sqrt(2/3) |q| |k| / sqrt(d),
+// sqrt(d) below the worst case (all errors aligned).  AUTO drops a key block's
+// lo terms while this estimate, taken with the largest transported query norm
+// of the tile and the largest key norm of the head, is at most half the lse
+// tolerance (kAutoRmsNats).  The scan kernels test
+//     |Qt|_max |khat|_max 2^-10 > tau
+// so tau = kAutoRmsNats log2(e) sqrt(6) sqrt(d).  This is an estimate, not a
+// bound: ACCURATE runs the split everywhere.
+constexpr float kAutoRmsNats = 0.5e-3f;
+float auto_tau(int64_t d) { return kAutoRmsNats * kLog2e * 2.449489743f * sqrtf(static_cast<float>(d)); }
 
 // Workspace of the forward.  fp32 inputs: khat, pT (fp32) and cum.  bf16
 // inputs: the matrix-core layout written by the prepare stage.
@@ -206,7 +218,7 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
   // one matrix-core scan per head dimension (64 or 128; check_d rejects others)
   auto scan = d == 64 ? path::launch_scan64 : path::launch_scan128;
   return hip_status(scan(
-      B * H, L, precision == PATH_PREC_ACCURATE ? 1 : 0, kAutoTau,
+      B * H, L, precision == PATH_PREC_ACCURATE ? 1 : 0, auto_tau(d),
       reinterpret_cast<const _Float16*>(ws + a.lay.vt), reinterpret_cast<const _Float16*>(ws + a.lay.khl),
       reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
       reinterpret_cast<const float*>(ws + a.lay.qhat),

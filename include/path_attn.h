@@ -53,9 +53,14 @@ typedef enum { PATH_F32 = 0, PATH_BF16 = 1 } path_dtype;
 /*
  * Precision policy of the bf16 forward.  ACCURATE feeds every matrix-core
  * product that involves a transported query or key with a two-term (hi + lo)
- * split of its fp32 value.  AUTO uses the split only where a run-time bound on
- * the logit rounding error exceeds a fixed budget and plain half precision
- * elsewhere.  fp32 inputs always take the fp32 path and ignore this flag.
+ * split of its fp32 value, on every key block.  AUTO uses the split only on
+ * the key blocks where a run-time estimate of the logit rounding error of
+ * plain half-precision operands (the rms of d independent roundings, with the
+ * tile's largest transported query norm and the head's largest key norm)
+ * exceeds half the lse tolerance of 1e-3; transported queries shrink block by
+ * block, so these are the blocks nearest the query.  AUTO's switch is an
+ * estimate, not a bound; ACCURATE is the mode with no such assumption.
+ * fp32 inputs always take the fp32 path and ignore this flag.
  */
 typedef enum { PATH_PREC_ACCURATE = 0, PATH_PREC_AUTO = 1 } path_precision;
 

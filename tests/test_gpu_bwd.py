@@ -8,11 +8,12 @@ largest element error is at most tol * max|G_ref|, with tol = 1e-4 for fp32
 storage and 2e-2 for bf16 storage (the gradients are rounded to bf16, and the
 softmax row terms D_i = dO_i . o_i use the bf16-rounded o).
 
-A gradient can vanish exactly: with one key (L = 1) the softmax weight is 1
-whatever the logit, so dq, dk, dw and dbeta are 0 and the kernel returns the
-fp32 rounding of dS = p (dO . v - dO . o), two equal dot products summed in
-different orders.  A relative bar is undefined there, so max|G_ref| is floored
-at 1 % of max|dv_ref|, the scale of the incoming gradient p^T dO.
+A gradient tensor can vanish exactly: with one key (L = 1) the softmax weight
+is 1 whatever the logit, so dq, dk, dw and dbeta are 0 and the kernel returns
+the fp32 rounding of dS = p (dO . v - dO . o), two equal dot products summed
+in different orders.  A relative bar is undefined there, so for a reference
+tensor that is exactly zero (and only then) the bar is tol times 1 % of
+max|dv_ref|, the scale of the incoming gradient p^T dO.
 """
 import numpy as np
 import pytest
@@ -35,7 +36,7 @@ def _cmp(name, got, ref, tol, floor):
     err = float(np.max(np.abs(_np(got) - ref))) if ref.size else 0.0
     mag = float(np.max(np.abs(ref))) if ref.size else 0.0
     print(f"  {name}: max|err|={err:.3e} max|ref|={mag:.3e} ratio={err / max(mag, 1e-30):.2e}", flush=True)
-    assert err <= tol * max(mag, floor), (name, err, mag, floor)
+    assert err <= tol * (mag if mag > 0 else floor), (name, err, mag, floor)
 
 
 def _bwd_case(B, H, L, d, dtype, scale, seed, fox, chain_forward=False):

@@ -200,12 +200,6 @@ def test_decode_small(dtype, d, n):
     _decode_case(2, 3, d, n, n + 7, dtype, 1.0, seed=n + d)
 
 
-def test_decode_config5_full_sampled():
-    c = synthetic.CONFIGS[5]
-    heads = [(0, 0), (17, 5), (40, 11), (63, 15)]
-    _decode_case(c.B, c.H, c.d, c.cache_len, c.capacity, c.dtype, c.scale, c.seed, heads)
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("n", [0, 1, 100, 1500])
@@ -221,13 +215,6 @@ def test_decode_fox_open_and_closed_gate(log_f_t):
     if log_f_t < -100:
         x = synthetic.decode_inputs(2, 2, 64, 700, 720, "f32", 5, fox=True)
         assert torch.allclose(o.cpu(), x["v_t"], atol=1e-6)
-
-
-def test_decode_fox_config5_full_sampled():
-    """The cache-8192 decode workload (B=64, H=16, d=64, bf16) with forget gates."""
-    c = synthetic.CONFIGS[5]
-    heads = [(0, 0), (17, 5), (40, 11), (63, 15)]
-    _decode_case(c.B, c.H, c.d, c.cache_len, c.capacity, c.dtype, c.scale, c.seed, heads, fox=True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
