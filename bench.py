@@ -49,7 +49,9 @@ computes in fp32 (matrix cores and vector ALUs), so its peak is MI355X's fp32
 The paged decode step (`path_decode_step_paged`) runs on the same caches
 scattered into 256-slot pages in a seeded random page order, every sequence at
 length 8192, and is reported in `decode_paged` on the decode's bytes (the page
-table adds 132 bytes per head), median of 50 launches after 20.
+table adds 132 bytes per head), median of 50 launches after 20.  The gated
+paged step (`path_decode_step_paged_fox`, the forget-gate prefix cache in the
+same pages) follows in `decode_paged_fox`, on those bytes plus 4 per cached key.
 
 The projection prologue (`path_project`: w and beta of every head from the
 tokens, model width Dm = H d) runs on the forward workload's tokens and is
@@ -210,7 +212,7 @@ def main():
                 "kernel": f"scan{cf.d}_kernel (right-to-left scan, d={cf.d})", "flops_per_launch": F,
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
-    paged = paged_leg(pa, xd, cd, dbytes)
+    paged, paged_fox = paged_leg(pa, xd, gd, cd, dbytes)
     bwd = None if args.no_bwd else bwd_leg(pa, fargs, gates, cf, o, lse)
     proj = project_leg(pa, cf)
 
@@ -238,6 +240,7 @@ def main():
                        "frac_hbm_peak": round(fox_gbs / PEAK_HBM_GBS, 4),
                        "what": "gated decode step, same cache, forget-gate prefix cache (fp32)"},
         "decode_paged": paged,
+        "decode_paged_fox": paged_fox,
         "bwd": bwd,
         "project": proj,
         "roofline": roofline,
@@ -275,9 +278,11 @@ def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):
                     f"{', log forget gates' if gates is not None else ''}), seeded dO, median of {steps}"}
 
 
-def paged_leg(pa, xd, cd, dbytes, page=256, warmup=20, steps=50):
-    """Times path_decode_step_paged on the decode workload's caches, scattered
-    into `page`-slot pages in a seeded random order (lengths all cache_len)."""
+def paged_leg(pa, xd, gd, cd, dbytes, page=256, warmup=20, steps=50):
+    """Times path_decode_step_paged and path_decode_step_paged_fox on the decode
+    workload's caches, scattered into `page`-slot pages in a seeded random order
+    (lengths all cache_len); the gated step reads the prefix cache from the same
+    pages.  Returns the two result records."""
     import torch
 
     B, H, n, d = cd.B, cd.H, cd.cache_len, cd.d
@@ -287,9 +292,10 @@ def paged_leg(pa, xd, cd, dbytes, page=256, warmup=20, steps=50):
     table = perm.view(B, mp).to(torch.int32)
 
     def scatter(c):
-        padded = torch.zeros(B, H, mp * page, d, dtype=c.dtype, device=c.device)
+        e = c.shape[3]
+        padded = torch.zeros(B, H, mp * page, e, dtype=c.dtype, device=c.device)
         padded[:, :, : c.shape[2]] = c
-        logical = padded.view(B, H, mp, page, d).permute(0, 2, 1, 3, 4).reshape(npg, H, page, d)
+        logical = padded.view(B, H, mp, page, e).permute(0, 2, 1, 3, 4).reshape(npg, H, page, e)
         pages = torch.empty_like(logical)
         pages[perm] = logical
         return pages
@@ -297,21 +303,38 @@ def paged_leg(pa, xd, cd, dbytes, page=256, warmup=20, steps=50):
     kp, vp = scatter(xd["k_cache"]), scatter(xd["v_cache"])
     lens = torch.full((B,), n, dtype=torch.int32, device="cuda:0")
     ws = torch.empty(max(256, pa.decode_workspace_bytes(B, H, d, n)), dtype=torch.uint8, device="cuda:0")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for k in range(warmup + steps):
-        if k >= warmup:
-            evs[k - warmup][0].record()
-        pa.path_decode_step_paged(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], kp, vp, table, lens, n,
-                                  scale=cd.scale, workspace=ws)
-        if k >= warmup:
-            evs[k - warmup][1].record()
-    torch.cuda.synchronize()
-    ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    # gated: the prefix cache in the same pages (one fp32 per key slot)
+    cum = torch.cumsum(gd["log_f_cache"].double(), dim=-1).float().to("cuda:0")
+    cp = scatter(cum.unsqueeze(-1)).squeeze(-1).contiguous()
+    log_f_t = gd["log_f_t"].to("cuda:0")
+
+    def timed(step):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(warmup + steps):
+            if k >= warmup:
+                evs[k - warmup][0].record()
+            step()
+            if k >= warmup:
+                evs[k - warmup][1].record()
+        torch.cuda.synchronize()
+        return statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+
+    ms = timed(lambda: pa.path_decode_step_paged(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], kp, vp,
+                                                 table, lens, n, scale=cd.scale, workspace=ws))
+    fms = timed(lambda: pa.path_decode_step_paged_fox(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"],
+                                                      log_f_t, kp, vp, cp, table, lens, n, scale=cd.scale,
+                                                      workspace=ws))
     gbs = dbytes / (ms * 1e-3) / 1e9
-    del kp, vp
-    return {"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "bytes_model": dbytes,
-            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "what": f"paged decode step, same caches in {page}-slot pages (random page order), length {n} each"}
+    fbytes = dbytes + 4 * B * H * n
+    fgbs = fbytes / (fms * 1e-3) / 1e9
+    del kp, vp, cp
+    return ({"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "bytes_model": dbytes,
+             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+             "what": f"paged decode step, same caches in {page}-slot pages (random page order), length {n} each"},
+            {"ms": round(fms, 4), "GB_per_s": round(fgbs, 1), "bytes_model": fbytes,
+             "frac_hbm_peak": round(fgbs / PEAK_HBM_GBS, 4),
+             "what": f"gated paged decode step, same pages plus the forget-gate prefix cache in the same "
+                     f"{page}-slot pages"})
 
 
 def project_leg(pa, cf, warmup=20, steps=50):
@@ -341,6 +364,18 @@ def project_leg(pa, cf, warmup=20, steps=50):
             "what": f"path_project, T={T} tokens, Dm={Dm}, H={cf.H}, d={cf.d} (bf16 in, w bf16 + beta fp32 out)"}
 
 
+def cpu_model():
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cf, budget_s=10.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     whole heads (all L query rows) in order until `budget_s` of wall time is spent."""
@@ -362,6 +397,7 @@ def cpu_baseline(cf, budget_s=10.0):
             break
     F = flops_path(1, done, cf.L, cf.d)
     return {"value": round(F / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} of {len(heads)} heads (all {cf.L} query rows each) of the L={cf.L} workload, "
                       f"{dt:.1f} s of oracle wall time"}
 

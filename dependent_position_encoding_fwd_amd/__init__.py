@@ -29,7 +29,8 @@ STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UN
 EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
            "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
            "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox",
-           "path_bwd_workspace_bytes", "path_attn_bwd", "path_project", "path_decode_step_paged"]
+           "path_bwd_workspace_bytes", "path_attn_bwd", "path_project", "path_decode_step_paged",
+           "path_decode_step_paged_fox"]
 
 _lib = None
 _I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.path_decode_step_paged.restype = _INT
         L.path_decode_step_paged.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 7 + [_I64, _I64, _VP, _I64, _VP,
                                              _I64, _VP, _VP, _VP, _SZ, _VP])
+        L.path_decode_step_paged_fox.restype = _INT
+        L.path_decode_step_paged_fox.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 9 + [_I64, _I64, _VP, _I64,
+                                                 _VP, _I64, _VP, _VP, _VP, _SZ, _VP])
         L.path_project.restype = _INT
         L.path_project.argtypes = [_I64] * 5 + [_VP] * 4 + [_F] + [_VP, _VP, _VP]
         L.path_decode_step_fox.restype = _INT
@@ -342,6 +346,21 @@ def path_decode_step_paged(q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, page_ta
     k_pages, v_pages [num_pages,H,page_size,d] (updated in place, new token appended);
     page_table [B,max_pages] int32 and cache_lens [B] int32 on the device; max_cache_len
     (host int) bounds every cache_lens[b].  Returns (o [B,H,d], lse [B,H] fp32)."""
+    return _paged(q_t, k_t, v_t, w_t, beta_t, None, k_pages, v_pages, None, page_table, cache_lens, max_cache_len,
+                  scale, workspace)
+
+
+def path_decode_step_paged_fox(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_pages, v_pages, cum_pages, page_table,
+                               cache_lens, max_cache_len, scale=1.0, workspace=None):
+    """Gated (PaTH-FoX) decode step over a paged cache: path_decode_step_paged plus
+    log_f_t [B,H] fp32 and the gate-prefix pages cum_pages [num_pages,H,page_size]
+    fp32 (c_j at key j's slot; the step writes c_t at the new key's slot)."""
+    return _paged(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_pages, v_pages, cum_pages, page_table, cache_lens,
+                  max_cache_len, scale, workspace)
+
+
+def _paged(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_pages, v_pages, cum_pages, page_table, cache_lens, max_cache_len,
+           scale, workspace):
     B, H, d = q_t.shape
     num_pages, _, page_size, _ = k_pages.shape
     max_pages = page_table.shape[1]
@@ -353,16 +372,24 @@ def path_decode_step_paged(q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, page_ta
     _check(v_pages, "v_pages", dt, (num_pages, H, page_size, d))
     _check(page_table, "page_table", torch.int32, (B, max_pages))
     _check(cache_lens, "cache_lens", torch.int32, (B,))
+    fox = log_f_t is not None
+    if fox:
+        _check(log_f_t, "log_f_t", torch.float32, (B, H))
+        _check(cum_pages, "cum_pages", torch.float32, (num_pages, H, page_size))
     o = torch.empty_like(q_t)
     lse = torch.empty((B, H), dtype=torch.float32, device=q_t.device)
     nbytes = decode_workspace_bytes(B, H, d, max_cache_len)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q_t.device)
     _check_workspace(workspace, q_t)
-    st = lib().path_decode_step_paged(B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t),
-                                      _ptr(w_t), _ptr(beta_t), _ptr(k_pages), _ptr(v_pages), int(num_pages),
-                                      int(page_size), _ptr(page_table), int(max_pages), _ptr(cache_lens),
-                                      int(max_cache_len), _ptr(o), _ptr(lse), _ptr(workspace),
-                                      int(workspace.numel()), _stream(q_t))
-    _raise(st, "path_decode_step_paged")
+    head = (B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(w_t), _ptr(beta_t))
+    tail = (int(num_pages), int(page_size), _ptr(page_table), int(max_pages), _ptr(cache_lens), int(max_cache_len),
+            _ptr(o), _ptr(lse), _ptr(workspace), int(workspace.numel()), _stream(q_t))
+    if fox:
+        st = lib().path_decode_step_paged_fox(*head, _ptr(log_f_t), _ptr(k_pages), _ptr(v_pages), _ptr(cum_pages),
+                                              *tail)
+        _raise(st, "path_decode_step_paged_fox")
+    else:
+        st = lib().path_decode_step_paged(*head, _ptr(k_pages), _ptr(v_pages), *tail)
+        _raise(st, "path_decode_step_paged")
     return o, lse

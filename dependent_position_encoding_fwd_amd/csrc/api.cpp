@@ -449,12 +449,13 @@ extern "C" int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t
   return hip_status(path::launch_project(B, L, Dm, H, d, x, Ww, u, bias, beta_max, w, beta, stream));
 }
 
-extern "C" int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
-                                      const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                                      void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
-                                      const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
-                                      int64_t max_cache_len, void* o, float* lse, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+int paged_common(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t, const void* k_t,
+                 const void* v_t, const void* w_t, const float* beta_t, const float* log_f_t, void* k_pages,
+                 void* v_pages, float* cum_pages, int64_t num_pages, int64_t page_size, const int32_t* page_table,
+                 int64_t max_pages, const int32_t* cache_lens, int64_t max_cache_len, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_d(d))) return st;
@@ -474,7 +475,34 @@ extern "C" int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype
   const size_t need = path_decode_workspace_bytes(B, H, d, max_cache_len);
   if (!workspace || need == 0 || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return PATH_ERR_WORKSPACE;
-  return hip_status(path::launch_decode_paged(dtype, B, H, d, scale, q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages,
-                                              num_pages, page_size, page_table, max_pages, cache_lens,
-                                              max_cache_len, o, lse, static_cast<float*>(workspace), stream));
+  return hip_status(path::launch_decode_paged(dtype, B, H, d, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_pages,
+                                              v_pages, cum_pages, num_pages, page_size, page_table, max_pages,
+                                              cache_lens, max_cache_len, o, lse, static_cast<float*>(workspace),
+                                              stream));
+}
+
+}  // namespace
+
+extern "C" int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                                      const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                                      void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
+                                      const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
+                                      int64_t max_cache_len, void* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return paged_common(B, H, d, dtype, scale, q_t, k_t, v_t, w_t, beta_t, nullptr, k_pages, v_pages, nullptr,
+                      num_pages, page_size, page_table, max_pages, cache_lens, max_cache_len, o, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" int path_decode_step_paged_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale,
+                                          const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                                          const float* beta_t, const float* log_f_t, void* k_pages, void* v_pages,
+                                          float* cum_pages, int64_t num_pages, int64_t page_size,
+                                          const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
+                                          int64_t max_cache_len, void* o, float* lse, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  if (!log_f_t || !cum_pages) return PATH_ERR_NULL;
+  return paged_common(B, H, d, dtype, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_pages, v_pages, cum_pages,
+                      num_pages, page_size, page_table, max_pages, cache_lens, max_cache_len, o, lse, workspace,
+                      workspace_bytes, stream);
 }

@@ -22,9 +22,11 @@
 // Gated variant (FOX) [same summary, §2 "Extensões: PaTH-FoX"]: the logit of
 // cached key j gains the forget-gate sum over j < s <= t, kept as a difference
 // of running prefixes c_t - c_j.  The prefix of every cached key sits in an
-// fp32 cache beside the key cache (4 bytes per key against 2 d-element rows),
-// is fetched in the same pipelined group as the key and value rows, and the
-// step appends c_t = c_{t-1} + log f_t for the new key, whose own bias is 0.
+// fp32 cache beside the key cache (4 bytes per key against 2 d-element rows)
+// with the key cache's row map (contiguous [B*H, capacity] or paged
+// [num_pages, H, page]), is fetched in the same pipelined group as the key and
+// value rows, and the step appends c_t = c_{t-1} + log f_t for the new key,
+// whose own bias is 0.
 #include <math.h>
 
 #include <type_traits>
@@ -201,12 +203,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
   constexpr float kLog2e = 1.4426950408889634f;
   const float scale2 = scale * kLog2e;  // logits in log2 units
   const int64_t len = rows.length(bh);
-  const float* cbase = nullptr;
   float ct = 0.f;
   if constexpr (FOX) {
-    // c_t of the new query; the gated kernel only runs with cache_len >= 1
-    cbase = cum_cache + bh * rows.capacity;
-    ct = cbase[len - 1] + log_f_t[bh];
+    // c_t of the new query.  The prefix cache has the key cache's row map (one
+    // float per key row); a sequence with no keys has no chunk work to bias.
+    const int64_t prow = len > 0 ? rows.row(bh, len - 1) : -1;
+    ct = (rows.ok(prow) ? cum_cache[prow] : 0.f) + log_f_t[bh];
   }
 
   const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
@@ -240,13 +242,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
         const int64_t rw = map.row(jc);
         kr[u] = __builtin_nontemporal_load(&kraw[rw * LPK + sub]);
         vr[u] = __builtin_nontemporal_load(&vraw[rw * LPK + sub]);
-        if constexpr (FOX) cr[u] = cbase[jc];
+        if constexpr (FOX) cr[u] = cum_cache[rw];
       } else {
         const int64_t rw = j < j1 ? map.row(j) : -1;
         const bool ok = rows.ok(rw);
         kr[u] = __builtin_nontemporal_load(ok ? &kraw[rw * LPK + sub] : trash_slot);
         vr[u] = __builtin_nontemporal_load(ok ? &vraw[rw * LPK + sub] : trash_slot);
-        cr[u] = 0.f;
+        // a slot that is not a key reads the trash slot's first word; its logit is discarded
+        if constexpr (FOX) cr[u] = *(ok ? &cum_cache[rw] : trash);
+        else cr[u] = 0.f;
       }
     }
   };
@@ -450,8 +454,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (lane == 0) {
     lse[bh] = (mm + __log2f(ll)) * 0.69314718055994531f;
     if constexpr (FOX) {
-      float* cbase = cum_cache + bh * rows.capacity;
-      cbase[len] = (len > 0 ? cbase[len - 1] : 0.f) + log_f_t[bh];
+      // c_t at the new key's row of the prefix cache (same row map as the keys)
+      const int64_t prow = len > 0 ? rows.row(bh, len - 1) : -1;
+      if (rows.ok(slot)) cum_cache[slot] = (rows.ok(prow) ? cum_cache[prow] : 0.f) + log_f_t[bh];
     }
   }
 }
@@ -510,34 +515,35 @@ hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const vo
                                nullptr, cache_len, capacity, o, lse, partials, stream);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FOX>
 static hipError_t launch_dec_paged_t(int64_t BH, float scale, const void* q_t, const void* k_t, const void* v_t,
-                                     const void* w_t, const float* beta_t, void* k_pages, void* v_pages,
-                                     const PagedRows& rows, int64_t max_len, void* o, float* lse, float* partials,
-                                     hipStream_t stream) {
+                                     const void* w_t, const float* beta_t, const float* log_f_t, void* k_pages,
+                                     void* v_pages, float* cum_pages, const PagedRows& rows, int64_t max_len,
+                                     void* o, float* lse, float* partials, hipStream_t stream) {
   const int nchunks = static_cast<int>(decode_num_chunks(max_len));
   float* trash = partials;
   partials += kDecTrashFloats;
   if (nchunks > 0) {
-    hipLaunchKernelGGL((decode_chunk_kernel<T, D, false, PagedRows>), dim3(static_cast<unsigned>(BH * nchunks)),
+    hipLaunchKernelGGL((decode_chunk_kernel<T, D, FOX, PagedRows>), dim3(static_cast<unsigned>(BH * nchunks)),
                        dim3(kDecThreads), 0, stream, rows, nchunks, scale, static_cast<const T*>(q_t),
-                       static_cast<const T*>(w_t), beta_t, nullptr, static_cast<T*>(k_pages),
-                       static_cast<const T*>(v_pages), nullptr, trash, partials);
+                       static_cast<const T*>(w_t), beta_t, log_f_t, static_cast<T*>(k_pages),
+                       static_cast<const T*>(v_pages), cum_pages, trash, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, false, PagedRows>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, FOX, PagedRows>), dim3(static_cast<unsigned>(BH)), dim3(64), 0,
                      stream, rows, nchunks, scale, static_cast<const T*>(q_t), static_cast<const T*>(k_t),
-                     static_cast<const T*>(v_t), nullptr, static_cast<T*>(k_pages), static_cast<T*>(v_pages),
-                     nullptr, partials, static_cast<T*>(o), lse);
+                     static_cast<const T*>(v_t), log_f_t, static_cast<T*>(k_pages), static_cast<T*>(v_pages),
+                     cum_pages, partials, static_cast<T*>(o), lse);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_paged(int dtype, int64_t B, int64_t H, int64_t d, float scale, const void* q_t,
                                const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                               void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
-                               const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
-                               int64_t max_len, void* o, float* lse, float* partials, hipStream_t stream) {
+                               const float* log_f_t, void* k_pages, void* v_pages, float* cum_pages,
+                               int64_t num_pages, int64_t page_size, const int32_t* page_table, int64_t max_pages,
+                               const int32_t* cache_lens, int64_t max_len, void* o, float* lse, float* partials,
+                               hipStream_t stream) {
   int shift = -1;
   if ((page_size & (page_size - 1)) == 0)
     for (shift = 0; (int64_t(1) << shift) < page_size; ++shift) {
@@ -545,11 +551,16 @@ hipError_t launch_decode_paged(int dtype, int64_t B, int64_t H, int64_t d, float
   const PagedRows rows{page_table, cache_lens, H, max_pages, num_pages, page_size, shift};
   const int64_t BH = B * H;
   auto go = [&](auto launch) {
-    return launch(BH, scale, q_t, k_t, v_t, w_t, beta_t, k_pages, v_pages, rows, max_len, o, lse, partials,
-                  stream);
+    return launch(BH, scale, q_t, k_t, v_t, w_t, beta_t, log_f_t, k_pages, v_pages, cum_pages, rows, max_len, o,
+                  lse, partials, stream);
   };
-  if (dtype == 0) return d == 64 ? go(launch_dec_paged_t<float, 64>) : go(launch_dec_paged_t<float, 128>);
-  return d == 64 ? go(launch_dec_paged_t<bf16_t, 64>) : go(launch_dec_paged_t<bf16_t, 128>);
+  if (log_f_t) {
+    if (dtype == 0)
+      return d == 64 ? go(launch_dec_paged_t<float, 64, true>) : go(launch_dec_paged_t<float, 128, true>);
+    return d == 64 ? go(launch_dec_paged_t<bf16_t, 64, true>) : go(launch_dec_paged_t<bf16_t, 128, true>);
+  }
+  if (dtype == 0) return d == 64 ? go(launch_dec_paged_t<float, 64, false>) : go(launch_dec_paged_t<float, 128, false>);
+  return d == 64 ? go(launch_dec_paged_t<bf16_t, 64, false>) : go(launch_dec_paged_t<bf16_t, 128, false>);
 }
 
 }  // namespace path

@@ -64,11 +64,15 @@ hipError_t launch_decode(int dtype, int64_t BH, int64_t d, float scale, const vo
 // Decode over a paged cache: pages [num_pages, H, page_size, d]; sequence b's
 // logical page lp is page_table[b * max_pages + lp] and its length
 // cache_lens[b] (both int32, device); the grid covers max_len keys.
+// With log_f_t != null the step is gated: cum_pages [num_pages, H, page_size]
+// fp32 holds the gate prefixes of the cached keys in the key pages' layout and
+// receives c_t at the new key's slot.
 hipError_t launch_decode_paged(int dtype, int64_t B, int64_t H, int64_t d, float scale, const void* q_t,
                                const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                               void* k_pages, void* v_pages, int64_t num_pages, int64_t page_size,
-                               const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
-                               int64_t max_len, void* o, float* lse, float* partials, hipStream_t stream);
+                               const float* log_f_t, void* k_pages, void* v_pages, float* cum_pages,
+                               int64_t num_pages, int64_t page_size, const int32_t* page_table, int64_t max_pages,
+                               const int32_t* cache_lens, int64_t max_len, void* o, float* lse, float* partials,
+                               hipStream_t stream);
 
 // Projection prologue (bf16 matrix cores): w [B,H,L,d] bf16 and beta [B,H,L]
 // fp32 from tokens x [B,L,Dm], Ww [H,d,Dm], u [H,Dm] (bf16) and bias [H].

@@ -229,6 +229,11 @@ int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale
  *   is outside [0, num_pages) or whose logical page is >= max_pages is skipped
  *   (never read or written), so a bad table gives wrong results, not an
  *   out-of-bounds access.
+ * Each physical page may appear at most once in the whole page table.  The
+ *   update k_j <- H_t k_j is per sequence (H_t is that sequence's transition),
+ *   so a page shared by two sequences (a shared prompt prefix) would receive
+ *   both transitions, and a page mapped twice would be updated twice
+ *   concurrently; PaTH's in-place cache cannot share pages.
  * Workspace: path_decode_workspace_bytes(B, H, d, max_cache_len).
  * Errors: as path_decode_step (PATH_ERR_CAPACITY when max_cache_len >=
  *   max_pages * page_size); PATH_ERR_SHAPE for page_size < 1, num_pages < 1,
@@ -241,6 +246,31 @@ int path_decode_step_paged(int64_t B, int64_t H, int64_t d, int dtype, float sca
                            const int32_t* page_table, int64_t max_pages, const int32_t* cache_lens,
                            int64_t max_cache_len, void* o, float* lse, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * path_decode_step_paged_fox - the gated (PaTH-FoX) step over a paged cache
+ * [PaTH summary §2 "Extensões: PaTH-FoX" with §3 "Inferência"]: for every
+ * sequence b and head h, exactly path_decode_step_fox on the first
+ * cache_lens[b] keys of that sequence, with the pages of
+ * path_decode_step_paged.  The gate prefix of key j, c_j, sits in cum_pages
+ * [num_pages, H, page_size] fp32 at the key's own slot (same page table, same
+ * row within the page); the step reads c_{len-1} (0 when len = 0), adds
+ * log_f_t[b,h] in fp32 and writes c_t at logical slot len, next to k_t, v_t.
+ * Inputs: as path_decode_step_paged, plus log_f_t [B,H] fp32 and cum_pages.
+ * Slots no sequence maps are not touched in any of the three page pools.
+ * Each physical page may appear at most once in the whole page table: the
+ * in-place update applies one sequence's transition to its keys, so pages
+ * cannot be shared between sequences (this holds for path_decode_step_paged
+ * too).
+ * Errors: as path_decode_step_paged; PATH_ERR_NULL also when log_f_t or
+ * cum_pages is NULL.
+ */
+int path_decode_step_paged_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                               const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                               const float* log_f_t, void* k_pages, void* v_pages, float* cum_pages,
+                               int64_t num_pages, int64_t page_size, const int32_t* page_table, int64_t max_pages,
+                               const int32_t* cache_lens, int64_t max_cache_len, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * path_project - projection prologue [PaTH summary §2 "Mecanismo Central":

@@ -154,3 +154,18 @@ def test_decode_paged_validation():
     assert _paged(table=None) == NULL
     assert _paged(ws=None) == WS
     assert _paged(wsb=8) == WS
+
+
+def _paged_fox(lf=FAKE, cum=FAKE, d=64, maxlen=20, ptr=FAKE, ws=FAKE):
+    # B=2 H=2 bf16, 8 pages of 16 slots, 4 logical pages per sequence
+    return pa.lib().path_decode_step_paged_fox(2, 2, d, 1, 1.0, ptr, ptr, ptr, ptr, ptr, lf, ptr, ptr, cum,
+                                               8, 16, FAKE, 4, ptr, maxlen, ptr, ptr, ws, 1 << 30, None)
+
+
+def test_decode_paged_fox_validation():
+    assert _paged_fox(lf=None) == NULL
+    assert _paged_fox(cum=None) == NULL
+    assert _paged_fox(ptr=None) == NULL
+    assert _paged_fox(d=80) == UNSUP
+    assert _paged_fox(maxlen=64) == CAP
+    assert _paged_fox(ws=None) == WS
