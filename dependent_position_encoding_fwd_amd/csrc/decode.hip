@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_chunk_kernel(
     // c_t of the new query.  The prefix cache has the key cache's row map (one
     // float per key row); a sequence with no keys has no chunk work to bias.
     const int64_t prow = len > 0 ? rows.row(bh, len - 1) : -1;
-    ct = (rows.ok(prow) ? cum_cache[prow] : 0.f) + log_f_t[bh];
+    ct = (len > 0 && rows.ok(prow) ? cum_cache[prow] : 0.f) + log_f_t[bh];
   }
 
   const int64_t j0 = static_cast<int64_t>(chunk) * kDecChunk;
@@ -455,8 +455,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     lse[bh] = (mm + __log2f(ll)) * 0.69314718055994531f;
     if constexpr (FOX) {
       // c_t at the new key's row of the prefix cache (same row map as the keys)
+      // (ContigRows reports every row as mapped: len > 0 keeps row -1 unread)
       const int64_t prow = len > 0 ? rows.row(bh, len - 1) : -1;
-      if (rows.ok(slot)) cum_cache[slot] = (rows.ok(prow) ? cum_cache[prow] : 0.f) + log_f_t[bh];
+      if (rows.ok(slot)) cum_cache[slot] = (len > 0 && rows.ok(prow) ? cum_cache[prow] : 0.f) + log_f_t[bh];
     }
   }
 }
