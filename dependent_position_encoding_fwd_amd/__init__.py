@@ -25,12 +25,12 @@ LIB_PATH = os.path.join(HERE, "libpath_attn.so")
 PATH_F32, PATH_BF16 = 0, 1
 PRECISION = {"accurate": 0, "auto": 1}
 STATUS = {0: "PATH_OK", 1: "PATH_ERR_NULL", 2: "PATH_ERR_SHAPE", 3: "PATH_ERR_UNSUPPORTED",
-          4: "PATH_ERR_WORKSPACE", 5: "PATH_ERR_CAPACITY", 6: "PATH_ERR_HIP"}
+          4: "PATH_ERR_WORKSPACE", 5: "PATH_ERR_CAPACITY", 6: "PATH_ERR_HIP", 7: "PATH_ERR_SCRATCH"}
 EXPORTS = ["path_status_string", "path_abi_version", "path_prepare", "path_fwd_workspace_bytes",
            "path_attn_fwd", "path_fwd_stage_prepare", "path_fwd_stage_scan",
            "path_decode_workspace_bytes", "path_decode_step", "path_decode_step_fox",
            "path_bwd_workspace_bytes", "path_attn_bwd", "path_project", "path_decode_step_paged",
-           "path_decode_step_paged_fox"]
+           "path_decode_step_noalloc", "path_decode_noalloc_max_bytes", "path_decode_step_paged_fox"]
 
 _lib = None
 _I64, _INT, _F, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -80,6 +80,11 @@ def lib() -> ctypes.CDLL:
                                                  _VP, _I64, _VP, _VP, _VP, _SZ, _VP])
         L.path_project.restype = _INT
         L.path_project.argtypes = [_I64] * 5 + [_VP] * 4 + [_F] + [_VP, _VP, _VP]
+        L.path_decode_step_noalloc.restype = _INT
+        L.path_decode_step_noalloc.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 7 + [_I64, _I64] +
+                                               [_VP, _VP, _VP])
+        L.path_decode_noalloc_max_bytes.restype = _SZ
+        L.path_decode_noalloc_max_bytes.argtypes = []
         L.path_decode_step_fox.restype = _INT
         L.path_decode_step_fox.argtypes = ([_I64, _I64, _I64, _INT, _F] + [_VP] * 9 + [_I64, _I64] +
                                            [_VP, _VP, _VP, _SZ, _VP])
@@ -278,6 +283,31 @@ def path_decode_step(q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, cache_len, sc
     Updates k_cache[:, :, :cache_len] in place, writes k_t, v_t at slot cache_len,
     returns (o [B,H,d], lse [B,H] fp32)."""
     return _decode(q_t, k_t, v_t, w_t, beta_t, None, k_cache, v_cache, None, cache_len, scale, workspace)
+
+
+def path_decode_step_noalloc(q_t, k_t, v_t, w_t, beta_t, k_cache, v_cache, cache_len, scale=1.0):
+    """path_decode_step without a workspace: the library's static device scratch
+    (path_decode_noalloc_max_bytes() per GPU) holds the step's partials.  Calls
+    that overlap in time on one GPU race.  Returns (o [B,H,d], lse [B,H] fp32)."""
+    B, H, d = q_t.shape
+    cap = k_cache.shape[2]
+    dt = q_t.dtype
+    for name, t in (("q_t", q_t), ("k_t", k_t), ("v_t", v_t), ("w_t", w_t)):
+        _check(t, name, dt, (B, H, d))
+    _check(beta_t, "beta_t", torch.float32, (B, H))
+    _check(k_cache, "k_cache", dt, (B, H, cap, d))
+    _check(v_cache, "v_cache", dt, (B, H, cap, d))
+    o = torch.empty_like(q_t)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_t.device)
+    st = lib().path_decode_step_noalloc(B, H, d, _dtype_code(q_t), float(scale), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+                                        _ptr(w_t), _ptr(beta_t), _ptr(k_cache), _ptr(v_cache), int(cache_len),
+                                        int(cap), _ptr(o), _ptr(lse), _stream(q_t))
+    _raise(st, "path_decode_step_noalloc")
+    return o, lse
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(lib().path_decode_noalloc_max_bytes())
 
 
 def path_decode_step_fox(q_t, k_t, v_t, w_t, beta_t, log_f_t, k_cache, v_cache, cum_cache, cache_len,

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace {
@@ -116,6 +118,7 @@ const char* path_status_string(int status) {
     case PATH_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case PATH_ERR_CAPACITY: return "decode cache is full (cache_len >= capacity)";
     case PATH_ERR_HIP: return "HIP kernel launch failed";
+    case PATH_ERR_SCRATCH: return "needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -317,6 +320,70 @@ int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, co
                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(B, H, d, dtype, scale, q_t, k_t, v_t, w_t, beta_t, nullptr, k_cache, v_cache, nullptr,
                        cache_len, capacity, o, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- allocation-free decode --------------------------------------------------------
+// path_decode_step_noalloc keeps the decode step's scratch (the store slot and the
+// per-chunk partials) in this file-scope device array instead of a caller
+// workspace.  Each GPU that runs the library holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel: its device address
+// is resolved once per device with hipGetSymbolAddress and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), resolved on the first call there.
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return PATH_ERR_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return PATH_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PATH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return PATH_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return PATH_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PATH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t path_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int path_decode_step_noalloc(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                             const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                             void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
+                             float* lse, hipStream_t stream) {
+  // the same checks as path_decode_step, in the same order, before the scratch size
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_d(d))) return st;
+  if (B < 1 || H < 1 || capacity < 1 || cache_len < 0) return PATH_ERR_SHAPE;
+  const size_t need = path_decode_workspace_bytes(B, H, d, cache_len);
+  if (need == 0) return PATH_ERR_SHAPE;
+  if (need > kScratchBytes) return PATH_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (cache_len < capacity && q_t && k_t && v_t && w_t && beta_t && k_cache && v_cache && o && lse) {
+    if ((st = scratch_address(stream, &ws))) return st;
+  }
+  return decode_common(B, H, d, dtype, scale, q_t, k_t, v_t, w_t, beta_t, nullptr, k_cache, v_cache, nullptr,
+                       cache_len, capacity, o, lse, ws, kScratchBytes, stream);
 }
 
 int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,

@@ -45,7 +45,8 @@ typedef enum {
   PATH_ERR_UNSUPPORTED = 3, /* d not 64/128, or unknown dtype / precision */
   PATH_ERR_WORKSPACE = 4,   /* workspace NULL, too small or not 256-byte aligned */
   PATH_ERR_CAPACITY = 5,    /* decode: cache_len >= capacity */
-  PATH_ERR_HIP = 6          /* a kernel launch failed (see hipGetLastError) */
+  PATH_ERR_HIP = 6,         /* a kernel launch failed (see hipGetLastError) */
+  PATH_ERR_SCRATCH = 7      /* path_decode_step_noalloc: the step needs more than the static scratch */
 } path_status;
 
 typedef enum { PATH_F32 = 0, PATH_BF16 = 1 } path_dtype;
@@ -185,6 +186,30 @@ int path_decode_step(int64_t B, int64_t H, int64_t d, int dtype, float scale, co
                      const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
                      void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * path_decode_step_noalloc - path_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same step, bit for bit, with its scratch (a
+ * 512-byte store slot and the per-chunk partials, path_decode_workspace_bytes
+ * of them) in a static device array of path_decode_noalloc_max_bytes() = 8 MiB
+ * that the library holds on each GPU it runs on until the process ends.
+ * Arguments, layouts, outputs and errors are those of path_decode_step without
+ * the workspace; PATH_ERR_SCRATCH (nothing enqueued) when
+ * path_decode_workspace_bytes(B, H, d, cache_len) exceeds 8 MiB, i.e. when
+ * B*H*ceil(cache_len/1024)*(d+2)*4 + 512 bytes, rounded up to 256, is larger.
+ * The first call on a GPU resolves the array's device address there (once,
+ * under a lock); no call allocates.  All calls on one GPU share the array: calls
+ * that overlap in time on one GPU (different streams or threads) race and
+ * must not be issued.  Nothing in the array needs to start at zero.
+ */
+int path_decode_step_noalloc(int64_t B, int64_t H, int64_t d, int dtype, float scale, const void* q_t,
+                             const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                             void* k_cache, void* v_cache, int64_t cache_len, int64_t capacity, void* o,
+                             float* lse, hipStream_t stream);
+
+/* Bytes of the static scratch path_decode_step_noalloc uses on each GPU. */
+size_t path_decode_noalloc_max_bytes(void);
 
 /*
  * path_decode_step_fox - one PaTH-FoX generation step [PaTH summary §2

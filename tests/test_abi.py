@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 def test_status_strings_and_version():
     L = pa.lib()
     assert L.path_abi_version() == 1
-    for st in range(7):
+    for st in range(8):
         assert len(L.path_status_string(st)) > 0
     assert L.path_status_string(99) == b"unknown status"
 
@@ -154,6 +154,26 @@ def test_decode_paged_validation():
     assert _paged(table=None) == NULL
     assert _paged(ws=None) == WS
     assert _paged(wsb=8) == WS
+
+
+def _noalloc(B=2, H=2, d=64, dtype=1, cache_len=10, capacity=11, ptr=FAKE):
+    return pa.lib().path_decode_step_noalloc(B, H, d, dtype, 1.0, ptr, ptr, ptr, ptr, ptr, ptr, ptr, cache_len,
+                                             capacity, ptr, ptr, None)
+
+
+def test_decode_noalloc_validation():
+    """Every failing check returns before the static scratch is looked up."""
+    SCRATCH = 7
+    assert pa.lib().path_decode_noalloc_max_bytes() == 8 << 20
+    assert _noalloc(d=100) == UNSUP
+    assert _noalloc(dtype=3) == UNSUP
+    assert _noalloc(cache_len=-1) == SHAPE
+    assert _noalloc(cache_len=11, capacity=11) == CAP
+    assert _noalloc(ptr=None) == NULL
+    # 64 x 16 heads x 64 chunks x 66 floats = 17.3 MB of partials > 8 MiB
+    assert _noalloc(B=64, H=16, cache_len=65536, capacity=65537) == SCRATCH
+    # the cache-8192 workload step fits: 1024 heads x 8 chunks x 66 floats + 512 B = 2.2 MB
+    assert pa.lib().path_decode_workspace_bytes(64, 16, 64, 8192) <= 8 << 20
 
 
 def _paged_fox(lf=FAKE, cum=FAKE, d=64, maxlen=20, ptr=FAKE, ws=FAKE):
