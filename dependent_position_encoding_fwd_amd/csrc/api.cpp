@@ -71,7 +71,7 @@ float auto_tau(int64_t d) { return kAutoRmsNats * kLog2e * 2.449489743f * sqrtf(
 // inputs: the matrix-core layout written by the prepare stage.
 struct FwdWs {
   size_t khat, pT, cum;                       // fp32 path
-  size_t khl, pmat, qhat, sdiag, kmax, kmaxh, pnorm, vt;  // bf16 path (cum shared)
+  size_t khl, pmat, qhat, sdiag, kmax, kmaxh, pnorm, vt, vexp, vexph;  // bf16 path (cum shared)
   size_t total;
 };
 
@@ -97,6 +97,8 @@ FwdWs fwd_layout(int dtype, int64_t BH, int64_t L, int64_t d, int64_t Nb, bool w
     w.kmaxh = take(sizeof(float) * bh);
     w.pnorm = take(sizeof(float) * bh * nb);
     w.vt = take(2 * bh * nb * dd * size_t(kBlk));
+    w.vexp = take(sizeof(int) * bh * nb);
+    w.vexph = take(sizeof(int) * bh);
     if (with_forget) w.cum = take(sizeof(float) * bh * lp);
   }
   w.total = off;
@@ -199,10 +201,11 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
       B, H, L, d, scale * kLog2e, q, k, w, v, beta, reinterpret_cast<_Float16*>(ws + a.lay.khl),
       reinterpret_cast<_Float16*>(ws + a.lay.pmat), reinterpret_cast<float*>(ws + a.lay.qhat),
       reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, reinterpret_cast<float*>(ws + a.lay.pnorm),
-      reinterpret_cast<_Float16*>(ws + a.lay.vt), stream));
+      reinterpret_cast<_Float16*>(ws + a.lay.vt), reinterpret_cast<int*>(ws + a.lay.vexp), stream));
   if (st) return st;
   return hip_status(path::launch_head_reduce(
-      a.BH, L, kmax, reinterpret_cast<float*>(ws + a.lay.kmaxh), log_forget, kLog2e,
+      a.BH, L, kmax, reinterpret_cast<float*>(ws + a.lay.kmaxh), reinterpret_cast<const int*>(ws + a.lay.vexp),
+      reinterpret_cast<int*>(ws + a.lay.vexph), log_forget, kLog2e,
       log_forget ? reinterpret_cast<float*>(ws + a.lay.cum) : nullptr, stream));
 }
 
@@ -227,7 +230,8 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
       reinterpret_cast<const float*>(ws + a.lay.qhat),
       reinterpret_cast<const float*>(ws + a.lay.sdiag),
       reinterpret_cast<const float*>(ws + a.lay.kmaxh), reinterpret_cast<const float*>(ws + a.lay.kmax),
-      reinterpret_cast<const float*>(ws + a.lay.pnorm), cum, o, lse, stream));
+      reinterpret_cast<const float*>(ws + a.lay.pnorm), reinterpret_cast<const int*>(ws + a.lay.vexp),
+      reinterpret_cast<const int*>(ws + a.lay.vexph), cum, o, lse, stream));
 }
 
 }  // namespace

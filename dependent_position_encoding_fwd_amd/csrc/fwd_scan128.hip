@@ -28,6 +28,11 @@
 //     of 8 chunks (V^T) at j ^ (r & 7), so that the MFMA operand reads (16
 //     rows, one chunk column) run at the full LDS read rate.
 // Each tile is its own LDS object and every access names it at compile time.
+// Value range: prepare stores block n's V^T times 2^-e_n (e_n > 0 only when
+// the block holds |v| >= 2^15) and E = max_n e_n per head.  O accumulates in
+// units of 2^E: on a block with e_n < E (never on an ordinary head, where all
+// are 0) a scalar branch multiplies the V^T operands by 2^(e_n - E).  The
+// epilogue multiplies by 2^E.
 #include <math.h>
 
 #include <type_traits>
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     const _Float16* __restrict__ khat, const _Float16* __restrict__ pmat,
     const float* __restrict__ qhat, const float* __restrict__ sdiag,
     const float* __restrict__ kmax_head, const float* __restrict__ kmax_blk, const float* __restrict__ pnorm,
-    const float* __restrict__ cum, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    const int* __restrict__ vexp, const int* __restrict__ vexp_head, const float* __restrict__ cum, uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int D = kD, C = kBlk, DT = D / 16, DC = D / 32;
 
   __shared__ __attribute__((aligned(1024))) _Float16 sK0[kKT], sV0[kVT];
@@ -118,6 +123,13 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   const bool live = mb < Nb;
   const int r0 = (wave % kWPB) * 16;  // first query row (local to block mb)
   const float khmax = kmax_head[bh];
+  const int vE = vexp_head[bh];  // 0 for a head whose values all stay below 2^15
+  // 2^(e_n - E) in fp16 for block n's V^T operands (0 below fp16's subnormals)
+  auto vscale = [&](int n) __attribute__((always_inline)) {
+    const int g = vE - vexp[bh * Nb + n];
+    const _Float16 f = static_cast<_Float16>(g > 24 ? 0.f : __uint_as_float(static_cast<uint32_t>(127 - g) << 23));
+    return h8{f, f, f, f, f, f, f, f};
+  };
   const float* cumh = FOX ? cum + bh * Nb * C : nullptr;
 
   // this head's prepared blocks (hi tile, then lo tile, per block)
@@ -249,11 +261,11 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) x[kt] -= sh;
   };
-  auto pv = [&](const _Float16* vtile, const h8 (&pb)[2]) __attribute__((always_inline)) {
+  auto pv = [&](const _Float16* vtile, const h8 (&pb)[2], bool vsc, h8 vs8) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] = mma16(rdV(vtile, t, c), pb[c], oacc[t]);
+      for (int t = 0; t < DT; ++t) oacc[t] = mma16(vsc ? rdV(vtile, t, c) * vs8 : rdV(vtile, t, c), pb[c], oacc[t]);
       lacc = mma16(ones, pb[c], lacc);
     }
   };
@@ -311,7 +323,8 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     for (int kt = 0; kt < 4; ++kt) x[kt] -= mrun - kOff;
     h8 pb[2];
     exps(x, pb);
-    pv(half == 0 ? sV0 : sV1, pb);
+    const bool dsc = vE != 0 && vexp[bh * Nb + mb] != vE;
+    pv(half == 0 ? sV0 : sV1, pb, dsc, dsc ? vscale(mb) : h8{});
   } else {
     mrun = 0.f;
 #pragma unroll
@@ -470,11 +483,22 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     }
     if (work) {
       // ---- PV beside the conversion of the transported queries
+      const bool vsn = vE != 0 && vexp[bh * Nb + n] != vE;  // rare: values in the head's units
+      if (vsn) {
+        const h8 f8 = vscale(n);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) ch0[t] *= f8;
+      }
       rdVc(ch1, 1);
       mmV(ch0, 0);
 #pragma unroll
       for (int c = 0; c < DC; ++c) qhi[c] = pack_h8(qf[2 * c], qf[2 * c + 1]);
       __builtin_amdgcn_sched_barrier(0);
+      if (vsn) {
+        const h8 f8 = vscale(n);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) ch1[t] *= f8;
+      }
       mmV(ch1, 1);
       if (acc_next) {
         asm volatile("");  // a real branch: the lo parts are rarely needed
@@ -512,7 +536,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     const int r = r0 + ln;
     const int64_t row = static_cast<int64_t>(mb) * C + r;
     if (row < L) {
-      const float inv = 1.f / l;
+      const float inv = __builtin_ldexpf(1.f / l, vE);
       uint16_t* dst = o + (bh * L + row) * D;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
@@ -529,18 +553,20 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
 
 hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                           const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
-                          void* o, float* lse, hipStream_t stream) {
+                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
+                          const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   const int NP = (Nb + 1) / 2;
   dim3 grid(static_cast<unsigned>(BH * NP));
   dim3 block(kNT);
   if (cum) {
     hipLaunchKernelGGL((scan128_kernel<true>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
-                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, static_cast<uint16_t*>(o), lse);
+                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, vexp, vexp_head, cum,
+                       static_cast<uint16_t*>(o), lse);
   } else {
     hipLaunchKernelGGL((scan128_kernel<false>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
-                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, static_cast<uint16_t*>(o), lse);
+                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, vexp, vexp_head, cum,
+                       static_cast<uint16_t*>(o), lse);
   }
   return hipGetLastError();
 }

@@ -27,6 +27,13 @@
 //     issued.
 // [§2 "Extensões: PaTH-FoX"] adds cum_i - cum_j (log2 units) to each logit.
 //
+// Value range: prepare stores block n's V^T times 2^-e_n (e_n > 0 only when
+// the block holds |v| >= 2^15) and E = max_n e_n per head.  O accumulates in
+// units of 2^E: on a block with e_n < E (never on an ordinary head, where all
+// are 0) a scalar branch multiplies the V^T operands by 2^(e_n - E) (exact, or
+// below fp16's range only where the contribution is far below the head's
+// largest values).  The epilogue multiplies by 2^E.
+//
 // LDS: 8 tiles x 8 KB = 64 KB per workgroup, so two workgroups share a CU.
 // Each tile is its own LDS object and every access names its object at
 // compile time (the scan is unrolled by the two stages), which lets the
@@ -74,7 +81,8 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
     const _Float16* __restrict__ khat, const _Float16* __restrict__ pmat,
     const float* __restrict__ qhat, const float* __restrict__ sdiag,
     const float* __restrict__ kmax_head, const float* __restrict__ kmax_blk, const float* __restrict__ pnorm,
-    const float* __restrict__ cum, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    const int* __restrict__ vexp, const int* __restrict__ vexp_head, const float* __restrict__ cum,
+    uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int D = kD, C = kBlk, NCT = 2, DT = 4, DC = 2;
 
   // stage s: Khat hi, P hi, V^T; one stage of lo parts
@@ -119,6 +127,13 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
   const bool live = mb < Nb;
   const int r0 = (wave % 2) * 32;     // first query row (local to block mb)
   const float khmax = kmax_head[bh];
+  const int vE = vexp_head[bh];  // 0 for a head whose values all stay below 2^15
+  // 2^(e_n - E) in fp16 for block n's V^T operands (0 below fp16's subnormals)
+  auto vscale = [&](int n) __attribute__((always_inline)) {
+    const int g = vE - vexp[bh * Nb + n];
+    const _Float16 f = static_cast<_Float16>(g > 24 ? 0.f : __uint_as_float(static_cast<uint32_t>(127 - g) << 23));
+    return h8{f, f, f, f, f, f, f, f};
+  };
   const float* cumh = FOX ? cum + bh * Nb * C : nullptr;
 
   // this head's prepared blocks (hi tile, then lo tile, per block)
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
 
   // ---- softmax step on logits relative to the running max -------------------------
   // x[ct][kt][i] = logit - mrun + kOff (log2 units) of key 16kt+4lg+i, query column ct.
-  auto softmax_pv = [&](f4 (&x)[NCT][4], const _Float16* vtile) __attribute__((always_inline)) {
+  auto softmax_pv = [&](f4 (&x)[NCT][4], const _Float16* vtile, bool vsc, h8 vs8) __attribute__((always_inline)) {
     float mx[NCT];
     bool need = false;
 #pragma unroll
@@ -268,7 +283,8 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const h8 a = rdA(vtile, t, c);
+        h8 a = rdA(vtile, t, c);
+        if (vsc) a *= vs8;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) oacc[ct][t] = mma16(a, pb[ct][c], oacc[ct][t]);
       }
@@ -343,7 +359,8 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) x[ct][kt] -= mrun[ct] - kOff;
     }
-    softmax_pv(x, half == 0 ? sV0 : sV1);
+    const bool dsc = vE != 0 && vexp[bh * Nb + mb] != vE;
+    softmax_pv(x, half == 0 ? sV0 : sV1, dsc, dsc ? vscale(mb) : h8{});
   } else {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -556,6 +573,13 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int t = 0; t < DT; ++t) av[c][t] = rdA(tV, t, c);
+      if (vE != 0 && vexp[bh * Nb + n] != vE) {  // rare: this block's values in the head's units
+        const h8 f8 = vscale(n);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) av[c][t] *= f8;
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -630,7 +654,7 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
       const int r = r0 + 16 * ct + ln;
       const int64_t row = static_cast<int64_t>(mb) * C + r;
       if (row < L) {
-        const float inv = 1.f / l;
+        const float inv = __builtin_ldexpf(1.f / l, vE);
         uint16_t* dst = o + (bh * L + row) * D;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
@@ -648,18 +672,20 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
 
 hipError_t launch_scan64(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
-                         void* o, float* lse, hipStream_t stream) {
+                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
+                         const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   const int NP = (Nb + 1) / 2;
   dim3 grid(static_cast<unsigned>(BH * NP));
   dim3 block(kNT);
   if (cum) {
     hipLaunchKernelGGL((scan64_kernel<true>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
-                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, static_cast<uint16_t*>(o), lse);
+                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, vexp, vexp_head, cum,
+                       static_cast<uint16_t*>(o), lse);
   } else {
     hipLaunchKernelGGL((scan64_kernel<false>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
-                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, cum, static_cast<uint16_t*>(o), lse);
+                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, vexp, vexp_head, cum,
+                       static_cast<uint16_t*>(o), lse);
   }
   return hipGetLastError();
 }

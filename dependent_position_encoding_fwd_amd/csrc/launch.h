@@ -19,27 +19,30 @@ hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_
 // computed on the matrix cores: khat and P (fp16 hi/lo rows, reduction index in
 // mfma_perm order), c2 * adjusted queries and c2 * in-block logits (fp32, c2 =
 // scale * log2(e)), kmax[bh][n] = max_c |khat_c|, pnorm[bh][n] >= |P_n|_2
-// (product of the transitions' spectral norms) and V^T (fp16, keys permuted).
+// (product of the transitions' spectral norms) and V^T (fp16, keys permuted),
+// each block times 2^-vexp[bh][n] (vexp = 0 unless the block holds |v| >= 2^15).
 hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
                                const void* k, const void* w, const void* v, const float* beta,
                                _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                               float* pnorm, _Float16* vt, hipStream_t stream);
+                               float* pnorm, _Float16* vt, int* vexp, hipStream_t stream);
 
-// Per head: kmax_head = max over blocks of kmax; cum = mult * prefix sum of
-// log_forget (fp64 accumulation, padded to whole blocks) when log_forget != null.
-hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head,
-                              const float* log_forget, float mult, float* cum, hipStream_t stream);
+// Per head: kmax_head = max over blocks of kmax; vexp_head = max over blocks of
+// vexp (when vexp != null); cum = mult * prefix sum of log_forget (fp64
+// accumulation, padded to whole blocks) when log_forget != null.
+hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head, const int* vexp,
+                              int* vexp_head, const float* log_forget, float mult, float* cum,
+                              hipStream_t stream);
 
 // Matrix-core right-to-left scan forward (bf16 storage), head dimension 64
 // and 128, from the prepared blocks; operands reach LDS by direct-to-LDS loads.
 hipError_t launch_scan64(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
-                         void* o, float* lse, hipStream_t stream);
+                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
+                         const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream);
 hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                           const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const float* cum,
-                          void* o, float* lse, hipStream_t stream);
+                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
+                          const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream);
 
 // c[bh, i] = sum_{s<=i} x[bh, s], accumulated in fp64.
 hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream);

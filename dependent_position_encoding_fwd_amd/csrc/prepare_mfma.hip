@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     _Float16* __restrict__ khat, _Float16* __restrict__ pmat, float* __restrict__ qhat,
     float* __restrict__ sdiag, float* __restrict__ kmax, float* __restrict__ pnorm,
-    _Float16* __restrict__ vt) {
+    _Float16* __restrict__ vt, int* __restrict__ vexp) {
   using G = PGeo<D>;
   constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
   constexpr int GP = 68;  // row pitch (floats) of G in GY; 64 rows of it fit the C x TP floats
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   __shared__ float bs[C];
   __shared__ float hn[C];
   __shared__ float kred[4];
+  __shared__ float vred[4];
 
   uint16_t* Wb = WK;
   uint16_t* Kb = WK + C * RP;
@@ -508,6 +509,19 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     s2 = wave_max(s2);
     if (lane == 0) kred[wave] = s2;
   }
+  {
+    // largest |v| of the block (this wave's rows; a clamped row repeats a valid one)
+    uint32_t m = 0;
+#pragma unroll
+    for (int h = 0; h < D / 32; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wd = (&vraw[h].x)[i];
+        m = max(m, max(wd & 0x7fffu, (wd >> 16) & 0x7fffu));
+      }
+    const float vm = wave_max(__uint_as_float(m << 16));
+    if (lane == 0) vred[wave] = vm;
+  }
   __syncthreads();  // -Y and -F^T rows complete; XT is free
 
   // V^T[e][perm(c)] in fp16, transposed on the matrix cores: with the value
@@ -515,6 +529,17 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   // product is V[:, slice] in the accumulator layout, where lane (lg, ln) holds
   // the 4 consecutive keys 16w + 4lg .. 16w + 4lg + 3 of column 32h + 16s + ln:
   // 8 contiguous bytes of a V^T row.  Exact: every product is by 1 or 0.
+  // The block is stored times 2^-e, e = max(0, exponent of max|v| - 14), so that
+  // every stored value is below 2^15 (fp16 holds 65504): e = 0 unless some
+  // |v| >= 2^15.  The scaling is exact (a power of two); e goes to vexp.
+  int ve;
+  float vsc;
+  {
+    const float vm = fmaxf(fmaxf(vred[0], vred[1]), fmaxf(vred[2], vred[3]));
+    const int ex = static_cast<int>((__float_as_uint(vm) >> 23) & 0xff) - 127;  // finite inputs
+    ve = ex > 14 ? ex - 14 : 0;
+    vsc = __uint_as_float(static_cast<uint32_t>(127 - ve) << 23);
+  }
   {
     const int r = 16 * wave + ln;
     _Float16* vtb = vt + (bh * Nb + n) * (D * C) + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
@@ -527,7 +552,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
           b8 v;
         } av;
         av.u = r < valid ? vraw[h] : make_uint4(0, 0, 0, 0);
-        const f4 y = mmb(av.v, ident[s], f4{0.f, 0.f, 0.f, 0.f});
+        const f4 y = mmb(av.v, ident[s], f4{0.f, 0.f, 0.f, 0.f}) * vsc;
         const H8u hv = {to_h8(y, y)};
         *reinterpret_cast<uint2*>(vtb + (32 * h + 16 * s + ln) * C) = make_uint2(hv.u.x, hv.u.y);
       }
@@ -543,6 +568,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
       kmax[bh * Nb + n] = sqrtf(mx);
       pnorm[bh * Nb + n] = g;
+      vexp[bh * Nb + n] = ve;
     }
   }
 
@@ -609,23 +635,23 @@ template <int D>
 static hipError_t launch_prepare_mfma_t(int64_t BH, int64_t L, float c2, const void* q, const void* k,
                                         const void* w, const void* v, const float* beta, _Float16* khat,
                                         _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                                        float* pnorm, _Float16* vt, hipStream_t stream) {
+                                        float* pnorm, _Float16* vt, int* vexp, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   hipLaunchKernelGGL((prepare_mfma_kernel<D>), dim3(static_cast<unsigned>(BH * Nb)), dim3(256), 0, stream,
                      L, Nb, c2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(v), beta, khat, pmat,
-                     qhat, sdiag, kmax, pnorm, vt);
+                     qhat, sdiag, kmax, pnorm, vt, vexp);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float c2, const void* q,
                                const void* k, const void* w, const void* v, const float* beta,
                                _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
-                               float* pnorm, _Float16* vt, hipStream_t stream) {
+                               float* pnorm, _Float16* vt, int* vexp, hipStream_t stream) {
   return d == 64 ? launch_prepare_mfma_t<64>(B * H, L, c2, q, k, w, v, beta, khat, pmat, qhat, sdiag, kmax,
-                                             pnorm, vt, stream)
+                                             pnorm, vt, vexp, stream)
                  : launch_prepare_mfma_t<128>(B * H, L, c2, q, k, w, v, beta, khat, pmat, qhat, sdiag, kmax,
-                                              pnorm, vt, stream);
+                                              pnorm, vt, vexp, stream);
 }
 
 }  // namespace path

@@ -103,11 +103,27 @@ size_t path_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  *   o_i  = sum_{j<=i} softmax_j(s_ij) v_j,   lse_i = log sum_{j<=i} exp(s_ij)  (natural log)
  * Runs the block prepare into `workspace`, then a right-to-left scan over key
  * blocks per query tile [§3 "Algoritmo Estilo FlashAttention"].
- * Inputs: q, k, v, w [B,H,L,d] (dtype); beta [B,H,L] (any finite beta >= 0);
- *   log_forget [B,H,L] or NULL; scale multiplies the PaTH term only.
+ * Inputs: q, k, v, w [B,H,L,d] (dtype); beta [B,H,L]; log_forget [B,H,L] or
+ *   NULL; scale multiplies the PaTH term only.  Every input must be finite.
  * Outputs: o [B,H,L,d] (dtype, bf16 rounded to nearest even), lse [B,H,L] fp32.
  * workspace: device buffer of at least path_fwd_workspace_bytes(...) bytes,
  *   256-byte aligned; its contents on entry are irrelevant.
+ * Range and accuracy.  PATH_F32 accepts any finite inputs with beta >= 0 and
+ *   computes in fp32 throughout.  PATH_BF16 feeds the matrix cores half
+ *   precision (fp16) operands, so it states its range:
+ *   - v: any finite bf16 value.  Each 64-token block of V is scaled by a power
+ *     of two before its fp16 conversion (exact) and o is scaled back, so o is
+ *     accurate to 2e-2 + 2^-8 * max_j |v_j| (the head's largest value) absolute.
+ *   - k, q: |k_j|_2 <= 2^15 and |scale| * |q_i|_2 <= 2^14 for every token, so
+ *     every fp16 operand (adjusted keys and queries, transported queries) is
+ *     finite.  lse is then accurate to 1e-3 + 2^-18 * max_j |s_ij| and o to
+ *     the bound above.
+ *   - w, beta: |w_s|_2 <= 1 + 2^-7 (unit vectors stored in bf16) and
+ *     0 <= beta_s <= 2 (the range 2 sigmoid(.) gives), so that no transition
+ *     expands a vector by more than rounding.
+ *   Outside these ranges the results are undefined (an fp16 operand may
+ *   overflow and turn o or lse into inf or NaN).  The gradients of
+ *   path_attn_bwd are fp32 throughout and have no such limit.
  */
 int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
                   int precision, const void* q, const void* k, const void* v, const void* w,
