@@ -33,12 +33,22 @@ _D = ctypes.POINTER(ctypes.c_double)
 _I64 = ctypes.c_int64
 
 
+# ORACLE_SANITIZE=1 selects a build of the same source under AddressSanitizer
+# and UndefinedBehaviorSanitizer (the process must then be started with the
+# sanitizer runtimes preloaded; tests/test_oracle_sanitized.py does that).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+if _SANITIZE:
+    _LIB_PATH = os.path.join(_OUT_DIR, "liboracle_asan_ubsan.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
 def build(force: bool = False) -> str:
     """Compile path_oracle.c into oracle/_build/liboracle.so (gcc -O2 -fopenmp)."""
     os.makedirs(_OUT_DIR, exist_ok=True)
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", *(_SAN_FLAGS if _SANITIZE else []), _SRC,
+               "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
