@@ -5,8 +5,10 @@ Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of
 package never imports the library: the two share no code.
 
 The arithmetic lives in `path_oracle.c` (plain C, fp64, OpenMP over query
-rows), for tiny explicit-matrix cross-checks in `tiny.py`, and for gradients
-in `grad.py` (float64 reverse-mode differentiation of the defining loop).  This module
+rows; it also holds the hand-written reverse mode of the defining loop for
+the gradients), for tiny explicit-matrix cross-checks in `tiny.py`, and for
+gradients in `grad.py` as well (float64 torch.autograd of the defining loop,
+the small-size reference the C reverse mode is pinned against).  This module
 only compiles the C file with the host compiler and marshals numpy arrays.
 
 Source pages: "PaTH Attention" technical summary (gist.science 2505.16381),
@@ -69,6 +71,8 @@ def _load():
             lib.oracle_ut_tinv.argtypes = [_I64, _I64, _D, _D, _D]
             lib.oracle_block_adjust.argtypes = [_I64, _I64, _D, _D, _D, _D, _D, _D, _D]
             lib.oracle_prefix_sum.argtypes = [_I64, _D, _D]
+            lib.oracle_path_bwd.argtypes = [_I64, _I64, _D, _D, _D, _D, _D, _D, ctypes.c_double, _D,
+                                            _D, _D, _D, _D, _D, _D]
             _lib = lib
     return _lib
 
@@ -126,6 +130,24 @@ def path_fwd(q, k, v, w, beta, log_forget=None, scale=1.0):
             o[b, h], lse[b, h] = path_fwd_head(q[b, h], k[b, h], v[b, h], w[b, h], beta[b, h],
                                                None if lf is None else lf[b, h], scale)
     return o, lse
+
+
+def path_bwd_head(q, k, v, w, beta, log_forget, scale, do):
+    """Gradients of <do, o> for one head by the C reverse mode of the defining
+    loop: dict dq, dk, dv, dw [L,d], dbeta [L], dlog_forget [L] (None without
+    gates), float64 numpy (the same layout as oracle.grad.path_bwd_head)."""
+    lib = _load()
+    q, k, v, w, beta, do = (_f64(x) for x in (q, k, v, w, beta, do))
+    L, d = q.shape
+    lf = _f64(log_forget) if log_forget is not None else None
+    out = {n: np.zeros((L, d)) for n in ("dq", "dk", "dv", "dw")}
+    out["dbeta"] = np.zeros((L,))
+    dlf = np.zeros((L,)) if lf is not None else None
+    lib.oracle_path_bwd(L, d, _p(q), _p(k), _p(v), _p(w), _p(beta), _p(lf) if lf is not None else _D(),
+                        float(scale), _p(do), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dw"]),
+                        _p(out["dbeta"]), _p(dlf) if dlf is not None else _D())
+    out["dlog_forget"] = dlf
+    return out
 
 
 def path_logits(q, k, w, beta, log_forget=None, scale=1.0):

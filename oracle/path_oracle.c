@@ -250,3 +250,136 @@ void oracle_prefix_sum(int64_t L, const double* x, double* c) {
     c[i] = acc;
   }
 }
+
+/*
+ * Gradients of the scalar <dO, o> for one head, by reverse-mode
+ * differentiation of the defining loop of oracle_path_fwd (lse receives no
+ * incoming gradient) [P1 §2 "Mecanismo Central", §2 "Extensões: PaTH-FoX";
+ * the pages describe no backward pass, so this is the exact derivative of the
+ * forward's definition].  For query i let u^(j) be the transported query the
+ * loop holds when it forms s_ij:  u^(i) = q_i,  u^(j-1) = H_j u^(j).
+ *   forward:  s_ij = scale k_j.u^(j) + c_i - c_j,  p_ij = softmax_j(s_ij),
+ *             o_i = sum_j p_ij v_j
+ *   reverse:  dv_j += p_ij dO_i
+ *             ds_ij = p_ij (dO_i.v_j - dO_i.o_i)         (softmax adjoint)
+ *             dk_j += scale ds_ij u^(j),  dc_i += ds_ij,  dc_j -= ds_ij
+ *             the query adjoint g^(j) = dloss/du^(j) runs j = 0 .. i:
+ *               g^(j) = scale ds_ij k_j + H_j^T g^(j-1)   (g^(-1) = 0; H_j = H_j^T),
+ *               and H_j, which forms u^(j-1) from u^(j), takes with
+ *               a = w_j.u^(j), b = w_j.g^(j-1):
+ *                 dbeta_j -= a b,   dw_j -= beta_j (b u^(j) + a g^(j-1));
+ *             dq_i = g^(i);   dlog_forget_s = sum_{i >= s} dc_i.
+ * The u^(j) of one query are kept (i+1 vectors): H may be singular, so they
+ * are not rebuilt backwards.  OpenMP spreads the queries over threads (static
+ * round robin, so the sums are reproducible for a given thread count); each
+ * thread accumulates into its own arrays, summed in thread order at the end.
+ * Inputs as oracle_path_fwd plus dO [L,d]; outputs dq, dk, dv, dw [L,d],
+ * dbeta [L], dlog_forget [L] (written only when log_forget != NULL).
+ */
+void oracle_path_bwd(int64_t L, int64_t d, const double* q, const double* k,
+                     const double* v, const double* w, const double* beta,
+                     const double* log_forget, double scale, const double* dO,
+                     double* dq, double* dk, double* dv, double* dw, double* dbeta,
+                     double* dlog_forget) {
+  int nt = 1;
+#ifdef _OPENMP
+  nt = omp_get_max_threads();
+#endif
+  const size_t Ld = (size_t)(L * d);
+  /* per-thread accumulators: dk, dv, dw [L,d] and dbeta, dc [L] */
+  double* acc = (double*)calloc((size_t)nt * (3 * Ld + 2 * (size_t)L), sizeof(double));
+  double* c = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double bias = 0.0;
+  for (int64_t i = 0; i < L; ++i) {
+    bias += log_forget ? log_forget[i] : 0.0;
+    c[i] = bias;
+  }
+  for (size_t t = 0; t < Ld; ++t) dq[t] = 0.0;
+#pragma omp parallel num_threads(nt)
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* my = acc + (size_t)tid * (3 * Ld + 2 * (size_t)L);
+    double *adk = my, *adv = my + Ld, *adw = my + 2 * Ld;
+    double *adb = my + 3 * Ld, *adc = my + 3 * Ld + L;
+    double* U = (double*)malloc(sizeof(double) * Ld);  /* U[j] = u^(j) */
+    double* s = (double*)malloc(sizeof(double) * (size_t)L);
+    double* g = (double*)malloc(sizeof(double) * (size_t)d);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(static, 1)
+    for (int64_t i = 0; i < L; ++i) {
+      /* forward of row i, keeping every transported query */
+      memcpy(U + i * d, q + i * d, sizeof(double) * (size_t)d);
+      for (int64_t j = i; j >= 0; --j) {
+        s[j] = scale * dot(k + j * d, U + j * d, d) + (c[i] - c[j]);
+        if (j > 0) {
+          memcpy(U + (j - 1) * d, U + j * d, sizeof(double) * (size_t)d);
+          apply_H(U + (j - 1) * d, w + j * d, beta[j], d);
+        }
+      }
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= i; ++j) m = s[j] > m ? s[j] : m;
+      double l = 0.0;
+      for (int64_t j = 0; j <= i; ++j) l += exp(s[j] - m);
+      for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        s[j] = exp(s[j] - m) / l; /* s now holds p_ij */
+        for (int64_t t = 0; t < d; ++t) o[t] += s[j] * v[j * d + t];
+      }
+      const double* dOi = dO + i * d;
+      const double Di = dot(dOi, o, d);
+      /* reverse of row i */
+      for (int64_t t = 0; t < d; ++t) g[t] = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        const double p = s[j];
+        for (int64_t t = 0; t < d; ++t) adv[j * d + t] += p * dOi[t];
+        const double ds = p * (dot(dOi, v + j * d, d) - Di);
+        adc[i] += ds;
+        adc[j] -= ds;
+        const double* u = U + j * d;
+        if (j > 0) { /* H_j maps u^(j) to u^(j-1), whose adjoint g holds */
+          const double a = dot(w + j * d, u, d), b = dot(w + j * d, g, d);
+          adb[j] -= a * b;
+          for (int64_t t = 0; t < d; ++t) adw[j * d + t] -= beta[j] * (b * u[t] + a * g[t]);
+          apply_H(g, w + j * d, beta[j], d);
+        }
+        for (int64_t t = 0; t < d; ++t) {
+          adk[j * d + t] += scale * ds * u[t];
+          g[t] += scale * ds * k[j * d + t];
+        }
+      }
+      memcpy(dq + i * d, g, sizeof(double) * (size_t)d);
+    }
+    free(o);
+    free(g);
+    free(s);
+    free(U);
+  }
+  for (size_t t = 0; t < Ld; ++t) dk[t] = dv[t] = dw[t] = 0.0;
+  for (int64_t i = 0; i < L; ++i) dbeta[i] = 0.0;
+  double* dc = c; /* reused: sum of the threads' dc */
+  for (int64_t i = 0; i < L; ++i) dc[i] = 0.0;
+  for (int th = 0; th < nt; ++th) {
+    const double* my = acc + (size_t)th * (3 * Ld + 2 * (size_t)L);
+    for (size_t t = 0; t < Ld; ++t) {
+      dk[t] += my[t];
+      dv[t] += my[Ld + t];
+      dw[t] += my[2 * Ld + t];
+    }
+    for (int64_t i = 0; i < L; ++i) {
+      dbeta[i] += my[3 * Ld + i];
+      dc[i] += my[3 * Ld + L + i];
+    }
+  }
+  if (dlog_forget) { /* c_i = sum_{s<=i} log f_s: d log f_s = sum_{i>=s} dc_i */
+    double run = 0.0;
+    for (int64_t s2 = L - 1; s2 >= 0; --s2) {
+      run += dc[s2];
+      dlog_forget[s2] = log_forget ? run : 0.0;
+    }
+  }
+  free(c);
+  free(acc);
+}

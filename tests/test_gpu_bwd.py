@@ -1,7 +1,10 @@
 """GPU parity of the backward pass: path_attn_bwd (through the C ABI) against
 the fp64 gradients of the oracle (oracle/grad.py) on identical seeded inputs.
 
-The oracle differentiates <dO, o> in float64 from the stored input values.
+The oracle differentiates <dO, o> in float64 from the stored input values:
+torch.autograd of the defining loop (oracle/grad.py) up to L = 600, and at
+training length (L = 4096 and 8192, whole heads) the hand-written C reverse
+mode of the same loop (oracle.path_bwd_head), pinned against the former.
 The backward is fed the oracle's o (stored in the input dtype) and lse (fp32),
 as a forward would hand them over.  Bar, for every gradient tensor G: the
 largest element error is at most tol * max|G_ref|, with tol = 1e-4 for fp32
@@ -20,6 +23,7 @@ import pytest
 import torch
 
 import dependent_position_encoding_fwd_amd as pa
+import oracle
 import synthetic
 from oracle import grad
 
@@ -36,6 +40,7 @@ def _cmp(name, got, ref, tol, floor):
     err = float(np.max(np.abs(_np(got) - ref))) if ref.size else 0.0
     mag = float(np.max(np.abs(ref))) if ref.size else 0.0
     print(f"  {name}: max|err|={err:.3e} max|ref|={mag:.3e} ratio={err / max(mag, 1e-30):.2e}", flush=True)
+    assert mag > 0 or floor is not None, (name, "reference is exactly zero")
     assert err <= tol * (mag if mag > 0 else floor), (name, err, mag, floor)
 
 
@@ -142,3 +147,45 @@ def test_bwd_full_length_directional(fox):
     fd = (f(1.0) - f(-1.0)) / 2.0
     print(f"  L={L} fox={fox}: <grad, v> = {dirder:.6e}, central difference = {fd:.6e}", flush=True)
     assert abs(dirder - fd) <= 1e-2 * abs(fd), (dirder, fd)
+
+
+def _bwd_full_heads(H, L, d, dtype, scale, seed, fox):
+    """Whole heads at training length, every gradient element against the C
+    reverse mode of the defining loop (oracle.path_bwd_head); the backward is
+    fed the oracle's o (stored in the input dtype) and lse."""
+    print(f"[bwd-full] H={H} L={L} d={d} {dtype} scale={scale} fox={fox} seed={seed}", flush=True)
+    x = synthetic.fwd_inputs(1, H, L, d, dtype, seed, fox=fox)
+    do = torch.randn(1, H, L, d, generator=torch.Generator().manual_seed(seed + 1000)).to(synthetic.DTYPES[dtype])
+    refs, o_ref, lse_ref = {}, np.zeros((1, H, L, d)), np.zeros((1, H, L))
+    for h in range(H):
+        lf = None if x["log_forget"] is None else x["log_forget"][0, h]
+        args = (x["q"][0, h], x["k"][0, h], x["v"][0, h], x["w"][0, h], x["beta"][0, h], lf, scale)
+        o_ref[0, h], lse_ref[0, h] = oracle.path_fwd_head(*args)
+        r = oracle.path_bwd_head(*args, do[0, h])
+        for n, val in r.items():
+            if val is not None:
+                refs.setdefault(n, np.zeros((1, H) + val.shape))[0, h] = val
+    gx = {n: (t.to(DEV) if t is not None else None) for n, t in x.items()}
+    o = torch.tensor(o_ref).to(synthetic.DTYPES[dtype]).to(DEV)
+    lse = torch.tensor(lse_ref, dtype=torch.float32).to(DEV)
+    grads = pa.path_attn_bwd(gx["q"], gx["k"], gx["v"], gx["w"], gx["beta"], o, lse, do.to(DEV), gx["log_forget"],
+                             scale=scale)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dw", "dbeta") + (("dlog_forget",) if fox else ())
+    for name, got in zip(names, grads):
+        _cmp(name, got, refs[name], TOL[dtype], None)
+
+
+def test_bwd_full_length_elementwise_bf16():
+    """Four whole heads of the L = 4096 workload (d = 64, scale 1/8, bf16): 64
+    blocks, 2016 block pairs per head, every gradient element."""
+    _bwd_full_heads(4, 4096, 64, "bf16", 0.125, 4100, False)
+
+
+def test_bwd_full_length_elementwise_f32_gated():
+    _bwd_full_heads(1, 4096, 64, "f32", 0.125, 4101, True)
+
+
+def test_bwd_full_length_elementwise_d128_gated():
+    """One whole head at the gated d = 128 workload's length (L = 8192, bf16)."""
+    _bwd_full_heads(1, 8192, 128, "bf16", 1.0, 4102, True)

@@ -425,3 +425,64 @@ def test_grad_single_token_has_no_transition_gradient():
     np.testing.assert_allclose(g["dv"], do, atol=1e-15)
     for n in ("dq", "dk", "dw", "dbeta"):
         assert np.all(g[n] == 0.0), n
+
+
+# ---- the C reverse mode of the defining loop (oracle.path_bwd_head) ---------------
+
+@pytest.mark.parametrize("fox", [False, True])
+@pytest.mark.parametrize("L", [1, 2, 37, 70])
+def test_c_reverse_mode_matches_autograd_of_the_loop(L, fox):
+    """The hand-derived reverse mode in C against torch.autograd of the same
+    definition written in torch ops (oracle/grad.py): every gradient."""
+    rng = np.random.default_rng(61 + L + fox)
+    q, k, v, w, beta, lf, do = _bwd_case(rng, L, 8, fox)
+    beta[min(3, L - 1)] = 1.0      # a singular H (unit w, beta = 1) must not matter
+    ref = grad.path_bwd_head(q, k, v, w, beta, lf, 0.7, do)
+    got = oracle.path_bwd_head(q, k, v, w, beta, lf, 0.7, do)
+    for n in ("dq", "dk", "dv", "dw", "dbeta") + (("dlog_forget",) if fox else ()):
+        np.testing.assert_allclose(got[n], ref[n], atol=1e-11, rtol=1e-11, err_msg=n)
+    assert (got["dlog_forget"] is None) == (not fox)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_c_reverse_mode_matches_central_differences(fox):
+    """Every gradient of the C reverse mode against central differences of the
+    C forward along a random direction."""
+    rng = np.random.default_rng(67 + fox)
+    L, d, scale = 33, 5, 0.8
+    q, k, v, w, beta, lf, do = _bwd_case(rng, L, d, fox)
+    g = oracle.path_bwd_head(q, k, v, w, beta, lf, scale, do)
+    args = {"q": q, "k": k, "v": v, "w": w, "beta": beta}
+    if fox:
+        args["log_forget"] = lf
+
+    def loss(a):
+        o, _ = oracle.path_fwd_head(a["q"], a["k"], a["v"], a["w"], a["beta"], a.get("log_forget"), scale)
+        return float(np.sum(o * do))
+
+    eps = 1e-5
+    for name in args:
+        delta = rng.standard_normal(np.shape(args[name]))
+        ap = dict(args); ap[name] = args[name] + eps * delta
+        am = dict(args); am[name] = args[name] - eps * delta
+        fd = (loss(ap) - loss(am)) / (2 * eps)
+        an = float(np.sum(g["d" + name] * delta))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_c_reverse_mode_beta_zero_is_softmax_attention_grad():
+    """beta = 0: dq, dk, dv are those of causal softmax attention (torch's
+    scaled_dot_product_attention differentiated in float64) and dw = 0."""
+    rng = np.random.default_rng(71)
+    L, d, scale = 40, 8, 0.6
+    q, k, v, w, _, _, do = _bwd_case(rng, L, d, False)
+    beta = np.zeros(L)
+    g = oracle.path_bwd_head(q, k, v, w, beta, None, scale, do)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], is_causal=True,
+                                                         scale=scale)[0]
+    rq, rk, rv = torch.autograd.grad((o * torch.tensor(do)).sum(), (tq, tk, tv))
+    np.testing.assert_allclose(g["dq"], rq.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dk"], rk.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dv"], rv.numpy(), atol=1e-12)
+    assert np.all(g["dw"] == 0.0)
