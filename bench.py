@@ -28,7 +28,10 @@ the same numbers of warm-up and timed launches and is reported in
 `decode_fox` on the decode bytes plus 4 bytes per cached key.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-ref]
-                    [--fwd-config {2,3,4}]
+                    [--fwd-config {2,3,4}] [--fwd-only]
+
+`--fwd-only` times the forward steps alone and prints a forward-only line (for
+counter runs under rocprofv3 --pmc).
 
 `--fwd-config` swaps the forward workload for another of the synthetic
 configurations (3: B=1 H=16 L=16384 d=64; 4: B=4 H=16 L=8192 d=128 with forget
@@ -119,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    # counter runs: only the forward (prepare + scan) steps; prints a forward-only line
+    ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--fwd-config", type=int, default=2, choices=[2, 3, 4])
     args = ap.parse_args()
     if args.gpus != 1:
@@ -167,8 +172,9 @@ def main():
         pa.path_fwd_stage_scan(*fargs, ws, gates, scale=cf.scale, precision=args.precision, out=(o, lse))
         if ev is not None:
             ev[2].record()
-        pa.path_decode_step(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], xd["k_cache"],
-                            xd["v_cache"], cd.cache_len, scale=cd.scale, workspace=dws)
+        if not args.fwd_only:
+            pa.path_decode_step(xd["q_t"], xd["k_t"], xd["v_t"], xd["w_t"], xd["beta_t"], xd["k_cache"],
+                                xd["v_cache"], cd.cache_len, scale=cd.scale, workspace=dws)
         if ev is not None:
             ev[3].record()
 
@@ -182,6 +188,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] {args.steps} timed steps done in {wall:.3f} s", file=sys.stderr, flush=True)
+    if args.fwd_only:
+        fwd_only_line(args, cf, evs, wall)
+        return
     # The gated (forget-gate) decode step on the same cache, timed on its own
     # after the steps above: the same number of launches, each bracketed by events.
     fox_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -247,6 +256,23 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def fwd_only_line(args, cf, evs, wall):
+    """The forward's figures alone (a --fwd-only run, as used under rocprofv3 --pmc)."""
+    prep_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    scan_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evs)
+    F = flops_path(cf.B, cf.H, cf.L, cf.d)
+    fwd_ms = prep_ms + scan_ms
+    print(json.dumps({
+        "metric": "PaTH fwd TFLOP/s (forward-only run)", "value": round(F / (fwd_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "dtype": "f16",
+        "config": {"workload": f"PaTH fwd B={cf.B} H={cf.H} L={cf.L} d={cf.d} scale={cf.scale:g}"
+                               f"{' forget gates' if cf.fox else ''} (bf16 in/out)", "global_batch": cf.B,
+                   "seq_len": cf.L, "heads": cf.H, "head_dim": cf.d, "precision": args.precision},
+        "fwd": {"ms": round(fwd_ms, 4), "prepare_ms": round(prep_ms, 4), "scan_ms": round(scan_ms, 4),
+                "flops_model": F}}), flush=True)
 
 
 def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):

@@ -18,6 +18,11 @@ the last device-copy dispatch before the first forward-prepare dispatch.
 With only --stats, --md and --cmd-stats it summarises the kernel trace alone
 (for example a run of `bench.py --fwd-config 4`).
 
+With --sq DIR... (several `--pmc` runs of `bench.py --fwd-only`, each with its
+own counter set) it writes the shader-counter table of the forward kernels:
+clock, matrix-pipe busy share, VALU instructions per MFMA, wait shares, LDS
+bank conflicts and the L1 -> L2 read latency (see sq_table for the formulas).
+
 Each DIR holds the run's CSV files and `bench.json`, the JSON line bench.py
 printed in that run.
 """
@@ -74,7 +79,8 @@ PAGED = (("decode_chunk_paged", "decode_chunk_kernel"), ("decode_merge_paged", "
 def classify(name: str):
     for cls, key in PAGED:
         if key in name and "PagedRows" in name:
-            return cls
+            gated = ", true," in name or ", true>" in name
+            return cls + "_fox" if gated else cls
     for cls, key in GATED:
         if key in name and (", true>" in name or ", true," in name):
             return cls
@@ -147,7 +153,9 @@ def short(name: str) -> str:
             "decode_chunk_fox": "decode_chunk_kernel<bf16,64,gated>",
             "decode_merge_fox": "decode_merge_kernel<bf16,64,gated>",
             "decode_chunk_paged": "decode_chunk_kernel<bf16,64,paged>",
-            "decode_merge_paged": "decode_merge_kernel<bf16,64,paged>"}.get(c, _short_other(name))
+            "decode_merge_paged": "decode_merge_kernel<bf16,64,paged>",
+            "decode_chunk_paged_fox": "decode_chunk_kernel<bf16,64,gated,paged>",
+            "decode_merge_paged_fox": "decode_merge_kernel<bf16,64,gated,paged>"}.get(c, _short_other(name))
 
 
 def _short_other(name: str) -> str:
@@ -222,17 +230,119 @@ def trace_only(a):
         f.write("\n".join(lines))
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.  GRBM_GUI_ACTIVE is summed over
+# the XCDs; the SQ_*_CYCLES counters count quad-cycles (units of 4 clocks).
+N_XCD, N_SIMD = 8, 1024
+MFMA_FLOP = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_f16
+
+
+def read_sq(dirs):
+    """{kernel: {counter: mean per dispatch, '_us': mean duration, '_n': dispatches}}
+    over the forward kernels of several --pmc runs (each counter from the run
+    that collected it)."""
+    out = {}
+    for d in dirs:
+        per = defaultdict(dict)
+        with open(_one(d, "*counter_collection.csv")) as f:
+            for row in csv.DictReader(f):
+                name = demangle(row["Kernel_Name"])
+                if not any(k in name for k in ("scan64_kernel", "scan128_kernel", "prepare_mfma_kernel")):
+                    continue
+                rec = per[(name, int(row["Dispatch_Id"]))]
+                rec[row["Counter_Name"]] = rec.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+                rec["_us"] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+        by = defaultdict(list)
+        for (name, _), rec in per.items():
+            by[name].append(rec)
+        for name, recs in by.items():
+            agg = out.setdefault(name, {})
+            for key in recs[0]:
+                vals = [r[key] for r in recs if key in r]
+                if key == "_us":
+                    agg.setdefault("_us_all", []).extend(vals)
+                else:
+                    agg[key] = statistics.mean(vals)
+            agg["_n"] = max(agg.get("_n", 0), len(recs))
+    for agg in out.values():
+        agg["_us"] = statistics.median(agg.pop("_us_all"))
+    return out
+
+
+def sq_table(sq, flops=None):
+    """Markdown rows of derived shader metrics per kernel.
+
+    clock = GRBM_GUI_ACTIVE / 8 / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (1024 SIMDs x GRBM_GUI_ACTIVE / 8); useful MFMA = model FLOP / 16384 per
+    instruction over SQ_INSTS_MFMA (scan kernels only); VALU/MFMA =
+    SQ_INSTS_VALU / SQ_INSTS_MFMA (SQ_INSTS_VALU includes the MFMAs); VALU
+    active, dependency wait and any wait = SQ_ACTIVE_INST_VALU, SQ_WAIT_INST_ANY
+    and SQ_WAIT_ANY over SQ_WAVE_CYCLES; LDS conflicts = SQ_LDS_BANK_CONFLICT /
+    SQ_ACTIVE_INST_LDS; L2 latency = TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum."""
+    def g(a, k):
+        return a.get(k)
+
+    def pct(x):
+        return "-" if x is None else f"{100 * x:.1f} %"
+
+    def ratio(a, b):
+        return None if a is None or not b else a / b
+
+    rows = ["| kernel | dispatches | median us | clock GHz | MFMA instr | MFMA busy | useful MFMA | VALU / MFMA "
+            "| VALU active | dependency wait | any wait | LDS conflict / LDS active | L1->L2 latency (cycles) |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(sq):
+        a = sq[name]
+        us = a["_us"]
+        grbm = g(a, "GRBM_GUI_ACTIVE")
+        clock = None if grbm is None else grbm / N_XCD / (us * 1e3)
+        busy = ratio(g(a, "SQ_VALU_MFMA_BUSY_CYCLES"), None if grbm is None else N_SIMD * grbm / N_XCD)
+        useful = None
+        if flops and "scan" in name and g(a, "SQ_INSTS_MFMA"):
+            useful = flops / MFMA_FLOP / a["SQ_INSTS_MFMA"]
+        vpm = ratio(g(a, "SQ_INSTS_VALU"), g(a, "SQ_INSTS_MFMA"))
+        wc = g(a, "SQ_WAVE_CYCLES")
+        lat = ratio(g(a, "TCP_TCC_READ_REQ_LATENCY_sum"), g(a, "TCP_TCC_READ_REQ_sum"))
+        nmfma = g(a, "SQ_INSTS_MFMA")
+        rows.append(
+            f"| {name} | {a['_n']} | {us:.1f} | {'-' if clock is None else f'{clock:.2f}'} | "
+            f"{'-' if nmfma is None else f'{nmfma:.4g}'} | {pct(busy)} | "
+            f"{pct(useful)} | {'-' if vpm is None else f'{vpm:.2f}'} | {pct(ratio(g(a, 'SQ_ACTIVE_INST_VALU'), wc))} | "
+            f"{pct(ratio(g(a, 'SQ_WAIT_INST_ANY'), wc))} | {pct(ratio(g(a, 'SQ_WAIT_ANY'), wc))} | "
+            f"{pct(ratio(g(a, 'SQ_LDS_BANK_CONFLICT'), g(a, 'SQ_ACTIVE_INST_LDS')))} | "
+            f"{'-' if lat is None else f'{lat:.0f}'} |")
+    return rows
+
+
+def sq_summary(a):
+    bench = read_bench(a.sq[0])
+    cfg = bench["config"]
+    sq = read_sq(a.sq)
+    lines = [f"# rocprofv3 shader counters: {cfg['workload']}", "",
+             f"Precision {cfg.get('precision')}.  Counter runs (from the repository root on one MI355X), one "
+             "counter set each:", ""]
+    lines += [f"    {c}" for c in a.cmds]
+    lines += ["", *sq_table(sq, bench["fwd"]["flops_model"]), "",
+              "Formulas: " + " ".join(sq_table.__doc__.split("\n\n", 1)[1].split()), ""]
+    with open(a.md, "w") as f:
+        f.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--sq", nargs="+")
+    ap.add_argument("--cmds", nargs="+")
+    ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--md", required=True)
     ap.add_argument("--json")
-    ap.add_argument("--cmd-stats", required=True)
+    ap.add_argument("--cmd-stats")
     ap.add_argument("--cmd-fetch")
     ap.add_argument("--cmd-write")
     a = ap.parse_args()
+    if a.sq:
+        sq_summary(a)
+        return
     if a.fetch is None:
         trace_only(a)
         return

@@ -17,6 +17,8 @@ def test_profsum_classifies_decode_variants():
         == "decode_chunk_fox"
     assert c("void path::decode_merge_kernel<path::bf16_t, 64, false, path::PagedRows>(path::PagedRows)") \
         == "decode_merge_paged"
+    assert c("void path::decode_chunk_kernel<path::bf16_t, 64, true, path::PagedRows>(path::PagedRows)") \
+        == "decode_chunk_paged_fox"
     assert c("_ZN4path13scan64_kernelILb0EEEvliiifPKDF16_S2_S2_PKfS4_S4_S4_S4_S4_PtPf") == "scan"
     assert c("_ZN4path19prepare_mfma_kernelILi64EEEvlifPKtS2_S2_S2_PKfPDF16_S5_PfS6_S6_S6_S5_") == "prepare"
     assert c("void path::bwd_pair_kernel<path::bf16_t, 64, false>(long)") is None
