@@ -64,7 +64,7 @@ constexpr int kVT = kD * 64;       // halfs of a V^T tile (128 x 64)
 // asm statement with a memory clobber).
 __device__ __forceinline__ void sync_dma() {
   __builtin_amdgcn_s_waitcnt(0x0070);
-  asm volatile("s_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 // Barrier after this wave's LDS reads are done (no wait on global loads).
 __device__ __forceinline__ void sync_lds() {
@@ -167,26 +167,26 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   auto dmaK = [&](int n, _Float16* ltile) __attribute__((always_inline)) {
     const char* g = kh_h + static_cast<int64_t>(n) * (2 * TBK);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(g + goffK[i], ltile + (2 * wave + i) * 512, 16, 0, 0);
+    for (int i = 0; i < 2; ++i) lds_dma16(g + goffK[i], ltile + (2 * wave + i) * 512);
   };
   auto dmaV = [&](int n, _Float16* ltile) __attribute__((always_inline)) {
     const char* g = vt_h + static_cast<int64_t>(n) * TBV;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(g + goffV[i], ltile + (2 * wave + i) * 512, 16, 0, 0);
+    for (int i = 0; i < 2; ++i) lds_dma16(g + goffV[i], ltile + (2 * wave + i) * 512);
   };
   auto dmaP = [&](int n) __attribute__((always_inline)) {
     const char* g = pm_h + static_cast<int64_t>(n) * (2 * TBP);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(g + goffP[i], sP + (4 * wave + i) * 512, 16, 0, 0);
+    for (int i = 0; i < 4; ++i) lds_dma16(g + goffP[i], sP + (4 * wave + i) * 512);
   };
   // lo parts: the same slots in the lo tiles
   auto dmaLo = [&](int n) __attribute__((always_inline)) {
     const char* gk = kh_h + static_cast<int64_t>(n) * (2 * TBK) + TBK;
     const char* gp = pm_h + static_cast<int64_t>(n) * (2 * TBP) + TBP;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(gk + goffK[i], sKl + (2 * wave + i) * 512, 16, 0, 0);
+    for (int i = 0; i < 2; ++i) lds_dma16(gk + goffK[i], sKl + (2 * wave + i) * 512);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(gp + goffP[i], sPl + (4 * wave + i) * 512, 16, 0, 0);
+    for (int i = 0; i < 4; ++i) lds_dma16(gp + goffP[i], sPl + (4 * wave + i) * 512);
   };
   // gate prefix of block n's keys: 16 lanes of wave 0 move its 256 bytes
   auto tileC = [&](auto st) __attribute__((always_inline)) {
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   };
   auto dmaC = [&](int n, float* ltile) __attribute__((always_inline)) {
     if (wave == 0 && lane < 16)
-      __builtin_amdgcn_global_load_lds(cumh + n * C + 4 * lane, ltile, 16, 0, 0);
+      lds_dma16(cumh + n * C + 4 * lane, ltile);
   };
   // MFMA A operands.  Khat / P (16 chunks per row): rows 16t + ln, logical chunk
   // 4c + lg.  V^T (8 chunks per row): rows 16t + ln, logical chunk 4c + lg, c < 2.
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   auto set_seeds = [&]() __attribute__((always_inline)) {
     const float sv = (FOX ? cq : 0.f) - mrun + kOff;
     seed = f4{sv, sv, sv, sv};
-    mrun_min = -wave_max(-mrun);
+    mrun_min = -wave_max_dpp(-mrun);
   };
   lacc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s2 += qf[t][i] * qf[t][i];
-    return sqrtf(wave_max(grp_sum(s2)));
+    return sqrtf(wave_max_dpp(grp_sum(s2)));
   };
 
   // ---- diagonal blocks, and the operands of key block 2p ------------------------------
@@ -342,16 +342,26 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   to_b_operands(acc_cur);
 
   // ---- right-to-left scan ----------------------------------------------------------
-  float pn = pnorm[bh * Nb + 2 * p];
-  float kn = kmax_blk[bh * Nb + 2 * p];
+  // Per-block transition norms and key maxima, 64 blocks per register window
+  // (lane j holds block wb - j).  Vector loads: the waits on LDS reads in the
+  // loop then never include a scalar-memory fetch.
+  int wb = 2 * p;
+  float pnw, knw;
+  auto load_window = [&]() __attribute__((always_inline)) {
+    const int64_t m = bh * Nb + (wb >= lane ? wb - lane : 0);
+    pnw = pnorm[m];
+    knw = kmax_blk[m];
+  };
+  load_window();
   auto step = [&](int n, auto st) __attribute__((always_inline)) {
     using SN = std::integral_constant<int, 1 - decltype(st)::value>;
     const _Float16* tK = tileK(st);
     const _Float16* tV = tileV(st);
-    const float pn_cur = pn, kn_cur = kn;
-    if (n > 0) {
-      pn = pnorm[bh * Nb + n - 1];
-      kn = kmax_blk[bh * Nb + n - 1];
+    const float pn_cur = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pnw), wb - n));
+    const float kn_cur = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(knw), wb - n));
+    if (n > 0 && wb - n == 63) {  // block n-1 opens the next window
+      wb = n - 1;
+      load_window();
     }
     if (n > 0) {
       dmaK(n - 1, tileK(SN{}));

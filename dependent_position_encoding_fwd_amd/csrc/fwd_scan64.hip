@@ -66,11 +66,13 @@ __device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // Barrier that also publishes every direct-to-LDS load this wave issued.  The
 // wait (vmcnt(0) lgkmcnt(0)) is a builtin so that the compiler knows every
-// earlier load has landed; the barrier itself is an asm statement with a
-// memory clobber so that no LDS access moves across it.
+// earlier load has landed; the asm statement repeats the vmcnt wait, since the
+// compiler does not see the direct-to-LDS loads (they are issued from asm),
+// and holds the barrier, with a memory clobber so that no LDS access moves
+// across it.
 __device__ __forceinline__ void sync_dma() {
   __builtin_amdgcn_s_waitcnt(0x0070);
-  asm volatile("s_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
   auto dma = [&](const char* gtile, _Float16* ltile) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(gtile + goff[i], ltile + (2 * wave + i) * 512, 16, 0, 0);
+      lds_dma16(gtile + goff[i], ltile + (2 * wave + i) * 512);
   };
   // stage tiles, selected at compile time
   using S0 = std::integral_constant<int, 0>;
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
       const float sv = (FOX ? cq[ct] : 0.f) - mrun[ct] + kOff;
       seed[ct] = f4{sv, sv, sv, sv};
     }
-    mrun_min = -wave_max(-fminf(mrun[0], mrun[1]));
+    mrun_min = -wave_max_dpp(-fminf(mrun[0], mrun[1]));
   };
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
         for (int i = 0; i < 4; ++i) s2 += qf[ct][t][i] * qf[ct][t][i];
       mx = fmaxf(mx, grp_sum(s2));
     }
-    return sqrtf(wave_max(mx));
+    return sqrtf(wave_max_dpp(mx));
   };
 
   // ---- diagonal blocks, and the operands of key block 2p ------------------------------
@@ -381,9 +383,17 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
   to_b_operands(acc_cur);
 
   // ---- right-to-left scan ----------------------------------------------------------
-  // pnorm of the block being scanned, fetched one block ahead
-  float pn = pnorm[bh * Nb + 2 * p];
-  float kn = kmax_blk[bh * Nb + 2 * p];
+  // Per-block transition norms and key maxima, 64 blocks per register window
+  // (lane j holds block wb - j).  Vector loads: the waits on LDS reads in the
+  // loop then never include a scalar-memory fetch.
+  int wb = 2 * p;
+  float pnw, knw;
+  auto load_window = [&]() __attribute__((always_inline)) {
+    const int64_t m = bh * Nb + (wb >= lane ? wb - lane : 0);
+    pnw = pnorm[m];
+    knw = kmax_blk[m];
+  };
+  load_window();
   // one key block; its stage (n & 1, block 2p in stage 0) is a compile-time constant
   auto step = [&](int n, auto st) __attribute__((always_inline)) {
     using SN = std::integral_constant<int, 1 - decltype(st)::value>;
@@ -398,10 +408,11 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
         if (n > 0) ckn[kt] = *reinterpret_cast<const f4*>(cumh + (n - 1) * C + 16 * kt + 4 * lg);
       }
     }
-    const float pn_cur = pn, kn_cur = kn;
-    if (n > 0) {
-      pn = pnorm[bh * Nb + n - 1];
-      kn = kmax_blk[bh * Nb + n - 1];
+    const float pn_cur = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pnw), wb - n));
+    const float kn_cur = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(knw), wb - n));
+    if (n > 0 && wb - n == 63) {  // block n-1 opens the next window
+      wb = n - 1;
+      load_window();
     }
     // this block's lo parts (fetched a block ahead) into their LDS stage; the
     // next block's hi parts, and its lo parts when it will need them

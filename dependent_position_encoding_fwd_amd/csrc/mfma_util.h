@@ -75,5 +75,32 @@ __device__ __forceinline__ float grp_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Direct-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at lds + 16 l.  Issued from asm: the compiler's wait insertion
+// treats an LDS DMA it can see as unordered with LDS reads and then waits for
+// every outstanding LDS read at each use (lgkmcnt(0)) until the DMA is waited
+// for.  Here the caller waits for the data (s_waitcnt vmcnt(0), then a
+// barrier) before any wave reads them, and compiler-counted waits on its own
+// loads stay safe because they only ever over-wait.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
+}
+
+// Max over the 64 lanes of a wave with no address registers: the four lane
+// groups through the lane swaps above, then the 16 lanes of a row through DPP
+// moves (neighbours within a quad, then the half-row and row mirrors).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = grp_max(x);
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+}
+
 }  // namespace mfma
 }  // namespace path
