@@ -92,7 +92,7 @@ FwdWs fwd_layout(int dtype, int64_t BH, int64_t L, int64_t d, int64_t Nb, bool w
     w.khl = take(2 * bh * nb * 2 * size_t(kBlk) * dd);
     w.pmat = take(2 * bh * nb * 2 * dd * dd);
     w.qhat = take(sizeof(float) * bh * lp * dd);
-    w.sdiag = take(sizeof(float) * bh * nb * size_t(kBlk) * size_t(kBlk));
+    w.sdiag = take(sizeof(float) * bh * nb * size_t(path::kDiagTri));
     w.kmax = take(sizeof(float) * bh * nb);
     w.kmaxh = take(sizeof(float) * bh);
     w.pnorm = take(sizeof(float) * bh * nb);

@@ -5,11 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace path {
 
 // Tokens per UT block.  The pages fix no block size; 64 matches the wave width
 // and the MFMA tiles (results do not depend on it).
 constexpr int kBlk = 64;
+
+// Start of query row r of a block's in-block logits (padded lower triangle of
+// kDiagTri floats, see launch.h).
+__host__ __device__ constexpr int diag_row(int r) {
+  return 8 * (r >> 2) * ((r >> 2) + 1) + 4 * (r & 3) * ((r >> 2) + 1);
+}
+static_assert(diag_row(kBlk - 1) + kBlk == kDiagTri, "padded triangle size");
 
 struct bf16_t {
   uint16_t bits;

@@ -290,10 +290,12 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   if constexpr (FOX) dmaC(2 * p, sC0);
   f4 sdv[4], ckd[4];
   if (live) {
-    const float* sd = sdiag + (bh * Nb + mb) * (C * C);
+    const float* sd = sdiag + (bh * Nb + mb) * kDiagTri + diag_row(r0 + ln);
     const int r = r0 + ln;
+    // the stored chunks of row r (padded triangle); the others are masked below
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) sdv[kt] = *reinterpret_cast<const f4*>(sd + r * C + 16 * kt + 4 * lg);
+    for (int kt = 0; kt < 4; ++kt)
+      sdv[kt] = 16 * kt + 4 * lg <= r ? *reinterpret_cast<const f4*>(sd + 16 * kt + 4 * lg) : f4{0.f, 0.f, 0.f, 0.f};
     const float* src = qhat + (bh * Nb * C + mb * C + r) * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t) qf[t] = *reinterpret_cast<const f4*>(src + 16 * t + 4 * lg);

@@ -324,12 +324,15 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
   // the first stage (one latency, not three)
   f4 sdv[NCT][4], ckd[4];
   if (live) {
-    const float* sd = sdiag + (bh * Nb + mb) * (C * C);
+    const float* sd = sdiag + (bh * Nb + mb) * kDiagTri;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int r = r0 + 16 * ct + ln;
+      // the stored chunks of row r (padded triangle); the others are masked below
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sdv[ct][kt] = *reinterpret_cast<const f4*>(sd + r * C + 16 * kt + 4 * lg);
+      for (int kt = 0; kt < 4; ++kt)
+        sdv[ct][kt] = 16 * kt + 4 * lg <= r ? *reinterpret_cast<const f4*>(sd + diag_row(r) + 16 * kt + 4 * lg)
+                                            : f4{0.f, 0.f, 0.f, 0.f};
       const float* src = qhat + (bh * Nb * C + mb * C + r) * D;
 #pragma unroll
       for (int t = 0; t < DT; ++t) qf[ct][t] = *reinterpret_cast<const f4*>(src + 16 * t + 4 * lg);

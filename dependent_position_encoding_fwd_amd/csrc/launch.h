@@ -8,6 +8,12 @@
 
 namespace path {
 
+// In-block logits of one block, stored as a padded lower triangle: query row r
+// keeps keys c = 0 .. 4 floor(r/4) + 3 (the keys past r are zeros), so rows
+// 4a .. 4a+3 hold 4 (a + 1) floats each and every row starts on a 16-byte
+// boundary: 2176 floats per block instead of 64 x 64.
+constexpr int kDiagTri = 2176;
+
 // Per-block UT transform in fp32 (one workgroup per 64-token block).  Any of
 // the outputs may be null.  Layouts as documented for path_prepare.
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,

@@ -12,7 +12,8 @@
 //     Qhat = Q - F^T Ut                 (adjusted queries: H_0..H_r applied to q_r)
 //     Sdiag^T = K Q^T - Y Ut            (in-block logits k_c^T H_{c+1}..H_r q_r, c <= r)
 // Outputs (per block): Khat and P as fp16 hi/lo rows with the reduction
-// index in mfma_perm order, c2*Qhat and c2*Sdiag in fp32, max |khat_c|, and
+// index in mfma_perm order, c2*Qhat and c2*Sdiag in fp32 (Sdiag as a padded
+// lower triangle, keys c <= r of query r), max |khat_c|, and
 // V^T in fp16 with the keys in mfma_perm order (zero past the sequence end),
 // the layout in which the scan feeds values to the matrix cores.
 //
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     // Sdiag^T[c][r] = (K Q^T)[c][r] - sum_b Y[c][b] Ut[b][r]   (tiles mt < 4)
     // Qhat^T[e][r] = Q^T[e][r] - sum_b F^T[e][b] Ut[b][r]     (tiles et < DT)
     // formed side by side: independent products on the same B operands
-    float* sd = sdiag + (bh * Nb + n) * (C * C);
+    float* sd = sdiag + (bh * Nb + n) * kDiagTri + diag_row(r);
     float* qd = qhat + ((bh * Nb + n) * C + r) * D;
     constexpr int NX = DT > 4 ? DT : 4;
 #pragma unroll
@@ -617,14 +618,14 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
         if (x < 4) sacc = mma(sh, ub[kc].hi, sacc);
         if (x < DT) qacc = mma(qh, ub[kc].hi, qacc);
       }
-      if (x < 4) {
+      if (x < 4 && 16 * x + 4 * lg <= r) {  // chunks of the padded triangle
         f4 out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = 16 * x + 4 * lg + i;
           out[i] = (c <= r && r < valid) ? c2 * sacc[i] : 0.f;
         }
-        *reinterpret_cast<f4*>(sd + r * C + 16 * x + 4 * lg) = out;
+        *reinterpret_cast<f4*>(sd + 16 * x + 4 * lg) = out;
       }
       if (x < DT) *reinterpret_cast<f4*>(qd + 16 * x + 4 * lg) = (r < valid) ? qacc * c2 : f4{0.f, 0.f, 0.f, 0.f};
     }
