@@ -59,8 +59,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 //     2^-11 sqrt(2/3) |q| |k| / sqrt(d),
 // sqrt(d) below the worst case (all errors aligned).  AUTO drops a key block's
 // lo terms while this estimate, taken with the largest transported query norm
-// of the tile and the largest key norm of the head, is at most half the lse
-// tolerance (kAutoRmsNats).  The scan kernels test
+// of the tile and the largest key norm of the block (its own logits) or of the
+// head (the query transport, whose error reaches every earlier block), is at
+// most half the lse tolerance (kAutoRmsNats).  The scan kernels test
 //     |Qt|_max |khat|_max 2^-10 > tau
 // so tau = kAutoRmsNats log2(e) sqrt(6) sqrt(d).  This is an estimate, not a
 // bound: ACCURATE runs the split everywhere.

@@ -428,7 +428,10 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     if (acc_cur) {
-      if (work) {  // the lo tiles were published by the previous block's barrier
+      // the lo tiles were published by the previous block's barrier.  The
+      // logits' own correction needs only this block's max |khat|; the
+      // transport's (below) reaches every later block and keeps the head's.
+      if (work && (accurate_all || qbound * kn_cur * 0.0009765625f > tau)) {
 #pragma unroll
         for (int c = 0; c < DC; ++c)
 #pragma unroll

@@ -467,7 +467,9 @@ __global__ __launch_bounds__(kNT, 2) void scan64_kernel(
     if (acc_cur) {
       // every thread's share of the lo tiles is in LDS (no wait on the prefetch)
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (work) {
+      // The logits' own correction needs only this block's max |khat|; the
+      // transport's (below) reaches every later block and keeps the head's.
+      if (work && (accurate_all || qbound * kn_cur * 0.0009765625f > tau)) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
 #pragma unroll

@@ -57,9 +57,11 @@ typedef enum { PATH_F32 = 0, PATH_BF16 = 1 } path_dtype;
  * split of its fp32 value, on every key block.  AUTO uses the split only on
  * the key blocks where a run-time estimate of the logit rounding error of
  * plain half-precision operands (the rms of d independent roundings, with the
- * tile's largest transported query norm and the head's largest key norm)
- * exceeds half the lse tolerance of 1e-3; transported queries shrink block by
- * block, so these are the blocks nearest the query.  AUTO's switch is an
+ * tile's largest transported query norm) exceeds half the lse tolerance of
+ * 1e-3: for the block's own logits with the block's largest key norm, for
+ * the query transport (whose error reaches every earlier key block) with the
+ * head's largest key norm.  Transported queries shrink block by block, so
+ * these are the blocks nearest the query.  AUTO's switch is an
  * estimate, not a bound; ACCURATE is the mode with no such assumption.
  * fp32 inputs always take the fp32 path and ignore this flag.
  */
