@@ -172,14 +172,15 @@ def _short_other(name: str) -> str:
 def scan_algorithmic_bytes(B, H, L, d):
     """Bytes the scan must move at least once: its workspace inputs (fp16
     hi/lo keys, fp16 hi/lo block transitions, fp32 adjusted queries, fp32
-    diagonal logits, fp16 V^T, per-block norms and prefix) and o, lse out."""
+    diagonal logits as a padded lower triangle of 2176 floats per block, fp16
+    V^T, per-block norms, value exponents and prefix) and o, lse out."""
     Nb = (L + 63) // 64
     bh = B * H
     khl = bh * Nb * 2 * 64 * d * 2
     pmat = bh * Nb * 2 * d * d * 2
     qhat = bh * Nb * 64 * d * 4
-    sdiag = bh * Nb * 64 * 64 * 4
-    small = bh * Nb * (4 + 4 + 64 * 4) + bh * 4
+    sdiag = bh * Nb * 2176 * 4
+    small = bh * Nb * (4 + 4 + 4 + 64 * 4) + bh * 8
     v = bh * L * d * 2
     o = bh * L * d * 2
     lse = bh * L * 4
