@@ -28,6 +28,8 @@
 //     of 8 chunks (V^T) at j ^ (r & 7), so that the MFMA operand reads (16
 //     rows, one chunk column) run at the full LDS read rate.
 // Each tile is its own LDS object and every access names it at compile time.
+// The direct loads are issued from asm (lds_dma16), so the compiler's waits on
+// LDS reads stay counted; the barriers that publish a stage wait for them.
 // Value range: prepare stores block n's V^T times 2^-e_n (e_n > 0 only when
 // the block holds |v| >= 2^15) and E = max_n e_n per head.  O accumulates in
 // units of 2^E: on a block with e_n < E (never on an ordinary head, where all

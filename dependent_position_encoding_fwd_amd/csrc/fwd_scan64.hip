@@ -8,8 +8,9 @@
 // boundary-adjusted queries, and walks key blocks n = 2p .. 0 with
 //     S^T = Khat_n Qt - m,  online softmax (exp2),  O^T += V_n^T P^T,  Qt = P_n Qt.
 // Products take fp16 operands and fp32 accumulators; a computed fp32 operand
-// (Qt) is split into fp16 hi + lo on the blocks where a bound says the lo part
-// matters (split precision), and probabilities are 2^(s - m + 7) in fp16.
+// (Qt) is split into fp16 hi + lo on the blocks where a run-time estimate of
+// the rounding error says the lo part matters (split precision), and
+// probabilities are 2^(s - m + 7) in fp16.
 //
 // The data movement is built for CDNA4:
 //   * Khat_n, P_n and V_n^T (fp16, 8 KB each) travel global -> LDS with
@@ -36,8 +37,9 @@
 //
 // LDS: 8 tiles x 8 KB = 64 KB per workgroup, so two workgroups share a CU.
 // Each tile is its own LDS object and every access names its object at
-// compile time (the scan is unrolled by the two stages), which lets the
-// compiler see that reading one stage need not wait for loads into the other.
+// compile time (the scan is unrolled by the two stages).  The direct loads are
+// issued from asm (lds_dma16), so the compiler's waits on LDS reads stay
+// counted; the barrier that publishes a stage waits for them.
 #include <math.h>
 
 #include <type_traits>
