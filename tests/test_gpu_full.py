@@ -8,6 +8,8 @@ oracle, element by element.
     The oracle runs once per workload and serves both precisions.
   * The cache-8192 decode step (B=64, H=16, d=64), plain and gated: every
     head's o, lse, updated key cache and appended slot.
+  * The scan variants those workloads leave out (gated at d = 64, ungated at
+    d = 128) at L = 4096, every row of 8 heads.
 
 The worst errors of each workload, and where they occur, are printed.  Bars
 (element-wise max-abs): o <= 2e-2 (bf16 storage), lse <= 1e-3; the updated
@@ -140,3 +142,26 @@ def test_decode_config5_full(fox):
     assert torch.equal(vc[:, :, :n], x["v_cache"][:, :, :n])
     if fox:
         assert torch.equal(cc[:, :, :n], cum[:, :, :n])
+
+
+@pytest.mark.parametrize("precision", ["auto", "accurate"])
+@pytest.mark.parametrize("d,fox", [(64, True), (128, False)])
+def test_long_other_kernel_variants(d, fox, precision):
+    """The scan variants the five workloads leave out, at training length: gated
+    attention at d = 64 and ungated at d = 128 (B=1, H=8, L=4096, scale 1/8),
+    every row of every head against the oracle."""
+    B, H, L, scale = 1, 8, 4096, 0.125
+    print(f"[full] B={B} H={H} L={L} d={d} fox={fox} precision={precision}", flush=True)
+    x = synthetic.fwd_inputs(B, H, L, d, "bf16", seed=4000 + d + int(fox), fox=fox)
+    ro, rl = oracle.path_fwd(x["q"], x["k"], x["v"], x["w"], x["beta"], x["log_forget"], scale)
+    g = {n: (t.to(DEV) if t is not None else None) for n, t in x.items()}
+    o, lse = pa.path_attn_fwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_forget"], scale=scale,
+                              precision=precision)
+    torch.cuda.synchronize()
+    on, ln = _np(o), _np(lse)
+    assert np.all(np.isfinite(on)) and np.all(np.isfinite(ln))
+    eo, wo = _worst(np.abs(on - ro))
+    el, wl = _worst(np.abs(ln - rl))
+    print(f"    all {B * H} heads x {L} rows: max|do|={eo:.3e} at {wo}  max|dlse|={el:.3e} at {wl}", flush=True)
+    assert eo <= TOL_O, (eo, wo)
+    assert el <= TOL_LSE, (el, wl)
