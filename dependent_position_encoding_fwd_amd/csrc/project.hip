@@ -14,8 +14,9 @@
 // normalised in the epilogue) or the u rows of 128 consecutive heads (their
 // beta logits).  Eight waves, each 32 tokens x 128 columns.
 // Products are 16x16x32 bf16 MFMAs with fp32 accumulation.  Dm is reduced in
-// chunks of 64 that travel global -> LDS with direct-to-LDS loads through a
-// ring of three stages: chunk c + 2 is in flight while chunk c is multiplied,
+// chunks of 64 that travel global -> LDS with direct-to-LDS loads (issued from
+// asm, lds_dma16) through a ring of three stages: chunk c + 2 is in flight
+// while chunk c is multiplied,
 // and one barrier per chunk both publishes the next stage and frees the oldest.
 // Every load is unconditional: rows past the tokens or the weight rows read a
 // clamped row, whose products land only in outputs that are not written.
@@ -70,11 +71,15 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// s_waitcnt with expcnt and lgkmcnt left open and vmcnt = N (N < 16).
+// s_waitcnt with expcnt and lgkmcnt left open and vmcnt = N (N < 16).  The
+// direct-to-LDS loads are issued from asm (lds_dma16: the compiler then keeps
+// its waits on LDS reads counted), so the compiler does not count them: the
+// wait is repeated in asm, where it cannot be dropped.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 16, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Calls f(integral_constant<int, I>) for each I of the sequence, in order.
@@ -149,10 +154,10 @@ __global__ __launch_bounds__(kPT, kOcc) void project_kernel(
     const int64_t off = static_cast<int64_t>(c) * (kPK * 2);
 #pragma unroll
     for (int i = 0; i < kALd; ++i)
-      __builtin_amdgcn_global_load_lds(asrc[i] + off, adst + (i * kPW + wv) * 512, 16, 0, 0);
+      mfma::lds_dma16(asrc[i] + off, adst + (i * kPW + wv) * 512);
 #pragma unroll
     for (int i = 0; i < kBLd; ++i)
-      __builtin_amdgcn_global_load_lds(bsrc[i] + off, bdst + (i * kPW + wv) * 512, 16, 0, 0);
+      mfma::lds_dma16(bsrc[i] + off, bdst + (i * kPW + wv) * 512);
   };
   auto dma = [&](int c, auto st) __attribute__((always_inline)) { dma_to(c, stageA(st), stageB(st)); };
 
