@@ -85,9 +85,6 @@ __device__ __forceinline__ int perm32(int d) {  // mfma_perm of the prepare stag
   return (d & ~31) | (((d >> 2) & 3) << 3) | (((d >> 4) & 1) << 2) | (d & 3);
 }
 
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
-
-
 // Broadcast lane k of each quad of lanes to the whole quad (k folds to a constant).
 __device__ __forceinline__ float quad_bcast(float x, int k) {
   const int v = __float_as_int(x);
@@ -112,7 +109,7 @@ struct PGeo {
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256) void prepare_mfma_kernel(
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
     int64_t L, int Nb, float c2, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     _Float16* __restrict__ khat, _Float16* __restrict__ pmat, float* __restrict__ qhat,
@@ -123,12 +120,12 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   constexpr int GP = 68;  // row pitch (floats) of G in GY; 64 rows of it fit the C x TP floats
 
   // LDS (halfs unless noted).  WK holds W rows then K rows; it is reused for
-  // -F^T rows once the products that read W and K rows are done.
+  // the blocks of T^{-1}, then for -F^T rows.  GY holds G (quarter layout),
+  // then X^T rows hi/lo, then -Y rows hi/lo.  The query rows never enter LDS:
+  // each wave reads its own 16 as B operands.
   __shared__ __attribute__((aligned(16))) uint16_t WK[2 * C * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qb[C * RP];
   __shared__ __attribute__((aligned(16))) _Float16 Wt[D * TP];      // W^T rows, perm(b)
-  __shared__ __attribute__((aligned(16))) _Float16 XT[2][C * TP];   // X^T rows hi/lo, perm(a)
-  __shared__ __attribute__((aligned(16))) float GY[C * TP];         // G (quarter layout), then -Y rows hi/lo
+  __shared__ __attribute__((aligned(16))) float GY[C * TP];
   __shared__ float bs[C];
   __shared__ float hn[C];
   __shared__ float kred[4];
@@ -137,6 +134,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   uint16_t* Wb = WK;
   uint16_t* Kb = WK + C * RP;
   _Float16* NY = reinterpret_cast<_Float16*>(GY);  // [2][C*TP]
+  _Float16* XT = NY;                               // [2][C*TP], perm(a)
   _Float16* NFT = reinterpret_cast<_Float16*>(WK); // [2][D*64] (pitch 64, no pad, swizzled chunks)
 
   const int tid = threadIdx.x;
@@ -158,7 +156,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
   // Every load is issued before any is used, from a row clamped into the
   // sequence (rows past its end are zeroed when stored), so they are all in
   // flight together.
-  uint4 wv[VCH], kv[VCH], qv[VCH];
+  uint4 wv[VCH], kv[VCH];
   float br[VCH];
 #pragma unroll
   for (int j = 0; j < VCH; ++j) {
@@ -167,17 +165,28 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     const int rr = r < valid ? r : valid - 1;
     wv[j] = *reinterpret_cast<const uint4*>(w + base + rr * D + 8 * c8);
     kv[j] = *reinterpret_cast<const uint4*>(k + base + rr * D + 8 * c8);
-    qv[j] = *reinterpret_cast<const uint4*>(q + base + rr * D + 8 * c8);
     br[j] = beta[bh * L + t0 + rr];
   }
-  // this lane's key entries for the adjusted keys: row 16w + ln, columns 16et + 4lg .. + 3
+  // this lane's key entries for the adjusted keys: row 16w + ln, columns 16et + 4lg .. + 3,
+  // and its query entries as the B operand of products over the head dim:
+  // row 16w + ln, columns 32c + 8lg .. + 7 (zero past the sequence end)
   uint2 kr[DT];
+  b8 bq[DC];
   {
     const int r = 16 * wave + ln;
     const int rr = r < valid ? r : valid - 1;
 #pragma unroll
     for (int et = 0; et < DT; ++et) {
       kr[et] = *reinterpret_cast<const uint2*>(k + base + rr * D + 16 * et + 4 * lg);  // masked at use
+    }
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      union {
+        uint4 u;
+        b8 v;
+      } t;
+      t.u = *reinterpret_cast<const uint4*>(q + base + rr * D + 32 * c + 8 * lg);
+      bq[c] = t.v;
     }
   }
   // value rows, already in the A-operand layout of the transposing product:
@@ -196,12 +205,11 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     const int r = idx / (D / 8), c8 = idx % (D / 8);
     const uint4 zero = make_uint4(0, 0, 0, 0);
     if (r >= valid) {
-      wv[j] = kv[j] = qv[j] = zero;
+      wv[j] = kv[j] = zero;
       br[j] = 0.f;
     }
     *reinterpret_cast<uint4*>(Wb + r * RP + 8 * c8) = wv[j];
     *reinterpret_cast<uint4*>(Kb + r * RP + 8 * c8) = kv[j];
-    *reinterpret_cast<uint4*>(Qb + r * RP + 8 * c8) = qv[j];
     const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
     float sq = 0.f;
 #pragma unroll
@@ -217,6 +225,10 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       // of a transported query across the block
       hn[r] = fmaxf(1.f, fabsf(1.f - br[j] * sq));
     }
+  }
+  if (16 * wave + ln >= valid) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) bq[c] = b8{};
   }
   __syncthreads();
 
@@ -239,15 +251,14 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     const int col = 32 * c + 8 * lg;
     const b8 bw = *reinterpret_cast<const b8*>(Wb + (16 * wave + ln) * RP + col);
     const b8 bk = *reinterpret_cast<const b8*>(Kb + (16 * wave + ln) * RP + col);
-    const b8 bq = *reinterpret_cast<const b8*>(Qb + (16 * wave + ln) * RP + col);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const b8 aw = *reinterpret_cast<const b8*>(Wb + (16 * mt + ln) * RP + col);
       const b8 ak = *reinterpret_cast<const b8*>(Kb + (16 * mt + ln) * RP + col);
       gt[mt] = mmb(aw, bw, gt[mt]);    // G[s][t]      = w_s . w_t
       zt[mt] = mmb(aw, bk, zt[mt]);    // Z^T[a][c]    = w_a . k_c
-      ut[mt] = mmb(aw, bq, ut[mt]);    // U[b][r]      = w_b . q_r
-      skq[mt] = mmb(ak, bq, skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
+      ut[mt] = mmb(aw, bq[c], ut[mt]);    // U[b][r]      = w_b . q_r
+      skq[mt] = mmb(ak, bq[c], skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -383,11 +394,11 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       for (int i = 0; i < 4; ++i) lo[i] = x[i] - static_cast<float>(hv.v[i]);
       lv.v = to_h8(lo, lo);
       const int off = cc * TP + 32 * (I >> 1) + 8 * lg + 4 * (I & 1);
-      *reinterpret_cast<uint2*>(&XT[0][off]) = make_uint2(hv.u.x, hv.u.y);
-      *reinterpret_cast<uint2*>(&XT[1][off]) = make_uint2(lv.u.x, lv.u.y);
+      *reinterpret_cast<uint2*>(&XT[off]) = make_uint2(hv.u.x, hv.u.y);
+      *reinterpret_cast<uint2*>(&XT[C * TP + off]) = make_uint2(lv.u.x, lv.u.y);
     }
   }
-  __syncthreads();  // XT ready; G no longer needed (GY becomes -Y)
+  __syncthreads();  // XT ready (in G's place: G was last read by the substitution)
 
   // ---- Y^T = X^T Z^T (wave w: columns c in tile w) and F = X^T W (rows b,
   // columns e in head-dim tiles et = ET*w .. ET*w + ET - 1): one pass over the
@@ -417,8 +428,8 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
-        const h8 ah = *reinterpret_cast<const h8*>(&XT[0][off]);
-        const h8 al = *reinterpret_cast<const h8*>(&XT[1][off]);
+        const h8 ah = *reinterpret_cast<const h8*>(&XT[off]);
+        const h8 al = *reinterpret_cast<const h8*>(&XT[C * TP + off]);
         yt[mt] = mma(al, b.hi, yt[mt]);
 #pragma unroll
         for (int j = 0; j < ET; ++j) ft[j][mt] = mma(al, bwt[j], ft[j][mt]);
@@ -429,6 +440,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
       }
     }
   }
+  __syncthreads();  // every wave's X^T reads are done: -Y rows take its place
   // -Y rows into NY: lane holds Y^T[b = 16mt+4lg+i][c] = Y[c][b]
   HL yb[2];
 #pragma unroll
@@ -523,7 +535,7 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
     const float vm = wave_max(__uint_as_float(m << 16));
     if (lane == 0) vred[wave] = vm;
   }
-  __syncthreads();  // -Y and -F^T rows complete; XT is free
+  __syncthreads();  // -Y and -F^T rows complete
 
   // V^T[e][perm(c)] in fp16, transposed on the matrix cores: with the value
   // rows as operand A and a 32x16 slice of the identity as operand B, the
@@ -595,8 +607,9 @@ __global__ __launch_bounds__(256) void prepare_mfma_kernel(
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
       f4 sacc = x < 4 ? skq[x < 4 ? x : 0] : f4{0.f, 0.f, 0.f, 0.f}, qacc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qacc[i] = bf2f(Qb[r * RP + 16 * x + 4 * lg + i]);
+      // Q^T tile x: 16 identity rows (offset 16(x&1)) times the query operand
+      // of chunk x/2, exact; the lane gets q_r[16x + 4lg .. + 3]
+      if (x < DT) qacc = mmb(ident[x & 1], bq[x < DT ? x >> 1 : 0], f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         h8 sh, sl, qh, ql;
