@@ -143,7 +143,10 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
   const int ln = lane & 15;
   const int lg = lane >> 4;
   const int n = blockIdx.x % Nb;
-  const int64_t bh = blockIdx.x / Nb;
+  // Heads run from the last to the first.  The scan starts from the first
+  // heads, and the blocks written last are the ones most likely to still sit
+  // in the 256 MB last-level cache when it reads them.
+  const int64_t bh = static_cast<int64_t>(gridDim.x / Nb) - 1 - blockIdx.x / Nb;
   const int64_t t0 = static_cast<int64_t>(n) * C;
   const int valid = static_cast<int>(L - t0 < C ? L - t0 : C);
   const int64_t base = (bh * L + t0) * D;
