@@ -27,8 +27,17 @@ reported the same way.  After the timed steps the gated decode step
 the same numbers of warm-up and timed launches and is reported in
 `decode_fox` on the decode bytes plus 4 bytes per cached key.
 
+Order: one forward call, then the secondary legs (paged decode, backward,
+projection, and the forward on configurations 4 and 3, each with warm-up
+launches of its own), then the W warm-up steps and the K timed steps, then
+the gated decode step and the CPU baseline.  The secondary legs come first so
+that the headline steps start on a GPU whose clocks have settled even when W
+is small: from a cold start the forward's per-step time falls by about a
+quarter over its first hundred steps.  The forward legs of configurations 3
+and 4 are reported in `fwd_config3` and `fwd_config4`.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-ref]
-                    [--fwd-config {2,3,4}] [--fwd-only]
+                    [--no-bwd] [--no-config-legs] [--fwd-config {2,3,4}] [--fwd-only]
 
 `--fwd-only` times the forward steps alone and prints a forward-only line (for
 counter runs under rocprofv3 --pmc).
@@ -122,6 +131,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    # leave out the forward legs of configurations 3 and 4 (profiling runs, whose
+    # per-kernel averages must hold the headline workload's launches only)
+    ap.add_argument("--no-config-legs", action="store_true")
     # counter runs: only the forward (prepare + scan) steps; prints a forward-only line
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--fwd-config", type=int, default=2, choices=[2, 3, 4])
@@ -178,6 +190,27 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    # The secondary legs (paged decode, backward, projection) run first, so the
+    # headline steps below start on a GPU whose clocks have settled: with only a
+    # few warm-up steps they would otherwise still be rising during the timed
+    # steps.  The backward needs the forward's o and lse: one forward call first.
+    # The forward legs of the other two forward configurations come last among
+    # them: from a cold start the forward's per-step time falls by about a
+    # quarter over its first hundred or so steps (0.1 s) while the chip's clocks
+    # settle, and these legs are that much forward work.
+    paged = paged_fox = bwd = proj = None
+    other_fwd = {}
+    if not args.fwd_only:
+        pa.path_fwd_stage_prepare(*fargs, gates, scale=cf.scale, precision=args.precision, workspace=ws)
+        pa.path_fwd_stage_scan(*fargs, ws, gates, scale=cf.scale, precision=args.precision, out=(o, lse))
+        dbytes = decode_bytes(cd.B, cd.H, cd.cache_len, cd.d, 2)
+        paged, paged_fox = paged_leg(pa, xd, gd, cd, dbytes)
+        bwd = None if args.no_bwd else bwd_leg(pa, fargs, gates, cf, o, lse)
+        proj = project_leg(pa, cf)
+        if cid == 2 and not args.no_config_legs:
+            for c in (4, 3):
+                other_fwd[f"fwd_config{c}"] = fwd_leg(pa, c, args.precision)
+
     for _ in range(args.warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -221,10 +254,6 @@ def main():
                 "kernel": f"scan{cf.d}_kernel (right-to-left scan, d={cf.d})", "flops_per_launch": F,
                 "launch_ms": round(scan_ms, 4), "source_sha256": source_hash("scan")}
 
-    paged, paged_fox = paged_leg(pa, xd, gd, cd, dbytes)
-    bwd = None if args.no_bwd else bwd_leg(pa, fargs, gates, cf, o, lse)
-    proj = project_leg(pa, cf)
-
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cf)
@@ -248,6 +277,7 @@ def main():
         "decode_fox": {"ms": round(fox_ms, 4), "GB_per_s": round(fox_gbs, 1), "bytes_model": fbytes,
                        "frac_hbm_peak": round(fox_gbs / PEAK_HBM_GBS, 4),
                        "what": "gated decode step, same cache, forget-gate prefix cache (fp32)"},
+        **other_fwd,
         "decode_paged": paged,
         "decode_paged_fox": paged_fox,
         "bwd": bwd,
@@ -361,6 +391,44 @@ def paged_leg(pa, xd, gd, cd, dbytes, page=256, warmup=20, steps=50):
              "frac_hbm_peak": round(fgbs / PEAK_HBM_GBS, 4),
              "what": f"gated paged decode step, same pages plus the forget-gate prefix cache in the same "
                      f"{page}-slot pages"})
+
+
+def fwd_leg(pa, cid, precision, warmup=20, steps=20):
+    """Times the forward (prepare + scan) on another synthetic configuration:
+    medians of `steps` launches of each stage, bracketed by HIP events on the
+    launch stream."""
+    import torch
+
+    import synthetic
+
+    c = synthetic.CONFIGS[cid]
+    print(f"[bench] forward leg: {c.desc}", file=sys.stderr, flush=True)
+    x = {n: (t.to("cuda:0") if t is not None else None) for n, t in synthetic.config_inputs(cid).items()}
+    g = x.get("log_forget")
+    args = (x["q"], x["k"], x["v"], x["w"], x["beta"])
+    ws = pa.fwd_workspace(x["q"], g)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty(x["beta"].shape, dtype=torch.float32, device="cuda:0")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(warmup + steps):
+        if k >= warmup:
+            evs[k - warmup][0].record()
+        pa.path_fwd_stage_prepare(*args, g, scale=c.scale, precision=precision, workspace=ws)
+        if k >= warmup:
+            evs[k - warmup][1].record()
+        pa.path_fwd_stage_scan(*args, ws, g, scale=c.scale, precision=precision, out=(o, lse))
+        if k >= warmup:
+            evs[k - warmup][2].record()
+    torch.cuda.synchronize()
+    prep = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    scan = statistics.median(e[1].elapsed_time(e[2]) for e in evs)
+    F = flops_path(c.B, c.H, c.L, c.d)
+    tf = F / ((prep + scan) * 1e-3) / 1e12
+    del x, ws, o, lse
+    return {"ms": round(prep + scan, 4), "prepare_ms": round(prep, 4), "scan_ms": round(scan, 4),
+            "flops_model": F, "TFLOP_per_s": round(tf, 3), "frac_bf16_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4),
+            "scan_frac_bf16_peak": round(F / (scan * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+            "what": f"{c.desc}, precision {precision}, median of {steps} after {warmup} warm-up launches"}
 
 
 def project_leg(pa, cf, warmup=20, steps=50):
