@@ -141,7 +141,7 @@ int path_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, const vo
   if (khat && !k) return PATH_ERR_NULL;
   if (cum && !log_forget) return PATH_ERR_NULL;
   if (tinv || qhat || khat || pT) {
-    st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, tinv, qhat, khat, pT,
+    st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, tinv, nullptr, qhat, khat, pT,
                                              stream));
     if (st) return st;
   }
@@ -188,7 +188,7 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
   if (dtype == PATH_F32) {
     float* khat = reinterpret_cast<float*>(ws + a.lay.khat);
     float* pT = reinterpret_cast<float*>(ws + a.lay.pT);
-    st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, nullptr, k, w, beta, nullptr,
+    st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, nullptr, k, w, beta, nullptr, nullptr,
                                              nullptr, khat, pT, stream));
     if (st) return st;
     if (log_forget) {
@@ -406,7 +406,7 @@ int path_decode_step_fox(int64_t B, int64_t H, int64_t d, int dtype, float scale
 namespace {
 
 struct BwdLayout {
-  size_t qhat, khat, pT, cum, Dv, dqh, rsum, dkh, dP, dV, csum, dc, scratch, total;
+  size_t qhat, khat, pT, minv, cum, Dv, dqh, rsum, dkh, dP, dV, csum, dc, scratch, total;
   int64_t zero_count;
 };
 
@@ -425,6 +425,7 @@ bool bwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget, 
   w->qhat = take(bh * l * dd);
   w->khat = take(bh * l * dd);
   w->pT = take(bh * nb * dd * dd);
+  w->minv = take(bh * nb * size_t(kBlk) * kBlk);
   if (with_forget) w->cum = take(bh * l);
   w->Dv = take(bh * l);
   w->dqh = take(bh * l * dd);
@@ -489,11 +490,12 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
   a.dw = dw;
   a.dbeta = dbeta;
   a.dlog_forget = log_forget ? dlog_forget : nullptr;
-  a.ws = path::BwdWs{at(lay.qhat), at(lay.khat), at(lay.pT), log_forget ? at(lay.cum) : nullptr, at(lay.Dv),
+  a.ws = path::BwdWs{at(lay.qhat), at(lay.khat), at(lay.pT), at(lay.minv), log_forget ? at(lay.cum) : nullptr,
+                     at(lay.Dv),
                      at(lay.dqh), at(lay.rsum), at(lay.dkh), at(lay.dP), at(lay.dV), at(lay.csum), at(lay.dc),
                      at(lay.scratch), at(lay.dkh), lay.zero_count};
-  if ((st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.qhat, a.ws.khat,
-                                                a.ws.pT, stream))))
+  if ((st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.minv, a.ws.qhat,
+                                                a.ws.khat, a.ws.pT, stream))))
     return st;
   if (log_forget && (st = hip_status(path::launch_prefix_sum(BH, L, log_forget, a.ws.cum, stream)))) return st;
   return hip_status(path::launch_bwd(dtype, d, a, stream));

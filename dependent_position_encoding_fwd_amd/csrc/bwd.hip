@@ -33,6 +33,8 @@
 // d log f_s = sum_{i>=s} dc_i (fp64 suffix sums).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "tile_f32.h"
@@ -683,12 +685,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      a.ws.qhat, a.ws.khat, a.ws.pT, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum,
                      a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.csum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(64 * block_waves<D>()), 0, stream, L, Nb, BH, a.scale,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k), v, static_cast<const T*>(a.w), a.beta, dO,
-                     a.ws.cum, a.lse, a.ws.Dv, a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum,
-                     static_cast<T*>(a.dq), static_cast<T*>(a.dk), static_cast<T*>(a.dv), static_cast<T*>(a.dw),
-                     a.dbeta, a.ws.dc);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (D == 64) {
+    const BwdBlockArgs b{BH, L, a.scale, a.q, a.k, a.v, a.w, a.dout, a.beta, a.ws.cum, a.lse, a.ws.Dv, a.ws.minv,
+                         a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum, a.dq, a.dk, a.dv, a.dw,
+                         a.dbeta, a.ws.dc};
+    if ((e = launch_bwd_block_ut(std::is_same_v<T, float> ? 0 : 1, b, stream)) != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(64 * block_waves<D>()), 0, stream, L, Nb, BH,
+                       a.scale, static_cast<const T*>(a.q), static_cast<const T*>(a.k), v, static_cast<const T*>(a.w),
+                       a.beta, dO, a.ws.cum, a.lse, a.ws.Dv, a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum,
+                       a.ws.csum, static_cast<T*>(a.dq), static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                       static_cast<T*>(a.dw), a.dbeta, a.ws.dc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (FOX) {
     hipLaunchKernelGGL(bwd_suffix_kernel, dim3(static_cast<unsigned>(BH)), dim3(kT), 0, stream, L, a.ws.dc,
                        a.dlog_forget);

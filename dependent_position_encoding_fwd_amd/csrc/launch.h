@@ -18,7 +18,7 @@ constexpr int kDiagTri = 2176;
 // the outputs may be null.  Layouts as documented for path_prepare.
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
                               const void* q, const void* k, const void* w, const float* beta,
-                              float* tinv, float* qhat, float* khat, float* pT,
+                              float* tinv, float* minv, float* qhat, float* khat, float* pT,
                               hipStream_t stream);
 
 // Per-block UT data in the layout of the matrix-core forward (bf16 inputs),
@@ -92,7 +92,7 @@ hipError_t launch_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d
 // Backward pass (fp32 arithmetic).  Workspace regions, all fp32; the run from
 // zero_begin over zero_count floats (dkh, dP, dV, csum) is cleared first.
 struct BwdWs {
-  float *qhat, *khat, *pT, *cum, *Dv, *dqh, *rsum, *dkh, *dP, *dV, *csum, *dc, *scratch;
+  float *qhat, *khat, *pT, *minv, *cum, *Dv, *dqh, *rsum, *dkh, *dP, *dV, *csum, *dc, *scratch;
   float* zero_begin;
   int64_t zero_count;
 };
@@ -111,5 +111,15 @@ struct BwdArgs {
 };
 // Launches everything after the fp32 prepare and the gate prefix sums.
 hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream);
+// The in-block part of the backward at d = 64 in matrix form (bwd_block_ut.hip).
+struct BwdBlockArgs {
+  int64_t BH, L;
+  float scale;
+  const void *q, *k, *v, *w, *dO;
+  const float *beta, *cum, *lse, *Dv, *minv, *dqh, *dkh, *dP, *dV, *rsum, *csum;
+  void *dq, *dk, *dv, *dw;
+  float *dbeta, *dc;
+};
+hipError_t launch_bwd_block_ut(int dtype, const BwdBlockArgs& a, hipStream_t stream);
 
 }  // namespace path

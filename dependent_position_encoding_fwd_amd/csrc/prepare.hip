@@ -6,8 +6,10 @@
 // H_0 H_1 ... H_63 with H_s = I - beta_s w_s w_s^T, equals I - W^T T^{-1} W
 // where W stacks the w_s and T is upper triangular,
 //     T = diag(1/beta) + strict_upper(W W^T).
-// T^{-1} is formed without dividing by beta (beta = 0 must give H = I) as the
-// solution of (I + diag(beta) strict_upper(W W^T)) X = diag(beta).
+// T^{-1} is formed without dividing by beta (beta = 0 must give H = I): the
+// unit upper triangular M = (I + diag(beta) strict_upper(W W^T))^{-1} by back
+// substitution, and T^{-1} = M diag(beta).  M itself is an output too (the
+// backward's in-block gradients use it).
 // [§3 "Algoritmo Estilo FlashAttention"]: the boundary-adjusted query of local
 // row r carries the block's transitions up to r, and the adjusted key of row c
 // the transitions after c:
@@ -26,14 +28,15 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void prepare_f32_kernel(
     int64_t L, int Nb, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ w, const float* __restrict__ beta, float* __restrict__ tinv_out,
-    float* __restrict__ qhat_out, float* __restrict__ khat_out, float* __restrict__ pT_out) {
+    float* __restrict__ minv_out, float* __restrict__ qhat_out, float* __restrict__ khat_out,
+    float* __restrict__ pT_out) {
   constexpr int C = kBlk;
   constexpr int CP = C + 1;
   constexpr int DP = D + 1;
   __shared__ float Ws[C][DP];  // rows w_s of the block (zero past L)
   __shared__ float Xs[C][DP];  // k rows, then q rows, then F = T^{-T} W
   __shared__ float Gs[C][CP];  // strict_upper(W W^T), then masked W k / W q products, then Y
-  __shared__ float Ts[C][CP];  // T^{-1}
+  __shared__ float Ts[C][CP];  // M (T^{-1} = M diag(beta))
   __shared__ float bs[C];      // (67 KB at d = 64: two workgroups per CU)
 
   const int tid = threadIdx.x;
@@ -68,16 +71,16 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
                    [&](int r, int t, float x) { Gs[r][t] = t > r ? x : 0.f; });
   __syncthreads();
 
-  // Back substitution, one column of X = T^{-1} per thread, last row first:
-  // X[r][c] = beta_r * (delta_rc - sum_{r<t<=c} G[r][t] X[t][c]).
+  // Back substitution, one column of M per thread, last row first:
+  // M[r][c] = delta_rc - beta_r * sum_{r<t<=c} G[r][t] M[t][c].
   if (tid < C) {
     const int c = tid;
     for (int r = C - 1; r >= 0; --r) {
       float x = 0.f;
       if (r <= c) {
-        float acc = (r == c) ? 1.f : 0.f;
-        for (int t = r + 1; t <= c; ++t) acc -= Gs[r][t] * Ts[t][c];
-        x = bs[r] * acc;
+        float acc = 0.f;
+        for (int t = r + 1; t <= c; ++t) acc += Gs[r][t] * Ts[t][c];
+        x = (r == c ? 1.f : 0.f) - bs[r] * acc;
       }
       Ts[r][c] = x;
     }
@@ -86,6 +89,10 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
 
   if (tinv_out) {
     float* dst = tinv_out + (bh * Nb + n) * (C * C);
+    for (int idx = tid; idx < C * C; idx += 256) dst[idx] = Ts[idx / C][idx % C] * bs[idx % C];
+  }
+  if (minv_out) {
+    float* dst = minv_out + (bh * Nb + n) * (C * C);
     for (int idx = tid; idx < C * C; idx += 256) dst[idx] = Ts[idx / C][idx % C];
   }
 
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     __syncthreads();
     // Y = Z T^{-1}: Y[c][a] = sum_{c<s<=a} Z[c][s] T^{-1}[s][a] (= (T^{-T} z_c)_a; both factors
     // vanish outside that range, so the full product is the same sum), into Gs
-    gs_times([&](int s2, int a) { return Ts[s2][a]; });
+    gs_times([&](int s2, int a) { return Ts[s2][a] * bs[a]; });
     __syncthreads();
     // khat = K - Y W  (Y[c][a] = 0 for a <= c)
     tile_mm<C, D, C>([&](int c, int a) { return Gs[c][a]; }, [&](int a, int e) { return Ws[a][e]; },
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
                      [&](int r, int t, float x) { Gs[r][t] = t <= r ? x : 0.f; });
     __syncthreads();
     // Y = A T^{-T}: Y[r][a] = sum_{a<=t<=r} T^{-1}[a][t] A[r][t] (= (T^{-1} a_r)_a, 0 for a > r), into Gs
-    gs_times([&](int t, int a) { return Ts[a][t]; });
+    gs_times([&](int t, int a) { return Ts[a][t] * bs[t]; });
     __syncthreads();
     // qhat = Q - Y W
     tile_mm<C, D, C>([&](int r, int a) { return Gs[r][a]; }, [&](int a, int e) { return Ws[a][e]; },
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
 
   if (pT_out) {
     // F = T^{-T} W: F[s][e] = sum_{t<=s} T^{-1}[t][s] W[t][e]
-    tile_mm<C, D, C>([&](int s2, int t) { return Ts[t][s2]; }, [&](int t, int e) { return Ws[t][e]; },
+    tile_mm<C, D, C>([&](int s2, int t) { return Ts[t][s2] * bs[s2]; }, [&](int t, int e) { return Ws[t][e]; },
                      [&](int s2, int e, float x) { Xs[s2][e] = x; });
     __syncthreads();
     // P^T = I - W^T F
@@ -247,26 +254,26 @@ hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* k
 
 template <typename T, int D>
 static hipError_t launch_prepare_t(int64_t B, int64_t H, int64_t L, const void* q, const void* k,
-                                   const void* w, const float* beta, float* tinv, float* qhat,
+                                   const void* w, const float* beta, float* tinv, float* minv, float* qhat,
                                    float* khat, float* pT, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   dim3 grid(static_cast<unsigned>(B * H * Nb));
   hipLaunchKernelGGL((prepare_f32_kernel<T, D>), grid, dim3(256), 0, stream, L, Nb,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(w),
-                     beta, tinv, qhat, khat, pT);
+                     beta, tinv, minv, qhat, khat, pT);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
                               const void* q, const void* k, const void* w, const float* beta,
-                              float* tinv, float* qhat, float* khat, float* pT,
+                              float* tinv, float* minv, float* qhat, float* khat, float* pT,
                               hipStream_t stream) {
   if (dtype == 0) {
-    return d == 64 ? launch_prepare_t<float, 64>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream)
-                   : launch_prepare_t<float, 128>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream);
+    return d == 64 ? launch_prepare_t<float, 64>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream)
+                   : launch_prepare_t<float, 128>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream);
   }
-  return d == 64 ? launch_prepare_t<bf16_t, 64>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream)
-                 : launch_prepare_t<bf16_t, 128>(B, H, L, q, k, w, beta, tinv, qhat, khat, pT, stream);
+  return d == 64 ? launch_prepare_t<bf16_t, 64>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream)
+                 : launch_prepare_t<bf16_t, 128>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream);
 }
 
 hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream) {
