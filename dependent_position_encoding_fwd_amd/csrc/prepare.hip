@@ -71,18 +71,19 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
                    [&](int r, int t, float x) { Gs[r][t] = t > r ? x : 0.f; });
   __syncthreads();
 
-  // Back substitution, one column of M per thread, last row first:
+  // Back substitution, last row first:
   // M[r][c] = delta_rc - beta_r * sum_{r<t<=c} G[r][t] M[t][c].
-  if (tid < C) {
-    const int c = tid;
+  // Four lanes (a quad of one wave) per column c: lane qq sums the terms
+  // t = qq (mod 4) and the quad adds its four partial sums; the lane that owns
+  // t = r writes M[r][c], so each lane reads back only its own writes.
+  {
+    const int c = tid >> 2, qq = tid & 3;
     for (int r = C - 1; r >= 0; --r) {
-      float x = 0.f;
-      if (r <= c) {
-        float acc = 0.f;
-        for (int t = r + 1; t <= c; ++t) acc += Gs[r][t] * Ts[t][c];
-        x = (r == c ? 1.f : 0.f) - bs[r] * acc;
-      }
-      Ts[r][c] = x;
+      float acc = 0.f;
+      for (int t = r + 1 + ((qq - r - 1) & 3); t <= c; t += 4) acc += Gs[r][t] * Ts[t][c];
+      acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
+      acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+      if ((r & 3) == qq) Ts[r][c] = r <= c ? (r == c ? 1.f : 0.f) - bs[r] * acc : 0.f;
     }
   }
   __syncthreads();
