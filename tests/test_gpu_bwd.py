@@ -44,10 +44,12 @@ def _cmp(name, got, ref, tol, floor):
     assert err <= tol * (mag if mag > 0 else floor), (name, err, mag, floor)
 
 
-def _bwd_case(B, H, L, d, dtype, scale, seed, fox, chain_forward=False):
+def _bwd_case(B, H, L, d, dtype, scale, seed, fox, chain_forward=False, mutate=None):
     print(f"[bwd] B={B} H={H} L={L} d={d} {dtype} scale={scale} fox={fox} seed={seed} "
-          f"chain_forward={chain_forward}", flush=True)
+          f"chain_forward={chain_forward} mutate={mutate is not None}", flush=True)
     x = synthetic.fwd_inputs(B, H, L, d, dtype, seed, fox=fox)
+    if mutate is not None:
+        mutate(x)
     g = torch.Generator().manual_seed(seed + 1000)
     do = torch.randn(B, H, L, d, generator=g).to(synthetic.DTYPES[dtype])
     refs = {}
@@ -93,6 +95,32 @@ def test_bwd_f32(L, d, fox):
 @pytest.mark.parametrize("L,d,fox", [(200, 64, True), (130, 128, False)])
 def test_bwd_bf16(L, d, fox):
     _bwd_case(1, 2, L, d, "bf16", 0.3, seed=L + d + 7 * fox, fox=fox)
+
+
+def _special_transitions(x):
+    """Tokens t = 0 (mod 7) get beta = 0 (H = I), t = 3 (mod 7) beta = 2 with a
+    unit w (an exact reflection), and t = 5 (mod 7) a w of norm 1.25 with
+    beta = 1 / |w|^2 (H a projection: singular)."""
+    L = x["beta"].shape[-1]
+    t = torch.arange(L)
+    dt = x["w"].dtype
+    w = x["w"].double()
+    beta = x["beta"].clone()
+    beta[..., t % 7 == 0] = 0.0
+    beta[..., t % 7 == 3] = 2.0
+    w[..., t % 7 == 5, :] *= 1.25
+    n2 = (w[..., t % 7 == 5, :] ** 2).sum(-1)
+    beta[..., t % 7 == 5] = (1.0 / n2).to(beta.dtype)
+    x["w"] = w.to(dt)
+    x["beta"] = beta
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_special_transitions_f32(fox):
+    """beta = 0, exact reflections and singular (projection) transitions, over
+    three blocks with a ragged end: the in-block gradients, whose triangular
+    factor carries no division by beta or by 1 - beta |w|^2, stay exact."""
+    _bwd_case(1, 2, 150, 64, "f32", 0.3, seed=150 + fox, fox=fox, mutate=_special_transitions)
 
 
 def test_bwd_long_f32():
