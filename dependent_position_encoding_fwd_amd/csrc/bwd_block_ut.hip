@@ -25,9 +25,10 @@
 //     T' = -M^T (X' X^T),   G' = strict_upper(diag(beta) T')
 // which are thirty 64 x 64 x 64 products on the fp32 matrix cores.
 //
-// Layout: 8 waves; each 64 x 64 matrix lives in registers, wave w holding the
-// 16 x 16 tiles (w & 3, 2 (w >> 2)) and (w & 3, 2 (w >> 2) + 1) (8 floats per
-// lane).  W, K, Q and M stay in LDS; the other operands of a product are
+// Layout: 16 waves (four per SIMD); each 64 x 64 matrix lives in registers,
+// wave w holding its 16 x 16 tile (w & 3, w >> 2) (4 floats per lane; with
+// PATH_UT_TPW = 2, 8 waves of two tiles each, which measured 10 % slower).
+// W, K, Q and M stay in LDS; the other operands of a product are
 // staged into four LDS slots between two barriers.  A slot row has 68 floats,
 // which keeps both the row reads (16 rows x 4 consecutive floats) and the
 // column reads (4 rows x 16 consecutive floats) of the products on distinct
@@ -44,24 +45,30 @@ constexpr int kC = kBlk;     // tokens per block
 constexpr int kD = 64;       // head dimension
 constexpr int kSP = 68;      // slot row pitch (floats)
 constexpr int kSlot = kC * kSP;
-constexpr int kUW = 8;       // waves
+#ifndef PATH_UT_TPW
+#define PATH_UT_TPW 1
+#endif
+constexpr int kTPW = PATH_UT_TPW;  // 16 x 16 tiles of a 64 x 64 matrix per wave
+constexpr int kUW = 16 / kTPW;     // waves
 constexpr int kUT = 64 * kUW;
+constexpr int kEPT = kC * kD / kUT;  // elements per thread of a 64 x 64 row copy
 
 // This wave's share of a 64 x 64 matrix: element i of t[j] is row
 // 16 rt + 4 lk + i, column 32 ch + 16 j + lr.
 struct Mat {
-  f4 t[2];
+  f4 t[kTPW];
 };
 
 struct Lane {
   int rt, ch, lr, lk;
   __device__ int row(int i) const { return 16 * rt + 4 * lk + i; }
-  __device__ int col(int j) const { return 32 * ch + 16 * j + lr; }
+  __device__ int col(int j) const { return 16 * (kTPW * ch + j) + lr; }
 };
 
 __device__ __forceinline__ Mat zero_mat() {
   Mat m;
-  m.t[0] = m.t[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) m.t[j] = f4{0.f, 0.f, 0.f, 0.f};
   return m;
 }
 
@@ -77,7 +84,7 @@ __device__ __forceinline__ void mm(Mat& acc, const Lane& L, const float* A, cons
 #pragma unroll
   for (int c = 0; c < kC / 16; ++c) {
     const int k0 = 16 * c + 4 * L.lk;
-    float av[4], bv[2][4];
+    float av[4], bv[kTPW][4];
     if constexpr (AK == kRow) {
       const f4 v = *reinterpret_cast<const f4*>(A + (16 * L.rt + L.lr) * kSP + k0);
 #pragma unroll
@@ -87,8 +94,8 @@ __device__ __forceinline__ void mm(Mat& acc, const Lane& L, const float* A, cons
       for (int j = 0; j < 4; ++j) av[j] = A[(k0 + j) * kSP + 16 * L.rt + L.lr];
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int n = 32 * L.ch + 16 * t + L.lr;
+    for (int t = 0; t < kTPW; ++t) {
+      const int n = 16 * (kTPW * L.ch + t) + L.lr;
       if constexpr (BK == kBCol) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) bv[t][j] = B[(k0 + j) * kSP + n];
@@ -102,7 +109,7 @@ __device__ __forceinline__ void mm(Mat& acc, const Lane& L, const float* A, cons
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[t][j], acc.t[t], 0, 0, 0);
+      for (int t = 0; t < kTPW; ++t) acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[t][j], acc.t[t], 0, 0, 0);
   }
 }
 
@@ -117,15 +124,15 @@ __device__ __forceinline__ void mm_xrow_bcol(Mat& acc, const Lane& L, const floa
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], B[(k0 + j) * kSP + 32 * L.ch + 16 * t + L.lr], acc.t[t],
+      for (int t = 0; t < kTPW; ++t)
+        acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], B[(k0 + j) * kSP + 16 * (kTPW * L.ch + t) + L.lr], acc.t[t],
                                                         0, 0, 0);
   }
 }
 
 __device__ __forceinline__ void stage(const Mat& m, const Lane& L, float* S) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kTPW; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[L.row(i) * kSP + L.col(j)] = m.t[j][i];
 }
@@ -133,7 +140,7 @@ __device__ __forceinline__ void stage(const Mat& m, const Lane& L, float* S) {
 __device__ __forceinline__ Mat from_slot(const Lane& L, const float* S) {
   Mat m;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kTPW; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) m.t[j][i] = S[L.row(i) * kSP + L.col(j)];
   return m;
@@ -143,7 +150,7 @@ __device__ __forceinline__ Mat from_slot(const Lane& L, const float* S) {
 template <typename F>
 __device__ __forceinline__ void each(Mat& m, const Lane& L, const F& f) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kTPW; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float x = m.t[j][i];
@@ -156,17 +163,17 @@ __device__ __forceinline__ void each(Mat& m, const Lane& L, const F& f) {
 template <typename T>
 __device__ __forceinline__ void load_rows(float* S, const T* src, int valid) {
   const int tid = threadIdx.x;
-  const int r = tid >> 3, c0 = 8 * (tid & 7);  // 512 threads: 64 rows x 8 chunks of 8
-  float x[8];
+  const int r = tid / (kD / kEPT), c0 = kEPT * (tid % (kD / kEPT));  // kEPT consecutive elements of row r
+  float x[kEPT];
   if (r < valid) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = load_f32(src + r * kD + c0 + e);
+    for (int e = 0; e < kEPT; ++e) x[e] = load_f32(src + r * kD + c0 + e);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int e = 0; e < kEPT; ++e) x[e] = 0.f;
   }
-  *reinterpret_cast<f4*>(S + r * kSP + c0) = f4{x[0], x[1], x[2], x[3]};
-  *reinterpret_cast<f4*>(S + r * kSP + c0 + 4) = f4{x[4], x[5], x[6], x[7]};
+#pragma unroll
+  for (int e = 0; e < kEPT; e += 4) *reinterpret_cast<f4*>(S + r * kSP + c0 + e) = f4{x[e], x[e + 1], x[e + 2], x[e + 3]};
 }
 
 // Sum over the 16 lanes of a row (the same bits in every lane of the row).
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
     Mat yu = zero_mat();
     mm<kRow, kBCol>(yu, Ln, S1, S2, sb);  // Y Ut
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Sd.t[j] -= yu.t[j];
+    for (int j = 0; j < kTPW; ++j) Sd.t[j] -= yu.t[j];
     each(Sd, Ln, [&](int r, int c, float& x) { x = c >= r ? x : 0.f; });  // S^T[c][r], c <= r
   }
 
@@ -271,9 +278,9 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
     Mat pd = zero_mat();
     mm<kRow, kBTr>(pd, Ln, S3, S0, sb);  // PD[c][r] = v_c . dO_r
     float csum_l[4] = {0.f, 0.f, 0.f, 0.f};
-    float rsum_l[2] = {0.f, 0.f};
+    float rsum_l[kTPW] = {};
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kTPW; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = Ln.row(i), r = Ln.col(j);
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
         if (Ln.lr == 0) atomicAdd(&cs[Ln.row(i)], s);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kTPW; ++j) {
         const float s = sum4rows(rsum_l[j]);
         if (Ln.lk == 0) atomicAdd(&rs[Ln.col(j)], s);
       }
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
   mm<kCol, kBCol>(Wb, Ln, S1, S3, sb);  // Y^T Khat'     (subtracted from W')
   mm<kCol, kBCol>(Utb, Ln, S1, S0, sb); // Y^T S'        (subtracted from Ut')
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kTPW; ++j) {
     Yb.t[j] = -Yb.t[j];
     Wb.t[j] = -Wb.t[j];
     Utb.t[j] = -Utb.t[j];
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
   {
     const Mat qh = from_slot(Ln, S3);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Qb.t[j] += qh.t[j];
+    for (int j = 0; j < kTPW; ++j) Qb.t[j] += qh.t[j];
   }
   Mat Fb = zero_mat();
   {
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
     mm<kRow, kBCol>(t3, Ln, S1, S0, sb);  // F P'
     (void)t2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kTPW; ++j) {
       Utb.t[j] -= t1.t[j];
       Fb.t[j] = -Fb.t[j];
       Wb.t[j] -= t3.t[j];
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
   {
     // beta'_j += sum_i M[i][j] X'[i][j]: this wave's 16 rows, then across waves
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kTPW; ++j) {
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) s += PM[Ln.row(i) * kSP + Ln.col(j)] * Xb.t[j][i];
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
     for (int i = 0; i < 4; ++i) {
       s[i] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) s[i] -= Tb.t[j][i] * N.t[j][i];
+      for (int j = 0; j < kTPW; ++j) s[i] -= Tb.t[j][i] * N.t[j][i];
       s[i] = sum16(s[i]);
     }
     if (Ln.lr == 0) {
@@ -430,10 +437,10 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
   stage(Wb, Ln, S2);
   __syncthreads();
   {
-    const int r = tid >> 3, c0 = 8 * (tid & 7);
+    const int r = tid / (kD / kEPT), c0 = kEPT * (tid % (kD / kEPT));
     if (r < valid) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kEPT; ++e) {
         store_f32(dq + rb + r * D + c0 + e, S0[r * kSP + c0 + e]);
         store_f32(dk + rb + r * D + c0 + e, S1[r * kSP + c0 + e]);
         store_f32(dw + rb + r * D + c0 + e, S2[r * kSP + c0 + e]);
