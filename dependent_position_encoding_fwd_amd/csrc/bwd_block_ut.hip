@@ -296,8 +296,8 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
         }
       }
     if (FOX) {
-      // key sums: over the 32 columns of this wave (16 lanes x 2 tiles); query
-      // sums: over the 16 rows of this wave (4 in-lane x 4 lane rows)
+      // key sums over this wave's columns (16 lanes of each of its tiles), query
+      // sums over its 16 rows (4 in-lane x 4 lane rows), then across waves
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float s = sum16(csum_l[i]);
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
   Mat Tb = zero_mat();
   mm<kCol, kBCol>(Tb, Ln, PM, S2, sb);  // M^T R; T' = -M^T R
   {
-    // beta'_a += sum_b T'[a][b] N[a][b]: this wave's 32 columns, then across waves
+    // beta'_a += sum_b T'[a][b] N[a][b]: this wave's columns, then across waves
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
