@@ -352,12 +352,11 @@ __global__ __launch_bounds__(kUT) void bwd_block_ut_kernel(
   }
   Mat Fb = zero_mat();
   {
-    Mat t1 = zero_mat(), t2 = zero_mat(), t3 = zero_mat();
+    Mat t1 = zero_mat(), t3 = zero_mat();
     mm<kRow, kBTr>(t1, Ln, S1, S3, sb);   // F Qhat'^T
     mm<kRow, kBCol>(Fb, Ln, S2, S3, sb);  // Ut Qhat'
     mm<kRow, kBTr>(Fb, Ln, PW, S0, sb);   // + W P'^T     (F' is the negation)
     mm<kRow, kBCol>(t3, Ln, S1, S0, sb);  // F P'
-    (void)t2;
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
       Utb.t[j] -= t1.t[j];
