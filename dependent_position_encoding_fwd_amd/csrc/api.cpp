@@ -59,9 +59,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 //     2^-11 sqrt(2/3) |q| |k| / sqrt(d),
 // sqrt(d) below the worst case (all errors aligned).  AUTO drops a key block's
 // lo terms while this estimate, taken with the largest transported query norm
-// of the tile and the largest key norm of the block (its own logits) or of the
-// head (the query transport, whose error reaches every earlier block), is at
-// most half the lse tolerance (kAutoRmsNats).  The scan kernels test
+// of the tile and the largest key norm of the block (its own logits) or of all
+// the key blocks the tile scans (the query transport, whose error reaches
+// every earlier block), is at most half the lse tolerance (kAutoRmsNats).  The scan kernels test
 //     |Qt|_max |khat|_max 2^-10 > tau
 // so tau = kAutoRmsNats log2(e) sqrt(6) sqrt(d).  This is an estimate, not a
 // bound: ACCURATE runs the split everywhere.
@@ -72,7 +72,7 @@ float auto_tau(int64_t d) { return kAutoRmsNats * kLog2e * 2.449489743f * sqrtf(
 // inputs: the matrix-core layout written by the prepare stage.
 struct FwdWs {
   size_t khat, pT, cum;                       // fp32 path
-  size_t khl, pmat, qhat, sdiag, kmax, kmaxh, pnorm, vt, vexp, vexph;  // bf16 path (cum shared)
+  size_t khl, pmat, qhat, sdiag, kmax, pnorm, vt, vexp;  // bf16 path (cum shared)
   size_t total;
 };
 
@@ -95,11 +95,9 @@ FwdWs fwd_layout(int dtype, int64_t BH, int64_t L, int64_t d, int64_t Nb, bool w
     w.qhat = take(sizeof(float) * bh * lp * dd);
     w.sdiag = take(sizeof(float) * bh * nb * size_t(path::kDiagTri));
     w.kmax = take(sizeof(float) * bh * nb);
-    w.kmaxh = take(sizeof(float) * bh);
     w.pnorm = take(sizeof(float) * bh * nb);
     w.vt = take(2 * bh * nb * dd * size_t(kBlk));
     w.vexp = take(sizeof(int) * bh * nb);
-    w.vexph = take(sizeof(int) * bh);
     if (with_forget) w.cum = take(sizeof(float) * bh * lp);
   }
   w.total = off;
@@ -203,11 +201,9 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
       reinterpret_cast<_Float16*>(ws + a.lay.pmat), reinterpret_cast<float*>(ws + a.lay.qhat),
       reinterpret_cast<float*>(ws + a.lay.sdiag), kmax, reinterpret_cast<float*>(ws + a.lay.pnorm),
       reinterpret_cast<_Float16*>(ws + a.lay.vt), reinterpret_cast<int*>(ws + a.lay.vexp), stream));
-  if (st) return st;
-  return hip_status(path::launch_head_reduce(
-      a.BH, L, kmax, reinterpret_cast<float*>(ws + a.lay.kmaxh), reinterpret_cast<const int*>(ws + a.lay.vexp),
-      reinterpret_cast<int*>(ws + a.lay.vexph), log_forget, kLog2e,
-      log_forget ? reinterpret_cast<float*>(ws + a.lay.cum) : nullptr, stream));
+  if (st || !log_forget) return st;
+  return hip_status(
+      path::launch_cum_padded(a.BH, L, log_forget, kLog2e, reinterpret_cast<float*>(ws + a.lay.cum), stream));
 }
 
 int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
@@ -230,9 +226,8 @@ int fwd_scan(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, int d
       reinterpret_cast<const _Float16*>(ws + a.lay.pmat),
       reinterpret_cast<const float*>(ws + a.lay.qhat),
       reinterpret_cast<const float*>(ws + a.lay.sdiag),
-      reinterpret_cast<const float*>(ws + a.lay.kmaxh), reinterpret_cast<const float*>(ws + a.lay.kmax),
-      reinterpret_cast<const float*>(ws + a.lay.pnorm), reinterpret_cast<const int*>(ws + a.lay.vexp),
-      reinterpret_cast<const int*>(ws + a.lay.vexph), cum, o, lse, stream));
+      reinterpret_cast<const float*>(ws + a.lay.kmax), reinterpret_cast<const float*>(ws + a.lay.pnorm),
+      reinterpret_cast<const int*>(ws + a.lay.vexp), cum, o, lse, stream));
 }
 
 }  // namespace

@@ -31,10 +31,10 @@
 // The direct loads are issued from asm (lds_dma16), so the compiler's waits on
 // LDS reads stay counted; the barriers that publish a stage wait for them.
 // Value range: prepare stores block n's V^T times 2^-e_n (e_n > 0 only when
-// the block holds |v| >= 2^15) and E = max_n e_n per head.  O accumulates in
-// units of 2^E: on a block with e_n < E (never on an ordinary head, where all
-// are 0) a scalar branch multiplies the V^T operands by 2^(e_n - E).  The
-// epilogue multiplies by 2^E.
+// the block holds |v| >= 2^15); a tile takes E = max e_n over the blocks its
+// queries weigh.  O accumulates in units of 2^E: on a block with e_n < E
+// (never where all are 0, as on an ordinary head) a scalar branch multiplies
+// the V^T operands by 2^(e_n - E).  The epilogue multiplies by 2^E.
 #include <math.h>
 
 #include <type_traits>
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     int64_t L, int Nb, int BH, int accurate_all, float tau, const _Float16* __restrict__ vt,
     const _Float16* __restrict__ khat, const _Float16* __restrict__ pmat,
     const float* __restrict__ qhat, const float* __restrict__ sdiag,
-    const float* __restrict__ kmax_head, const float* __restrict__ kmax_blk, const float* __restrict__ pnorm,
-    const int* __restrict__ vexp, const int* __restrict__ vexp_head, const float* __restrict__ cum, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    const float* __restrict__ kmax_blk, const float* __restrict__ pnorm,
+    const int* __restrict__ vexp, const float* __restrict__ cum, uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int D = kD, C = kBlk, DT = D / 16, DC = D / 32;
 
   __shared__ __attribute__((aligned(1024))) _Float16 sK0[kKT], sV0[kVT];
@@ -124,8 +124,23 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
   const int mb = 2 * p + half;        // this wave's query block
   const bool live = mb < Nb;
   const int r0 = (wave % kWPB) * 16;  // first query row (local to block mb)
-  const float khmax = kmax_head[bh];
-  const int vE = vexp_head[bh];  // 0 for a head whose values all stay below 2^15
+  // The largest key norm over the key blocks this tile scans (0 .. 2p: the
+  // only logits that a transported query's rounding reaches) and the largest
+  // value exponent over the blocks whose values it weighs (0 .. 2p+1), from
+  // the per-block figures of the prepare stage.
+  float khmax;
+  int vE;  // 0 unless some value of those blocks reaches 2^15
+  {
+    const int nlast = 2 * p + 1 < Nb ? 2 * p + 1 : Nb - 1;
+    float km = 0.f, vm = 0.f;
+    for (int b0 = 0; b0 <= nlast; b0 += 64) {
+      const int nb = b0 + lane;
+      if (nb <= 2 * p) km = fmaxf(km, kmax_blk[bh * Nb + nb]);
+      if (nb <= nlast) vm = fmaxf(vm, static_cast<float>(vexp[bh * Nb + nb]));
+    }
+    khmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max_dpp(km))));
+    vE = __builtin_amdgcn_readfirstlane(static_cast<int>(wave_max_dpp(vm)));
+  }
   // 2^(e_n - E) in fp16 for block n's V^T operands (0 below fp16's subnormals)
   auto vscale = [&](int n) __attribute__((always_inline)) {
     const int g = vE - vexp[bh * Nb + n];
@@ -432,7 +447,8 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     if (acc_cur) {
       // the lo tiles were published by the previous block's barrier.  The
       // logits' own correction needs only this block's max |khat|; the
-      // transport's (below) reaches every later block and keeps the head's.
+      // transport's (below) reaches every earlier block and keeps the maximum
+      // over all the key blocks the tile scans.
       if (work && (accurate_all || qbound * kn_cur * 0.0009765625f > tau)) {
 #pragma unroll
         for (int c = 0; c < DC; ++c)
@@ -500,7 +516,7 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
     }
     if (work) {
       // ---- PV beside the conversion of the transported queries
-      const bool vsn = vE != 0 && vexp[bh * Nb + n] != vE;  // rare: values in the head's units
+      const bool vsn = vE != 0 && vexp[bh * Nb + n] != vE;  // rare: values in the tile's units
       if (vsn) {
         const h8 f8 = vscale(n);
 #pragma unroll
@@ -570,19 +586,19 @@ __global__ __launch_bounds__(kNT, 1) void scan128_kernel(
 
 hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                           const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
-                          const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream) {
+                          const float* kmax_blk, const float* pnorm, const int* vexp,
+                          const float* cum, void* o, float* lse, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   const int NP = (Nb + 1) / 2;
   dim3 grid(static_cast<unsigned>(BH * NP));
   dim3 block(kNT);
   if (cum) {
     hipLaunchKernelGGL((scan128_kernel<true>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
-                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, vexp, vexp_head, cum,
+                       vt, khat, pmat, qhat, sdiag, kmax_blk, pnorm, vexp, cum,
                        static_cast<uint16_t*>(o), lse);
   } else {
     hipLaunchKernelGGL((scan128_kernel<false>), grid, block, 0, stream, L, Nb, static_cast<int>(BH), accurate, tau,
-                       vt, khat, pmat, qhat, sdiag, kmax_head, kmax_blk, pnorm, vexp, vexp_head, cum,
+                       vt, khat, pmat, qhat, sdiag, kmax_blk, pnorm, vexp, cum,
                        static_cast<uint16_t*>(o), lse);
   }
   return hipGetLastError();

@@ -32,23 +32,21 @@ hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float
                                _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
                                float* pnorm, _Float16* vt, int* vexp, hipStream_t stream);
 
-// Per head: kmax_head = max over blocks of kmax; vexp_head = max over blocks of
-// vexp (when vexp != null); cum = mult * prefix sum of log_forget (fp64
-// accumulation, padded to whole blocks) when log_forget != null.
-hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head, const int* vexp,
-                              int* vexp_head, const float* log_forget, float mult, float* cum,
-                              hipStream_t stream);
+// Per head: cum = mult * prefix sum of log_forget (fp64 accumulation), padded
+// to whole 64-token blocks by repeating the last value.
+hipError_t launch_cum_padded(int64_t BH, int64_t L, const float* log_forget, float mult, float* cum,
+                             hipStream_t stream);
 
 // Matrix-core right-to-left scan forward (bf16 storage), head dimension 64
 // and 128, from the prepared blocks; operands reach LDS by direct-to-LDS loads.
 hipError_t launch_scan64(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                          const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                         const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
-                         const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream);
+                         const float* kmax_blk, const float* pnorm, const int* vexp, const float* cum,
+                         void* o, float* lse, hipStream_t stream);
 hipError_t launch_scan128(int64_t BH, int64_t L, int accurate, float tau, const _Float16* vt,
                           const _Float16* khat, const _Float16* pmat, const float* qhat, const float* sdiag,
-                          const float* kmax_head, const float* kmax_blk, const float* pnorm, const int* vexp,
-                          const int* vexp_head, const float* cum, void* o, float* lse, hipStream_t stream);
+                          const float* kmax_blk, const float* pnorm, const int* vexp, const float* cum,
+                          void* o, float* lse, hipStream_t stream);
 
 // c[bh, i] = sum_{s<=i} x[bh, s], accumulated in fp64.
 hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream);

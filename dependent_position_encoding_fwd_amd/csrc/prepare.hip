@@ -183,47 +183,24 @@ __global__ __launch_bounds__(256) void prefix_sum_kernel(int64_t L, const float*
   }
 }
 
-// One workgroup per (b,h): the largest adjusted-key norm over all blocks, and
-// (with forget gates) the fp64-accumulated prefix sum of log f times `mult`,
-// padded to Nb*64 entries by repeating the last value.
-__global__ __launch_bounds__(256) void head_reduce_kernel(int64_t L, int Nb, const float* __restrict__ kmax,
-                                                          float* __restrict__ kmax_head,
-                                                          const int* __restrict__ vexp,
-                                                          int* __restrict__ vexp_head,
-                                                          const float* __restrict__ x, float mult,
-                                                          float* __restrict__ c) {
+// One workgroup per (b,h): the fp64-accumulated prefix sum of log f times
+// `mult`, padded to Nb*64 entries by repeating the last value.  Each thread
+// sums a contiguous run of the gates, the runs' totals are scanned in order,
+// and each thread then writes its run from its starting total.
+__global__ __launch_bounds__(256) void cum_padded_kernel(int64_t L, int Nb, const float* __restrict__ x,
+                                                         float mult, float* __restrict__ c) {
   __shared__ double part[256];
-  __shared__ float mx[256];
-  __shared__ int ve[256];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
-  float m = 0.f;
-  int e = 0;
-  for (int n = tid; n < Nb; n += 256) {
-    m = fmaxf(m, kmax[bh * Nb + n]);
-    if (vexp) e = max(e, vexp[bh * Nb + n]);
-  }
-  mx[tid] = m;
-  ve[tid] = e;
   const int64_t Lp = static_cast<int64_t>(Nb) * kBlk;
   const int64_t per = (L + 255) / 256;
   const int64_t lo = tid * per;
   const int64_t hi = lo + per < L ? lo + per : L;
   double acc = 0.0;
-  if (x) {
-    for (int64_t i = lo; i < hi; ++i) acc += static_cast<double>(x[bh * L + i]);
-  }
+  for (int64_t i = lo; i < hi; ++i) acc += static_cast<double>(x[bh * L + i]);
   part[tid] = acc;
   __syncthreads();
   if (tid == 0) {
-    float mm = 0.f;
-    int ee = 0;
-    for (int t = 0; t < 256; ++t) {
-      mm = fmaxf(mm, mx[t]);
-      ee = max(ee, ve[t]);
-    }
-    kmax_head[bh] = mm;
-    if (vexp_head) vexp_head[bh] = ee;
     double run = 0.0;
     for (int t = 0; t < 256; ++t) {
       double v = part[t];
@@ -232,7 +209,6 @@ __global__ __launch_bounds__(256) void head_reduce_kernel(int64_t L, int Nb, con
     }
   }
   __syncthreads();
-  if (!x) return;
   double run = part[tid];
   float* cs = c + bh * Lp;
   for (int64_t i = lo; i < hi; ++i) {
@@ -244,12 +220,11 @@ __global__ __launch_bounds__(256) void head_reduce_kernel(int64_t L, int Nb, con
   for (int64_t i = L + tid; i < Lp; i += 256) cs[i] = last;
 }
 
-hipError_t launch_head_reduce(int64_t BH, int64_t L, const float* kmax, float* kmax_head, const int* vexp,
-                              int* vexp_head, const float* log_forget, float mult, float* cum,
-                              hipStream_t stream) {
+hipError_t launch_cum_padded(int64_t BH, int64_t L, const float* log_forget, float mult, float* cum,
+                             hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
-  hipLaunchKernelGGL(head_reduce_kernel, dim3(static_cast<unsigned>(BH)), dim3(256), 0, stream, L, Nb,
-                     kmax, kmax_head, vexp, vexp_head, log_forget, mult, cum);
+  hipLaunchKernelGGL(cum_padded_kernel, dim3(static_cast<unsigned>(BH)), dim3(256), 0, stream, L, Nb,
+                     log_forget, mult, cum);
   return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ def source_hash(kind: str) -> str:
 CLASSES = (
     ("scan", "scan64_kernel"),
     ("prepare", "prepare_mfma_kernel"),
-    ("head_reduce", "head_reduce_kernel"),
+    ("cum_padded", "cum_padded_kernel"),
     ("decode_chunk", "decode_chunk_kernel"),
     ("decode_merge", "decode_merge_kernel"),
     ("copy", "copyBuffer"),
@@ -148,7 +148,7 @@ def read_bench(d: str):
 def short(name: str) -> str:
     c = classify(name)
     return {"scan": "scan64_kernel (d=64 scan)", "prepare": "prepare_mfma_kernel<64>",
-            "head_reduce": "head_reduce_kernel", "decode_chunk": "decode_chunk_kernel<bf16,64>",
+            "cum_padded": "cum_padded_kernel", "decode_chunk": "decode_chunk_kernel<bf16,64>",
             "decode_merge": "decode_merge_kernel<bf16,64>", "copy": "__amd_rocclr_copyBuffer",
             "decode_chunk_fox": "decode_chunk_kernel<bf16,64,gated>",
             "decode_merge_fox": "decode_merge_kernel<bf16,64,gated>",
@@ -369,7 +369,7 @@ def main():
     B, H, L, d = cfg["global_batch"], cfg["heads"], cfg["seq_len"], cfg["head_dim"]
     scan_f, scan_w = traffic(["scan"])
     dec_f, dec_w = traffic(["decode_chunk", "decode_merge"])
-    prep_f, prep_w = traffic(["prepare", "head_reduce"])
+    prep_f, prep_w = traffic(["prepare", "cum_padded"])
     alg_scan = scan_algorithmic_bytes(B, H, L, d)
     alg_dec = bs["decode"]["bytes_model"]
     out = {
@@ -382,7 +382,7 @@ def main():
         "decode": {"kernel": "decode_chunk_kernel + decode_merge_kernel", "source_sha256":
                    bs["decode"]["source_sha256"], "fetch_bytes_per_launch": dec_f, "write_bytes_per_launch": dec_w,
                    "bytes_per_launch": dec_f + dec_w, "algorithmic_bytes": alg_dec},
-        "prepare": {"kernel": "prepare_mfma_kernel + head_reduce_kernel", "fetch_bytes_per_launch": prep_f,
+        "prepare": {"kernel": "prepare_mfma_kernel (+ cum_padded_kernel with gates)", "fetch_bytes_per_launch": prep_f,
                     "write_bytes_per_launch": prep_w, "bytes_per_launch": prep_f + prep_w},
         "commands": {"fetch": a.cmd_fetch, "write": a.cmd_write},
     }
@@ -429,7 +429,7 @@ def main():
         "| kernel | fetch MiB/launch | write MiB/launch | total MiB | algorithmic MiB |",
         "|---|---|---|---|---|",
         f"| scan | {scan_f / MiB:.1f} | {scan_w / MiB:.1f} | {(scan_f + scan_w) / MiB:.1f} | {alg_scan / MiB:.1f} |",
-        f"| prepare + head reduce | {prep_f / MiB:.1f} | {prep_w / MiB:.1f} | {(prep_f + prep_w) / MiB:.1f} | - |",
+        f"| prepare | {prep_f / MiB:.1f} | {prep_w / MiB:.1f} | {(prep_f + prep_w) / MiB:.1f} | - |",
         f"| decode (chunk + merge) | {dec_f / MiB:.1f} | {dec_w / MiB:.1f} | {(dec_f + dec_w) / MiB:.1f} | "
         f"{alg_dec / MiB:.1f} |",
         "",
