@@ -91,6 +91,7 @@ hipError_t launch_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d
 // zero_begin over zero_count floats (dkh, dP, dV, csum) is cleared first.
 struct BwdWs {
   float *qhat, *khat, *pT, *minv, *cum, *Dv, *dqh, *rsum, *dkh, *dP, *dV, *csum, *dc, *scratch;
+  void* packed;  // split bf16 key-side operands (bf16 storage at d = 64), else null
   float* zero_begin;
   int64_t zero_count;
 };
@@ -109,6 +110,10 @@ struct BwdArgs {
 };
 // Launches everything after the fp32 prepare and the gate prefix sums.
 hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream);
+// The cross-block part for bf16 storage at d = 64 on the 16-bit matrix cores
+// (bwd_pair16.hip): packs the key-side operands into ws.packed, then runs the
+// pair kernel.
+hipError_t launch_bwd_pair16(const BwdArgs& a, hipStream_t stream);
 // The in-block part of the backward at d = 64 in matrix form (bwd_block_ut.hip).
 struct BwdBlockArgs {
   int64_t BH, L;
