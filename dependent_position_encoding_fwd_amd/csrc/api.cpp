@@ -140,7 +140,7 @@ int path_prepare(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, const vo
   if (cum && !log_forget) return PATH_ERR_NULL;
   if (tinv || qhat || khat || pT) {
     st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, tinv, nullptr, qhat, khat, pT,
-                                             stream));
+                                             nullptr, stream));
     if (st) return st;
   }
   if (cum) st = hip_status(path::launch_prefix_sum(BH, L, log_forget, cum, stream));
@@ -187,7 +187,7 @@ int fwd_prepare(const FwdArgs& a, int64_t B, int64_t H, int64_t L, int64_t d, in
     float* khat = reinterpret_cast<float*>(ws + a.lay.khat);
     float* pT = reinterpret_cast<float*>(ws + a.lay.pT);
     st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, nullptr, k, w, beta, nullptr, nullptr,
-                                             nullptr, khat, pT, stream));
+                                             nullptr, khat, pT, nullptr, stream));
     if (st) return st;
     if (log_forget) {
       float* cum = reinterpret_cast<float*>(ws + a.lay.cum);
@@ -420,8 +420,8 @@ bool bwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget, 
   };
   *w = BwdLayout{};
   w->qhat = take(bh * l * dd);
-  w->khat = take(bh * l * dd);
-  w->pT = take(bh * nb * dd * dd);
+  w->khat = pack16 ? 0 : take(bh * l * dd);
+  w->pT = pack16 ? 0 : take(bh * nb * dd * dd);
   w->minv = take(bh * nb * size_t(kBlk) * kBlk);
   if (with_forget) w->cum = take(bh * l);
   w->Dv = take(bh * l);
@@ -489,13 +489,15 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
   a.dw = dw;
   a.dbeta = dbeta;
   a.dlog_forget = log_forget ? dlog_forget : nullptr;
-  a.ws = path::BwdWs{at(lay.qhat), at(lay.khat), at(lay.pT), at(lay.minv), log_forget ? at(lay.cum) : nullptr,
+  a.ws = path::BwdWs{at(lay.qhat), pack16 ? nullptr : at(lay.khat), pack16 ? nullptr : at(lay.pT), at(lay.minv), log_forget ? at(lay.cum) : nullptr,
                      at(lay.Dv),
                      at(lay.dqh), at(lay.rsum), at(lay.dkh), at(lay.dP), at(lay.dV), at(lay.csum), at(lay.dc),
                      at(lay.scratch), pack16 ? static_cast<void*>(ws + lay.packed) : nullptr,
                      at(lay.dkh), lay.zero_count};
+  // bf16 at d = 64: Khat and P_n go straight to the split bf16 operands
   if ((st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.minv, a.ws.qhat,
-                                                a.ws.khat, a.ws.pT, stream))))
+                                                pack16 ? nullptr : a.ws.khat, pack16 ? nullptr : a.ws.pT,
+                                                a.ws.packed, stream))))
     return st;
   if (log_forget && (st = hip_status(path::launch_prefix_sum(BH, L, log_forget, a.ws.cum, stream)))) return st;
   return hip_status(path::launch_bwd(dtype, d, a, stream));

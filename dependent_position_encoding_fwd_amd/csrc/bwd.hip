@@ -110,16 +110,42 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 }  // namespace
 
-// D_i = dO_i . o_i, one thread per row.
+// Eight consecutive elements as fp32 (16-byte aligned: one or two vector loads).
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(wd[e] << 16);
+    x[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+  }
+}
+
+// D_i = dO_i . o_i: D/8 consecutive lanes per row, 8 elements each (one
+// 16- or 32-byte load per operand), summed across the lanes by shuffles.
 template <typename T, int D>
 __global__ __launch_bounds__(kT) void bwd_rowdot_kernel(int64_t rows, const T* __restrict__ dO,
                                                         const T* __restrict__ o, float* __restrict__ out) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kT + threadIdx.x;
-  if (r >= rows) return;
+  constexpr int G = D / 8;  // lanes per row
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kT + threadIdx.x;
+  const int64_t r = idx / G;
+  const int part = static_cast<int>(idx % G);
   float s = 0.f;
-#pragma unroll 8
-  for (int e = 0; e < D; ++e) s = fmaf(load_f32(dO + r * D + e), load_f32(o + r * D + e), s);
-  out[r] = s;
+  if (r < rows) {
+    float x[8], y[8];
+    load8(dO + r * D + 8 * part, x);
+    load8(o + r * D + 8 * part, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(x[e], y[e], s);
+  }
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) s += __shfl_xor(s, off, 64);
+  if (r < rows && part == 0) out[r] = s;
 }
 
 __global__ __launch_bounds__(kT) void bwd_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -674,8 +700,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   const T* v = static_cast<const T*>(a.v);
   const T* dO = static_cast<const T*>(a.dout);
-  hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3(static_cast<unsigned>((BH * L + kT - 1) / kT)), dim3(kT), 0,
-                     stream, BH * L, dO, static_cast<const T*>(a.o), a.ws.Dv);
+  hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3(static_cast<unsigned>((BH * L * (D / 8) + kT - 1) / kT)),
+                     dim3(kT), 0, stream, BH * L, dO, static_cast<const T*>(a.o), a.ws.Dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(2048), dim3(kT), 0, stream, a.ws.zero_begin, a.ws.zero_count);

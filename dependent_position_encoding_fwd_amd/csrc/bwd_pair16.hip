@@ -23,9 +23,10 @@
 // Wave w owns output rows 16w .. 16w+15 of every product: lane (g, l) of its
 // accumulators holds rows 16w + 4g + r (r < 4) of column l of each 16-column
 // tile.  A operands are the wave's own rows:
-//   * Khat_n, Khat_n^T, P_n and P_n^T as split bf16 rows, packed once per key
-//     block by bwd_pack16_kernel and fetched from global memory one block
-//     ahead, right after their last use; the value rows straight from v;
+//   * Khat_n, Khat_n^T, P_n and P_n^T as split bf16 rows (written by the
+//     backward's fp32 prepare, columns in perm32 order), fetched from global
+//     memory one block ahead, right after their last use; the value rows
+//     straight from v;
 //   * p, scale dS and Lam, whose accumulators hold 4 consecutive rows of one
 //     column per lane.  A 16x16x16 MFMA against the identity transposes each
 //     16x16 tile in registers (exact: every product is by 1 or 0), leaving 4
@@ -138,56 +139,12 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x + dpp<0x140>(x);
 }
 
-// Packed matrices of a key block, each a hi matrix followed by its lo matrix.
+// Packed matrices of a key block, each a hi matrix followed by its lo matrix:
+// Khat rows j (columns e), Khat^T rows a (columns j), P_n rows a (columns b),
+// P_n^T rows a (columns b), columns in perm32 order.
 enum : int { kKh = 0, kKt = 2, kPa = 4, kPt = 6, kPacked = 8 };
 
 }  // namespace
-
-// Packs each key block's Khat_n and P_n (fp32, from the backward's prepare) as
-// split bf16 rows in the order the pair kernel reads them:
-//   kKh: Khat rows j, column e at perm32(e)      (A of S = Khat Qt^T)
-//   kKt: Khat^T rows a, column j at perm32(j)    (A of Khat^T dS)
-//   kPa: P_n rows a, column b at perm32(b)       (A of the transport P_n Qt)
-//   kPt: P_n^T rows a, column b at perm32(b)     (A of P_n^T Lam)
-// The last block is never a key block of a later query block and is skipped.
-__global__ __launch_bounds__(kNT) void bwd_pack16_kernel(int64_t L, int Nb, const float* __restrict__ khat,
-                                                         const float* __restrict__ pT,
-                                                         __bf16* __restrict__ packed) {
-  __shared__ float Ks[kC][kD + 1];  // Khat[j][e]
-  __shared__ float Ps[kD][kD + 1];  // Ps[b][a] = P_n[a][b]
-  const int nk = Nb - 1;
-  const int64_t bh = blockIdx.x / nk;
-  const int n = static_cast<int>(blockIdx.x % nk);
-  const int tid = threadIdx.x;
-  const float* kb = khat + (bh * L + static_cast<int64_t>(n) * kC) * kD;
-  const float* pb = pT + (bh * Nb + n) * static_cast<int64_t>(kMat);
-  for (int idx = tid; idx < kMat; idx += kNT) {
-    Ks[idx / kD][idx % kD] = kb[idx];
-    Ps[idx / kD][idx % kD] = pb[idx];
-  }
-  __syncthreads();
-  __bf16* out = packed + (bh * Nb + n) * static_cast<int64_t>(kPacked * kMat);
-  for (int grp = tid; grp < kMat / 4; grp += kNT) {
-    const int row = grp / 16, pos = 4 * (grp % 16);
-    f4 kh, kt, pa, pt;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int col = unperm32(pos + r);
-      kh[r] = Ks[row][col];
-      kt[r] = Ks[col][row];
-      pa[r] = Ps[col][row];
-      pt[r] = Ps[row][col];
-    }
-    const f4 src[4] = {kh, kt, pa, pt};
-    const int at[4] = {kKh, kKt, kPa, kPt};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const Split4 sp = split4(src[s]);
-      *reinterpret_cast<bf4*>(out + at[s] * kMat + row * kD + pos) = sp.hi;
-      *reinterpret_cast<bf4*>(out + (at[s] + 1) * kMat + row * kD + pos) = sp.lo;
-    }
-  }
-}
 
 template <bool FOX>
 __global__ __launch_bounds__(kNT, 2) void bwd_pair16_kernel(
@@ -467,7 +424,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_pair16_kernel(
 // the same wave index wrote there); p and dS are formed from it exactly as in
 // that kernel.
 template <bool FOX>
-__global__ __launch_bounds__(kNT, 2) void bwd_key16_kernel(
+__global__ __launch_bounds__(kNT, FOX ? 2 : 3) void bwd_key16_kernel(
     int64_t L, int Nb, int64_t BH, float scale, const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
     const __bf16* __restrict__ packed, const float* __restrict__ cum, const float* __restrict__ lse,
     const float* __restrict__ Dv, const float* __restrict__ qt_scratch, float* __restrict__ dkh,
@@ -577,8 +534,9 @@ __global__ __launch_bounds__(kNT, 2) void bwd_key16_kernel(
         s[t] = mma32(kh.hi[c], bhv, s[t]);
         pd[t] = mma32(vf[c], bd, pd[t]);
       }
-    // p and scale dS (row j = 16w + 4g + r, column i = 16t + l), then by rows j
-    bf4 tph[4], tpl[4], tdh[4], tdl[4];
+    // p and scale dS (row j = 16w + 4g + r, column i = 16t + l); p by rows j
+    bf4 th[4], tl[4];
+    Split4 dsp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bool ok = 16 * t + l < valid;
@@ -592,22 +550,33 @@ __global__ __launch_bounds__(kNT, 2) void bwd_key16_kernel(
         dss[r] = scale * ds;
         rowp[r] += ds;
       }
-      const Split4 ps = split4(pv), dsp = split4(dss);
-      tph[t] = transpose4(ps.hi, ident);
-      tpl[t] = transpose4(ps.lo, ident);
-      tdh[t] = transpose4(dsp.hi, ident);
-      tdl[t] = transpose4(dsp.lo, ident);
+      const Split4 ps = split4(pv);
+      th[t] = transpose4(ps.hi, ident);
+      tl[t] = transpose4(ps.lo, ident);
+      dsp[t] = split4(dss);
     }
-    // dV_n += p dO_m, dKhat_n += scale dS Qt^(n)_m
+    // dV_n += p dO_m
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const bf8 ph = cat8(tph[2 * c], tph[2 * c + 1]), pl = cat8(tpl[2 * c], tpl[2 * c + 1]);
-      const bf8 dh = cat8(tdh[2 * c], tdh[2 * c + 1]), dl = cat8(tdl[2 * c], tdl[2 * c + 1]);
+      const bf8 ph = cat8(th[2 * c], th[2 * c + 1]), pl = cat8(tl[2 * c], tl[2 * c + 1]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bf8 bo = rd8(DOe, 16 * u + l, 4 * c + g);
         dv[u] = mma32(pl, bo, dv[u]);
         dv[u] = mma32(ph, bo, dv[u]);
+      }
+    }
+    // scale dS by rows j; dKhat_n += scale dS Qt^(n)_m
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      th[t] = transpose4(dsp[t].hi, ident);
+      tl[t] = transpose4(dsp[t].lo, ident);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf8 dh = cat8(th[2 * c], th[2 * c + 1]), dl = cat8(tl[2 * c], tl[2 * c + 1]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
         const bf8 bhv = rd8(QBh, 16 * u + l, 4 * c + g), blv = rd8(QBl, 16 * u + l, 4 * c + g);
         dk[u] = mma32(dl, bhv, dk[u]);
         dk[u] = mma32(dh, blv, dk[u]);
@@ -639,13 +608,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_key16_kernel(
 hipError_t launch_bwd_pair16(const BwdArgs& a, hipStream_t stream) {
   const int64_t BH = a.BH, L = a.L;
   const int Nb = static_cast<int>((L + kC - 1) / kC);
-  __bf16* packed = static_cast<__bf16*>(a.ws.packed);
-  if (Nb >= 2) {
-    hipLaunchKernelGGL(bwd_pack16_kernel, dim3(static_cast<unsigned>(BH * (Nb - 1))), dim3(kNT), 0, stream, L,
-                       Nb, a.ws.khat, a.ws.pT, packed);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const __bf16* packed = static_cast<const __bf16*>(a.ws.packed);
   const dim3 grid(static_cast<unsigned>(BH * Nb));
   const __bf16* v = static_cast<const __bf16*>(a.v);
   const __bf16* dO = static_cast<const __bf16*>(a.dout);

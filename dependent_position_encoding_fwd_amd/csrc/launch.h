@@ -15,10 +15,12 @@ namespace path {
 constexpr int kDiagTri = 2176;
 
 // Per-block UT transform in fp32 (one workgroup per 64-token block).  Any of
-// the outputs may be null.  Layouts as documented for path_prepare.
+// the outputs may be null.  Layouts as documented for path_prepare.  `packed`
+// (d = 64 only) replaces khat and pT by the split bf16 operands of the 16-bit
+// backward (eight 64 x 64 bf16 matrices per block, see prepare.hip).
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
                               const void* q, const void* k, const void* w, const float* beta,
-                              float* tinv, float* minv, float* qhat, float* khat, float* pT,
+                              float* tinv, float* minv, float* qhat, float* khat, float* pT, void* packed,
                               hipStream_t stream);
 
 // Per-block UT data in the layout of the matrix-core forward (bf16 inputs),
@@ -111,8 +113,8 @@ struct BwdArgs {
 // Launches everything after the fp32 prepare and the gate prefix sums.
 hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream);
 // The cross-block part for bf16 storage at d = 64 on the 16-bit matrix cores
-// (bwd_pair16.hip): packs the key-side operands into ws.packed, then runs the
-// pair kernel.
+// (bwd_pair16.hip), from the split operands the fp32 prepare wrote to
+// ws.packed: the query-major pair kernel, then the key-major one.
 hipError_t launch_bwd_pair16(const BwdArgs& a, hipStream_t stream);
 // The in-block part of the backward at d = 64 in matrix form (bwd_block_ut.hip).
 struct BwdBlockArgs {

@@ -23,13 +23,48 @@
 #include "tile_f32.h"
 
 namespace path {
+namespace {
+
+// Position p of a row holds reduction index unperm32(p): index k = 32c + 16h +
+// 4g + r sits at 32c + 8g + 4h + r, the order in which the 16-bit backward's
+// matrix-core operands take a 32-wide slice.
+__device__ constexpr int unperm32(int p) {
+  return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
+
+// Writes a 64 x 64 fp32 matrix held in LDS (pitch 65) as split bf16 rows,
+// hi = bf16(x) then lo = bf16(x - hi), the columns in unperm32 order:
+// out[row][p] = src(row, unperm32(p)).
+typedef float pk_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pk_b2 __attribute__((ext_vector_type(2)));
+
+template <typename F>
+__device__ __forceinline__ void pack_split(const F& src, uint16_t* __restrict__ out) {
+  constexpr int N = kBlk;
+  for (int grp = threadIdx.x; grp < N * N / 4; grp += blockDim.x) {
+    const int row = grp / (N / 4), pos = 4 * (grp % (N / 4));
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const pk_f2 x = {src(row, unperm32(pos + 2 * h)), src(row, unperm32(pos + 2 * h + 1))};
+      const pk_b2 xh = __builtin_convertvector(x, pk_b2);  // round to nearest even
+      const pk_f2 r = x - pk_f2{static_cast<float>(xh[0]), static_cast<float>(xh[1])};
+      hi[h] = __builtin_bit_cast(uint32_t, xh);
+      lo[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, pk_b2));
+    }
+    *reinterpret_cast<uint2*>(out + row * N + pos) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2*>(out + N * N + row * N + pos) = make_uint2(lo[0], lo[1]);
+  }
+}
+
+}  // namespace
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prepare_f32_kernel(
     int64_t L, int Nb, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ w, const float* __restrict__ beta, float* __restrict__ tinv_out,
     float* __restrict__ minv_out, float* __restrict__ qhat_out, float* __restrict__ khat_out,
-    float* __restrict__ pT_out) {
+    float* __restrict__ pT_out, uint16_t* __restrict__ packed_out) {
   constexpr int C = kBlk;
   constexpr int CP = C + 1;
   constexpr int DP = D + 1;
@@ -97,7 +132,14 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     for (int idx = tid; idx < C * C; idx += 256) dst[idx] = Ts[idx / C][idx % C];
   }
 
-  if (khat_out) {
+  // packed_out (d = 64 only): instead of khat_out and pT_out, each block's
+  // Khat and P_n as split bf16 rows for the 16-bit backward, eight 64 x 64
+  // matrices: Khat rows j (columns e), Khat^T rows a (columns j), P_n rows a
+  // (columns b), P_n^T rows a (columns b), each hi then lo, columns in
+  // unperm32 order.
+  uint16_t* const pk = (D == kBlk && packed_out) ? packed_out + (bh * Nb + n) * int64_t(8 * C * C) : nullptr;
+
+  if (khat_out || pk) {
     for (int idx = tid; idx < C * D; idx += 256) {
       int r = idx / D, e = idx % D;
       Xs[r][e] = r < valid ? load_f32(k + base + (t0 + r) * D + e) : 0.f;
@@ -114,9 +156,20 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     // khat = K - Y W  (Y[c][a] = 0 for a <= c)
     tile_mm<C, D, C>([&](int c, int a) { return Gs[c][a]; }, [&](int a, int e) { return Ws[a][e]; },
                      [&](int c, int e, float x) {
-                       if (c < valid) khat_out[base + (t0 + c) * D + e] = Xs[c][e] - x;
+                       if (pk) {
+                         Xs[c][e] -= x;  // each element read and written by one lane
+                       } else if (c < valid) {
+                         khat_out[base + (t0 + c) * D + e] = Xs[c][e] - x;
+                       }
                      });
     __syncthreads();
+    if constexpr (D == kBlk) {
+      if (pk) {
+        pack_split([&](int j, int e) { return Xs[j][e]; }, pk);
+        pack_split([&](int a, int j) { return Xs[j][a]; }, pk + 2 * C * C);
+        __syncthreads();
+      }
+    }
   }
 
   if (qhat_out) {
@@ -140,15 +193,29 @@ __global__ __launch_bounds__(256) void prepare_f32_kernel(
     __syncthreads();
   }
 
-  if (pT_out) {
+  if (pT_out || pk) {
     // F = T^{-T} W: F[s][e] = sum_{t<=s} T^{-1}[t][s] W[t][e]
     tile_mm<C, D, C>([&](int s2, int t) { return Ts[t][s2] * bs[s2]; }, [&](int t, int e) { return Ws[t][e]; },
                      [&](int s2, int e, float x) { Xs[s2][e] = x; });
     __syncthreads();
-    // P^T = I - W^T F
-    float* dst = pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D);
+    // P^T = I - W^T F (into Gs for packing: Y's last reader passed the barrier above)
+    float* dst = pT_out ? pT_out + (bh * Nb + n) * (static_cast<int64_t>(D) * D) : nullptr;
     tile_mm<D, D, C>([&](int a, int s2) { return Ws[s2][a]; }, [&](int s2, int b) { return Xs[s2][b]; },
-                     [&](int a, int b, float x) { dst[a * D + b] = (a == b ? 1.f : 0.f) - x; });
+                     [&](int a, int b, float x) {
+                       const float v = (a == b ? 1.f : 0.f) - x;
+                       if (pk) {
+                         Gs[a][b] = v;
+                       } else {
+                         dst[a * D + b] = v;
+                       }
+                     });
+    if constexpr (D == kBlk) {
+      if (pk) {
+        __syncthreads();
+        pack_split([&](int a, int b) { return Gs[b][a]; }, pk + 4 * C * C);  // P_n[a][b] = P^T[b][a]
+        pack_split([&](int a, int b) { return Gs[a][b]; }, pk + 6 * C * C);
+      }
+    }
   }
 }
 
@@ -231,25 +298,26 @@ hipError_t launch_cum_padded(int64_t BH, int64_t L, const float* log_forget, flo
 template <typename T, int D>
 static hipError_t launch_prepare_t(int64_t B, int64_t H, int64_t L, const void* q, const void* k,
                                    const void* w, const float* beta, float* tinv, float* minv, float* qhat,
-                                   float* khat, float* pT, hipStream_t stream) {
+                                   float* khat, float* pT, uint16_t* packed, hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
   dim3 grid(static_cast<unsigned>(B * H * Nb));
   hipLaunchKernelGGL((prepare_f32_kernel<T, D>), grid, dim3(256), 0, stream, L, Nb,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(w),
-                     beta, tinv, minv, qhat, khat, pT);
+                     beta, tinv, minv, qhat, khat, pT, packed);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare_f32(int dtype, int64_t B, int64_t H, int64_t L, int64_t d,
                               const void* q, const void* k, const void* w, const float* beta,
-                              float* tinv, float* minv, float* qhat, float* khat, float* pT,
+                              float* tinv, float* minv, float* qhat, float* khat, float* pT, void* packed,
                               hipStream_t stream) {
+  uint16_t* pk = static_cast<uint16_t*>(packed);
   if (dtype == 0) {
-    return d == 64 ? launch_prepare_t<float, 64>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream)
-                   : launch_prepare_t<float, 128>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream);
+    return d == 64 ? launch_prepare_t<float, 64>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, pk, stream)
+                   : launch_prepare_t<float, 128>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, pk, stream);
   }
-  return d == 64 ? launch_prepare_t<bf16_t, 64>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream)
-                 : launch_prepare_t<bf16_t, 128>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, stream);
+  return d == 64 ? launch_prepare_t<bf16_t, 64>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, pk, stream)
+                 : launch_prepare_t<bf16_t, 128>(B, H, L, q, k, w, beta, tinv, minv, qhat, khat, pT, pk, stream);
 }
 
 hipError_t launch_prefix_sum(int64_t BH, int64_t L, const float* x, float* c, hipStream_t stream) {
