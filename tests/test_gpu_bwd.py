@@ -123,6 +123,14 @@ def test_bwd_special_transitions_f32(fox):
     _bwd_case(1, 2, 150, 64, "f32", 0.3, seed=150 + fox, fox=fox, mutate=_special_transitions)
 
 
+@pytest.mark.parametrize("fox", [False, True])
+def test_bwd_special_transitions_bf16(fox):
+    """The same transitions with bf16 storage, through the 16-bit cross-block
+    kernels (d = 64): w is rounded to bf16 after scaling, so the projections
+    are singular only up to that rounding."""
+    _bwd_case(1, 2, 150, 64, "bf16", 0.3, seed=151 + fox, fox=fox, mutate=_special_transitions)
+
+
 def test_bwd_long_f32():
     """Ten blocks: transports across up to nine block transitions."""
     _bwd_case(1, 1, 600, 64, "f32", 0.25, seed=600, fox=True)
@@ -208,6 +216,13 @@ def test_bwd_full_length_elementwise_bf16():
     """Four whole heads of the L = 4096 workload (d = 64, scale 1/8, bf16): 64
     blocks, 2016 block pairs per head, every gradient element."""
     _bwd_full_heads(4, 4096, 64, "bf16", 0.125, 4100, False)
+
+
+def test_bwd_full_length_elementwise_bf16_gated_ragged():
+    """One gated head past the workload length with a ragged end (L = 4133:
+    65 blocks, the last of 37 tokens), bf16 at d = 64: the 16-bit cross-block
+    kernels with gates, every gradient element."""
+    _bwd_full_heads(1, 4133, 64, "bf16", 0.125, 4103, True)
 
 
 def test_bwd_full_length_elementwise_f32_gated():
