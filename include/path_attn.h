@@ -124,8 +124,8 @@ size_t path_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  *     0 <= beta_s <= 2 (the range 2 sigmoid(.) gives), so that no transition
  *     expands a vector by more than rounding.
  *   Outside these ranges the results are undefined (an fp16 operand may
- *   overflow and turn o or lse into inf or NaN).  The gradients of
- *   path_attn_bwd are fp32 throughout and have no such limit.
+ *   overflow and turn o or lse into inf or NaN).  path_attn_bwd keeps fp32
+ *   range throughout (bf16 operands have it) and has no such limit.
  */
 int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale,
                   int precision, const void* q, const void* k, const void* v, const void* w,
@@ -166,12 +166,18 @@ size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  * Outputs (caller-allocated): dq, dk, dv, dw [B,H,L,d] in dtype (bf16 rounded
  *   to nearest even); dbeta [B,H,L] fp32; dlog_forget [B,H,L] fp32, required
  *   when log_forget is given and ignored otherwise.
- * Arithmetic is fp32 throughout (a fp32 re-run of the prepare stage, then the
- *   cross-block and in-block gradient kernels); the cross-block sums use fp32
- *   atomics, so results may differ in the last bits between runs.
+ * Arithmetic: an fp32 re-run of the prepare stage, then the cross-block and
+ *   in-block gradient kernels, all accumulating in fp32.  With PATH_F32, or
+ *   d = 128, every product is fp32.  With PATH_BF16 at d = 64 the cross-block
+ *   products take each fp32 operand as bf16 hi + lo (16 significant bits,
+ *   fp32's exponent range), well below the bf16 rounding of the outputs.
+ *   Some cross-block sums use fp32 atomics, so results may differ in the
+ *   last bits between runs.
  * workspace: >= path_bwd_workspace_bytes(...) bytes, 256-byte aligned.  It
  *   holds, among fp32 intermediates, the transported queries of every
- *   (query block, earlier key block) pair: B*H*Nb*(Nb-1)/2 * d * 64 floats.
+ *   (query block, earlier key block) pair: B*H*Nb*(Nb-1)/2 * d * 64 floats
+ *   (plus 64 KB per block of split bf16 key-side operands with PATH_BF16 at
+ *   d = 64).
  */
 int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale, const void* q,
                   const void* k, const void* v, const void* w, const float* beta, const float* log_forget,
