@@ -494,11 +494,13 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
                      at(lay.dqh), at(lay.rsum), at(lay.dkh), at(lay.dP), at(lay.dV), at(lay.csum), at(lay.dc),
                      at(lay.scratch), pack16 ? static_cast<void*>(ws + lay.packed) : nullptr,
                      at(lay.dkh), lay.zero_count};
-  // bf16 at d = 64: Khat and P_n go straight to the split bf16 operands
-  if ((st = hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.minv, a.ws.qhat,
-                                                pack16 ? nullptr : a.ws.khat, pack16 ? nullptr : a.ws.pT,
-                                                a.ws.packed, stream))))
-    return st;
+  // bf16 at d = 64: the matrix-core prepare writes Khat and P_n straight into
+  // the split bf16 operands of the 16-bit kernels; otherwise the fp32 prepare
+  st = pack16 ? hip_status(path::launch_prepare_mfma_bwd(BH, L, q, k, w, beta, a.ws.packed, a.ws.qhat, a.ws.minv,
+                                                         stream))
+              : hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.minv, a.ws.qhat,
+                                                    a.ws.khat, a.ws.pT, nullptr, stream));
+  if (st) return st;
   if (log_forget && (st = hip_status(path::launch_prefix_sum(BH, L, log_forget, a.ws.cum, stream)))) return st;
   return hip_status(path::launch_bwd(dtype, d, a, stream));
 }

@@ -34,6 +34,12 @@ hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float
                                _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
                                float* pnorm, _Float16* vt, int* vexp, hipStream_t stream);
 
+// The backward's block prepare at d = 64 with bf16 storage, on the matrix
+// cores: Khat and P_n (both orientations) as split bf16 operands into
+// `packed`, Qhat [BH, L, 64] fp32 and M [BH, Nb, 64, 64] fp32 (prepare_mfma.hip).
+hipError_t launch_prepare_mfma_bwd(int64_t BH, int64_t L, const void* q, const void* k, const void* w,
+                                   const float* beta, void* packed, float* qhat, float* minv, hipStream_t stream);
+
 // Per head: cum = mult * prefix sum of log_forget (fp64 accumulation), padded
 // to whole 64-token blocks by repeating the last value.
 hipError_t launch_cum_padded(int64_t BH, int64_t L, const float* log_forget, float mult, float* cum,

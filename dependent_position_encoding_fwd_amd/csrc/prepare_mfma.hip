@@ -43,9 +43,6 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ f4 mma(const h8& a, const h8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f4 mmb(const b8& a, const b8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -64,23 +61,6 @@ __device__ __forceinline__ h8 to_h8(const f4& x, const f4& y) {
   r.p[3] = __builtin_convertvector(f2{y[2], y[3]}, h2);
   return r.v;
 }
-// hi/lo split of 8 fp32 values (two accumulator quads)
-struct HL {
-  h8 hi, lo;
-};
-__device__ __forceinline__ HL split8(const f4& x, const f4& y) {
-  HL r;
-  r.hi = to_h8(x, y);
-  f4 a, b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = x[i] - static_cast<float>(r.hi[i]);
-    b[i] = y[i] - static_cast<float>(r.hi[4 + i]);
-  }
-  r.lo = to_h8(a, b);
-  return r;
-}
-
 __device__ __forceinline__ int perm32(int d) {  // mfma_perm of the prepare stage
   return (d & ~31) | (((d >> 2) & 3) << 3) | (((d >> 4) & 1) << 2) | (d & 3);
 }
@@ -106,25 +86,109 @@ struct PGeo {
   static constexpr int ET = DT / 4;  // head-dim tiles per wave
 };
 
+// Element type of the split (hi + lo) operands: fp16 for the forward (11
+// significant bits per part), bf16 for the backward's run of this stage (16
+// bits in all, with fp32's exponent range, so the backward keeps no range
+// limit).
+template <bool BWD>
+struct Split16 {
+  typedef _Float16 e;
+  typedef _Float16 e8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 e2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f4 mma(const e8& a, const e8& b, const f4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Split16<true> {
+  typedef __bf16 e;
+  typedef __bf16 e8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 e2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f4 mma(const e8& a, const e8& b, const f4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <bool BWD>
+__device__ __forceinline__ typename Split16<BWD>::e8 to_e8(const f4& x, const f4& y) {
+  typedef typename Split16<BWD>::e2 e2;
+  union {
+    typename Split16<BWD>::e8 v;
+    e2 p[4];
+  } r;
+  r.p[0] = __builtin_convertvector(f2{x[0], x[1]}, e2);
+  r.p[1] = __builtin_convertvector(f2{x[2], x[3]}, e2);
+  r.p[2] = __builtin_convertvector(f2{y[0], y[1]}, e2);
+  r.p[3] = __builtin_convertvector(f2{y[2], y[3]}, e2);
+  return r.v;
+}
+template <bool BWD>
+struct SplitHL {
+  typename Split16<BWD>::e8 hi, lo;
+};
+template <bool BWD>
+__device__ __forceinline__ SplitHL<BWD> split8t(const f4& x, const f4& y) {
+  SplitHL<BWD> r;
+  r.hi = to_e8<BWD>(x, y);
+  f4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = x[i] - static_cast<float>(r.hi[i]);
+    b[i] = y[i] - static_cast<float>(r.hi[4 + i]);
+  }
+  r.lo = to_e8<BWD>(a, b);
+  return r;
+}
+// The first four elements of an 8-element 16-bit vector (8 bytes).
+template <typename V>
+__device__ __forceinline__ uint2 low4(const V& v) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  return make_uint2(u.x, u.y);
+}
+// An accumulator tile of 4 bf16 per lane (rows 4lg + i, column ln) transposed
+// by a 16x16x16 product with the identity (exact): the lane receives row ln,
+// columns 4lg .. 4lg + 3, as 8 bytes.
+__device__ __forceinline__ uint2 transpose_bits(const uint2& x, const uint2& ident) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const f4 y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, x), __builtin_bit_cast(s4, ident),
+                                                         f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 a = __builtin_convertvector(f2{y[0], y[1]}, bf2), b = __builtin_convertvector(f2{y[2], y[3]}, bf2);
+  return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
+// One 64-token block.  BWD (d = 64 only) is the backward's run of the stage:
+// bf16 splits, unscaled Qhat rows, M = T^{-1} diag(beta)^{-1}, and Khat and
+// P_n in both orientations (kt_out, pt_out) for its 16-bit kernels; no
+// in-block logits, V^T or bounds.
+template <int D, bool BWD>
+__device__ __forceinline__ void prepare_block(
     int64_t L, int Nb, float c2, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    _Float16* __restrict__ khat, _Float16* __restrict__ pmat, float* __restrict__ qhat,
-    float* __restrict__ sdiag, float* __restrict__ kmax, float* __restrict__ pnorm,
-    _Float16* __restrict__ vt, int* __restrict__ vexp) {
+    typename Split16<BWD>::e* __restrict__ khat, typename Split16<BWD>::e* __restrict__ pmat,
+    float* __restrict__ qhat, float* __restrict__ sdiag, float* __restrict__ kmax, float* __restrict__ pnorm,
+    _Float16* __restrict__ vt, int* __restrict__ vexp, typename Split16<BWD>::e* __restrict__ kt_out,
+    typename Split16<BWD>::e* __restrict__ pt_out, float* __restrict__ minv_out) {
+  static_assert(!BWD || D == 64, "the backward's prepare is for d = 64");
+  using SP = Split16<BWD>;
+  using E = typename SP::e;
+  using e8 = typename SP::e8;
   using G = PGeo<D>;
   constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
   constexpr int GP = 68;  // row pitch (floats) of G in GY; 64 rows of it fit the C x TP floats
+  // elements per block of the khat and pmat outputs (the backward's run packs
+  // eight matrices per block)
+  constexpr int64_t kst = BWD ? 8 * C * D : 2 * C * D;
+  constexpr int64_t pst = BWD ? 8 * D * D : 2 * D * D;
 
   // LDS (halfs unless noted).  WK holds W rows then K rows; it is reused for
   // the blocks of T^{-1}, then for -F^T rows.  GY holds G (quarter layout),
   // then X^T rows hi/lo, then -Y rows hi/lo.  The query rows never enter LDS:
   // each wave reads its own 16 as B operands.
   __shared__ __attribute__((aligned(16))) uint16_t WK[2 * C * RP];
-  __shared__ __attribute__((aligned(16))) _Float16 Wt[D * TP];      // W^T rows, perm(b)
+  __shared__ __attribute__((aligned(16))) E Wt[D * TP];             // W^T rows, perm(b)
   __shared__ __attribute__((aligned(16))) float GY[C * TP];
   __shared__ float bs[C];
   __shared__ float hn[C];
@@ -133,15 +197,24 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
 
   uint16_t* Wb = WK;
   uint16_t* Kb = WK + C * RP;
-  _Float16* NY = reinterpret_cast<_Float16*>(GY);  // [2][C*TP]
-  _Float16* XT = NY;                               // [2][C*TP], perm(a)
-  _Float16* NFT = reinterpret_cast<_Float16*>(WK); // [2][D*64] (pitch 64, no pad, swizzled chunks)
+  E* NY = reinterpret_cast<E*>(GY);   // [2][C*TP]
+  E* XT = NY;                         // [2][C*TP], perm(a)
+  E* NFT = reinterpret_cast<E*>(WK);  // [2][D*64] (pitch 64, no pad, swizzled chunks)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int ln = lane & 15;
   const int lg = lane >> 4;
+  // B operand of the backward's transposing products: lane (lg, ln) gives rows
+  // 4lg .. 4lg + 3 of column ln of the 16 x 16 identity, as bf16 bits
+  uint2 ident4 = make_uint2(0u, 0u);
+  if constexpr (BWD) {
+    uint32_t e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r] = 4 * lg + r == ln ? 0x3F80u : 0u;
+    ident4 = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+  }
   const int n = blockIdx.x % Nb;
   // Heads run from the last to the first.  The scan starts from the first
   // heads, and the blocks written last are the ones most likely to still sit
@@ -195,7 +268,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
   // value rows, already in the A-operand layout of the transposing product:
   // lane (ln, lg) of wave w holds row 16w + ln, columns 32h + 8lg .. 32h + 8lg + 7
   uint4 vraw[D / 32];
-  {
+  if constexpr (!BWD) {
     const int r = 16 * wave + ln;
     const int rr = r < valid ? r : valid - 1;
 #pragma unroll
@@ -226,7 +299,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
       bs[r] = br[j];
       // |H_s|_2 = max(1, |1 - beta_s |w_s|^2|): its product bounds the growth
       // of a transported query across the block
-      hn[r] = fmaxf(1.f, fabsf(1.f - br[j] * sq));
+      if constexpr (!BWD) hn[r] = fmaxf(1.f, fabsf(1.f - br[j] * sq));
     }
   }
   if (16 * wave + ln >= valid) {
@@ -248,7 +321,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int t = 0; t < 8; ++t) ident[s][t] = static_cast<__bf16>((lg == ln / 8 + 2 * s && t == ln % 8) ? 1.f : 0.f);
-  _Float16* wtb = Wt + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
+  E* wtb = Wt + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     const int col = 32 * c + 8 * lg;
@@ -261,13 +334,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
       gt[mt] = mmb(aw, bw, gt[mt]);    // G[s][t]      = w_s . w_t
       zt[mt] = mmb(aw, bk, zt[mt]);    // Z^T[a][c]    = w_a . k_c
       ut[mt] = mmb(aw, bq[c], ut[mt]);    // U[b][r]      = w_b . q_r
-      skq[mt] = mmb(ak, bq[c], skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
+      if constexpr (!BWD) skq[mt] = mmb(ak, bq[c], skq[mt]);  // (K Q^T)[c][r] = k_c . q_r
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const f4 y = mmb(bw, ident[s], f4{0.f, 0.f, 0.f, 0.f});
-      const H8u hv = {to_h8(y, y)};
-      *reinterpret_cast<uint2*>(wtb + (32 * c + 16 * s + ln) * TP) = make_uint2(hv.u.x, hv.u.y);
+      *reinterpret_cast<uint2*>(wtb + (32 * c + 16 * s + ln) * TP) = low4(to_e8<BWD>(y, y));
     }
   }
   // Diagonal 16x16 blocks of G by columns in the quarter layout
@@ -389,16 +461,21 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
     const float bc = bs[cc];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
+      if constexpr (BWD) {
+        // M = T^{-1}, fp32 rows a = 16I + 4lg + i, column cc
+        float* mo = minv_out + (bh * Nb + n) * (C * C) + (16 * I + 4 * lg) * C + cc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mo[i * C] = tc[I][i];
+      }
       f4 x = tc[I] * bc;
-      H8u hv, lv;
-      hv.v = to_h8(x, x);
+      const e8 hv = to_e8<BWD>(x, x);
       f4 lo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo[i] = x[i] - static_cast<float>(hv.v[i]);
-      lv.v = to_h8(lo, lo);
+      for (int i = 0; i < 4; ++i) lo[i] = x[i] - static_cast<float>(hv[i]);
+      const e8 lv = to_e8<BWD>(lo, lo);
       const int off = cc * TP + 32 * (I >> 1) + 8 * lg + 4 * (I & 1);
-      *reinterpret_cast<uint2*>(&XT[off]) = make_uint2(hv.u.x, hv.u.y);
-      *reinterpret_cast<uint2*>(&XT[C * TP + off]) = make_uint2(lv.u.x, lv.u.y);
+      *reinterpret_cast<uint2*>(&XT[off]) = low4(hv);
+      *reinterpret_cast<uint2*>(&XT[C * TP + off]) = low4(lv);
     }
   }
   __syncthreads();  // XT ready (in G's place: G was last read by the substitution)
@@ -423,48 +500,48 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
         if (16 * mt + 4 * lg + i <= cc) zt[mt][i] = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const HL b = split8(zt[2 * kc], zt[2 * kc + 1]);
-      h8 bwt[ET];
+      const SplitHL<BWD> b = split8t<BWD>(zt[2 * kc], zt[2 * kc + 1]);
+      e8 bwt[ET];
 #pragma unroll
       for (int j = 0; j < ET; ++j)
-        bwt[j] = *reinterpret_cast<const h8*>(&Wt[(16 * (ET * wave + j) + ln) * TP + 32 * kc + 8 * lg]);
+        bwt[j] = *reinterpret_cast<const e8*>(&Wt[(16 * (ET * wave + j) + ln) * TP + 32 * kc + 8 * lg]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int off = (16 * mt + ln) * TP + 32 * kc + 8 * lg;
-        const h8 ah = *reinterpret_cast<const h8*>(&XT[off]);
-        const h8 al = *reinterpret_cast<const h8*>(&XT[C * TP + off]);
-        yt[mt] = mma(al, b.hi, yt[mt]);
+        const e8 ah = *reinterpret_cast<const e8*>(&XT[off]);
+        const e8 al = *reinterpret_cast<const e8*>(&XT[C * TP + off]);
+        yt[mt] = SP::mma(al, b.hi, yt[mt]);
 #pragma unroll
-        for (int j = 0; j < ET; ++j) ft[j][mt] = mma(al, bwt[j], ft[j][mt]);
-        yt[mt] = mma(ah, b.lo, yt[mt]);
+        for (int j = 0; j < ET; ++j) ft[j][mt] = SP::mma(al, bwt[j], ft[j][mt]);
+        yt[mt] = SP::mma(ah, b.lo, yt[mt]);
 #pragma unroll
-        for (int j = 0; j < ET; ++j) ft[j][mt] = mma(ah, bwt[j], ft[j][mt]);
-        yt[mt] = mma(ah, b.hi, yt[mt]);
+        for (int j = 0; j < ET; ++j) ft[j][mt] = SP::mma(ah, bwt[j], ft[j][mt]);
+        yt[mt] = SP::mma(ah, b.hi, yt[mt]);
       }
     }
   }
   __syncthreads();  // every wave's X^T reads are done: -Y rows take its place
   // -Y rows into NY: lane holds Y^T[b = 16mt+4lg+i][c] = Y[c][b]
-  HL yb[2];
+  SplitHL<BWD> yb[2];
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
-    yb[kc] = split8(yt[2 * kc], yt[2 * kc + 1]);
+    yb[kc] = split8t<BWD>(yt[2 * kc], yt[2 * kc + 1]);
     const int off = (16 * wave + ln) * TP + 32 * kc + 8 * lg;
-    *reinterpret_cast<h8*>(&NY[off]) = -yb[kc].hi;
-    *reinterpret_cast<h8*>(&NY[C * TP + off]) = -yb[kc].lo;
+    *reinterpret_cast<e8*>(&NY[off]) = -yb[kc].hi;
+    *reinterpret_cast<e8*>(&NY[C * TP + off]) = -yb[kc].lo;
   }
   // lane holds F[b = 16mt+4lg+i][e = 16et+ln] = F^T[e][b] -> -F^T rows (pitch 64, perm b;
   // unpadded, so the 16-byte chunks of a row are swizzled to keep 16-row reads off one bank)
-  HL fb[ET][2];
+  SplitHL<BWD> fb[ET][2];
 #pragma unroll
   for (int j = 0; j < ET; ++j)
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      fb[j][kc] = split8(ft[j][2 * kc], ft[j][2 * kc + 1]);
+      fb[j][kc] = split8t<BWD>(ft[j][2 * kc], ft[j][2 * kc + 1]);
       const int row = 16 * (ET * wave + j) + ln;
       const int off = row * 64 + (((4 * kc + lg) ^ (row & 7)) << 3);  // 16-byte chunk j at slot j ^ (row & 7)
-      *reinterpret_cast<h8*>(&NFT[off]) = -fb[j][kc].hi;
-      *reinterpret_cast<h8*>(&NFT[D * 64 + off]) = -fb[j][kc].lo;
+      *reinterpret_cast<e8*>(&NFT[off]) = -fb[j][kc].hi;
+      *reinterpret_cast<e8*>(&NFT[D * 64 + off]) = -fb[j][kc].lo;
     }
 
   // ---- Khat^T = K^T - W^T Y^T (rows e, columns c in tile w) and
@@ -484,13 +561,13 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const h8 a = *reinterpret_cast<const h8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
-        acc = mma(a, yb[kc].lo, acc);
+        const e8 a = *reinterpret_cast<const e8*>(&Wt[(16 * et + ln) * TP + 32 * kc + 8 * lg]);
+        acc = SP::mma(a, yb[kc].lo, acc);
 #pragma unroll
-        for (int j = 0; j < ET; ++j) pacc[j] = mma(a, fb[j][kc].lo, pacc[j]);
-        acc = mma(a, yb[kc].hi, acc);
+        for (int j = 0; j < ET; ++j) pacc[j] = SP::mma(a, fb[j][kc].lo, pacc[j]);
+        acc = SP::mma(a, yb[kc].hi, acc);
 #pragma unroll
-        for (int j = 0; j < ET; ++j) pacc[j] = mma(a, fb[j][kc].hi, pacc[j]);
+        for (int j = 0; j < ET; ++j) pacc[j] = SP::mma(a, fb[j][kc].hi, pacc[j]);
       }
       acc = -acc;  // Khat[c][e], e = 16et + 4lg + i
 #pragma unroll
@@ -498,34 +575,49 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
       // rows with perm columns: e = 32(et/2) + 16(et%2) + 4lg + i -> 32(et/2) + 8lg + 4(et%2) + i
       const int pcol = 32 * (et / 2) + 8 * lg + 4 * (et % 2);
       {
-        _Float16* dst = khat + (bh * Nb + n) * (2 * C * D) + cc * D + pcol;
-        const H8u hv = {to_h8(acc, acc)};
+        E* dst = khat + (bh * Nb + n) * kst + cc * D + pcol;
+        const e8 hv = to_e8<BWD>(acc, acc);
         f4 lo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lo[i] = acc[i] - static_cast<float>(hv.v[i]);
-        const H8u lv = {to_h8(lo, lo)};
-        *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
-        *reinterpret_cast<uint2*>(dst + C * D) = make_uint2(lv.u.x, lv.u.y);
+        for (int i = 0; i < 4; ++i) lo[i] = acc[i] - static_cast<float>(hv[i]);
+        const e8 lv = to_e8<BWD>(lo, lo);
+        *reinterpret_cast<uint2*>(dst) = low4(hv);
+        *reinterpret_cast<uint2*>(dst + C * D) = low4(lv);
+        if constexpr (BWD) {
+          // Khat^T: row e = 16et + ln, columns perm(c) for c = 16w + 4lg .. + 3
+          E* dt = kt_out + (bh * Nb + n) * kst + (16 * et + ln) * C + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
+          *reinterpret_cast<uint2*>(dt) = transpose_bits(low4(hv), ident4);
+          *reinterpret_cast<uint2*>(dt + C * D) = transpose_bits(low4(lv), ident4);
+        }
       }
 #pragma unroll
       for (int j = 0; j < ET; ++j) {
         const f4 pv = -pacc[j];  // P[e][f], e = 16(ET w + j) + ln, f = 16et + 4lg + i
-        _Float16* dst = pmat + (bh * Nb + n) * (2 * D * D) + (16 * (ET * wave + j) + ln) * D + pcol;
-        const H8u hv = {to_h8(pv, pv)};
+        E* dst = pmat + (bh * Nb + n) * pst + (16 * (ET * wave + j) + ln) * D + pcol;
+        const e8 hv = to_e8<BWD>(pv, pv);
         f4 lo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lo[i] = pv[i] - static_cast<float>(hv.v[i]);
-        const H8u lv = {to_h8(lo, lo)};
-        *reinterpret_cast<uint2*>(dst) = make_uint2(hv.u.x, hv.u.y);
-        *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lv.u.x, lv.u.y);
+        for (int i = 0; i < 4; ++i) lo[i] = pv[i] - static_cast<float>(hv[i]);
+        const e8 lv = to_e8<BWD>(lo, lo);
+        *reinterpret_cast<uint2*>(dst) = low4(hv);
+        *reinterpret_cast<uint2*>(dst + D * D) = low4(lv);
+        if constexpr (BWD) {
+          // P^T: row a = f = 16et + ln, columns perm(b) for b = e = 16E + 4lg .. + 3
+          const int E0 = ET * wave + j;
+          E* dt = pt_out + (bh * Nb + n) * pst + (16 * et + ln) * D + 32 * (E0 >> 1) + 8 * lg + 4 * (E0 & 1);
+          *reinterpret_cast<uint2*>(dt) = transpose_bits(low4(hv), ident4);
+          *reinterpret_cast<uint2*>(dt + D * D) = transpose_bits(low4(lv), ident4);
+        }
       }
     }
-    s2 += __shfl_xor(s2, 16, 64);
-    s2 += __shfl_xor(s2, 32, 64);
-    s2 = wave_max(s2);
-    if (lane == 0) kred[wave] = s2;
+    if constexpr (!BWD) {
+      s2 += __shfl_xor(s2, 16, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      s2 = wave_max(s2);
+      if (lane == 0) kred[wave] = s2;
+    }
   }
-  {
+  if constexpr (!BWD) {
     // largest |v| of the block (this wave's rows; a clamped row repeats a valid one)
     uint32_t m = 0;
 #pragma unroll
@@ -548,43 +640,45 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
   // The block is stored times 2^-e, e = max(0, exponent of max|v| - 14), so that
   // every stored value is below 2^15 (fp16 holds 65504): e = 0 unless some
   // |v| >= 2^15.  The scaling is exact (a power of two); e goes to vexp.
-  int ve;
-  float vsc;
-  {
-    const float vm = fmaxf(fmaxf(vred[0], vred[1]), fmaxf(vred[2], vred[3]));
-    const int ex = static_cast<int>((__float_as_uint(vm) >> 23) & 0xff) - 127;  // finite inputs
-    ve = ex > 14 ? ex - 14 : 0;
-    vsc = __uint_as_float(static_cast<uint32_t>(127 - ve) << 23);
-  }
-  {
-    const int r = 16 * wave + ln;
-    _Float16* vtb = vt + (bh * Nb + n) * (D * C) + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int h = 0; h < D / 32; ++h) {
-        union {
-          uint4 u;
-          b8 v;
-        } av;
-        av.u = r < valid ? vraw[h] : make_uint4(0, 0, 0, 0);
-        const f4 y = mmb(av.v, ident[s], f4{0.f, 0.f, 0.f, 0.f}) * vsc;
-        const H8u hv = {to_h8(y, y)};
-        *reinterpret_cast<uint2*>(vtb + (32 * h + 16 * s + ln) * C) = make_uint2(hv.u.x, hv.u.y);
+  if constexpr (!BWD) {
+    int ve;
+    float vsc;
+    {
+      const float vm = fmaxf(fmaxf(vred[0], vred[1]), fmaxf(vred[2], vred[3]));
+      const int ex = static_cast<int>((__float_as_uint(vm) >> 23) & 0xff) - 127;  // finite inputs
+      ve = ex > 14 ? ex - 14 : 0;
+      vsc = __uint_as_float(static_cast<uint32_t>(127 - ve) << 23);
+    }
+    {
+      const int r = 16 * wave + ln;
+      _Float16* vtb = vt + (bh * Nb + n) * (D * C) + 32 * (wave >> 1) + 8 * lg + 4 * (wave & 1);
+  #pragma unroll
+      for (int s = 0; s < 2; ++s) {
+  #pragma unroll
+        for (int h = 0; h < D / 32; ++h) {
+          union {
+            uint4 u;
+            b8 v;
+          } av;
+          av.u = r < valid ? vraw[h] : make_uint4(0, 0, 0, 0);
+          const f4 y = mmb(av.v, ident[s], f4{0.f, 0.f, 0.f, 0.f}) * vsc;
+          const H8u hv = {to_h8(y, y)};
+          *reinterpret_cast<uint2*>(vtb + (32 * h + 16 * s + ln) * C) = make_uint2(hv.u.x, hv.u.y);
+        }
       }
     }
-  }
 
-  if (wave == 0) {
-    // product of the 64 factors |H_s|_2 by a butterfly over the wave
-    float g = hn[lane];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) g *= __shfl_xor(g, off, 64);
-    if (lane == 0) {
-      const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
-      kmax[bh * Nb + n] = sqrtf(mx);
-      pnorm[bh * Nb + n] = g;
-      vexp[bh * Nb + n] = ve;
+    if (wave == 0) {
+      // product of the 64 factors |H_s|_2 by a butterfly over the wave
+      float g = hn[lane];
+  #pragma unroll
+      for (int off = 1; off < 64; off <<= 1) g *= __shfl_xor(g, off, 64);
+      if (lane == 0) {
+        const float mx = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
+        kmax[bh * Nb + n] = sqrtf(mx);
+        pnorm[bh * Nb + n] = g;
+        vexp[bh * Nb + n] = ve;
+      }
     }
   }
 
@@ -597,44 +691,46 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (16 * mt + 4 * lg + i > r) ut[mt][i] = 0.f;
-    HL ub[2];
+    SplitHL<BWD> ub[2];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) ub[kc] = split8(ut[2 * kc], ut[2 * kc + 1]);
+    for (int kc = 0; kc < 2; ++kc) ub[kc] = split8t<BWD>(ut[2 * kc], ut[2 * kc + 1]);
 
     // Sdiag^T[c][r] = (K Q^T)[c][r] - sum_b Y[c][b] Ut[b][r]   (tiles mt < 4)
     // Qhat^T[e][r] = Q^T[e][r] - sum_b F^T[e][b] Ut[b][r]     (tiles et < DT)
     // formed side by side: independent products on the same B operands
-    float* sd = sdiag + (bh * Nb + n) * kDiagTri + diag_row(r);
-    float* qd = qhat + ((bh * Nb + n) * C + r) * D;
-    constexpr int NX = DT > 4 ? DT : 4;
+    // (the backward's run forms no in-block logits and keeps Qhat in rows of length L)
+    constexpr bool SD = !BWD;
+    float* sd = SD ? sdiag + (bh * Nb + n) * kDiagTri + diag_row(r) : nullptr;
+    float* qd = BWD ? qhat + (bh * L + t0 + r) * D : qhat + ((bh * Nb + n) * C + r) * D;
+    constexpr int NX = DT > 4 || !SD ? DT : 4;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      f4 sacc = x < 4 ? skq[x < 4 ? x : 0] : f4{0.f, 0.f, 0.f, 0.f}, qacc;
+      f4 sacc = SD && x < 4 ? skq[x < 4 ? x : 0] : f4{0.f, 0.f, 0.f, 0.f}, qacc;
       // Q^T tile x: 16 identity rows (offset 16(x&1)) times the query operand
       // of chunk x/2, exact; the lane gets q_r[16x + 4lg .. + 3]
       if (x < DT) qacc = mmb(ident[x & 1], bq[x < DT ? x >> 1 : 0], f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        h8 sh, sl, qh, ql;
-        if (x < 4) {
+        e8 sh, sl, qh, ql;
+        if (SD && x < 4) {
           const int off = (16 * x + ln) * TP + 32 * kc + 8 * lg;
-          sh = *reinterpret_cast<const h8*>(&NY[off]);
-          sl = *reinterpret_cast<const h8*>(&NY[C * TP + off]);
+          sh = *reinterpret_cast<const e8*>(&NY[off]);
+          sl = *reinterpret_cast<const e8*>(&NY[C * TP + off]);
         }
         if (x < DT) {
           const int row = 16 * x + ln;
           const int off = row * 64 + (((4 * kc + lg) ^ (row & 7)) << 3);
-          qh = *reinterpret_cast<const h8*>(&NFT[off]);
-          ql = *reinterpret_cast<const h8*>(&NFT[D * 64 + off]);
+          qh = *reinterpret_cast<const e8*>(&NFT[off]);
+          ql = *reinterpret_cast<const e8*>(&NFT[D * 64 + off]);
         }
-        if (x < 4) sacc = mma(sl, ub[kc].hi, sacc);
-        if (x < DT) qacc = mma(ql, ub[kc].hi, qacc);
-        if (x < 4) sacc = mma(sh, ub[kc].lo, sacc);
-        if (x < DT) qacc = mma(qh, ub[kc].lo, qacc);
-        if (x < 4) sacc = mma(sh, ub[kc].hi, sacc);
-        if (x < DT) qacc = mma(qh, ub[kc].hi, qacc);
+        if (SD && x < 4) sacc = SP::mma(sl, ub[kc].hi, sacc);
+        if (x < DT) qacc = SP::mma(ql, ub[kc].hi, qacc);
+        if (SD && x < 4) sacc = SP::mma(sh, ub[kc].lo, sacc);
+        if (x < DT) qacc = SP::mma(qh, ub[kc].lo, qacc);
+        if (SD && x < 4) sacc = SP::mma(sh, ub[kc].hi, sacc);
+        if (x < DT) qacc = SP::mma(qh, ub[kc].hi, qacc);
       }
-      if (x < 4 && 16 * x + 4 * lg <= r) {  // chunks of the padded triangle
+      if (SD && x < 4 && 16 * x + 4 * lg <= r) {  // chunks of the padded triangle
         f4 out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -643,9 +739,36 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
         }
         *reinterpret_cast<f4*>(sd + 16 * x + 4 * lg) = out;
       }
-      if (x < DT) *reinterpret_cast<f4*>(qd + 16 * x + 4 * lg) = (r < valid) ? qacc * c2 : f4{0.f, 0.f, 0.f, 0.f};
+      if (x < DT && (!BWD || r < valid))
+        *reinterpret_cast<f4*>(qd + 16 * x + 4 * lg) = (r < valid) ? qacc * c2 : f4{0.f, 0.f, 0.f, 0.f};
     }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
+    int64_t L, int Nb, float c2, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    _Float16* __restrict__ khat, _Float16* __restrict__ pmat, float* __restrict__ qhat,
+    float* __restrict__ sdiag, float* __restrict__ kmax, float* __restrict__ pnorm,
+    _Float16* __restrict__ vt, int* __restrict__ vexp) {
+  prepare_block<D, false>(L, Nb, c2, q, k, w, v, beta, khat, pmat, qhat, sdiag, kmax, pnorm, vt, vexp, nullptr,
+                          nullptr, nullptr);
+}
+
+// The backward's prepare at d = 64 for bf16 storage: per block, into
+// `packed` (eight 64 x 64 bf16 matrices, each a hi matrix then its lo
+// matrix): Khat rows j (columns e), Khat^T rows a (columns j), P_n rows a
+// (columns b), P_n^T rows a (columns b), columns in mfma_perm order; Qhat
+// unscaled in rows of length L; M = (I + diag(beta) strict_upper(W W^T))^{-1}
+// in fp32.
+__global__ __launch_bounds__(256, 3) void prepare_mfma_bwd_kernel(
+    int64_t L, int Nb, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ w, const float* __restrict__ beta, __bf16* __restrict__ packed,
+    float* __restrict__ qhat, float* __restrict__ minv) {
+  constexpr int M2 = 64 * 64;
+  prepare_block<64, true>(L, Nb, 1.f, q, k, w, nullptr, beta, packed, packed + 4 * M2, qhat, nullptr, nullptr,
+                          nullptr, nullptr, nullptr, packed + 2 * M2, packed + 6 * M2, minv);
 }
 
 template <int D>
@@ -658,6 +781,15 @@ static hipError_t launch_prepare_mfma_t(int64_t BH, int64_t L, float c2, const v
                      L, Nb, c2, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(v), beta, khat, pmat,
                      qhat, sdiag, kmax, pnorm, vt, vexp);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_mfma_bwd(int64_t BH, int64_t L, const void* q, const void* k, const void* w,
+                                   const float* beta, void* packed, float* qhat, float* minv, hipStream_t stream) {
+  const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL(prepare_mfma_bwd_kernel, dim3(static_cast<unsigned>(BH * Nb)), dim3(256), 0, stream, L, Nb,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(w), beta, static_cast<__bf16*>(packed), qhat, minv);
   return hipGetLastError();
 }
 
