@@ -57,8 +57,8 @@ the adjoint of the queries) and three block transports (queries again, their
 adjoint, the transitions' gradient).  The in-block chains earn no FLOPs.  With
 bf16 storage at d = 64 the cross-block products run on the 16-bit matrix cores
 with every fp32 operand split into bf16 hi + lo (two or three products each,
-fp32 accumulation) and the rest on the fp32 matrix cores; otherwise it
-computes in fp32 throughout.  `frac_fp32_peak` relates the rate to MI355X's
+fp32 accumulation), the block prepare the same way, and the in-block part on
+the fp32 matrix cores; otherwise it computes in fp32 throughout.  `frac_fp32_peak` relates the rate to MI355X's
 fp32 157.3 TFLOP/s.  `--no-bwd` skips it.
 
 The paged decode step (`path_decode_step_paged`) runs on the same caches
@@ -333,8 +333,8 @@ def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):
     print(f"[bench] backward: {ms:.3f} ms", file=sys.stderr, flush=True)
     split16 = q.dtype == torch.bfloat16 and cf.d == 64
     return {"ms": round(ms, 3), "TFLOP_per_s": round(tf, 3), "flops_model": F,
-            "arith": ("cross-block products as split-bf16 MFMA (fp32 operands as bf16 hi + lo, fp32 accumulate); "
-                      "in-block part and block prepare on fp32 MFMA") if split16 else "fp32 MFMA and vector ALU",
+            "arith": ("block prepare and cross-block products as split-bf16 MFMA (computed operands as bf16 hi + lo, "
+                      "fp32 accumulate); in-block part on fp32 MFMA") if split16 else "fp32 MFMA and vector ALU",
             "frac_fp32_peak": round(tf / PEAK_F32_TFLOPS, 4),
             "what": "path_attn_bwd on the forward workload (gradients of q, k, v, w, beta"
                     f"{', log forget gates' if gates is not None else ''}), seeded dO, median of {steps}"}

@@ -69,7 +69,7 @@ CLASSES = (
 # the gated decode kernels (template flag true) form classes of their own
 GATED = (("decode_chunk_fox", "decode_chunk_kernel"), ("decode_merge_fox", "decode_merge_kernel"))
 BWD = ("bwd_pair_kernel", "bwd_pair16_kernel", "bwd_key16_kernel", "bwd_block_kernel", "bwd_block_ut_kernel",
-       "prepare_f32_kernel", "bwd_rowdot_kernel",
+       "prepare_f32_kernel", "prepare_mfma_bwd_kernel", "bwd_rowdot_kernel",
        "bwd_zero_kernel", "bwd_suffix_kernel")
 
 
@@ -165,6 +165,8 @@ def _short_other(name: str) -> str:
         return "project_kernel (projection)"
     for key in BWD:
         if key in name:
+            if name.startswith("_Z"):  # left mangled (bf16 arguments): the kernel's name alone
+                return f"{key} (backward)"
             head = name.split("(")[0].replace("void ", "").replace("path::", "")
             return f"{head} (backward)"
     return name[:60]
