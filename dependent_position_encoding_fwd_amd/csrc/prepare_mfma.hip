@@ -1,4 +1,5 @@
-// Matrix-core prepare stage of the bf16 PaTH forward (gfx950).
+// Matrix-core prepare stage of the bf16 PaTH forward (gfx950), and the same
+// block work for the bf16 backward at d = 64 (prepare_mfma_bwd_kernel).
 //
 // One workgroup (4 waves) per 64-token block n of one head.  It computes the
 // UT factor of the block [PaTH Attention summary (gist.science 2505.16381),
@@ -29,6 +30,13 @@
 // The transposes W^T and V^T are products too: the rows times a 32x16 slice of
 // the identity leave 4 consecutive rows of one column in each lane.
 // All global loads of a block are issued before the first is used.
+//
+// The backward's run of the stage (same block body, BWD = true) splits the
+// computed operands into bf16 hi + lo instead (fp32's exponent range), and
+// writes M = T^{-1} (fp32), Qhat unscaled in rows of length L, and Khat and P
+// as bf16 hi/lo rows in both orientations (the second by a 16x16x16 product
+// with the identity in registers).  It forms no in-block logits, V^T or
+// bounds.
 #include <math.h>
 
 #include "common.h"
