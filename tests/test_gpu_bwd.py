@@ -92,7 +92,7 @@ def test_bwd_f32(L, d, fox):
     _bwd_case(1, 2, L, d, "f32", 0.3, seed=L + d + fox, fox=fox)
 
 
-@pytest.mark.parametrize("L,d,fox", [(200, 64, True), (130, 128, False)])
+@pytest.mark.parametrize("L,d,fox", [(200, 64, True), (130, 128, False), (40, 64, False), (128, 64, True)])
 def test_bwd_bf16(L, d, fox):
     _bwd_case(1, 2, L, d, "bf16", 0.3, seed=L + d + 7 * fox, fox=fox)
 
