@@ -405,9 +405,9 @@ struct BwdLayout {
   int64_t zero_count;
 };
 
-// Returns false when the sizes overflow.  `pack16` (bf16 storage at d = 64)
-// adds the split bf16 key-side operands of the 16-bit pair kernel: eight
-// 64 x 64 bf16 matrices per block.
+// Returns false when the sizes overflow.  `pack16` (bf16 storage) adds the
+// split bf16 key-side operands of the 16-bit pair kernels: Khat, Khat^T, P_n
+// and P_n^T, each hi and lo, 4*64*d + 4*d*d bf16 per block.
 bool bwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget, bool pack16, BwdLayout* w) {
   int64_t pairs, scr;
   if (!mul_ok(BH, Nb * (Nb - 1) / 2, &pairs) || !mul_ok(pairs, d * kBlk, &scr)) return false;
@@ -435,7 +435,7 @@ bool bwd_layout(int64_t BH, int64_t L, int64_t d, int64_t Nb, bool with_forget, 
   w->csum = take(bh * l);
   w->zero_count = int64_t((off - w->dkh) / sizeof(float));
   w->scratch = take(size_t(scr));
-  w->packed = pack16 ? take(bh * nb * 8 * size_t(kBlk) * kBlk / 2) : 0;
+  w->packed = pack16 ? take(bh * nb * (4 * size_t(kBlk) * dd + 4 * dd * dd) / 2) : 0;
   w->total = off;
   return true;
 }
@@ -448,7 +448,7 @@ size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
   int64_t BH, Nb;
   if (check_dtype(dtype) || check_shape(B, H, L, d, &BH, &Nb)) return 0;
   BwdLayout lay;
-  if (!bwd_layout(BH, L, d, Nb, with_forget != 0, dtype == PATH_BF16 && d == 64, &lay)) return 0;
+  if (!bwd_layout(BH, L, d, Nb, with_forget != 0, dtype == PATH_BF16, &lay)) return 0;
   return lay.total;
 }
 
@@ -465,7 +465,7 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
     return PATH_ERR_NULL;
   if (log_forget && !dlog_forget) return PATH_ERR_NULL;
   BwdLayout lay;
-  const bool pack16 = dtype == PATH_BF16 && d == 64;
+  const bool pack16 = dtype == PATH_BF16;
   if (!bwd_layout(BH, L, d, Nb, log_forget != nullptr, pack16, &lay)) return PATH_ERR_SHAPE;
   if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return PATH_ERR_WORKSPACE;
@@ -494,10 +494,10 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
                      at(lay.dqh), at(lay.rsum), at(lay.dkh), at(lay.dP), at(lay.dV), at(lay.csum), at(lay.dc),
                      at(lay.scratch), pack16 ? static_cast<void*>(ws + lay.packed) : nullptr,
                      at(lay.dkh), lay.zero_count};
-  // bf16 at d = 64: the matrix-core prepare writes Khat and P_n straight into
-  // the split bf16 operands of the 16-bit kernels; otherwise the fp32 prepare
-  st = pack16 ? hip_status(path::launch_prepare_mfma_bwd(BH, L, q, k, w, beta, a.ws.packed, a.ws.qhat, a.ws.minv,
-                                                         stream))
+  // bf16: the matrix-core prepare writes Khat and P_n straight into the split
+  // bf16 operands of the 16-bit kernels; fp32: the fp32 prepare
+  st = pack16 ? hip_status(path::launch_prepare_mfma_bwd(BH, L, d, q, k, w, beta, a.ws.packed, a.ws.qhat,
+                                                         a.ws.minv, stream))
               : hip_status(path::launch_prepare_f32(dtype, B, H, L, d, q, k, w, beta, nullptr, a.ws.minv, a.ws.qhat,
                                                     a.ws.khat, a.ws.pT, nullptr, stream));
   if (st) return st;

@@ -707,8 +707,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_zero_kernel, dim3(2048), dim3(kT), 0, stream, a.ws.zero_begin, a.ws.zero_count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>(BH * Nb));
-  if constexpr (D == 64 && std::is_same_v<T, bf16_t>) {
-    if ((e = launch_bwd_pair16(a, stream)) != hipSuccess) return e;
+  if constexpr (std::is_same_v<T, bf16_t>) {
+    if ((e = launch_bwd_pair16(D, a, stream)) != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL((bwd_pair_kernel<T, D, FOX>), grid, dim3(kT), 0, stream, L, Nb, BH, a.scale, v, dO,
                        a.ws.qhat, a.ws.khat, a.ws.pT, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum,

@@ -34,11 +34,13 @@ hipError_t launch_prepare_mfma(int64_t B, int64_t H, int64_t L, int64_t d, float
                                _Float16* khat, _Float16* pmat, float* qhat, float* sdiag, float* kmax,
                                float* pnorm, _Float16* vt, int* vexp, hipStream_t stream);
 
-// The backward's block prepare at d = 64 with bf16 storage, on the matrix
-// cores: Khat and P_n (both orientations) as split bf16 operands into
-// `packed`, Qhat [BH, L, 64] fp32 and M [BH, Nb, 64, 64] fp32 (prepare_mfma.hip).
-hipError_t launch_prepare_mfma_bwd(int64_t BH, int64_t L, const void* q, const void* k, const void* w,
-                                   const float* beta, void* packed, float* qhat, float* minv, hipStream_t stream);
+// The backward's block prepare with bf16 storage, on the matrix cores: Khat
+// and P_n (both orientations) as split bf16 operands into `packed`
+// (4*64*d + 4*d*d bf16 per block), Qhat [BH, L, d] fp32 and M [BH, Nb, 64, 64]
+// fp32 (prepare_mfma.hip).
+hipError_t launch_prepare_mfma_bwd(int64_t BH, int64_t L, int64_t d, const void* q, const void* k,
+                                   const void* w, const float* beta, void* packed, float* qhat, float* minv,
+                                   hipStream_t stream);
 
 // Per head: cum = mult * prefix sum of log_forget (fp64 accumulation), padded
 // to whole 64-token blocks by repeating the last value.
@@ -99,7 +101,7 @@ hipError_t launch_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t d
 // zero_begin over zero_count floats (dkh, dP, dV, csum) is cleared first.
 struct BwdWs {
   float *qhat, *khat, *pT, *minv, *cum, *Dv, *dqh, *rsum, *dkh, *dP, *dV, *csum, *dc, *scratch;
-  void* packed;  // split bf16 key-side operands (bf16 storage at d = 64), else null
+  void* packed;  // split bf16 key-side operands (bf16 storage), else null
   float* zero_begin;
   int64_t zero_count;
 };
@@ -118,10 +120,10 @@ struct BwdArgs {
 };
 // Launches everything after the fp32 prepare and the gate prefix sums.
 hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream);
-// The cross-block part for bf16 storage at d = 64 on the 16-bit matrix cores
-// (bwd_pair16.hip), from the split operands the fp32 prepare wrote to
-// ws.packed: the query-major pair kernel, then the key-major one.
-hipError_t launch_bwd_pair16(const BwdArgs& a, hipStream_t stream);
+// The cross-block part for bf16 storage (d = 64 or 128) on the 16-bit matrix
+// cores (bwd_pair16.hip), from the split operands the matrix-core prepare wrote
+// to ws.packed: the query-major pair kernel, then the key-major one.
+hipError_t launch_bwd_pair16(int64_t d, const BwdArgs& a, hipStream_t stream);
 // The in-block part of the backward at d = 64 in matrix form (bwd_block_ut.hip).
 struct BwdBlockArgs {
   int64_t BH, L;

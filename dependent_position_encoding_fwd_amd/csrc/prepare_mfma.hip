@@ -167,7 +167,7 @@ __device__ __forceinline__ uint2 transpose_bits(const uint2& x, const uint2& ide
 
 }  // namespace
 
-// One 64-token block.  BWD (d = 64 only) is the backward's run of the stage:
+// One 64-token block.  BWD is the backward's run of the stage:
 // bf16 splits, unscaled Qhat rows, M = T^{-1} diag(beta)^{-1}, and Khat and
 // P_n in both orientations (kt_out, pt_out) for its 16-bit kernels; no
 // in-block logits, V^T or bounds.
@@ -179,7 +179,6 @@ __device__ __forceinline__ void prepare_block(
     float* __restrict__ qhat, float* __restrict__ sdiag, float* __restrict__ kmax, float* __restrict__ pnorm,
     _Float16* __restrict__ vt, int* __restrict__ vexp, typename Split16<BWD>::e* __restrict__ kt_out,
     typename Split16<BWD>::e* __restrict__ pt_out, float* __restrict__ minv_out) {
-  static_assert(!BWD || D == 64, "the backward's prepare is for d = 64");
   using SP = Split16<BWD>;
   using E = typename SP::e;
   using e8 = typename SP::e8;
@@ -187,9 +186,9 @@ __device__ __forceinline__ void prepare_block(
   constexpr int C = G::C, RP = G::RP, TP = G::TP, DT = G::DT, DC = G::DC, ET = G::ET;
   constexpr int GP = 68;  // row pitch (floats) of G in GY; 64 rows of it fit the C x TP floats
   // elements per block of the khat and pmat outputs (the backward's run packs
-  // eight matrices per block)
-  constexpr int64_t kst = BWD ? 8 * C * D : 2 * C * D;
-  constexpr int64_t pst = BWD ? 8 * D * D : 2 * D * D;
+  // Khat, Khat^T, P_n and P_n^T, each hi and lo, per block)
+  constexpr int64_t kst = BWD ? 4 * C * D + 4 * D * D : 2 * C * D;
+  constexpr int64_t pst = BWD ? 4 * C * D + 4 * D * D : 2 * D * D;
 
   // LDS (halfs unless noted).  WK holds W rows then K rows; it is reused for
   // the blocks of T^{-1}, then for -F^T rows.  GY holds G (quarter layout),
@@ -764,19 +763,19 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_kernel(
                           nullptr, nullptr);
 }
 
-// The backward's prepare at d = 64 for bf16 storage: per block, into
-// `packed` (eight 64 x 64 bf16 matrices, each a hi matrix then its lo
-// matrix): Khat rows j (columns e), Khat^T rows a (columns j), P_n rows a
-// (columns b), P_n^T rows a (columns b), columns in mfma_perm order; Qhat
-// unscaled in rows of length L; M = (I + diag(beta) strict_upper(W W^T))^{-1}
-// in fp32.
-__global__ __launch_bounds__(256, 3) void prepare_mfma_bwd_kernel(
+// The backward's prepare for bf16 storage: per block, into `packed`
+// (4*64*D + 4*D*D bf16, each matrix a hi matrix then its lo matrix): Khat
+// rows j (columns e), Khat^T rows a (columns j), P_n rows a (columns b), P_n^T
+// rows a (columns b), columns in mfma_perm order; Qhat unscaled in rows of
+// length L; M = (I + diag(beta) strict_upper(W W^T))^{-1} in fp32.
+template <int D>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prepare_mfma_bwd_kernel(
     int64_t L, int Nb, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ w, const float* __restrict__ beta, __bf16* __restrict__ packed,
     float* __restrict__ qhat, float* __restrict__ minv) {
-  constexpr int M2 = 64 * 64;
-  prepare_block<64, true>(L, Nb, 1.f, q, k, w, nullptr, beta, packed, packed + 4 * M2, qhat, nullptr, nullptr,
-                          nullptr, nullptr, nullptr, packed + 2 * M2, packed + 6 * M2, minv);
+  constexpr int CD = 64 * D, DD = D * D;
+  prepare_block<D, true>(L, Nb, 1.f, q, k, w, nullptr, beta, packed, packed + 4 * CD, qhat, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, packed + 2 * CD, packed + 4 * CD + 2 * DD, minv);
 }
 
 template <int D>
@@ -792,12 +791,22 @@ static hipError_t launch_prepare_mfma_t(int64_t BH, int64_t L, float c2, const v
   return hipGetLastError();
 }
 
-hipError_t launch_prepare_mfma_bwd(int64_t BH, int64_t L, const void* q, const void* k, const void* w,
-                                   const float* beta, void* packed, float* qhat, float* minv, hipStream_t stream) {
+hipError_t launch_prepare_mfma_bwd(int64_t BH, int64_t L, int64_t d, const void* q, const void* k,
+                                   const void* w, const float* beta, void* packed, float* qhat, float* minv,
+                                   hipStream_t stream) {
   const int Nb = static_cast<int>((L + kBlk - 1) / kBlk);
-  hipLaunchKernelGGL(prepare_mfma_bwd_kernel, dim3(static_cast<unsigned>(BH * Nb)), dim3(256), 0, stream, L, Nb,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(w), beta, static_cast<__bf16*>(packed), qhat, minv);
+  const dim3 grid(static_cast<unsigned>(BH * Nb));
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kk = static_cast<const uint16_t*>(k);
+  const auto* ww = static_cast<const uint16_t*>(w);
+  auto* pk = static_cast<__bf16*>(packed);
+  if (d == 64) {
+    hipLaunchKernelGGL(prepare_mfma_bwd_kernel<64>, grid, dim3(256), 0, stream, L, Nb, qq, kk, ww, beta, pk, qhat,
+                       minv);
+  } else {
+    hipLaunchKernelGGL(prepare_mfma_bwd_kernel<128>, grid, dim3(256), 0, stream, L, Nb, qq, kk, ww, beta, pk, qhat,
+                       minv);
+  }
   return hipGetLastError();
 }
 
