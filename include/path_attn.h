@@ -167,8 +167,8 @@ size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  *   to nearest even); dbeta [B,H,L] fp32; dlog_forget [B,H,L] fp32, required
  *   when log_forget is given and ignored otherwise.
  * Arithmetic: an fp32 re-run of the prepare stage, then the cross-block and
- *   in-block gradient kernels, all accumulating in fp32.  With PATH_F32, or
- *   d = 128, every product is fp32.  With PATH_BF16 at d = 64 the cross-block
+ *   in-block gradient kernels, all accumulating in fp32.  With PATH_F32 every
+ *   product is fp32.  With PATH_BF16 the block prepare and the cross-block
  *   products take each fp32 operand as bf16 hi + lo (16 significant bits,
  *   fp32's exponent range), well below the bf16 rounding of the outputs.
  *   Some cross-block sums use fp32 atomics, so results may differ in the
@@ -176,8 +176,8 @@ size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  * workspace: >= path_bwd_workspace_bytes(...) bytes, 256-byte aligned.  It
  *   holds, among fp32 intermediates, the transported queries of every
  *   (query block, earlier key block) pair: B*H*Nb*(Nb-1)/2 * d * 64 floats
- *   (plus 64 KB per block of split bf16 key-side operands with PATH_BF16 at
- *   d = 64).
+ *   (plus 8*64*d + 8*d*d bytes per block of split bf16 key-side operands
+ *   with PATH_BF16: 64 KB at d = 64, 192 KB at d = 128).
  */
 int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float scale, const void* q,
                   const void* k, const void* v, const void* w, const float* beta, const float* log_forget,
