@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libpath_attn.so")
 SOURCES = ["api.cpp", "prepare.hip", "fwd_scan.hip", "fwd_scan64.hip", "fwd_scan128.hip", "prepare_mfma.hip",
-           "decode.hip", "bwd.hip", "bwd_block_ut.hip", "bwd_pair16.hip", "project.hip"]
+           "decode.hip", "bwd.hip", "bwd_block_ut.hip", "bwd_pair16.hip", "bwd_block_ut128.hip", "project.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

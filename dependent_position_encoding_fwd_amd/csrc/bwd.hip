@@ -715,11 +715,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                        a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.csum);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  const BwdBlockArgs b{BH, L, a.scale, a.q, a.k, a.v, a.w, a.dout, a.beta, a.ws.cum, a.lse, a.ws.Dv, a.ws.minv,
+                       a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum, a.dq, a.dk, a.dv, a.dw,
+                       a.dbeta, a.ws.dc};
   if constexpr (D == 64) {
-    const BwdBlockArgs b{BH, L, a.scale, a.q, a.k, a.v, a.w, a.dout, a.beta, a.ws.cum, a.lse, a.ws.Dv, a.ws.minv,
-                         a.ws.dqh, a.ws.dkh, a.ws.dP, a.ws.dV, a.ws.rsum, a.ws.csum, a.dq, a.dk, a.dv, a.dw,
-                         a.dbeta, a.ws.dc};
     if ((e = launch_bwd_block_ut(std::is_same_v<T, float> ? 0 : 1, b, stream)) != hipSuccess) return e;
+  } else if constexpr (std::is_same_v<T, bf16_t>) {
+    if ((e = launch_bwd_block_ut128(b, stream)) != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL((bwd_block_kernel<T, D, FOX>), grid, dim3(64 * block_waves<D>()), 0, stream, L, Nb, BH,
                        a.scale, static_cast<const T*>(a.q), static_cast<const T*>(a.k), v, static_cast<const T*>(a.w),

@@ -124,7 +124,7 @@ hipError_t launch_bwd(int dtype, int64_t d, const BwdArgs& a, hipStream_t stream
 // cores (bwd_pair16.hip), from the split operands the matrix-core prepare wrote
 // to ws.packed: the query-major pair kernel, then the key-major one.
 hipError_t launch_bwd_pair16(int64_t d, const BwdArgs& a, hipStream_t stream);
-// The in-block part of the backward at d = 64 in matrix form (bwd_block_ut.hip).
+// The in-block part of the backward in matrix form: d = 64 (bwd_block_ut.hip).
 struct BwdBlockArgs {
   int64_t BH, L;
   float scale;
@@ -134,5 +134,7 @@ struct BwdBlockArgs {
   float *dbeta, *dc;
 };
 hipError_t launch_bwd_block_ut(int dtype, const BwdBlockArgs& a, hipStream_t stream);
+// The same at d = 128 for bf16 storage (bwd_block_ut128.hip).
+hipError_t launch_bwd_block_ut128(const BwdBlockArgs& a, hipStream_t stream);
 
 }  // namespace path

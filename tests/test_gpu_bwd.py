@@ -92,7 +92,8 @@ def test_bwd_f32(L, d, fox):
     _bwd_case(1, 2, L, d, "f32", 0.3, seed=L + d + fox, fox=fox)
 
 
-@pytest.mark.parametrize("L,d,fox", [(200, 64, True), (130, 128, False), (40, 64, False), (128, 64, True)])
+@pytest.mark.parametrize("L,d,fox", [(200, 64, True), (130, 128, False), (40, 64, False), (128, 64, True),
+                                     (40, 128, False), (200, 128, True)])
 def test_bwd_bf16(L, d, fox):
     _bwd_case(1, 2, L, d, "bf16", 0.3, seed=L + d + 7 * fox, fox=fox)
 
@@ -123,12 +124,12 @@ def test_bwd_special_transitions_f32(fox):
     _bwd_case(1, 2, 150, 64, "f32", 0.3, seed=150 + fox, fox=fox, mutate=_special_transitions)
 
 
-@pytest.mark.parametrize("fox", [False, True])
-def test_bwd_special_transitions_bf16(fox):
+@pytest.mark.parametrize("fox,d", [(False, 64), (True, 64), (False, 128), (True, 128)])
+def test_bwd_special_transitions_bf16(fox, d):
     """The same transitions with bf16 storage, through the 16-bit cross-block
-    kernels (d = 64): w is rounded to bf16 after scaling, so the projections
-    are singular only up to that rounding."""
-    _bwd_case(1, 2, 150, 64, "bf16", 0.3, seed=151 + fox, fox=fox, mutate=_special_transitions)
+    kernels and the matrix-form in-block kernels: w is rounded to bf16 after
+    scaling, so the projections are singular only up to that rounding."""
+    _bwd_case(1, 2, 150, d, "bf16", 0.3, seed=151 + fox + (d - 64), fox=fox, mutate=_special_transitions)
 
 
 def test_bwd_long_f32():
