@@ -21,6 +21,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// bf16 rows move in 16-byte pieces, so bf16 tensors must start on 16 bytes.
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
   if (a != 0 && b > kMaxElems / a) return false;
@@ -171,6 +174,8 @@ int fwd_check(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, int precisi
   if (precision != PATH_PREC_ACCURATE && precision != PATH_PREC_AUTO) return PATH_ERR_UNSUPPORTED;
   if ((st = check_shape(B, H, L, d, &a->BH, &a->Nb))) return st;
   if (!q || !k || !v || !w || !beta) return PATH_ERR_NULL;
+  if (dtype == PATH_BF16 && (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(w)))
+    return PATH_ERR_UNSUPPORTED;
   a->lay = fwd_layout(dtype, a->BH, L, d, a->Nb, log_forget != nullptr);
   if (!workspace || workspace_bytes < a->lay.total ||
       (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
@@ -254,6 +259,7 @@ int path_fwd_stage_scan(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, f
                      workspace_bytes, &a);
   if (st) return st;
   if (!o || !lse) return PATH_ERR_NULL;
+  if (dtype == PATH_BF16 && misaligned16(o)) return PATH_ERR_UNSUPPORTED;
   return fwd_scan(a, B, H, L, d, dtype, scale, precision, q, k, v, w, beta, log_forget, o, lse,
                   workspace, stream);
 }
@@ -267,6 +273,7 @@ int path_attn_fwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
                      workspace_bytes, &a);
   if (st) return st;
   if (!o || !lse) return PATH_ERR_NULL;
+  if (dtype == PATH_BF16 && misaligned16(o)) return PATH_ERR_UNSUPPORTED;
   if ((st = fwd_prepare(a, B, H, L, d, dtype, scale, q, k, v, w, beta, log_forget, workspace, stream)))
     return st;
   return fwd_scan(a, B, H, L, d, dtype, scale, precision, q, k, v, w, beta, log_forget, o, lse,
@@ -464,6 +471,11 @@ int path_attn_bwd(int64_t B, int64_t H, int64_t L, int64_t d, int dtype, float s
   if (!q || !k || !v || !w || !beta || !o || !lse || !dout || !dq || !dk || !dv || !dw || !dbeta)
     return PATH_ERR_NULL;
   if (log_forget && !dlog_forget) return PATH_ERR_NULL;
+  if (dtype == PATH_BF16) {
+    for (const void* p : {q, k, v, w, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv), static_cast<const void*>(dw)})
+      if (misaligned16(p)) return PATH_ERR_UNSUPPORTED;
+  }
   BwdLayout lay;
   const bool pack16 = dtype == PATH_BF16;
   if (!bwd_layout(BH, L, d, Nb, log_forget != nullptr, pack16, &lay)) return PATH_ERR_SHAPE;
@@ -522,8 +534,7 @@ extern "C" int path_project(int64_t B, int64_t L, int64_t Dm, int64_t H, int64_t
   if (!mul_ok(((T + 127) / 128 + 7) / 8 * 8, ncol, &tiles_cols) || tiles_cols > (int64_t(1) << 31) - 1)
     return PATH_ERR_SHAPE;
   if (!x || !Ww || !u || !bias || !w || !beta) return PATH_ERR_NULL;
-  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
-  if (misaligned(x) || misaligned(Ww) || misaligned(u) || misaligned(w)) return PATH_ERR_UNSUPPORTED;
+  if (misaligned16(x) || misaligned16(Ww) || misaligned16(u) || misaligned16(w)) return PATH_ERR_UNSUPPORTED;
   return hip_status(path::launch_project(B, L, Dm, H, d, x, Ww, u, bias, beta_max, w, beta, stream));
 }
 

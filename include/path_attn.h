@@ -42,7 +42,8 @@ typedef enum {
   PATH_OK = 0,
   PATH_ERR_NULL = 1,        /* a required pointer is NULL */
   PATH_ERR_SHAPE = 2,       /* a size is out of range or the sizes overflow */
-  PATH_ERR_UNSUPPORTED = 3, /* d not 64/128, or unknown dtype / precision */
+  PATH_ERR_UNSUPPORTED = 3, /* d not 64/128, unknown dtype / precision, or a
+                               bf16 tensor not 16-byte aligned */
   PATH_ERR_WORKSPACE = 4,   /* workspace NULL, too small or not 256-byte aligned */
   PATH_ERR_CAPACITY = 5,    /* decode: cache_len >= capacity */
   PATH_ERR_HIP = 6,         /* a kernel launch failed (see hipGetLastError) */
@@ -108,6 +109,8 @@ size_t path_fwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  * Inputs: q, k, v, w [B,H,L,d] (dtype); beta [B,H,L]; log_forget [B,H,L] or
  *   NULL; scale multiplies the PaTH term only.  Every input must be finite.
  * Outputs: o [B,H,L,d] (dtype, bf16 rounded to nearest even), lse [B,H,L] fp32.
+ * Alignment: with PATH_BF16, q, k, v, w and o must be 16-byte aligned (rows
+ *   move in 16-byte pieces); PATH_ERR_UNSUPPORTED otherwise, before any launch.
  * workspace: device buffer of at least path_fwd_workspace_bytes(...) bytes,
  *   256-byte aligned; its contents on entry are irrelevant.
  * Range and accuracy.  PATH_F32 accepts any finite inputs with beta >= 0 and
@@ -166,6 +169,8 @@ size_t path_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int 
  * Outputs (caller-allocated): dq, dk, dv, dw [B,H,L,d] in dtype (bf16 rounded
  *   to nearest even); dbeta [B,H,L] fp32; dlog_forget [B,H,L] fp32, required
  *   when log_forget is given and ignored otherwise.
+ * Alignment: with PATH_BF16, q, k, v, w, o, dout, dq, dk, dv and dw must be
+ *   16-byte aligned; PATH_ERR_UNSUPPORTED otherwise, before any launch.
  * Arithmetic: an fp32 re-run of the prepare stage, then the cross-block and
  *   in-block gradient kernels, all accumulating in fp32.  With PATH_F32 every
  *   product is fp32.  With PATH_BF16 the block prepare and the cross-block

@@ -56,6 +56,30 @@ def test_fwd_validation():
     assert _fwd(ws=None) == WS
     assert _fwd(wsb=16) == WS
     assert _fwd(ws=ctypes.c_void_p(0x1010)) == WS  # not 256-byte aligned
+    odd = ctypes.c_void_p(0x1008)  # 8-byte but not 16-byte aligned
+    assert _fwd(ptr=odd) == UNSUP                  # bf16 rows move in 16-byte pieces
+    assert _fwd(o=odd) == UNSUP
+    assert _fwd(dtype=0, ptr=odd, ws=None) == WS   # fp32 has no such rule: next check fails
+
+
+def _bwd(B=1, H=1, Lq=128, d=64, dtype=1, ptr=FAKE, lf=None, dlf=None, ws=FAKE, wsb=1 << 40, dq=FAKE,
+         dout=FAKE):
+    return pa.lib().path_attn_bwd(B, H, Lq, d, dtype, 1.0, ptr, ptr, ptr, ptr, ptr, lf, ptr, ptr, dout, dq, ptr,
+                                  ptr, ptr, ptr, dlf, ws, wsb, None)
+
+
+def test_bwd_validation():
+    assert _bwd(d=96) == UNSUP
+    assert _bwd(dtype=7) == UNSUP
+    assert _bwd(Lq=0) == SHAPE
+    assert _bwd(ptr=None) == NULL
+    assert _bwd(lf=FAKE) == NULL                   # gates given without their gradient
+    assert _bwd(ws=None) == WS
+    assert _bwd(ws=ctypes.c_void_p(0x1010)) == WS  # not 256-byte aligned
+    odd = ctypes.c_void_p(0x1008)
+    assert _bwd(dq=odd) == UNSUP                   # bf16 tensors start on 16 bytes
+    assert _bwd(dout=odd) == UNSUP
+    assert _bwd(dtype=0, dq=odd, ws=None) == WS    # fp32 has no such rule
 
 
 def test_workspace_sizes():
