@@ -58,8 +58,7 @@ adjoint, the transitions' gradient).  The in-block chains earn no FLOPs.  With
 bf16 storage the cross-block products run on the 16-bit matrix cores
 with every fp32 operand split into bf16 hi + lo (two or three products each,
 fp32 accumulation), the block prepare the same way, and the in-block part on
-the fp32 matrix cores (d = 64) or the vector ALUs (d = 128); with fp32
-storage it computes in fp32 throughout.  `frac_fp32_peak` relates the rate to MI355X's
+the fp32 matrix cores; with fp32 storage it computes in fp32 throughout.  `frac_fp32_peak` relates the rate to MI355X's
 fp32 157.3 TFLOP/s.  `--no-bwd` skips it.
 
 The paged decode step (`path_decode_step_paged`) runs on the same caches
@@ -335,7 +334,7 @@ def bwd_leg(pa, fargs, gates, cf, o, lse, warmup=2, steps=5):
     split16 = q.dtype == torch.bfloat16
     return {"ms": round(ms, 3), "TFLOP_per_s": round(tf, 3), "flops_model": F,
             "arith": ("block prepare and cross-block products as split-bf16 MFMA (computed operands as bf16 hi + lo, "
-                      "fp32 accumulate); in-block part in fp32") if split16 else "fp32 MFMA and vector ALU",
+                      "fp32 accumulate); in-block part on fp32 MFMA") if split16 else "fp32 MFMA and vector ALU",
             "frac_fp32_peak": round(tf / PEAK_F32_TFLOPS, 4),
             "what": "path_attn_bwd on the forward workload (gradients of q, k, v, w, beta"
                     f"{', log forget gates' if gates is not None else ''}), seeded dO, median of {steps}"}
