@@ -10,10 +10,12 @@
 //     Lam^(n) = P_n^T Lam^(n-1) + scale Khat_n^T dS_n   (Lam^(-1) = 0),
 //     dP_n += Lam^(n-1) Qt^(n)^T,  dV_n += p dO,  dKhat_n += scale dS Qt^(n),
 // the last three summed over query blocks; Lam^(m-1) is the gradient reaching
-// Qhat_m.  Two kernels:
-//   bwd_pair16_kernel, one workgroup per query block m:
-//     pass 1, right to left: Qt^(n) for n = m-1 .. 0, into a scratch buffer;
-//     pass 2, left to right: p, dS, the adjoint Lam and dP_n (fp32 atomics);
+// Qhat_m.  Three kernels:
+//   bwd_transport16_kernel, one workgroup per group of kQG query blocks of a
+//     head: right to left, Qt^(n) for n = m-1 .. 0 of every block m of the
+//     group, into a scratch buffer; the group's blocks share each P_n fetch;
+//   bwd_pair16_kernel, one workgroup per query block m: left to right, p, dS,
+//     the adjoint Lam and dP_n (fp32 atomics);
 //   bwd_key16_kernel, one workgroup per key block n: for m = n+1 .. Nb-1,
 //     p and dS again from Qt^(n)_m in the scratch buffer, with dV_n, dKhat_n
 //     and the gates' key sums in registers, stored once.
@@ -168,12 +170,116 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 }  // namespace
 
+// Scratch slot of Qt^(n)_m for the pair (m, n), n < m: the 64 x D fp32 matrix
+// in the accumulator layout of wave w's tile h, query tile t (the query- and
+// key-major kernels read back what the same wave index wrote).
+__device__ __forceinline__ int64_t pair_index(int64_t bh, int Nb, int m, int n) {
+  return bh * (static_cast<int64_t>(Nb) * (Nb - 1) / 2) + static_cast<int64_t>(m) * (m - 1) / 2 + n;
+}
+
+constexpr int kQG = 4;  // query blocks per transport workgroup
+
+template <int D>
+__global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_transport16_kernel(
+    int64_t L, int Nb, int64_t BH, const float* __restrict__ qhat, const __bf16* __restrict__ packed,
+    float* __restrict__ qt_scratch) {
+  using G = Geo<D>;
+  constexpr int RT = G::RT, DK = G::DK, QD = G::QD;
+  // per query block of the group: Qt by query rows, hi then lo (row i, column a at perm32(a)) [W = D]
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kQG * 4 * QD];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l = lane & 15;
+  const int ngroups = (Nb - 1 + kQG - 1) / kQG;                      // groups of query blocks 1 .. Nb-1
+  const int grp = ngroups - 1 - static_cast<int>(blockIdx.x / BH);   // longest first
+  const int64_t bh = blockIdx.x % BH;
+  const int mlo = 1 + kQG * grp;
+  const int mhi = mlo + kQG - 1 < Nb - 1 ? mlo + kQG - 1 : Nb - 1;  // blocks mlo .. mhi
+  const int64_t hb = bh * L;
+  const __bf16* const pk = packed + bh * Nb * G::kBlock + G::kPa;
+  const int64_t lane_off = ((w * RT) * 4 * 64 + lane) * 4;  // this lane's place in a slot (tile h, query tile t added below)
+
+  // qs[q][h][t] holds Qt[i = 16t + l][a = 16(RT w + h) + 4g + r] of block mlo + q
+  f4 qs[kQG][RT][4];
+  SplitRows<D> pa[RT];
+#pragma unroll
+  for (int h = 0; h < RT; ++h) load_rows<D, D>(pk + static_cast<int64_t>(mhi - 1) * G::kBlock, 16 * (RT * w + h) + l, g, pa[h]);
+  for (int n = mhi - 1;; --n) {
+#pragma unroll
+    for (int q = 0; q < kQG; ++q) {
+      const int m = mlo + q;
+      if (m > mhi || n > m - 1) continue;  // block not (yet) on the path
+      if (n == m - 1) {  // Qt^(m-1) = Qhat_m (rows past the sequence end are zero)
+        const int64_t i0 = static_cast<int64_t>(m) * kC;
+        const int valid = static_cast<int>(L - i0 < kC ? L - i0 : kC);
+#pragma unroll
+        for (int h = 0; h < RT; ++h)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int i = 16 * t + l;
+            qs[q][h][t] = i < valid ? *reinterpret_cast<const f4*>(qhat + (hb + i0 + i) * D + 16 * (RT * w + h) + 4 * g)
+                                    : f4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+      float* const slot = qt_scratch + pair_index(bh, Nb, m, n) * QD + lane_off;
+#pragma unroll
+      for (int h = 0; h < RT; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) *reinterpret_cast<f4*>(slot + (h * 4 + t) * 256) = qs[q][h][t];
+    }
+    if (n == 0) break;
+    // Qt^(n-1) = P_n Qt^(n) for every block on the path: stage, then multiply
+#pragma unroll
+    for (int q = 0; q < kQG; ++q) {
+      if (mlo + q > mhi || n > mlo + q - 1) continue;
+      uint8_t* const sh = sm + q * 4 * QD;
+      uint8_t* const sl = sh + 2 * QD;
+#pragma unroll
+      for (int h = 0; h < RT; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const Split4 sp = split4(qs[q][h][t]);
+          wr4<D>(sh, 16 * t + l, tile_pos(RT * w + h, g), sp.hi);
+          wr4<D>(sl, 16 * t + l, tile_pos(RT * w + h, g), sp.lo);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kQG; ++q) {
+      if (mlo + q > mhi || n > mlo + q - 1) continue;
+      const uint8_t* const sh = sm + q * 4 * QD;
+      const uint8_t* const sl = sh + 2 * QD;
+#pragma unroll
+      for (int h = 0; h < RT; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qs[q][h][t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DK; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf8 bhv = rd8<D>(sh, 16 * t + l, 4 * c + g), blv = rd8<D>(sl, 16 * t + l, 4 * c + g);
+#pragma unroll
+          for (int h = 0; h < RT; ++h) {
+            qs[q][h][t] = mma32(pa[h].lo[c], bhv, qs[q][h][t]);
+            qs[q][h][t] = mma32(pa[h].hi[c], blv, qs[q][h][t]);
+            qs[q][h][t] = mma32(pa[h].hi[c], bhv, qs[q][h][t]);
+          }
+        }
+    }
+    if (n >= 2) {
+#pragma unroll
+      for (int h = 0; h < RT; ++h)
+        load_rows<D, D>(pk + static_cast<int64_t>(n - 1) * G::kBlock, 16 * (RT * w + h) + l, g, pa[h]);
+    }
+    __syncthreads();  // the staged tiles are read before the next step overwrites them
+  }
+}
+
 template <int D, bool FOX>
 __global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_pair16_kernel(
     int64_t L, int Nb, int64_t BH, float scale, const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
-    const float* __restrict__ qhat, const __bf16* __restrict__ packed, const float* __restrict__ cum,
-    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ qt_scratch,
-    float* __restrict__ dqh, float* __restrict__ rsum, float* __restrict__ dPacc) {
+    const __bf16* __restrict__ packed, const float* __restrict__ cum, const float* __restrict__ lse,
+    const float* __restrict__ Dv, const float* __restrict__ qt_scratch, float* __restrict__ dqh,
+    float* __restrict__ rsum, float* __restrict__ dPacc) {
   using G = Geo<D>;
   constexpr int RT = G::RT, DK = G::DK, DT = G::DT, QD = G::QD;
   // bytes: QA, QB, LB (hi and lo, 64 x D each), XB (hi and lo, 64 x 64), DOq (64 x D)
@@ -224,79 +330,15 @@ __global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_pair16_kernel(
     c_i[t] = (FOX && ok) ? cum[hb + i0 + i] : 0.f;
   }
 
-  const int64_t npairs = static_cast<int64_t>(Nb) * (Nb - 1) / 2;
-  float* const scr = qt_scratch + (bh * npairs + static_cast<int64_t>(m) * (m - 1) / 2) * QD;
-  // Qt^(n) in the accumulator layout of the transport: each wave keeps its own rows
+  // Qt^(n) as the transport kernel left it, in its accumulator layout: each wave reads its own rows
+  const float* const scr = qt_scratch + pair_index(bh, Nb, m, 0) * QD;
   const auto slot = [&](int n, int h, int t) {
     return scr + static_cast<int64_t>(n) * QD + (((w * RT + h) * 4 + t) * 64 + lane) * 4;
   };
   const __bf16* const pk = packed + bh * Nb * G::kBlock;
   const auto mat = [&](int n, int64_t which) { return pk + static_cast<int64_t>(n) * G::kBlock + which; };
 
-  // ---- pass 1: Qt^(n), n = m-1 .. 0.  qs[h][t] holds Qt[i = 16t + l][a = 16(RT w + h) + 4g + r].
-  f4 qs[RT][4];
-#pragma unroll
-  for (int h = 0; h < RT; ++h)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = 16 * t + l;
-      qs[h][t] = i < valid ? *reinterpret_cast<const f4*>(qhat + (hb + i0 + i) * D + 16 * (RT * w + h) + 4 * g)
-                           : f4{0.f, 0.f, 0.f, 0.f};
-    }
-  {
-    SplitRows<D> pa[RT];
-    if (m >= 2) {
-#pragma unroll
-      for (int h = 0; h < RT; ++h) load_rows<D, D>(mat(m - 1, G::kPa), 16 * (RT * w + h) + l, g, pa[h]);
-    }
-    for (int n = m - 1;; --n) {
-#pragma unroll
-      for (int h = 0; h < RT; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) *reinterpret_cast<f4*>(slot(n, h, t)) = qs[h][t];
-      if (n == 0) break;
-      // two staging buffers in turn (QA's layout in QB's space): one barrier per step
-      uint8_t* const sh = (n & 1) ? QAh : QBh;
-      uint8_t* const sl = (n & 1) ? QAl : QBl;
-#pragma unroll
-      for (int h = 0; h < RT; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const Split4 s = split4(qs[h][t]);
-          wr4<D>(sh, 16 * t + l, tile_pos(RT * w + h, g), s.hi);
-          wr4<D>(sl, 16 * t + l, tile_pos(RT * w + h, g), s.lo);
-        }
-      __syncthreads();
-      f4 acc[RT][4];
-#pragma unroll
-      for (int h = 0; h < RT; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[h][t] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < DK; ++c)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf8 bhv = rd8<D>(sh, 16 * t + l, 4 * c + g), blv = rd8<D>(sl, 16 * t + l, 4 * c + g);
-#pragma unroll
-          for (int h = 0; h < RT; ++h) {
-            acc[h][t] = mma32(pa[h].lo[c], bhv, acc[h][t]);
-            acc[h][t] = mma32(pa[h].hi[c], blv, acc[h][t]);
-            acc[h][t] = mma32(pa[h].hi[c], bhv, acc[h][t]);
-          }
-        }
-      if (n >= 2) {
-#pragma unroll
-        for (int h = 0; h < RT; ++h) load_rows<D, D>(mat(n - 1, G::kPa), 16 * (RT * w + h) + l, g, pa[h]);
-      }
-#pragma unroll
-      for (int h = 0; h < RT; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) qs[h][t] = acc[h][t];
-    }
-  }
-  __syncthreads();  // the last transport's operand reads are done
-
-  // ---- pass 2: key blocks left to right
+  // ---- key blocks left to right
   SplitRows<D> kh, pt[RT];
   SplitRows<kC> kt[RT];
   bf8 vf[DK];
@@ -699,14 +741,21 @@ static hipError_t launch_pair16_t(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(BH * Nb));
   const __bf16* v = static_cast<const __bf16*>(a.v);
   const __bf16* dO = static_cast<const __bf16*>(a.dout);
-  if (a.ws.cum) {
-    hipLaunchKernelGGL((bwd_pair16_kernel<D, true>), grid, dim3(kNT), 0, stream, L, Nb, BH, a.scale, v, dO,
-                       a.ws.qhat, packed, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum, a.ws.dP);
-  } else {
-    hipLaunchKernelGGL((bwd_pair16_kernel<D, false>), grid, dim3(kNT), 0, stream, L, Nb, BH, a.scale, v, dO,
-                       a.ws.qhat, packed, a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum, a.ws.dP);
+  hipError_t e;
+  if (Nb >= 2) {
+    const dim3 tgrid(static_cast<unsigned>(BH * ((Nb - 1 + kQG - 1) / kQG)));
+    hipLaunchKernelGGL((bwd_transport16_kernel<D>), tgrid, dim3(kNT), 0, stream, L, Nb, BH, a.ws.qhat, packed,
+                       a.ws.scratch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
+  if (a.ws.cum) {
+    hipLaunchKernelGGL((bwd_pair16_kernel<D, true>), grid, dim3(kNT), 0, stream, L, Nb, BH, a.scale, v, dO, packed,
+                       a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum, a.ws.dP);
+  } else {
+    hipLaunchKernelGGL((bwd_pair16_kernel<D, false>), grid, dim3(kNT), 0, stream, L, Nb, BH, a.scale, v, dO, packed,
+                       a.ws.cum, a.lse, a.ws.Dv, a.ws.scratch, a.ws.dqh, a.ws.rsum, a.ws.dP);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess || Nb < 2) return e;
   const dim3 kgrid(static_cast<unsigned>(BH * (Nb - 1)));
   if (a.ws.cum) {
