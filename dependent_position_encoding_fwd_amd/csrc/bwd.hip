@@ -11,7 +11,8 @@
 // and inside a block the logit of keys c <= r is scale * k_c . (H_{c+1}...H_r q_r).
 // The pages say nothing about training; this file differentiates that forward.
 //
-// Cross-block part (bwd_pair_kernel, one workgroup per query block m):
+// Cross-block part (bwd_pair_kernel for fp32 storage, one workgroup per query
+// block m; bwd_pair16.hip splits the same two passes over kernels for bf16):
 //   pass 1, right to left: Qt^(n) for n = m-1..0, kept in a scratch buffer;
 //   pass 2, left to right: with dS_ij = p_ij (dO_i . v_j - D_i), D_i = dO_i . o_i,
 //     the adjoint of the transported queries obeys
