@@ -68,7 +68,8 @@ CLASSES = (
 
 # the gated decode kernels (template flag true) form classes of their own
 GATED = (("decode_chunk_fox", "decode_chunk_kernel"), ("decode_merge_fox", "decode_merge_kernel"))
-BWD = ("bwd_pair_kernel", "bwd_pair16_kernel", "bwd_key16_kernel", "bwd_block_kernel", "bwd_block_ut_kernel",
+BWD = ("bwd_pair_kernel", "bwd_transport16_kernel", "bwd_pair16_kernel", "bwd_key16_kernel", "bwd_block_kernel", "bwd_block_ut_kernel",
+       "bwd_block_ut128_kernel",
        "prepare_f32_kernel", "prepare_mfma_bwd_kernel", "bwd_rowdot_kernel",
        "bwd_zero_kernel", "bwd_suffix_kernel")
 
