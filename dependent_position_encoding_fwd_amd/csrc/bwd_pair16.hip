@@ -172,7 +172,10 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 // Scratch slot of Qt^(n)_m for the pair (m, n), n < m: the 64 x D fp32 matrix
 // in the accumulator layout of wave w's tile h, query tile t (the query- and
-// key-major kernels read back what the same wave index wrote).
+// key-major kernels read back what the same wave index wrote).  The scratch
+// is written and read with non-temporal accesses: each slot is read once per
+// kernel, long after it was written, and kept out of the caches it leaves more
+// room there for the key blocks' operands and the dP_n accumulators.
 __device__ __forceinline__ int64_t pair_index(int64_t bh, int Nb, int m, int n) {
   return bh * (static_cast<int64_t>(Nb) * (Nb - 1) / 2) + static_cast<int64_t>(m) * (m - 1) / 2 + n;
 }
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_transport16_kernel(
 #pragma unroll
       for (int h = 0; h < RT; ++h)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) *reinterpret_cast<f4*>(slot + (h * 4 + t) * 256) = qs[q][h][t];
+        for (int t = 0; t < 4; ++t) __builtin_nontemporal_store(qs[q][h][t], reinterpret_cast<f4*>(slot + (h * 4 + t) * 256));
     }
     if (n == 0) break;
     // Qt^(n-1) = P_n Qt^(n) for every block on the path: stage, then multiply
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_pair16_kernel(
   for (int h = 0; h < RT; ++h)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      qn[h][t] = *reinterpret_cast<const f4*>(slot(0, h, t));
+      qn[h][t] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(slot(0, h, t)));
       lam[h][t] = f4{0.f, 0.f, 0.f, 0.f};
     }
   load_key(0);
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(kNT, D == 64 ? 2 : 1) void bwd_pair16_kernel(
 #pragma unroll
       for (int h = 0; h < RT; ++h)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) qn[h][t] = *reinterpret_cast<const f4*>(slot(n + 1, h, t));
+        for (int t = 0; t < 4; ++t) qn[h][t] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(slot(n + 1, h, t)));
     }
     __syncthreads();  // Qt staged, Lam^(n-1) (written at the end of the last step) in LB
 
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(kNT, D == 64 ? (FOX ? 2 : 3) : 1) void bwd_key16_ke
 #pragma unroll
   for (int h = 0; h < RT; ++h)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qn[h][t] = *reinterpret_cast<const f4*>(slot(n + 1, h, t));
+    for (int t = 0; t < 4; ++t) qn[h][t] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(slot(n + 1, h, t)));
   load_do(n + 1, dn);
 
   for (int m = n + 1; m < Nb; ++m) {
@@ -643,7 +646,7 @@ __global__ __launch_bounds__(kNT, D == 64 ? (FOX ? 2 : 3) : 1) void bwd_key16_ke
 #pragma unroll
       for (int h = 0; h < RT; ++h)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) qn[h][t] = *reinterpret_cast<const f4*>(slot(m + 1, h, t));
+        for (int t = 0; t < 4; ++t) qn[h][t] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(slot(m + 1, h, t)));
       load_do(m + 1, dn);
     }
     __syncthreads();  // Qt and dO staged
